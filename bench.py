@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Throughput of the routed-expert W4A16 MoE layer on one MI355X.
+
+One step = one forward pass of the whole layer (route -> group pairs by
+expert -> expert SwiGLU FFN with in-kernel dequantization -> combine) over
+one batch of synthetic tokens, through the C ABI, with inputs and weights
+already resident in HBM.  The headline workload is the OLMoE-shaped decode
+layer (d=2048, E=64, top-8, f=1024, symmetric int4 group-128) at T=16.
+
+Honest HBM numbers: the decode weight set (207.6 MB) fits the 256 MB
+Infinity Cache, so the timed loop rotates over several device copies of the
+packed experts (>= 1 GiB touched between reuses of a copy) and over 16
+distinct token batches.
+
+Prints ONE JSON line (rank 0).  --gpus must be 1: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "MoE-layer tokens/s; decode HBM GB/s on expert bytes; prefill MFMA util %"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only-headline", action="store_true",
+                    help="skip the secondary workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--workloads", default="",
+                    help="comma list of name filters for secondary workloads")
+    return ap.parse_args()
+
+
+class Hip:
+    """hipEvent helpers from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, ev, stream):
+        assert self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) == 0
+
+    def ms(self, a, b):
+        t = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(a),
+                                            ctypes.c_void_p(b)) == 0
+        return t.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def expert_bytes(cfg, planes=None):
+    """Packed bytes of one expert: (gate/up, down) = codes + fp16 scales."""
+    d, f = cfg.d, cfg.f
+    if cfg.fmt == "w4":
+        return 2 * f * d // 2 + 2 * f * (d // 128) * 2, d * f // 2 + d * (f // 128) * 2
+    b = 8 if planes is None else planes
+    return b * 2 * f * d // 8 + 2 * f * (d // 128) * 2, b * d * f // 8 + d * (f // 128) * 2
+
+
+class Workload:
+    def __init__(self, name, cid, T, steps, path=0):
+        self.name, self.cid, self.T, self.steps, self.path = name, cid, T, steps, path
+
+
+def run_workload(wl, warmup, hip, torch, np, synth, moe):
+    cfg = synth.CONFIGS[wl.cid]
+    T, d, E, k, f = wl.T, cfg.d, cfg.E, cfg.k, cfg.f
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    bp = cfg.fmt == "bp8"
+    quant = moe.moe_quantize_bitplane8 if bp else moe.moe_quantize_w4
+
+    # packed experts (offline, untimed), then copies for cache-cold rotation
+    w = torch.empty((E, 2 * f, d), dtype=torch.float32, device=dev)
+    synth.dev_fill_weight(cfg, synth.T_W_GATE_UP, w.data_ptr(), stream)
+    gu = quant(w)
+    del w
+    w = torch.empty((E, d, f), dtype=torch.float32, device=dev)
+    synth.dev_fill_weight(cfg, synth.T_W_DOWN, w.data_ptr(), stream)
+    dn = quant(w)
+    del w
+    set_bytes = sum(t.numel() * t.element_size() for t in (*gu, *dn))
+    ncopies = max(1, min(8, math.ceil(1.1 * 2**30 / set_bytes)))
+    copies = [(gu[0], gu[1], dn[0], dn[1])]
+    for _ in range(ncopies - 1):
+        copies.append(tuple(t.clone() for t in copies[0]))
+
+    wr = torch.empty((E, d), dtype=torch.int16, device=dev)
+    synth.dev_fill_router(cfg, wr.data_ptr(), stream)
+    bias = None
+    if cfg.bias_sigma is not None:
+        bias = torch.empty((E,), dtype=torch.float32, device=dev)
+        synth.dev_fill_bias(cfg, bias.data_ptr(), stream)
+    nx = 16 if T <= 64 else 2
+    xs = []
+    for i in range(nx):
+        x = torch.empty((T, d), dtype=torch.int16, device=dev)
+        synth.dev_fill_x(cfg, x.data_ptr(), T, stream, step=i)
+        xs.append(x)
+    fmt = moe.MOE_FMT_BITPLANE8 if bp else moe.MOE_FMT_W4_SYM
+    bmode = moe.MOE_BITS_RANK_RULE if (bp and cfg.bits_rule == "rank") else moe.MOE_BITS_NONE
+    layer = moe.MoeLayer(wr, bias, k, f, *copies[0], fmt, bmode, None)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+
+    # algorithmic work of each x batch (routing is re-run here, untimed)
+    gu_bytes, dn_bytes, active = [], [], []
+    for x in xs:
+        layer.forward(x, out=out, path=wl.path)
+        torch.cuda.synchronize()
+        idx = layer.topk_idx.cpu().numpy()
+        experts = np.unique(idx)
+        active.append(len(experts))
+        if bp:
+            rank_bits = np.array([8, 4, 4, 4, 2, 2, 2, 2])[:k]
+            gsum = dsum = 0
+            for e in experts:
+                mb = int(rank_bits[np.nonzero(idx == e)[1]].max())
+                g1, d1 = expert_bytes(cfg, mb)
+                gsum, dsum = gsum + g1, dsum + d1
+            gu_bytes.append(gsum)
+            dn_bytes.append(dsum)
+        else:
+            g1, d1 = expert_bytes(cfg)
+            gu_bytes.append(len(experts) * g1)
+            dn_bytes.append(len(experts) * d1)
+    P = T * k
+    flops_gu, flops_dn = 4.0 * P * d * f, 2.0 * P * d * f
+
+    steps = wl.steps
+    ev = [[hip.event() for _ in range(4)] for _ in range(steps)]
+    for i in range(warmup):
+        layer.forward(xs[i % nx], out=out, path=wl.path, weights=copies[i % ncopies])
+    torch.cuda.synchronize()
+    t_start, t_end = hip.event(), hip.event()
+    hip.record(t_start, stream)
+    wall0 = time.perf_counter()
+    for i in range(steps):
+        moe.moe_set_ffn_events(*ev[i])
+        layer.forward(xs[i % nx], out=out, path=wl.path, weights=copies[i % ncopies])
+    hip.record(t_end, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = hip.ms(t_start, t_end)
+    gu_ms = [hip.ms(e[0], e[1]) for e in ev]
+    dn_ms = [hip.ms(e[2], e[3]) for e in ev]
+    gu_b = sum(gu_bytes[i % nx] for i in range(steps))
+    dn_b = sum(dn_bytes[i % nx] for i in range(steps))
+    for e in ev:
+        for h in e:
+            hip.destroy(h)
+    hip.destroy(t_start)
+    hip.destroy(t_end)
+
+    ms_step = total_ms / steps
+    rec = {
+        "workload": wl.name, "config": cfg.name, "T": T, "d": d, "E": E, "k": k,
+        "f": f, "format": "bitplane8-rank" if bp else "int4-g128",
+        "ms_per_step": round(ms_step, 5), "tokens_per_s": round(T / (ms_step / 1e3), 1),
+        "wall_s": round(wall, 3), "weight_copies": ncopies,
+        "active_experts_avg": round(float(np.mean(active)), 2),
+        "gateup_us": round(1e3 * float(np.mean(gu_ms)), 3),
+        "down_us": round(1e3 * float(np.mean(dn_ms)), 3),
+        "gateup_bytes_avg": int(gu_b / steps), "down_bytes_avg": int(dn_b / steps),
+        "gateup_GBps": round(gu_b / (sum(gu_ms) * 1e-3) / 1e9, 1),
+        "down_GBps": round(dn_b / (sum(dn_ms) * 1e-3) / 1e9, 1),
+        "ffn_GBps": round((gu_b + dn_b) / ((sum(gu_ms) + sum(dn_ms)) * 1e-3) / 1e9, 1),
+        "gateup_TFLOPs": round(flops_gu * steps / (sum(gu_ms) * 1e-3) / 1e12, 2),
+        "down_TFLOPs": round(flops_dn * steps / (sum(dn_ms) * 1e-3) / 1e12, 2),
+    }
+    rec["ffn_mfma_util_pct"] = round(100 * (flops_gu + flops_dn) * steps /
+                                     ((sum(gu_ms) + sum(dn_ms)) * 1e-3) / 1e12 /
+                                     MFMA_BF16_PEAK_TFS, 2)
+    del copies, layer, xs
+    torch.cuda.empty_cache()
+    return rec
+
+
+def cpu_baseline(target_s, np, synth, oracle):
+    """The oracle as it stands on the host cores: whole layer for batches of
+    the headline workload until about target_s seconds of work."""
+    cfg = synth.CONFIGS[1]
+    T = 16
+    wr = synth.host_router(cfg)
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache[e] = (oracle.quantize_w4(synth.host_expert(cfg, synth.T_W_GATE_UP, e)),
+                        oracle.quantize_w4(synth.host_expert(cfg, synth.T_W_DOWN, e)))
+        return cache[e]
+
+    xs = [synth.host_x(cfg, T, step=i) for i in range(64)]
+    # experts are packed offline on the GPU side too: quantize outside timing
+    for x in xs[:4]:
+        _, idx, _ = oracle.route(x, wr, None, cfg.k)
+        for e in np.unique(idx):
+            expert(int(e))
+    done, t0 = 0, time.perf_counter()
+    while True:
+        x = xs[done % 4]
+        oracle.layer(x, wr, None, cfg.k, cfg.f, expert)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or done >= 64:
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return {"value": round(done * T / el, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} batches of the headline workload (olmoe-decode-w4, "
+                      f"T={T} tokens = {T * cfg.k} pairs each): the whole layer in "
+                      f"the fp64 oracle (route, grouping, per-expert dequantization "
+                      f"and SwiGLU FFN, combine) with OpenMP over rows; expert "
+                      f"quantization excluded; {el:.1f} s"}
+
+
+def load_traffic(np):
+    """HBM traffic of the dominant kernel from the committed rocprofv3 counter
+    summary, valid only while the kernel source is unchanged."""
+    import hashlib
+    p = os.path.join(ROOT, "profiles", "traffic_gateup_decode.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    src = os.path.join(ROOT, "quantized_mixture_experts_fp32_amd", "csrc", "ffn.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if rec.get("ffn_source_sha256_16") != h:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this layer benchmark runs on exactly one GPU (--gpus 1); "
+              "no multi-GPU path is built.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    import quantized_mixture_experts_fp32_amd as moe
+
+    moe.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    hip = Hip()
+    head = Workload("olmoe-decode-w4 T=16", 1, 16, args.steps)
+    secondary = [
+        Workload("olmoe-decode-w4 T=1", 1, 1, args.steps),
+        Workload("olmoe-decode-w4 T=4", 1, 4, args.steps),
+        Workload("olmoe-decode-w4 T=8", 1, 8, args.steps),
+        Workload("olmoe-bitplane-decode T=16", 3, 16, args.steps),
+        Workload("e256-w4 T=1", 4, 1, args.steps),
+        Workload("e256-w4 T=64", 4, 64, args.steps),
+        Workload("olmoe-prefill-w4 T=4096", 2, 4096, max(5, args.steps // 10)),
+        Workload("e256-w4 T=8192", 4, 8192, max(3, args.steps // 40)),
+    ]
+    if args.workloads:
+        keys = args.workloads.split(",")
+        secondary = [w for w in secondary if any(k in w.name for k in keys)]
+    head_rec = run_workload(head, args.warmup, hip, torch, np, synth, moe)
+    others = []
+    if not args.only_headline:
+        for wl in secondary:
+            others.append(run_workload(wl, max(2, args.warmup // 4), hip, torch, np,
+                                       synth, moe))
+    base = None
+    if not args.no_cpu_baseline:
+        import oracle
+        base = cpu_baseline(args.cpu_seconds, np, synth, oracle)
+
+    achieved = head_rec["gateup_GBps"]
+    line = {
+        "metric": METRIC, "value": head_rec["tokens_per_s"], "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head_rec["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "olmoe-decode-w4: one MoE layer, d=2048, E=64, top-8, "
+                               "f=1024, SwiGLU, symmetric int4 group-128 experts, "
+                               "T=16 tokens per step",
+                   "T": 16, "d": 2048, "E": 64, "k": 8, "f": 1024,
+                   "weights": "int4-g128 codes + fp16 scales",
+                   "weight_copies_rotated": head_rec["weight_copies"],
+                   "token_batches_rotated": 16},
+        "roofline": {"bound": "hbm", "kernel": "expert gate/up (moe_expert_ffn_wq)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(np),
+                     "algorithmic_bytes_per_launch": head_rec["gateup_bytes_avg"],
+                     "avg_launch_us": head_rec["gateup_us"]},
+        "cpu_baseline": base,
+        "headline_detail": head_rec,
+        "workloads": others,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,232 @@
+/*
+ * moe_wq.h -- C ABI of the MI355X (gfx950) routed-expert MoE FFN with
+ * low-bit weight-only quantized experts (W4A16 and bitplane prefixes).
+ *
+ * One forward pass of the layer is four calls on one HIP stream:
+ *
+ *   moe_route          x, router weights -> top-k expert ids and weights
+ *   moe_permute        top-k ids -> pairs grouped by expert
+ *   moe_expert_ffn_wq  grouped pairs -> per-pair SwiGLU expert outputs
+ *   moe_combine        per-pair outputs -> layer output
+ *
+ * plus the offline quantizers moe_quantize_w4 / moe_quantize_bitplane8.
+ *
+ * The pages this follows:
+ *  [ExactMoE] "Every Expert Counts: ExactMoE for Memory-Efficient W4A16
+ *    Inference", Abstract: symmetric group-128 four-bit quantization of the
+ *    routed experts only; router in BF16; unchanged top-k routing; all
+ *    selected experts executed (none pruned or substituted) by fused grouped
+ *    MoE kernels.
+ *  [PagedMoE] "PagedMoE: Cross-Precision Expert Caching for Token-Level
+ *    Dynamic Precision in SSD-Resident MoE Inference", abstract: each expert
+ *    stored once as bitplanes whose lower precisions are prefixes of higher
+ *    ones; 1-8-bit prefixes executed directly, chosen per token from the
+ *    routing.
+ *  [MatMoE] "MatMoE: Matryoshka Mixture-of-Experts with Dynamic
+ *    Mixed-Precision Quantization for Efficient Inference", abstract:
+ *    floor-and-compensation dequantization of the nested representation;
+ *    per-expert bit-width from routing scores.
+ *
+ * Conventions (all calls):
+ *  - Every pointer is a DEVICE pointer (hipMalloc / torch CUDA memory) unless
+ *    stated otherwise.  The caller owns all memory; the library allocates
+ *    nothing.  Scratch memory is a caller-provided workspace whose size the
+ *    *_ws_bytes queries return.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work; they never synchronise the host.  Kernel faults surface at
+ *    the caller's next synchronisation.
+ *  - Arguments are validated before anything is enqueued: a call that
+ *    returns an error has written nothing.  T == 0 is a valid no-op.
+ *  - Integer results (top-k ids, grouping, codes, scales) are deterministic
+ *    and bit-identical to the plain CPU definition; floating-point results
+ *    are deterministic run to run (no floating-point atomics).
+ *  - Calls are re-entrant; concurrent calls must use distinct outputs and
+ *    workspaces.
+ */
+#ifndef MOE_WQ_H
+#define MOE_WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG 1 /* null / misaligned pointer, bad size      */
+#define MOE_ERR_UNSUPPORTED 2 /* valid but outside the supported shapes   */
+#define MOE_ERR_WORKSPACE 3   /* workspace missing or too small           */
+#define MOE_ERR_HIP 4         /* the HIP runtime rejected a launch        */
+
+/* ---- enumerations ---------------------------------------------------- */
+#define MOE_FMT_W4_SYM 0    /* int4 codes, two per byte, fp16 group scales */
+#define MOE_FMT_BITPLANE8 1 /* 8 bitplanes of an 8-bit offset code         */
+
+#define MOE_BITS_NONE 0       /* int4 format: no bit-width argument         */
+#define MOE_BITS_PER_PAIR 1   /* bits[T*k], pair p = t*k + j                */
+#define MOE_BITS_PER_EXPERT 2 /* bits[E]                                    */
+#define MOE_BITS_RANK_RULE 3  /* rank 1 -> 8, ranks 2-4 -> 4, 5-8 -> 2; k=8 */
+
+#define MOE_OUT_BF16 0 /* layer output as bf16 (round to nearest even)     */
+#define MOE_OUT_F32 1  /* layer output as fp32 (same sum, before rounding)  */
+
+#define MOE_PATH_AUTO 0    /* pick the FFN kernels from T*k and E          */
+#define MOE_PATH_DECODE 1  /* weight-streaming kernels (small batches)     */
+#define MOE_PATH_PREFILL 2 /* LDS-tiled grouped MFMA kernels               */
+
+/* ---- limits ---------------------------------------------------------- */
+#define MOE_GROUP 128     /* quantization group along the input dimension */
+#define MOE_MAX_EXPERTS 512
+#define MOE_MAX_TOPK 16
+/* d and f must be multiples of 128; T*k must be below 2^31. */
+
+/* Human-readable name of a status code. */
+const char *moe_status_str(int status);
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+/* ---------------------------------------------------------------------
+ * moe_route -- router logits, softmax, top-k, renormalised weights.
+ * [ExactMoE] Abstract: the router stays BF16 and the top-k procedure is
+ * unchanged.  Definition:
+ *   logit[t][e] = sum_i x[t][i] * wr[e][i] in fp32, in a FIXED order: 16
+ *     partial sums, partial l adding elements i = 128c + 8l + r for c = 0,1,..
+ *     and r = 0..7 in that order; partials combined as acc_l += acc_(l^o) for
+ *     o = 8,4,2,1; then + bias[e] (one fp32 add; no add term if bias NULL
+ *     other than +0).  bf16*bf16 products are exact in fp32, so the logits
+ *     are bit-identical to the CPU definition.
+ *   topk_idx[t][0..k-1]: the k experts with the largest logits, larger
+ *     first, equal logits toward the lower index (= order of the softmax
+ *     scores).
+ *   topk_w[t][j] = softmax(logit[t])[idx_j] / sum_j softmax(logit[t])[idx_j]
+ *     (fp32; computed as the softmax over the k selected logits).
+ * Arguments:
+ *   x      bf16 [T][d] row-major, 16-byte aligned.
+ *   wr     bf16 [E][d] (router matrix stored expert-major), 16-byte aligned.
+ *   bias   fp32 [E] logit bias, or NULL.
+ *   topk_idx int32 [T][k]; topk_w fp32 [T][k]  (outputs).
+ * Requires d % 128 == 0, 1 <= k <= min(E, 16), E <= 512.
+ * ------------------------------------------------------------------- */
+int moe_route(const void *x_bf16, const void *wr_bf16, const float *bias,
+              int T, int d, int E, int k, int32_t *topk_idx, float *topk_w,
+              void *stream);
+
+/* ---------------------------------------------------------------------
+ * moe_permute -- group the P = T*k token-expert pairs by expert.
+ * [ExactMoE] Abstract: fused grouped execution of all selected experts.
+ * Deterministic counting sort: pair p = t*k + j; expert_offsets[e] =
+ * number of pairs with expert < e (so expert_offsets[E] = P); within an
+ * expert, pairs keep ascending p.  sorted_pair[slot] = p and pair_pos[p] =
+ * slot (inverse maps).
+ * Arguments:
+ *   topk_idx int32 [T][k] with values in [0, E).  Out-of-range ids make the
+ *     kernels skip the pair (results then undefined; not checked on host).
+ *   expert_offsets int32 [E+1]; sorted_pair, pair_pos int32 [T*k] (outputs).
+ *   ws / ws_bytes: workspace of at least moe_permute_ws_bytes(T, k, E).
+ * ------------------------------------------------------------------- */
+size_t moe_permute_ws_bytes(int T, int k, int E);
+int moe_permute(const int32_t *topk_idx, int T, int k, int E,
+                int32_t *expert_offsets, int32_t *sorted_pair,
+                int32_t *pair_pos, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------
+ * moe_expert_ffn_wq -- SwiGLU FFN of every grouped pair with quantized,
+ * in-kernel dequantized expert weights.
+ * [ExactMoE] Abstract (W4A16, grouped kernels); [PagedMoE] abstract
+ * (bitplane prefixes executed directly); [MatMoE] abstract (floor and
+ * compensation).  For the pair in slot r (token t = sorted_pair[r] / k,
+ * expert e):
+ *   g = Wg' x_t, u = Wu' x_t   (fp32 sums over d)
+ *   h = bf16_rne(silu(g) * u),  silu(g) = g / (1 + exp(-g))     ("A16")
+ *   y_pairs[r] = Wd' h          (fp32 sums over f)
+ * with dequantized weights W' = s * q (int4) or W' = s * v_b(u) (bitplane,
+ * b = the pair's bit-width): v_b = (u with its 8-b low bits cleared)
+ * + 2^(7-b) - 128 for b < 8, and u - 128 for b = 8.  Only the top max_b(e)
+ * planes of expert e are read, where max_b(e) is the largest b among its
+ * pairs.  Dequantized weights are never rounded: integer codes enter the
+ * bf16 MFMA exactly and the fp16 scale multiplies each 128-group partial sum
+ * in fp32.
+ * Weight layouts (K = input dimension, contiguous; groups of 128 along K):
+ *   MOE_FMT_W4_SYM:
+ *     gate_up_codes u8 [E][2f][d/2]: rows 0..f-1 gate, f..2f-1 up; byte j of
+ *       a row holds element 2j in the low nibble and 2j+1 in the high nibble,
+ *       two's complement in [-7, 7].
+ *     gate_up_scales fp16 [E][2f][d/128];  down_codes u8 [E][d][f/2];
+ *     down_scales fp16 [E][d][f/128].
+ *   MOE_FMT_BITPLANE8 (u = 8-bit offset code, w ~ s * (u - 128)):
+ *     gate_up_codes u8 [E][8][2f][d/8]: plane slab p holds bit 7-p of u
+ *       (most significant first: the top b planes are slabs 0..b-1); bit i
+ *       of byte (n, j) belongs to element 8j + i.
+ *     down_codes u8 [E][8][d][f/8]; scales as for int4.
+ * Bit-widths (bitplane only): bits_mode MOE_BITS_PER_PAIR (bits u8 [T*k],
+ *   indexed by pair p), MOE_BITS_PER_EXPERT (bits u8 [E]) or
+ *   MOE_BITS_RANK_RULE (bits NULL; requires k == 8); values in [1, 8].
+ *   The int4 format takes MOE_BITS_NONE and bits NULL.
+ * Other arguments:
+ *   x bf16 [T][d]; expert_offsets, sorted_pair as from moe_permute.
+ *   y_pairs fp32 [T*k][d] in grouped (slot) order (output).
+ *   ws / ws_bytes: at least moe_ffn_ws_bytes(T, k, E, d, f, format).
+ *   path_hint: MOE_PATH_AUTO / _DECODE / _PREFILL (all give results within
+ *     the same tolerance of the CPU definition).
+ * Alignment: x, codes and y_pairs 16-byte aligned; scales 4-byte aligned.
+ * Requires d % 128 == 0, f % 128 == 0, E <= 512, 1 <= k <= 16.
+ * ------------------------------------------------------------------- */
+size_t moe_ffn_ws_bytes(int T, int k, int E, int d, int f, int format);
+int moe_expert_ffn_wq(const void *x_bf16, const int32_t *expert_offsets,
+                      const int32_t *sorted_pair, int T, int k, int E, int d,
+                      int f, int format, int group_size,
+                      const uint8_t *gate_up_codes,
+                      const uint16_t *gate_up_scales_f16,
+                      const uint8_t *down_codes,
+                      const uint16_t *down_scales_f16, const uint8_t *bits,
+                      int bits_mode, float *y_pairs, void *ws,
+                      size_t ws_bytes, int path_hint, void *stream);
+
+/* ---------------------------------------------------------------------
+ * moe_combine -- weighted sum of each token's k expert outputs.
+ * [ExactMoE] Abstract: every selected expert contributes.
+ *   o[t][m] = sum_{j<k} topk_w[t][j] * y_pairs[pair_pos[t*k+j]][m]
+ * summed in rank order in fp32 from +0; out = o (MOE_OUT_F32) or
+ * bf16_rne(o) (MOE_OUT_BF16).  out is [T][d], 16-byte aligned.
+ * ------------------------------------------------------------------- */
+int moe_combine(const float *y_pairs, const int32_t *pair_pos,
+                const float *topk_w, int T, int k, int d, void *out,
+                int out_dtype, void *stream);
+
+/* ---------------------------------------------------------------------
+ * moe_set_ffn_events -- optional timing instrumentation (no page defines
+ * it; it serves throughput measurement).  Arms, for the NEXT
+ * moe_expert_ffn_wq call made by the calling thread only, four hipEvent_t
+ * handles (any may be NULL) that the call records on its stream
+ * immediately before and after its gate/up kernel and its down kernel.
+ * The events are created and owned by the caller.  Returns MOE_OK.
+ * ------------------------------------------------------------------- */
+int moe_set_ffn_events(void *gateup_begin, void *gateup_end,
+                       void *down_begin, void *down_end);
+
+/* ---------------------------------------------------------------------
+ * Offline quantizers (untimed packing of fp32 expert weights on the GPU).
+ * w is fp32 [E][N][K] (K = input dimension); groups of 128 along K.
+ * moe_quantize_w4 ([ExactMoE] Abstract, symmetric group-128 4-bit):
+ *   s = fp16_rne(max|w| / 7) (exact quotient), q = clamp(rne(w / s), -7, 7),
+ *   q = 0 when s == 0.  codes u8 [E][N][K/2] (nibble order as above),
+ *   scales fp16 [E][N][K/128].
+ * moe_quantize_bitplane8 ([PagedMoE] abstract, bitplane prefixes):
+ *   s = fp16_rne(max|w| / 127), u = clamp(rne(w / s) + 128, 0, 255), u = 128
+ *   when s == 0.  planes u8 [E][8][N][K/8] (layout as above), scales fp16
+ *   [E][N][K/128].
+ * Codes and scales are bit-identical to the CPU definition.  Weights with
+ * max|w| above 7 * 65504 (fp16 overflow of the scale) are unsupported.
+ * ------------------------------------------------------------------- */
+int moe_quantize_w4(const float *w, int E, int N, int K, int group_size,
+                    uint8_t *codes, uint16_t *scales_f16, void *stream);
+int moe_quantize_bitplane8(const float *w, int E, int N, int K,
+                           int group_size, uint8_t *planes,
+                           uint16_t *scales_f16, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_WQ_H */

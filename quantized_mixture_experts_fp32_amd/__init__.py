@@ -1,0 +1,258 @@
+"""MI355X (gfx950) routed-expert MoE FFN with low-bit weight-only experts.
+
+Thin Python binding of the C ABI in `include/moe_wq.h` (libmoe_wq.so).  The
+functions below only marshal torch tensors into pointers and sizes; every
+step of the layer runs in the library's HIP kernels.  PyTorch provides
+device memory and the current HIP stream.  There is no CPU fallback: the
+library must be built (`build.build()`) and a GPU present, or calls raise.
+
+Layer = moe_route -> moe_permute -> moe_expert_ffn_wq -> moe_combine.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_wq.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_FMT_W4_SYM, MOE_FMT_BITPLANE8 = 0, 1
+MOE_BITS_NONE, MOE_BITS_PER_PAIR, MOE_BITS_PER_EXPERT, MOE_BITS_RANK_RULE = 0, 1, 2, 3
+MOE_OUT_BF16, MOE_OUT_F32 = 0, 1
+MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
+MOE_GROUP = 128
+
+# Every symbol the header declares (checked by the CPU tests).
+EXPORTS = ("moe_status_str", "moe_last_error", "moe_route", "moe_permute_ws_bytes",
+           "moe_permute", "moe_ffn_ws_bytes", "moe_expert_ffn_wq", "moe_combine",
+           "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        super().__init__(f"{fn} failed: {status_str(status)} ({detail})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library():
+    """Load libmoe_wq.so; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} not built: run "
+                           "quantized_mixture_experts_fp32_amd.build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, vp, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    lib.moe_status_str.argtypes, lib.moe_status_str.restype = [i32], ctypes.c_char_p
+    lib.moe_last_error.argtypes, lib.moe_last_error.restype = [], ctypes.c_char_p
+    lib.moe_route.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.moe_permute_ws_bytes.argtypes, lib.moe_permute_ws_bytes.restype = [i32, i32, i32], sz
+    lib.moe_permute.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.moe_ffn_ws_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.moe_ffn_ws_bytes.restype = sz
+    lib.moe_expert_ffn_wq.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                      vp, vp, vp, vp, vp, i32, vp, vp, sz, i32, vp]
+    lib.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, vp]
+    lib.moe_quantize_w4.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.moe_quantize_bitplane8.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.moe_set_ffn_events.argtypes = [vp, vp, vp, vp]
+    for name in ("moe_route", "moe_permute", "moe_expert_ffn_wq", "moe_combine",
+                 "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events"):
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().moe_status_str(int(status)).decode()
+
+
+def _check(fn, rc):
+    if rc != MOE_OK:
+        raise MoeError(fn, rc, load_library().moe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _empty(shape, dtype, like):
+    import torch
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# ----------------------------------------------------------------- the ABI
+def moe_route(x, wr, bias, k, topk_idx=None, topk_w=None, stream=None):
+    """x bf16 [T][d], wr bf16 [E][d], bias fp32 [E] or None -> (idx, w)."""
+    import torch
+    T, d = x.shape
+    E = wr.shape[0]
+    if topk_idx is None:
+        topk_idx = _empty((T, k), torch.int32, x)
+    if topk_w is None:
+        topk_w = _empty((T, k), torch.float32, x)
+    _check("moe_route", load_library().moe_route(
+        _ptr(x), _ptr(wr), _ptr(bias), T, d, E, k, _ptr(topk_idx), _ptr(topk_w),
+        _stream(stream)))
+    return topk_idx, topk_w
+
+
+def moe_permute_ws_bytes(T, k, E):
+    return int(load_library().moe_permute_ws_bytes(T, k, E))
+
+
+def moe_permute(topk_idx, E, ws=None, offsets=None, sorted_pair=None,
+                pair_pos=None, stream=None):
+    """topk_idx int32 [T][k] -> (expert_offsets [E+1], sorted_pair, pair_pos)."""
+    import torch
+    T, k = topk_idx.shape
+    P = T * k
+    if offsets is None:
+        offsets = _empty((E + 1,), torch.int32, topk_idx)
+    if sorted_pair is None:
+        sorted_pair = _empty((P,), torch.int32, topk_idx)
+    if pair_pos is None:
+        pair_pos = _empty((P,), torch.int32, topk_idx)
+    need = moe_permute_ws_bytes(T, k, E)
+    if ws is None:
+        ws = _empty((max(need, 16),), torch.uint8, topk_idx)
+    _check("moe_permute", load_library().moe_permute(
+        _ptr(topk_idx), T, k, E, _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return offsets, sorted_pair, pair_pos
+
+
+def moe_ffn_ws_bytes(T, k, E, d, f, fmt=MOE_FMT_W4_SYM):
+    return int(load_library().moe_ffn_ws_bytes(T, k, E, d, f, fmt))
+
+
+def moe_expert_ffn_wq(x, expert_offsets, sorted_pair, k, f, gate_up_codes,
+                      gate_up_scales, down_codes, down_scales,
+                      fmt=MOE_FMT_W4_SYM, bits=None, bits_mode=MOE_BITS_NONE,
+                      y_pairs=None, ws=None, path=MOE_PATH_AUTO, stream=None):
+    """Per-pair SwiGLU outputs y_pairs fp32 [T*k][d] in grouped order."""
+    import torch
+    T, d = x.shape
+    E = expert_offsets.numel() - 1
+    if y_pairs is None:
+        y_pairs = _empty((T * k, d), torch.float32, x)
+    need = moe_ffn_ws_bytes(T, k, E, d, f, fmt)
+    if ws is None:
+        ws = _empty((max(need, 256),), torch.uint8, x)
+    _check("moe_expert_ffn_wq", load_library().moe_expert_ffn_wq(
+        _ptr(x), _ptr(expert_offsets), _ptr(sorted_pair), T, k, E, d, f, fmt,
+        MOE_GROUP, _ptr(gate_up_codes), _ptr(gate_up_scales), _ptr(down_codes),
+        _ptr(down_scales), _ptr(bits), bits_mode, _ptr(y_pairs), _ptr(ws),
+        ws.numel() * ws.element_size(), path, _stream(stream)))
+    return y_pairs
+
+
+def moe_combine(y_pairs, pair_pos, topk_w, out=None, out_dtype=MOE_OUT_BF16,
+                stream=None):
+    """Layer output [T][d] (bf16 bits in an int16 tensor, or fp32)."""
+    import torch
+    T, k = topk_w.shape
+    d = y_pairs.shape[1]
+    if out is None:
+        out = _empty((T, d), torch.bfloat16 if out_dtype == MOE_OUT_BF16
+                     else torch.float32, y_pairs)
+    _check("moe_combine", load_library().moe_combine(
+        _ptr(y_pairs), _ptr(pair_pos), _ptr(topk_w), T, k, d, _ptr(out), out_dtype,
+        _stream(stream)))
+    return out
+
+
+def moe_quantize_w4(w, codes=None, scales=None, stream=None):
+    """fp32 [E][N][K] -> (codes u8 [E][N][K/2], scales fp16-bits [E][N][K/128])."""
+    import torch
+    E, N, K = w.shape
+    if codes is None:
+        codes = _empty((E, N, K // 2), torch.uint8, w)
+    if scales is None:
+        scales = _empty((E, N, K // 128), torch.int16, w)
+    _check("moe_quantize_w4", load_library().moe_quantize_w4(
+        _ptr(w), E, N, K, MOE_GROUP, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def moe_quantize_bitplane8(w, planes=None, scales=None, stream=None):
+    """fp32 [E][N][K] -> (planes u8 [E][8][N][K/8], scales [E][N][K/128])."""
+    import torch
+    E, N, K = w.shape
+    if planes is None:
+        planes = _empty((E, 8, N, K // 8), torch.uint8, w)
+    if scales is None:
+        scales = _empty((E, N, K // 128), torch.int16, w)
+    _check("moe_quantize_bitplane8", load_library().moe_quantize_bitplane8(
+        _ptr(w), E, N, K, MOE_GROUP, _ptr(planes), _ptr(scales), _stream(stream)))
+    return planes, scales
+
+
+def moe_set_ffn_events(gateup_begin=None, gateup_end=None, down_begin=None,
+                       down_end=None):
+    """Arm raw hipEvent_t handles (ints) for the next moe_expert_ffn_wq call."""
+    def h(e):
+        return None if e is None else ctypes.c_void_p(e)
+    _check("moe_set_ffn_events", load_library().moe_set_ffn_events(
+        h(gateup_begin), h(gateup_end), h(down_begin), h(down_end)))
+
+
+# --------------------------------------------------------- one whole layer
+class MoeLayer:
+    """Resident quantized expert weights plus preallocated buffers for one
+    batch size; `forward(x)` enqueues the four ABI calls on one stream."""
+
+    def __init__(self, wr, bias, k, f, gate_up_codes, gate_up_scales,
+                 down_codes, down_scales, fmt=MOE_FMT_W4_SYM,
+                 bits_mode=MOE_BITS_NONE, bits=None):
+        self.wr, self.bias, self.k, self.f = wr, bias, k, f
+        self.E, self.d = wr.shape
+        self.gu, self.gus, self.dn, self.dns = (gate_up_codes, gate_up_scales,
+                                                down_codes, down_scales)
+        self.fmt, self.bits_mode, self.bits = fmt, bits_mode, bits
+        self._T = None
+
+    def _alloc(self, T, like):
+        import torch
+        E, k, d, f = self.E, self.k, self.d, self.f
+        P = T * k
+        dev = like.device
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        self.sorted_pair = torch.empty((P,), dtype=torch.int32, device=dev)
+        self.pair_pos = torch.empty((P,), dtype=torch.int32, device=dev)
+        self.ws_perm = torch.empty((max(moe_permute_ws_bytes(T, k, E), 16),),
+                                   dtype=torch.uint8, device=dev)
+        self.ws_ffn = torch.empty((max(moe_ffn_ws_bytes(T, k, E, d, f, self.fmt), 256),),
+                                  dtype=torch.uint8, device=dev)
+        self.y_pairs = torch.empty((P, d), dtype=torch.float32, device=dev)
+        self._T = T
+
+    def forward(self, x, out=None, out_dtype=MOE_OUT_BF16, path=MOE_PATH_AUTO,
+                stream=None, weights=None):
+        T = x.shape[0]
+        if self._T != T:
+            self._alloc(T, x)
+        gu, gus, dn, dns = weights if weights is not None else (
+            self.gu, self.gus, self.dn, self.dns)
+        moe_route(x, self.wr, self.bias, self.k, self.topk_idx, self.topk_w, stream)
+        moe_permute(self.topk_idx, self.E, self.ws_perm, self.offsets,
+                    self.sorted_pair, self.pair_pos, stream)
+        moe_expert_ffn_wq(x, self.offsets, self.sorted_pair, self.k, self.f, gu, gus,
+                          dn, dns, self.fmt, self.bits, self.bits_mode,
+                          self.y_pairs, self.ws_ffn, path, stream)
+        return moe_combine(self.y_pairs, self.pair_pos, self.topk_w, out, out_dtype,
+                           stream)

@@ -1,0 +1,229 @@
+// C ABI of the MoE layer library: argument validation (before anything is
+// enqueued), status codes and dispatch to the gfx950 kernel launchers.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/moe_wq.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local hipEvent_t g_ffn_ev[4] = {nullptr, nullptr, nullptr, nullptr};
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int check_dims(int T, int d, int E, int k) {
+  if (T < 0 || d <= 0 || E <= 0 || k <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "negative or zero size (T=%d d=%d E=%d k=%d)",
+                T, d, E, k);
+  if (k > E) return fail(MOE_ERR_INVALID_ARG, "k=%d > E=%d", k, E);
+  if (E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_UNSUPPORTED, "E=%d > %d", E, MOE_MAX_EXPERTS);
+  if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k=%d > %d", k, MOE_MAX_TOPK);
+  if ((long long)T * k >= (1LL << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T*k must be below 2^31");
+  if (d % MOE_GROUP) return fail(MOE_ERR_UNSUPPORTED, "d=%d not a multiple of 128", d);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_route(const void* x_bf16, const void* wr_bf16, const float* bias,
+              int T, int d, int E, int k, int32_t* topk_idx, float* topk_w,
+              void* stream) {
+  int rc = check_dims(T, d, E, k);
+  if (rc) return rc;
+  if (T == 0) return ok();
+  if (!x_bf16 || !wr_bf16 || !topk_idx || !topk_w)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: null pointer");
+  if (!aligned(x_bf16, 16) || !aligned(wr_bf16, 16) || !aligned(topk_idx, 4) ||
+      !aligned(topk_w, 4) || (bias && !aligned(bias, 4)))
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: misaligned pointer");
+  return hip_status(moe::launch_route(x_bf16, wr_bf16, bias, T, d, E, k,
+                                      topk_idx, topk_w, (hipStream_t)stream),
+                    "moe_route");
+}
+
+size_t moe_permute_ws_bytes(int T, int k, int E) {
+  if (T < 0 || k <= 0 || E <= 0) return 0;
+  return moe::permute_ws_bytes(T, k, E);
+}
+
+int moe_permute(const int32_t* topk_idx, int T, int k, int E,
+                int32_t* expert_offsets, int32_t* sorted_pair,
+                int32_t* pair_pos, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(T, MOE_GROUP, E, k);
+  if (rc) return rc;
+  if (!expert_offsets) return fail(MOE_ERR_INVALID_ARG, "moe_permute: null offsets");
+  if (T > 0 && (!topk_idx || !sorted_pair || !pair_pos))
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: null pointer");
+  const size_t need = moe::permute_ws_bytes(T, k, E);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_permute: workspace %zu < %zu bytes",
+                ws ? ws_bytes : (size_t)0, need);
+  if (!aligned(ws, 16) || !aligned(expert_offsets, 4) ||
+      (T > 0 && (!aligned(topk_idx, 4) || !aligned(sorted_pair, 4) ||
+                 !aligned(pair_pos, 4))))
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: misaligned pointer");
+  return hip_status(moe::launch_permute(topk_idx, T, k, E, expert_offsets,
+                                        sorted_pair, pair_pos, ws,
+                                        (hipStream_t)stream),
+                    "moe_permute");
+}
+
+size_t moe_ffn_ws_bytes(int T, int k, int E, int d, int f, int format) {
+  if (T < 0 || k <= 0 || E <= 0 || d <= 0 || f <= 0) return 0;
+  return moe::ffn_ws_bytes(T, k, E, d, f, format);
+}
+
+int moe_expert_ffn_wq(const void* x_bf16, const int32_t* expert_offsets,
+                      const int32_t* sorted_pair, int T, int k, int E, int d,
+                      int f, int format, int group_size,
+                      const uint8_t* gate_up_codes,
+                      const uint16_t* gate_up_scales_f16,
+                      const uint8_t* down_codes,
+                      const uint16_t* down_scales_f16, const uint8_t* bits,
+                      int bits_mode, float* y_pairs, void* ws, size_t ws_bytes,
+                      int path_hint, void* stream) {
+  int rc = check_dims(T, d, E, k);
+  if (rc) return rc;
+  if (f <= 0) return fail(MOE_ERR_INVALID_ARG, "f=%d", f);
+  if (f % MOE_GROUP) return fail(MOE_ERR_UNSUPPORTED, "f=%d not a multiple of 128", f);
+  if (group_size != MOE_GROUP)
+    return fail(MOE_ERR_UNSUPPORTED, "group_size=%d (only 128)", group_size);
+  if (format != MOE_FMT_W4_SYM && format != MOE_FMT_BITPLANE8)
+    return fail(MOE_ERR_INVALID_ARG, "unknown format %d", format);
+  if (path_hint < MOE_PATH_AUTO || path_hint > MOE_PATH_PREFILL)
+    return fail(MOE_ERR_INVALID_ARG, "unknown path_hint %d", path_hint);
+  if (format == MOE_FMT_W4_SYM) {
+    if (bits_mode != MOE_BITS_NONE || bits)
+      return fail(MOE_ERR_INVALID_ARG, "int4 format takes MOE_BITS_NONE and bits NULL");
+  } else {
+    if (bits_mode == MOE_BITS_RANK_RULE) {
+      if (k != 8)
+        return fail(MOE_ERR_UNSUPPORTED, "the rank bit-width rule needs k == 8");
+    } else if (bits_mode == MOE_BITS_PER_PAIR || bits_mode == MOE_BITS_PER_EXPERT) {
+      if (T > 0 && !bits) return fail(MOE_ERR_INVALID_ARG, "bits is NULL");
+    } else {
+      return fail(MOE_ERR_INVALID_ARG, "bitplane format needs a bits mode");
+    }
+  }
+  if (T == 0) return ok();
+  if (!x_bf16 || !expert_offsets || !sorted_pair || !gate_up_codes ||
+      !gate_up_scales_f16 || !down_codes || !down_scales_f16 || !y_pairs)
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_wq: null pointer");
+  if (!aligned(x_bf16, 16) || !aligned(gate_up_codes, 16) ||
+      !aligned(down_codes, 16) || !aligned(y_pairs, 16) ||
+      !aligned(gate_up_scales_f16, 4) || !aligned(down_scales_f16, 4) ||
+      !aligned(expert_offsets, 4) || !aligned(sorted_pair, 4))
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_wq: misaligned pointer");
+  const size_t need = moe::ffn_ws_bytes(T, k, E, d, f, format);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn_wq: workspace %zu < %zu bytes",
+                ws ? ws_bytes : (size_t)0, need);
+  if (!aligned(ws, 256))
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_wq: workspace not 256-byte aligned");
+  const long long P = (long long)T * k;
+  int path = path_hint;
+  if (path == MOE_PATH_AUTO) path = (P <= 8LL * E) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+  moe::FfnArgs a{(const uint16_t*)x_bf16, expert_offsets, sorted_pair, T, k, E,
+                 d, f, format, gate_up_codes, gate_up_scales_f16, down_codes,
+                 down_scales_f16, bits, bits_mode, y_pairs, ws, path,
+                 {g_ffn_ev[0], g_ffn_ev[1], g_ffn_ev[2], g_ffn_ev[3]}};
+  for (auto& ev : g_ffn_ev) ev = nullptr;  // one-shot
+  return hip_status(moe::launch_ffn(a, (hipStream_t)stream), "moe_expert_ffn_wq");
+}
+
+int moe_set_ffn_events(void* gateup_begin, void* gateup_end, void* down_begin,
+                       void* down_end) {
+  g_ffn_ev[0] = (hipEvent_t)gateup_begin;
+  g_ffn_ev[1] = (hipEvent_t)gateup_end;
+  g_ffn_ev[2] = (hipEvent_t)down_begin;
+  g_ffn_ev[3] = (hipEvent_t)down_end;
+  return ok();
+}
+
+int moe_combine(const float* y_pairs, const int32_t* pair_pos,
+                const float* topk_w, int T, int k, int d, void* out,
+                int out_dtype, void* stream) {
+  if (T < 0 || k <= 0 || d <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: bad size");
+  if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k=%d > %d", k, MOE_MAX_TOPK);
+  if (d % 4) return fail(MOE_ERR_UNSUPPORTED, "d must be a multiple of 4");
+  if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32)
+    return fail(MOE_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+  if (T == 0) return ok();
+  if (!y_pairs || !pair_pos || !topk_w || !out)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: null pointer");
+  if (!aligned(y_pairs, 16) || !aligned(out, 16) || !aligned(pair_pos, 4) ||
+      !aligned(topk_w, 4))
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: misaligned pointer");
+  return hip_status(moe::launch_combine(y_pairs, pair_pos, topk_w, T, k, d, out,
+                                        out_dtype == MOE_OUT_F32,
+                                        (hipStream_t)stream),
+                    "moe_combine");
+}
+
+static int quantize_common(const float* w, int E, int N, int K, int group,
+                           uint8_t* codes, uint16_t* scales, int bitplane,
+                           void* stream) {
+  if (E < 0 || N < 0 || K <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "quantize: bad size");
+  if (group != MOE_GROUP) return fail(MOE_ERR_UNSUPPORTED, "group_size=%d", group);
+  if (K % MOE_GROUP) return fail(MOE_ERR_UNSUPPORTED, "K=%d not a multiple of 128", K);
+  if ((long long)E * N == 0) return ok();
+  if (!w || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "quantize: null pointer");
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 2))
+    return fail(MOE_ERR_INVALID_ARG, "quantize: misaligned pointer");
+  return hip_status(moe::launch_quantize(w, E, N, K, bitplane, codes, scales,
+                                         (hipStream_t)stream),
+                    "quantize");
+}
+
+int moe_quantize_w4(const float* w, int E, int N, int K, int group_size,
+                    uint8_t* codes, uint16_t* scales_f16, void* stream) {
+  return quantize_common(w, E, N, K, group_size, codes, scales_f16, 0, stream);
+}
+
+int moe_quantize_bitplane8(const float* w, int E, int N, int K, int group_size,
+                           uint8_t* planes, uint16_t* scales_f16, void* stream) {
+  return quantize_common(w, E, N, K, group_size, planes, scales_f16, 1, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// fp16 bits -> fp32 (exact).
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  uint32_t sign = (h & 0x8000u) << 16;
+  uint32_t ex = (h >> 10) & 0x1Fu, man = h & 0x3FFu;
+  if (ex == 0x1Fu) return __uint_as_float(sign | 0x7F800000u | (man << 13));
+  if (ex == 0) {  // zero or subnormal: man * 2^-24
+    float v = (float)man * 5.9604644775390625e-8f;
+    return __uint_as_float(__float_as_uint(v) | sign);
+  }
+  return __uint_as_float(sign | ((ex + 112u) << 23) | (man << 13));
+}
+
+// fp64 -> fp16 bits, round to nearest even, from the full 53-bit significand
+// (a single rounding of the double value).
+__device__ __forceinline__ uint32_t f64_to_f16_rne(double v) {
+  uint64_t b = (uint64_t)__double_as_longlong(v);
+  uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
+  int ex = (int)((b >> 52) & 0x7FF);
+  uint64_t man = b & ((1ull << 52) - 1);
+  if (ex == 0x7FF) return sign | (man ? 0x7E00u : 0x7C00u);
+  if (ex == 0) return sign;  // fp64 subnormals are far below fp16's range
+  int e = ex - 1023;
+  if (e > 15) return sign | 0x7C00u;
+  if (e < -25) return sign;  // below half the smallest fp16 subnormal
+  uint64_t full = man | (1ull << 52);
+  int shift = (e >= -14) ? 42 : 42 + (-14 - e);  // <= 53
+  uint64_t q = full >> shift;
+  uint64_t rem = full & ((1ull << shift) - 1);
+  uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (q & 1))) ++q;
+  if (e >= -14) {
+    int e16 = e + 15;
+    if (q == (1ull << 11)) {
+      q >>= 1;
+      ++e16;
+    }
+    if (e16 >= 31) return sign | 0x7C00u;
+    return sign | ((uint32_t)e16 << 10) | ((uint32_t)q & 0x3FFu);
+  }
+  return sign | (uint32_t)q;  // subnormal (q == 1024 encodes the min normal)
+}
+
+// Eight two's-complement nibbles (element 2j low, 2j+1 high of byte j) ->
+// eight exact bf16 values, natural element order.
+__device__ __forceinline__ bf16x8 w4_dword_to_bf16x8(uint32_t w) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int q = ((int)(w << (28 - 4 * i))) >> 28;
+    r[i] = (__bf16)(float)q;
+  }
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu_f32(float g) {
+  return g / (1.0f + expf(-g));
+}
+
+}  // namespace moe

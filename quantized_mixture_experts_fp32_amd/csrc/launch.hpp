@@ -1,0 +1,47 @@
+// Host-side launchers of the gfx950 kernels (called by the C ABI in abi.cpp
+// after argument validation).  Each returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route(const void* x, const void* wr, const float* bias,
+                        int T, int d, int E, int k, int32_t* topk_idx,
+                        float* topk_w, hipStream_t s);
+
+size_t permute_ws_bytes(int T, int k, int E);
+hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int E,
+                          int32_t* offsets, int32_t* sorted_pair,
+                          int32_t* pair_pos, void* ws, hipStream_t s);
+
+hipError_t launch_quantize(const float* w, long long E, long long N, int K,
+                           int bitplane, uint8_t* codes, uint16_t* scales,
+                           hipStream_t s);
+
+struct FfnArgs {
+  const uint16_t* x;
+  const int32_t* offsets;
+  const int32_t* sorted_pair;
+  int T, k, E, d, f, format;
+  const uint8_t* gu_codes;
+  const uint16_t* gu_scales;
+  const uint8_t* dn_codes;
+  const uint16_t* dn_scales;
+  const uint8_t* bits;
+  int bits_mode;
+  float* y;
+  void* ws;
+  int path;  // resolved: 1 decode, 2 prefill
+  hipEvent_t ev[4];  // optional: gate/up begin/end, down begin/end
+};
+size_t ffn_ws_bytes(int T, int k, int E, int d, int f, int format);
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+
+hipError_t launch_combine(const float* y, const int32_t* pair_pos,
+                          const float* topk_w, int T, int k, int d, void* out,
+                          int out_f32, hipStream_t s);
+
+}  // namespace moe

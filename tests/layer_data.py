@@ -1,0 +1,124 @@
+"""Shared setup of the GPU parity tests: device-resident layer inputs drawn by
+the seeded generator (synth/), and the oracle's view of the same inputs."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+import quantized_mixture_experts_fp32_amd as moe
+
+DEV = torch.device("cuda:0")
+
+
+def stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def custom_cfg(cid, d, E, k, f, fmt="w4", bias_sigma=None):
+    return synth.LayerConfig(cid, f"custom{cid}", d, E, k, f, (), fmt,
+                             bias_sigma=bias_sigma)
+
+
+class DevLayer:
+    """Device inputs of one layer configuration for a batch of T tokens."""
+
+    def __init__(self, cfg, T, step=0):
+        self.cfg, self.T = cfg, T
+        d, E, f = cfg.d, cfg.E, cfg.f
+        s = stream()
+        self.x = torch.empty((T, d), dtype=torch.int16, device=DEV)
+        if T:
+            synth.dev_fill_x(cfg, self.x.data_ptr(), T, s, step=step)
+        self.wr = torch.empty((E, d), dtype=torch.int16, device=DEV)
+        synth.dev_fill_router(cfg, self.wr.data_ptr(), s)
+        self.bias = None
+        if cfg.bias_sigma is not None:
+            self.bias = torch.empty((E,), dtype=torch.float32, device=DEV)
+            synth.dev_fill_bias(cfg, self.bias.data_ptr(), s)
+        q = moe.moe_quantize_w4 if cfg.fmt == "w4" else moe.moe_quantize_bitplane8
+        w = torch.empty((E, 2 * f, d), dtype=torch.float32, device=DEV)
+        synth.dev_fill_weight(cfg, synth.T_W_GATE_UP, w.data_ptr(), s)
+        self.guc, self.gus = q(w)
+        del w
+        w = torch.empty((E, d, f), dtype=torch.float32, device=DEV)
+        synth.dev_fill_weight(cfg, synth.T_W_DOWN, w.data_ptr(), s)
+        self.dnc, self.dns = q(w)
+        del w
+        torch.cuda.synchronize()
+
+    def layer(self, bits_mode=moe.MOE_BITS_NONE, bits=None):
+        fmt = moe.MOE_FMT_W4_SYM if self.cfg.fmt == "w4" else moe.MOE_FMT_BITPLANE8
+        return moe.MoeLayer(self.wr, self.bias, self.cfg.k, self.cfg.f, self.guc,
+                            self.gus, self.dnc, self.dns, fmt, bits_mode, bits)
+
+    def expert_codes(self, e):
+        return ((self.guc[e].cpu().numpy(), self.gus[e].cpu().numpy().view(np.uint16)),
+                (self.dnc[e].cpu().numpy(), self.dns[e].cpu().numpy().view(np.uint16)))
+
+
+class HostLayer:
+    """The oracle's copy of the same inputs (host generator + oracle quantizer)."""
+
+    def __init__(self, cfg, T, step=0):
+        self.cfg, self.T = cfg, T
+        self.x = synth.host_x(cfg, T, step=step)
+        self.wr = synth.host_router(cfg)
+        self.bias = synth.host_bias(cfg)
+        self._cache = {}
+
+    def expert(self, e):
+        if e not in self._cache:
+            c = self.cfg
+            q = oracle.quantize_w4 if c.fmt == "w4" else oracle.quantize_bp8
+            self._cache[e] = (q(synth.host_expert(c, synth.T_W_GATE_UP, e)),
+                              q(synth.host_expert(c, synth.T_W_DOWN, e)))
+        return self._cache[e]
+
+
+def assert_codes_equal(dev_layer, host_layer, experts):
+    """Packed codes and fp16 scales of the listed experts are bit-identical."""
+    for e in experts:
+        g, h = dev_layer.expert_codes(int(e)), host_layer.expert(int(e))
+        for (dq, ds), (hq, hs) in zip(g, h):
+            assert np.array_equal(dq, hq.reshape(dq.shape)), f"codes of expert {e}"
+            assert np.array_equal(ds, hs.reshape(ds.shape)), f"scales of expert {e}"
+
+
+def errors(a, ref):
+    """(relative L2 error, max abs error / rms(ref)) in fp64."""
+    a = np.asarray(a, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    rel = np.linalg.norm(a - ref) / max(np.linalg.norm(ref), 1e-300)
+    return rel, np.abs(a - ref).max() / max(rms, 1e-300)
+
+
+REL_L2_TOL = 2e-3      # floating-point bar of the layer outputs
+MAX_ABS_TOL = 3e-2     # max |a - ref| <= 3e-2 * rms(ref)
+
+
+def record(line):
+    """Append a measured error line to $MOE_PARITY_LOG (if set)."""
+    import os
+    path = os.environ.get("MOE_PARITY_LOG")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(line + "\n")
+
+
+def assert_close(a, ref, what):
+    rel, mx = errors(a, ref)
+    import os
+    line = f"{os.environ.get('PYTEST_CURRENT_TEST', '?').split(' ')[0]} {what}: " \
+           f"rel_l2={rel:.3e} max_abs/rms={mx:.3e}"
+    print("  " + line, flush=True)
+    record(line)
+    assert rel <= REL_L2_TOL and mx <= MAX_ABS_TOL, (what, rel, mx)
+    return rel, mx
+
+
+def bf16_rne_bits(a32):
+    u = np.asarray(a32, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)

@@ -1,0 +1,124 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and rejects invalid arguments before anything is enqueued (no GPU needed:
+every call here fails validation, so no HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_mixture_experts_fp32_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_wq.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        from quantized_mixture_experts_fp32_amd import build
+        build.build()
+    return moe.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    assert sorted(moe.EXPORTS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert moe.status_str(0) == "MOE_OK"
+    assert moe.status_str(3) == "MOE_ERR_WORKSPACE"
+    assert moe.status_str(99) == "MOE_ERR_UNKNOWN"
+
+
+FAKE = ctypes.c_void_p(0x10000)      # 16-byte-aligned non-null pointer
+ODD = ctypes.c_void_p(0x10002)       # misaligned
+NULL = None
+
+
+def err(lib):
+    return lib.moe_last_error().decode()
+
+
+def test_route_validation(lib):
+    r = lib.moe_route
+    assert r(FAKE, FAKE, NULL, 4, 200, 8, 2, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
+    assert "128" in err(lib)
+    assert r(FAKE, FAKE, NULL, 4, 256, 8, 9, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert r(FAKE, FAKE, NULL, 4, 256, 600, 2, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
+    assert r(FAKE, FAKE, NULL, 4, 256, 64, 17, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
+    assert r(NULL, FAKE, NULL, 4, 256, 8, 2, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert r(ODD, FAKE, NULL, 4, 256, 8, 2, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert r(FAKE, FAKE, NULL, -1, 256, 8, 2, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID_ARG
+    # T = 0 is a valid no-op, even with null pointers
+    assert r(NULL, NULL, NULL, 0, 256, 8, 2, NULL, NULL, NULL) == moe.MOE_OK
+
+
+def test_permute_validation(lib):
+    need = lib.moe_permute_ws_bytes(100, 8, 64)
+    assert need >= 64 * 4
+    p = lib.moe_permute
+    assert p(FAKE, 100, 8, 64, FAKE, FAKE, FAKE, FAKE, need - 4, NULL) == moe.MOE_ERR_WORKSPACE
+    assert p(FAKE, 100, 8, 64, FAKE, FAKE, FAKE, NULL, need, NULL) == moe.MOE_ERR_WORKSPACE
+    assert p(FAKE, 100, 8, 64, NULL, FAKE, FAKE, FAKE, need, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert p(FAKE, 100, 9, 8, FAKE, FAKE, FAKE, FAKE, need, NULL) == moe.MOE_ERR_INVALID_ARG
+
+
+def _ffn(lib, **kw):
+    a = dict(x=FAKE, off=FAKE, sp=FAKE, T=4, k=2, E=8, d=256, f=512, fmt=0, group=128,
+             guc=FAKE, gus=FAKE, dnc=FAKE, dns=FAKE, bits=NULL, mode=0, y=FAKE,
+             ws=FAKE, wsb=1 << 30, path=0)
+    a.update(kw)
+    return lib.moe_expert_ffn_wq(a["x"], a["off"], a["sp"], a["T"], a["k"], a["E"],
+                                 a["d"], a["f"], a["fmt"], a["group"], a["guc"],
+                                 a["gus"], a["dnc"], a["dns"], a["bits"], a["mode"],
+                                 a["y"], a["ws"], a["wsb"], a["path"], NULL)
+
+
+def test_ffn_validation(lib):
+    U, I, W = moe.MOE_ERR_UNSUPPORTED, moe.MOE_ERR_INVALID_ARG, moe.MOE_ERR_WORKSPACE
+    assert _ffn(lib, group=64) == U
+    assert _ffn(lib, f=500) == U
+    assert _ffn(lib, d=200) == U
+    assert _ffn(lib, fmt=7) == I
+    assert _ffn(lib, path=5) == I
+    assert _ffn(lib, mode=1) == I                      # int4 takes no bits
+    assert _ffn(lib, fmt=1, mode=0) == I               # bitplane needs a mode
+    assert _ffn(lib, fmt=1, mode=1, bits=NULL) == I
+    assert _ffn(lib, fmt=1, mode=3, k=2) == U          # rank rule needs k = 8
+    assert _ffn(lib, guc=ODD) == I
+    assert _ffn(lib, y=NULL) == I
+    need = lib.moe_ffn_ws_bytes(4, 2, 8, 256, 512, 0)
+    assert _ffn(lib, wsb=need - 1) == W
+    assert _ffn(lib, ws=ctypes.c_void_p(0x10010)) == I  # ws needs 256-byte alignment
+    assert _ffn(lib, T=0, x=NULL, off=NULL, sp=NULL, y=NULL, ws=NULL, wsb=0) == moe.MOE_OK
+
+
+def test_combine_and_quantize_validation(lib):
+    c = lib.moe_combine
+    assert c(FAKE, FAKE, FAKE, 4, 2, 256, FAKE, 5, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert c(FAKE, FAKE, FAKE, 4, 17, 256, FAKE, 0, NULL) == moe.MOE_ERR_UNSUPPORTED
+    assert c(FAKE, FAKE, FAKE, 4, 2, 256, ODD, 0, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert c(NULL, NULL, NULL, 0, 2, 256, NULL, 0, NULL) == moe.MOE_OK
+    q = lib.moe_quantize_w4
+    assert q(FAKE, 2, 4, 256, 64, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
+    assert q(FAKE, 2, 4, 100, 128, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
+    assert q(NULL, 2, 4, 256, 128, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_bitplane8(FAKE, 0, 4, 256, 128, NULL, NULL, NULL) == moe.MOE_OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(moe, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        moe.load_library()

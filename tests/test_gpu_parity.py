@@ -1,0 +1,330 @@
+"""GPU parity of every step of the layer against the CPU oracle, through the
+C ABI.  Integer results (top-k ids, grouping, codes, scales) must be
+bit-identical; floating-point outputs must be within rel-L2 <= 2e-3 and
+max|err| <= 3e-2 * rms(ref) of the oracle (fp64 accumulation, same
+dequantized weights)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import quantized_mixture_experts_fp32_amd as moe
+from layer_data import (DEV, DevLayer, HostLayer, assert_close, assert_codes_equal,
+                        bf16_rne_bits, custom_cfg, record,
+                        stream)
+
+pytestmark = pytest.mark.gpu
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+def t_i16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV)
+
+
+# ----------------------------------------------------------------- inputs
+def test_generator_device_equals_host():
+    cfg = synth.CONFIGS[4]
+    note("generator: cfg4 x/router/bias/weight slices")
+    x = torch.empty((64, cfg.d), dtype=torch.int16, device=DEV)
+    synth.dev_fill_x(cfg, x.data_ptr(), 64, stream())
+    wr = torch.empty((cfg.E, cfg.d), dtype=torch.int16, device=DEV)
+    synth.dev_fill_router(cfg, wr.data_ptr(), stream())
+    b = torch.empty((cfg.E,), dtype=torch.float32, device=DEV)
+    synth.dev_fill_bias(cfg, b.data_ptr(), stream())
+    n = 1 << 20
+    start = 3 * 2 * cfg.f * cfg.d + 12345
+    w = torch.empty((n,), dtype=torch.float32, device=DEV)
+    synth.dev_fill_weight(cfg, synth.T_W_GATE_UP, w.data_ptr(), stream(), start=start, n=n)
+    torch.cuda.synchronize()
+    assert np.array_equal(x.cpu().numpy().view(np.uint16), synth.host_x(cfg, 64))
+    assert np.array_equal(wr.cpu().numpy().view(np.uint16), synth.host_router(cfg))
+    assert np.array_equal(b.cpu().numpy(), synth.host_bias(cfg))
+    host = np.empty(n, np.float32)
+    synth._load_host().synth_fill_weight_f32(42, cfg.cid, synth.T_W_GATE_UP, start, n,
+                                             synth.W_SIGMA, synth._ptr(host))
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), host.view(np.uint32))
+
+
+# ------------------------------------------------------------- quantizers
+def _edge_weights(rng, R, K):
+    w = (rng.normal(0, 0.14, (R, K)) * np.where(rng.random((R, K)) < 0.01, 10, 1))
+    w = w.astype(np.float32)
+    w[0, :128] = 0.0                                   # all-zero group: s = 0
+    w[1, :128] = 0.0
+    w[1, 5] = 1e-30                                    # scale below fp16 range
+    w[2, :128] = np.float32(0.4375) * np.arange(-64, 64) / 64  # exact ties at .5
+    w[3, 128:256] = -np.abs(w[3, 128:256])             # negative group maximum
+    w[4, :128] = 7 * 65000.0 * rng.uniform(-1, 1, 128).astype(np.float32)  # near fp16 max
+    return w
+
+
+@pytest.mark.parametrize("fmt", ["w4", "bp8"])
+def test_quantize_bit_exact(fmt):
+    rng = np.random.default_rng(7)
+    for (E, N, K) in [(2, 8, 256), (3, 40, 384), (1, 5, 2048)]:
+        note(f"quantize {fmt} E={E} N={N} K={K}")
+        w = np.stack([_edge_weights(rng, N, K) for _ in range(E)])
+        wd = torch.from_numpy(w).to(DEV)
+        if fmt == "w4":
+            codes, scales = moe.moe_quantize_w4(wd)
+            ref = [oracle.quantize_w4(w[e]) for e in range(E)]
+        else:
+            codes, scales = moe.moe_quantize_bitplane8(wd)
+            ref = [oracle.quantize_bp8(w[e]) for e in range(E)]
+        torch.cuda.synchronize()
+        c, s = codes.cpu().numpy(), scales.cpu().numpy().view(np.uint16)
+        for e in range(E):
+            assert np.array_equal(c[e], ref[e][0]), (fmt, e)
+            assert np.array_equal(s[e], ref[e][1]), (fmt, e)
+
+
+# ----------------------------------------------------------------- router
+ROUTE_CASES = [(0, 16), (1, 16), (2, 4096), (3, 16), (4, 1), (4, 64), (4, 8192)]
+
+
+@pytest.mark.parametrize("cid,T", ROUTE_CASES)
+def test_route_bit_exact(cid, T):
+    cfg = synth.CONFIGS[cid]
+    note(f"route cfg{cid} T={T}")
+    x, wr, bias = synth.host_x(cfg, T), synth.host_router(cfg), synth.host_bias(cfg)
+    idx, w = moe.moe_route(t_i16(x), t_i16(wr),
+                           None if bias is None else torch.from_numpy(bias).to(DEV), cfg.k)
+    torch.cuda.synchronize()
+    _, ridx, rw = oracle.route(x, wr, bias, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
+
+
+def test_route_ties_and_shapes():
+    rng = np.random.default_rng(3)
+    cases = []
+    # duplicated router rows -> exactly equal logits, ties to the lower index
+    d, E = 256, 12
+    wr = (rng.normal(0, 1 / 16, (E, d)) * 256).round() / 256
+    wr[7] = wr[2]
+    wr[9] = wr[2]
+    wr[11] = wr[4]
+    cases.append(("dup-rows", d, E, 5, wr, None))
+    # zero router: logits are the bias; equal biases tie
+    cases.append(("zero-router", 128, 33, 6, np.zeros((33, 128)),
+                  np.repeat(np.array([0.5, -1.0, 0.5], np.float32), 11)))
+    cases.append(("E=1", 128, 1, 1, rng.normal(0, 0.1, (1, 128)), None))
+    cases.append(("k=E", 384, 6, 6, rng.normal(0, 0.1, (6, 384)), None))
+    cases.append(("E=500", 128, 500, 16, rng.normal(0, 0.1, (500, 128)), None))
+    for name, d, E, k, wrf, bias in cases:
+        note(f"route {name}")
+        T = 37
+        x = np.round(rng.normal(0, 1, (T, d)) * 64) / 64
+        xb = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        wb = (np.asarray(wrf, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        bt = None if bias is None else torch.from_numpy(bias).to(DEV)
+        idx, w = moe.moe_route(t_i16(xb), t_i16(wb), bt, k)
+        torch.cuda.synchronize()
+        _, ridx, rw = oracle.route(xb, wb, bias, k)
+        assert np.array_equal(idx.cpu().numpy(), ridx), name
+        np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
+
+
+# ---------------------------------------------------------------- permute
+@pytest.mark.parametrize("T,k,E,mode", [(0, 8, 16, "rand"), (1, 1, 1, "rand"),
+                                        (33, 3, 5, "rand"), (1000, 8, 64, "one"),
+                                        (4096, 8, 64, "skew"), (8192, 8, 256, "skew"),
+                                        (777, 16, 512, "rand")])
+def test_permute_bit_exact(T, k, E, mode):
+    note(f"permute T={T} k={k} E={E} {mode}")
+    rng = np.random.default_rng(T + k + E)
+    if mode == "one":
+        idx = np.full((T, k), 3 % E, np.int32)
+    elif mode == "skew":
+        p = rng.dirichlet(np.full(E, 0.3))
+        idx = rng.choice(E, size=(T, k), p=p).astype(np.int32)
+    else:
+        idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    off, sp, pp = moe.moe_permute(torch.from_numpy(idx).to(DEV), E)
+    torch.cuda.synchronize()
+    roff, rsp, rpp = oracle.permute(idx, E)
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(sp.cpu().numpy(), rsp)
+    assert np.array_equal(pp.cpu().numpy(), rpp)
+
+
+# ---------------------------------------------------------------- combine
+def test_combine_fp32_and_bf16():
+    rng = np.random.default_rng(5)
+    for T, k, d in [(1, 8, 2048), (37, 3, 256), (513, 8, 4096)]:
+        note(f"combine T={T} k={k} d={d}")
+        y = rng.normal(0, 1, (T * k, d)).astype(np.float32)
+        pp = rng.permutation(T * k).astype(np.int32)
+        w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+        yd, pd, wd = (torch.from_numpy(a).to(DEV) for a in (y, pp, w))
+        o32 = moe.moe_combine(yd, pd, wd, out_dtype=moe.MOE_OUT_F32)
+        o16 = moe.moe_combine(yd, pd, wd, out_dtype=moe.MOE_OUT_BF16)
+        torch.cuda.synchronize()
+        ref, _ = oracle.combine(y.astype(np.float64), pp, w.astype(np.float64))
+        a = o32.cpu().numpy()
+        assert np.all(np.abs(a - ref) <= 1e-5 * (np.abs(ref) + 1))
+        assert np.array_equal(o16.cpu().view(torch.int16).numpy().view(np.uint16),
+                              bf16_rne_bits(a))
+
+
+# ------------------------------------------------------------ whole layer
+def run_layer(dl, path, bits_mode=moe.MOE_BITS_NONE, bits=None):
+    lay = dl.layer(bits_mode, bits)
+    o32 = lay.forward(dl.x, out_dtype=moe.MOE_OUT_F32, path=path).clone()
+    o16 = moe.moe_combine(lay.y_pairs, lay.pair_pos, lay.topk_w, out_dtype=moe.MOE_OUT_BF16)
+    torch.cuda.synchronize()
+    return lay, o32.cpu().numpy(), o16.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def check_layer(dl, hl, path, bits_mode=moe.MOE_BITS_NONE, bits_np=None):
+    bits = None if bits_np is None else torch.from_numpy(bits_np).to(DEV)
+    lay, o32, o16 = run_layer(dl, path, bits_mode, bits)
+    cfg = dl.cfg
+    ref = oracle.layer(hl.x, hl.wr, hl.bias, cfg.k, cfg.f, hl.expert, cfg.fmt,
+                       bits_mode, bits_np)
+    assert np.array_equal(lay.topk_idx.cpu().numpy(), ref["topk_idx"])
+    np.testing.assert_allclose(lay.topk_w.cpu().numpy(), ref["topk_w"], rtol=2e-6, atol=1e-7)
+    assert np.array_equal(lay.offsets.cpu().numpy(), ref["expert_offsets"])
+    assert np.array_equal(lay.sorted_pair.cpu().numpy(), ref["sorted_pair"])
+    assert np.array_equal(lay.pair_pos.cpu().numpy(), ref["pair_pos"])
+    active = np.nonzero(np.diff(ref["expert_offsets"]))[0]
+    assert_codes_equal(dl, hl, active)
+    assert_close(lay.y_pairs.cpu().numpy(), ref["y_pairs"], "y_pairs")
+    assert_close(o32, ref["o"], "out fp32")
+    # bf16 output: exactly the rounding of the fp32 output (whose max-abs and
+    # rel-L2 errors are checked above).  Against the fp64 oracle the bf16
+    # output is held to the rel-L2 bar only: its own rounding (2^-9
+    # relative) alone exceeds the max-abs bar wherever |o| > 15 rms(o).
+    assert np.array_equal(o16, bf16_rne_bits(o32))
+    o16f = (o16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    rel = np.linalg.norm(o16f - ref["o"]) / np.linalg.norm(ref["o"])
+    ndiff = int((o16 != ref["out"]).sum())
+    record(f"{cfg.name} bf16 out: rel_l2={rel:.3e}; {ndiff} of {o16.size} differ "
+           f"from the oracle's bf16 rounding")
+    assert rel <= 2e-3
+    return lay, o32
+
+
+PATHS = [moe.MOE_PATH_DECODE, moe.MOE_PATH_PREFILL]
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_layer_cfg0(path):
+    note(f"layer cfg0 path={path}")
+    cfg = synth.CONFIGS[0]
+    check_layer(DevLayer(cfg, 16), HostLayer(cfg, 16), path)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_layer_ragged_tiles(path):
+    # several token tiles per expert and a ragged tail, f not a power of two
+    cfg = custom_cfg(11, d=256, E=5, k=3, f=384, bias_sigma=1.0)
+    note(f"layer custom ragged T=100 path={path}")
+    check_layer(DevLayer(cfg, 100), HostLayer(cfg, 100), path)
+
+
+def test_layer_all_pairs_one_expert_and_empty_experts():
+    cfg = custom_cfg(12, d=128, E=16, k=2, f=128, bias_sigma=30.0)
+    note("layer skew: bias 30 sigma -> nearly all pairs on two experts")
+    dl, hl = DevLayer(cfg, 70), HostLayer(cfg, 70)
+    lay, _ = check_layer(dl, hl, moe.MOE_PATH_AUTO)
+    cnt = np.diff(lay.offsets.cpu().numpy())
+    assert (cnt == 0).sum() >= 8
+
+
+@pytest.mark.parametrize("T", [1, 4, 8, 16])
+def test_layer_cfg1_decode(T):
+    note(f"layer cfg1 T={T}")
+    cfg = synth.CONFIGS[1]
+    check_layer(DevLayer(cfg, T), HostLayer(cfg, T), moe.MOE_PATH_AUTO)
+
+
+def test_layer_cfg3_bitplane_rank_rule():
+    note("layer cfg3 T=16 bitplane rank rule")
+    cfg = synth.CONFIGS[3]
+    check_layer(DevLayer(cfg, 16), HostLayer(cfg, 16), moe.MOE_PATH_AUTO,
+                moe.MOE_BITS_RANK_RULE)
+
+
+@pytest.mark.parametrize("mode", ["pair", "expert"])
+def test_layer_bitplane_bit_modes(mode):
+    cfg = custom_cfg(13, d=256, E=6, k=4, f=256, fmt="bp8", bias_sigma=0.5)
+    T = 40
+    rng = np.random.default_rng(11)
+    if mode == "pair":
+        bits, bm = rng.integers(1, 9, T * cfg.k).astype(np.uint8), moe.MOE_BITS_PER_PAIR
+    else:
+        bits, bm = np.array([1, 8, 3, 5, 2, 7], np.uint8), moe.MOE_BITS_PER_EXPERT
+    for path in PATHS:
+        note(f"layer bitplane bits={mode} path={path}")
+        check_layer(DevLayer(cfg, T), HostLayer(cfg, T), path, bm, bits)
+
+
+def test_layer_zero_tokens():
+    cfg = synth.CONFIGS[0]
+    dl = DevLayer(cfg, 0)
+    lay = dl.layer()
+    out = lay.forward(dl.x, out_dtype=moe.MOE_OUT_F32)
+    torch.cuda.synchronize()
+    assert out.shape == (0, cfg.d)
+    assert np.array_equal(lay.offsets.cpu().numpy(), np.zeros(cfg.E + 1, np.int32))
+
+
+def test_layer_deterministic():
+    cfg = synth.CONFIGS[1]
+    dl = DevLayer(cfg, 16)
+    lay = dl.layer()
+    a = lay.forward(dl.x, out_dtype=moe.MOE_OUT_F32).clone()
+    ya = lay.y_pairs.clone()
+    b = lay.forward(dl.x, out_dtype=moe.MOE_OUT_F32).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(ya.view(torch.int32), lay.y_pairs.view(torch.int32))
+
+
+# ----------------------------------------- full-size configs, sampled outputs
+FULL = [(2, 4096, moe.MOE_PATH_AUTO), (4, 1, moe.MOE_PATH_AUTO),
+        (4, 64, moe.MOE_PATH_AUTO), (4, 8192, moe.MOE_PATH_AUTO)]
+
+
+@pytest.mark.parametrize("cid,T,path", FULL)
+def test_layer_full_size_sampled(cid, T, path):
+    """Full-size layer in the benchmark's launch configuration: routing and
+    grouping bit-exact over every token; codes of every touched expert
+    bit-exact; outputs of sampled tokens against the oracle."""
+    cfg = synth.CONFIGS[cid]
+    note(f"full-size cfg{cid} T={T}: device setup")
+    dl = DevLayer(cfg, T)
+    hl = HostLayer(cfg, T)
+    lay, o32, o16 = run_layer(dl, path)
+    note("  routing + grouping vs oracle")
+    _, ridx, rw = oracle.route(hl.x, hl.wr, hl.bias, cfg.k)
+    idx = lay.topk_idx.cpu().numpy()
+    assert np.array_equal(idx, ridx)
+    np.testing.assert_allclose(lay.topk_w.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
+    roff, rsp, rpp = oracle.permute(ridx, cfg.E)
+    assert np.array_equal(lay.offsets.cpu().numpy(), roff)
+    assert np.array_equal(lay.sorted_pair.cpu().numpy(), rsp)
+    assert np.array_equal(lay.pair_pos.cpu().numpy(), rpp)
+    cnt = np.diff(roff)
+    hot = int(np.argmax(cnt))
+    toks = sorted({0, T - 1, T // 2, int(rsp[roff[hot]]) // cfg.k})[:4]
+    note(f"  sampled tokens {toks} (hottest expert {hot} has {cnt[hot]} pairs)")
+    y = lay.y_pairs.cpu().numpy()
+    for t in toks:
+        experts = ridx[t]
+        assert_codes_equal(dl, hl, experts)
+        o = np.zeros(cfg.d)
+        for j, e in enumerate(experts):
+            (gq, gs), (dq, ds) = hl.expert(int(e))
+            _, yy = oracle.expert_ffn(hl.x[t:t + 1], oracle.dequant_w4(gq, gs),
+                                      oracle.dequant_w4(dq, ds))
+            assert_close(y[rpp[t * cfg.k + j]], yy[0], f"y t={t} e={e}")
+            o += rw[t, j] * yy[0]
+        assert_close(o32[t], o, f"out t={t}")
+        assert np.array_equal(o16[t], bf16_rne_bits(o32[t]))
+
