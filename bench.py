@@ -43,7 +43,7 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--workloads", default="",
-                    help="comma list of name filters for secondary workloads")
+                    help="comma list of name filters (spaces as _) for secondary workloads")
     return ap.parse_args()
 
 
@@ -288,7 +288,8 @@ def main():
     ]
     if args.workloads:
         keys = args.workloads.split(",")
-        secondary = [w for w in secondary if any(k in w.name for k in keys)]
+        secondary = [w for w in secondary
+                     if any(k in w.name.replace(" ", "_") for k in keys)]
     head_rec = run_workload(head, args.warmup, hip, torch, np, synth, moe)
     others = []
     if not args.only_headline:

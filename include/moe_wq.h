@@ -80,7 +80,8 @@ extern "C" {
 #define MOE_GROUP 128     /* quantization group along the input dimension */
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_TOPK 16
-/* d and f must be multiples of 128; T*k must be below 2^31. */
+#define MOE_MAX_D 8192   /* router stages eight activation rows in LDS */
+/* d and f must be multiples of 128, d <= MOE_MAX_D; T*k below 2^31. */
 
 /* Human-readable name of a status code. */
 const char *moe_status_str(int status);
@@ -107,7 +108,7 @@ const char *moe_last_error(void);
  *   wr     bf16 [E][d] (router matrix stored expert-major), 16-byte aligned.
  *   bias   fp32 [E] logit bias, or NULL.
  *   topk_idx int32 [T][k]; topk_w fp32 [T][k]  (outputs).
- * Requires d % 128 == 0, 1 <= k <= min(E, 16), E <= 512.
+ * Requires d % 128 == 0, d <= 8192, 1 <= k <= min(E, 16), E <= 512.
  * ------------------------------------------------------------------- */
 int moe_route(const void *x_bf16, const void *wr_bf16, const float *bias,
               int T, int d, int E, int k, int32_t *topk_idx, float *topk_w,
@@ -171,7 +172,7 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E,
  *   path_hint: MOE_PATH_AUTO / _DECODE / _PREFILL (all give results within
  *     the same tolerance of the CPU definition).
  * Alignment: x, codes and y_pairs 16-byte aligned; scales 4-byte aligned.
- * Requires d % 128 == 0, f % 128 == 0, E <= 512, 1 <= k <= 16.
+ * Requires d % 128 == 0, d <= 8192, f % 128 == 0, E <= 512, 1 <= k <= 16.
  * ------------------------------------------------------------------- */
 size_t moe_ffn_ws_bytes(int T, int k, int E, int d, int f, int format);
 int moe_expert_ffn_wq(const void *x_bf16, const int32_t *expert_offsets,

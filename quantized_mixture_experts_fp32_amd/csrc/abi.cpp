@@ -44,6 +44,7 @@ int check_dims(int T, int d, int E, int k) {
   if ((long long)T * k >= (1LL << 31))
     return fail(MOE_ERR_UNSUPPORTED, "T*k must be below 2^31");
   if (d % MOE_GROUP) return fail(MOE_ERR_UNSUPPORTED, "d=%d not a multiple of 128", d);
+  if (d > MOE_MAX_D) return fail(MOE_ERR_UNSUPPORTED, "d=%d > %d", d, MOE_MAX_D);
   return MOE_OK;
 }
 

@@ -428,7 +428,13 @@ size_t ffn_ws_bytes(int T, int k, int E, int d, int f, int format) {
 }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
-  if ((long long)a.T * a.k == 0) return hipSuccess;
+  const long long P = (long long)a.T * a.k;
+  if (P == 0) return hipSuccess;
+  if (a.format == 0 && a.path == 1) {
+    uint16_t* h = (uint16_t*)((char*)a.ws + 256 +
+                              align256(max_tiles(P, a.E, 16) * sizeof(Tile)));
+    return launch_ffn_decode_w4(a, h, s);
+  }
   if (a.path == 2) return run_ffn<4>(a, s);
   return run_ffn<2>(a, s);
 }

@@ -1,0 +1,455 @@
+// Decode-path expert FFN for int4 experts (small batches, HBM-bound).
+//  ExactMoE ("Every Expert Counts ...", Abstract): symmetric group-128 W4A16
+//  routed experts executed by grouped kernels; decode is bound by moving the
+//  expert weights, so each selected expert's packed codes stream from HBM
+//  once per token tile with 16-byte loads and are dequantized in registers.
+//
+// Arithmetic.  A code nibble n (two's complement q) is turned into the bf16
+// value 24 + q with one v_bitop3 (exponent of 16 plus (q+8) in the top four
+// mantissa bits); 24 + q is an exact bf16 integer.  The MFMA accumulator of
+// every 128-group starts from -24 * sum(x over the group), produced by four
+// MFMAs with a constant -24 A-operand, so the group's sum is
+// sum((24+q) x) - 24 sum(x) = sum(q x) with fp32 accumulation only.  The
+// fp16 scale then multiplies the group sum (fp32) and the product is added to
+// the running fp32 total.  Dequantized weights are never rounded.
+//
+// K order.  The conversion yields the nibbles of a dword in the order
+// 0,4,1,5,2,6,3,7; the activation fragment is permuted the same way with
+// v_perm, so A and B enumerate the same K elements.
+//
+// Work decomposition.  Work item = (token tile of up to 16*NT grouped
+// pairs of one expert, 4/KS row tiles of 16 output features).  Each wave
+// streams one row tile over one of KS slices of K, keeping kDepth 128-groups
+// of codes and activations in flight; the K slices are reduced through LDS in
+// a fixed order.  Blocks are persistent: they walk the work items with a
+// grid stride and decode their tile from expert_offsets staged in LDS (no
+// separate preparation launch).
+#include <algorithm>
+
+#include "kcommon.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct TileInfo {
+  int e, r0, cnt;
+};
+
+// Tile b of the list "every expert's slot range cut into tiles of tok
+// pairs, experts in ascending order".  Wave-cooperative (all lanes call it
+// with the same b and get the same answer); returns false past the end.
+__device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int tok,
+                          int b, TileInfo& t) {
+  const int lane = threadIdx.x & 63;
+  int carry = 0;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    const int lo = (e < E) ? offsets[e] : 0;
+    const int n = (e < E) ? offsets[e + 1] - lo : 0;
+    const int c = (n + tok - 1) / tok;
+    int s = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(s, o, kWave);
+      if (lane >= o) s += v;
+    }
+    const int total = __shfl(s, 63, kWave);
+    if (b < carry + total) {
+      const uint64_t m = __ballot(carry + s > b);
+      const int L = __ffsll((unsigned long long)m) - 1;
+      const int sL = __shfl(s, L, kWave), cL = __shfl(c, L, kWave);
+      const int loL = __shfl(lo, L, kWave), nL = __shfl(n, L, kWave);
+      const int chunk = b - (carry + sL - cL);
+      t.e = base + L;
+      t.r0 = loL + chunk * tok;
+      t.cnt = min(tok, nL - chunk * tok);
+      return true;
+    }
+    carry += total;
+  }
+  return false;
+}
+
+// 8 nibbles -> bf16 (24 + q) in element order 0,4,1,5,2,6,3,7.
+// bitop3 LUT 0x6A: out = B ? (x ^ D) : D, with B = nibble field (bits 3-6 of
+// each half), D = 0x41C0 per half (exponent bits of 16.0, plus the inversion
+// of the nibble's top bit that maps two's complement q to q + 8).
+__device__ __forceinline__ bf16x8 w4_magic(uint32_t w) {
+  const uint32_t B = 0x00780078u, D = 0x41C041C0u;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_bitop3_b32(w << 3, B, D, 0x6A);
+  r[1] = __builtin_amdgcn_bitop3_b32(w >> 1, B, D, 0x6A);
+  r[2] = __builtin_amdgcn_bitop3_b32(w >> 5, B, D, 0x6A);
+  r[3] = __builtin_amdgcn_bitop3_b32(w >> 9, B, D, 0x6A);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// 8 consecutive bf16 (x0..x7 in a u32x4) -> order 0,4,1,5,2,6,3,7.
+__device__ __forceinline__ bf16x8 x_perm(u32x4 v) {
+  u32x4 r;
+  r[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
+  r[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
+  r[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ bf16x8 bf16_splat(uint32_t bits16) {
+  const uint32_t p = bits16 | (bits16 << 16);
+  u32x4 r = {p, p, p, p};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+constexpr uint32_t kBf16Neg24 = 0xC1C0u;  // -24.0
+
+
+// The kernels below stage expert_offsets and (when it fits) sorted_pair in
+// LDS once per persistent block; a work item then needs one round trip to
+// HBM: all of a wave's code, scale and activation loads are issued together.
+constexpr int kPairsInLds = 4096;
+
+__device__ __forceinline__ int stage_routing(const int32_t* __restrict__ offsets,
+                                             const int32_t* __restrict__ sorted_pair,
+                                             int E, int P, int32_t* off_lds,
+                                             int32_t* sp_lds) {
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) off_lds[i] = offsets[i];
+  const int np = P <= kPairsInLds ? P : 0;
+  for (int i = threadIdx.x; i < np; i += blockDim.x) sp_lds[i] = sorted_pair[i];
+  return np;
+}
+
+
+
+
+// Scales of a work item, staged once as fp32 in LDS: [matrix][group][row].
+// rows_src: first scale row of matrix 0; matrices are mat_stride rows apart.
+__device__ __forceinline__ void stage_scales_f32(const uint16_t* __restrict__ rows_src,
+                                                 size_t mat_stride, int nmat, int rows,
+                                                 int G, float* __restrict__ dst) {
+  const int total = nmat * rows * G;
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    const int g = i % G, r = (i / G) % rows, m = i / (G * rows);
+    dst[(m * G + g) * rows + r] =
+        f16_bits_to_f32(rows_src[(size_t)m * mat_stride * G + (size_t)r * G + g]);
+  }
+}
+
+
+// One 128-group of one 16-row matrix tile: offset-corrected MFMA sum,
+// scaled and accumulated.  xp/seed are shared by the tiles of a group.
+__device__ __forceinline__ void tile_group(const bf16x8 (&xp)[4], const f32x4 seed,
+                                           const u32x4 q, const f32x4 sv, f32x4& acc) {
+  f32x4 p = seed;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p = mfma16(w4_magic(q[j]), xp[j], p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = fmaf(sv[i], p[i], acc[i]);
+}
+
+// ------------------------------------------------------------- gate / up
+// Work item = (token tile of up to 16*NT pairs, row group of RT = 4/KS row
+// tiles of 16 features).  Wave (rt, ks) streams gate and up codes of its row
+// tile over K slice ks with kDepth groups of codes and activations in flight.
+template <int KS, int NT, int kDepth, int kWaves>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
+void gateup_w4_decode(const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
+                      const int32_t* __restrict__ sorted_pair, int E, int k, int P,
+                      int d, int f, const uint8_t* __restrict__ codes,
+                      const uint16_t* __restrict__ scales, uint16_t* __restrict__ h) {
+  constexpr int RT = 4 / KS;
+  extern __shared__ int32_t lds_i[];
+  const int G = d >> 7, RG = f / (16 * RT);
+  int32_t* off_lds = lds_i;
+  int32_t* sp_lds = lds_i + ((E + 1 + 3) & ~3);
+  float* sc_lds = (float*)(sp_lds + ((min(P, kPairsInLds) + 3) & ~3));  // [2][G][16 RT]
+  f32x4* red = (f32x4*)(sc_lds + 2 * G * 16 * RT);                       // [4][NT][2][64]
+  const int np = stage_routing(offsets, sorted_pair, E, P, off_lds, sp_lds);
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int rt = wave / KS, ks = wave % KS;
+  const int gps = (G + KS - 1) / KS;
+  const int gb = ks * gps, ge = min(G, gb + gps);
+  const bf16x8 neg24 = bf16_splat(kBf16Neg24);
+
+  for (int w = blockIdx.x;; w += gridDim.x) {
+    TileInfo tl;
+    if (!find_tile(off_lds, E, 16 * NT, w / RG, tl)) break;
+    const int nb = (w % RG) * 16 * RT, n0 = nb + 16 * rt;
+    const size_t erow = (size_t)tl.e * 2 * f;
+    const int nch = (tl.cnt + 15) >> 4;
+
+    // Token columns past the tile's end read the tile's first row instead:
+    // a B column only feeds its own output column, which is not stored.
+    const uint16_t* xr[NT];
+    bool valid[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      const int j = 16 * c + col;
+      valid[c] = j < tl.cnt;
+      const int jj = valid[c] ? j : 0;
+      const int p = np ? sp_lds[tl.r0 + jj] : sorted_pair[tl.r0 + jj];
+      xr[c] = x + (size_t)(p / k) * d + 32 * kq;
+    }
+    const uint8_t* cg = codes + (erow + n0 + col) * (size_t)(d >> 1) + 16 * kq;
+    const uint8_t* cu = cg + (size_t)f * (d >> 1);
+
+    u32x4 qg[kDepth], qu[kDepth], xv[kDepth][NT][4];
+    auto load = [&](int g, u32x4& a, u32x4& b, u32x4 (&v)[NT][4]) {
+      a = *(const u32x4*)(cg + 64 * g);
+      b = *(const u32x4*)(cu + 64 * g);
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        if (c >= nch) break;
+        const uint16_t* xg = xr[c] + 128 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[c][j] = *(const u32x4*)(xg + 8 * j);
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i)
+      if (gb + i < ge) load(gb + i, qg[i], qu[i], xv[i]);
+
+    __syncthreads();  // previous item is done with sc_lds / red
+    stage_scales_f32(scales + (erow + nb) * G, (size_t)f, 2, 16 * RT, G, sc_lds);
+    __syncthreads();
+
+    f32x4 tg[NT], tu[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) tg[c] = tu[c] = f32x4{0, 0, 0, 0};
+    for (int g = gb; g < ge; g += kDepth) {
+#pragma unroll
+      for (int i = 0; i < kDepth; ++i) {
+        const int gi = g + i;
+        if (gi >= ge) break;
+        const f32x4 sg = *(const f32x4*)(sc_lds + gi * (16 * RT) + 16 * rt + 4 * kq);
+        const f32x4 su = *(const f32x4*)(sc_lds + (G + gi) * (16 * RT) + 16 * rt + 4 * kq);
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          if (c >= nch) break;
+          bf16x8 xp[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xp[j] = x_perm(xv[i][c][j]);
+          f32x4 seed = {0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) seed = mfma16(neg24, xp[j], seed);
+          tile_group(xp, seed, qg[i], sg, tg[c]);
+          tile_group(xp, seed, qu[i], su, tu[c]);
+        }
+        if (gi + kDepth < ge) load(gi + kDepth, qg[i], qu[i], xv[i]);
+      }
+    }
+
+    if (KS > 1) {
+      if (ks > 0) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          red[((wave * NT + c) * 2 + 0) * 64 + lane] = tg[c];
+          red[((wave * NT + c) * 2 + 1) * 64 + lane] = tu[c];
+        }
+      }
+      __syncthreads();
+      if (ks == 0) {
+        for (int s2 = 1; s2 < KS; ++s2)
+#pragma unroll
+          for (int c = 0; c < NT; ++c) {
+            const f32x4 g2 = red[(((wave + s2) * NT + c) * 2 + 0) * 64 + lane];
+            const f32x4 u2 = red[(((wave + s2) * NT + c) * 2 + 1) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              tg[c][i] = tg[c][i] + g2[i];
+              tu[c][i] = tu[c][i] + u2[i];
+            }
+          }
+      }
+    }
+    if (ks == 0) {
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        if (!valid[c]) continue;
+        uint32_t hb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          hb[i] = f32_to_bf16_rne(silu_f32(tg[c][i]) * tu[c][i]);
+        uint2 pk;
+        pk.x = hb[0] | (hb[1] << 16);
+        pk.y = hb[2] | (hb[3] << 16);
+        *(uint2*)(h + (size_t)(tl.r0 + 16 * c + col) * f + n0 + 4 * kq) = pk;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ down
+template <int KS, int NT, int kDepth, int kWaves>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
+void down_w4_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ offsets,
+                    int E, int d, int f, const uint8_t* __restrict__ codes,
+                    const uint16_t* __restrict__ scales, float* __restrict__ y) {
+  constexpr int RT = 4 / KS;
+  extern __shared__ int32_t lds_i[];
+  const int G = f >> 7, RG = d / (16 * RT);
+  int32_t* off_lds = lds_i;
+  float* sc_lds = (float*)(lds_i + ((E + 1 + 3) & ~3));  // [G][16 RT]
+  f32x4* red = (f32x4*)(sc_lds + G * 16 * RT);           // [4][NT][64]
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) off_lds[i] = offsets[i];
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int rt = wave / KS, ks = wave % KS;
+  const int gps = (G + KS - 1) / KS;
+  const int gb = ks * gps, ge = min(G, gb + gps);
+  const bf16x8 neg24 = bf16_splat(kBf16Neg24);
+
+  for (int w = blockIdx.x;; w += gridDim.x) {
+    TileInfo tl;
+    if (!find_tile(off_lds, E, 16 * NT, w / RG, tl)) break;
+    const int mb = (w % RG) * 16 * RT, m0 = mb + 16 * rt;
+    const size_t erow = (size_t)tl.e * d;
+    const int nch = (tl.cnt + 15) >> 4;
+
+    const uint16_t* hr[NT];  // columns past the tile read its first row
+    bool valid[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      const int j = 16 * c + col;
+      valid[c] = j < tl.cnt;
+      hr[c] = h + (size_t)(tl.r0 + (valid[c] ? j : 0)) * f + 32 * kq;
+    }
+    const uint8_t* cd = codes + (erow + m0 + col) * (size_t)(f >> 1) + 16 * kq;
+
+    u32x4 q[kDepth], hv[kDepth][NT][4];
+    auto load = [&](int g, u32x4& a, u32x4 (&v)[NT][4]) {
+      a = *(const u32x4*)(cd + 64 * g);
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        if (c >= nch) break;
+        const uint16_t* hg = hr[c] + 128 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[c][j] = *(const u32x4*)(hg + 8 * j);
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i)
+      if (gb + i < ge) load(gb + i, q[i], hv[i]);
+
+    __syncthreads();
+    stage_scales_f32(scales + (erow + mb) * G, 0, 1, 16 * RT, G, sc_lds);
+    __syncthreads();
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) acc[c] = f32x4{0, 0, 0, 0};
+    for (int g = gb; g < ge; g += kDepth) {
+#pragma unroll
+      for (int i = 0; i < kDepth; ++i) {
+        const int gi = g + i;
+        if (gi >= ge) break;
+        const f32x4 sv = *(const f32x4*)(sc_lds + gi * (16 * RT) + 16 * rt + 4 * kq);
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          if (c >= nch) break;
+          bf16x8 hp[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) hp[j] = x_perm(hv[i][c][j]);
+          f32x4 seed = {0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) seed = mfma16(neg24, hp[j], seed);
+          tile_group(hp, seed, q[i], sv, acc[c]);
+        }
+        if (gi + kDepth < ge) load(gi + kDepth, q[i], hv[i]);
+      }
+    }
+
+    if (KS > 1) {
+      if (ks > 0) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) red[(wave * NT + c) * 64 + lane] = acc[c];
+      }
+      __syncthreads();
+      if (ks == 0) {
+        for (int s2 = 1; s2 < KS; ++s2)
+#pragma unroll
+          for (int c = 0; c < NT; ++c) {
+            const f32x4 v = red[((wave + s2) * NT + c) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[c][i] = acc[c][i] + v[i];
+          }
+      }
+    }
+    if (ks == 0) {
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+        if (valid[c])
+          *(f32x4*)(y + (size_t)(tl.r0 + 16 * c + col) * d + m0 + 4 * kq) = acc[c];
+    }
+  }
+}
+
+// kDepth: 128-groups of codes + activations in flight per wave; kWaves:
+// the occupancy the register allocation is held to (measured on MI355X:
+// occupancy matters more than prefetch depth, and spilling variants lose).
+template <int KS, int NT> constexpr int gu_depth() { return 1; }
+template <int KS, int NT> constexpr int gu_waves() { return NT == 1 ? (KS == 1 ? 4 : 3) : 2; }
+template <int KS, int NT> constexpr int dn_depth() { return NT == 1 ? 2 : 1; }
+template <int KS, int NT> constexpr int dn_waves() { return NT == 1 ? 4 : 2; }
+
+template <int KS, int NT>
+void launch_decode_pair(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
+  constexpr int RT = 4 / KS;
+  const int tok = 16 * NT;
+  const long long mt = (P + tok - 1) / tok + (P < a.E ? P : a.E);
+  const size_t off_b = sizeof(int32_t) * ((a.E + 1 + 3) & ~3);
+  const long long cap = 256LL * 8;
+  {
+    const int G = a.d / 128;
+    const long long work = mt * (a.f / (16 * RT));
+    const int grid = (int)(work < cap ? work : cap);
+    const size_t lds = off_b + sizeof(int32_t) * ((std::min<long long>(P, kPairsInLds) + 3) & ~3) +
+                       sizeof(float) * 2 * G * 16 * RT + sizeof(f32x4) * 4 * NT * 2 * 64;
+    if (a.ev[0]) hipEventRecord(a.ev[0], s);
+    hipLaunchKernelGGL((gateup_w4_decode<KS, NT, gu_depth<KS, NT>(), gu_waves<KS, NT>()>), dim3(grid), dim3(256), lds, s, a.x,
+                       a.offsets, a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes,
+                       a.gu_scales, h);
+    if (a.ev[1]) hipEventRecord(a.ev[1], s);
+  }
+  {
+    const int G = a.f / 128;
+    const long long work = mt * (a.d / (16 * RT));
+    const int grid = (int)(work < cap ? work : cap);
+    const size_t lds = off_b + sizeof(float) * G * 16 * RT + sizeof(f32x4) * 4 * NT * 64;
+    if (a.ev[2]) hipEventRecord(a.ev[2], s);
+    hipLaunchKernelGGL((down_w4_decode<KS, NT, dn_depth<KS, NT>(), dn_waves<KS, NT>()>), dim3(grid), dim3(256), lds, s, h,
+                       a.offsets, a.E, a.d, a.f, a.dn_codes, a.dn_scales, a.y);
+    if (a.ev[3]) hipEventRecord(a.ev[3], s);
+  }
+}
+
+}  // namespace
+
+// Split K over 1, 2 or 4 waves so that few active experts (a single
+// token touches k of them) still put enough waves on every CU.
+hipError_t launch_ffn_decode_w4(const FfnArgs& a, uint16_t* h, hipStream_t s) {
+  const long long P = (long long)a.T * a.k;
+  const long long active = P < a.E ? P : a.E;
+  const long long row_tiles = active * (a.f / 16);
+  const int KS = row_tiles < 2048 ? 4 : (row_tiles < 4096 ? 2 : 1);
+  const bool nt2 = P > 2LL * a.E;
+  if (nt2) {
+    if (KS == 4) launch_decode_pair<4, 2>(a, h, P, s);
+    else if (KS == 2) launch_decode_pair<2, 2>(a, h, P, s);
+    else launch_decode_pair<1, 2>(a, h, P, s);
+  } else {
+    if (KS == 4) launch_decode_pair<4, 1>(a, h, P, s);
+    else if (KS == 2) launch_decode_pair<2, 1>(a, h, P, s);
+    else launch_decode_pair<1, 1>(a, h, P, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -24,16 +24,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// fp16 bits -> fp32 (exact).
+// fp16 bits -> fp32 (exact, subnormals included: v_cvt_f32_f16).
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
-  uint32_t sign = (h & 0x8000u) << 16;
-  uint32_t ex = (h >> 10) & 0x1Fu, man = h & 0x3FFu;
-  if (ex == 0x1Fu) return __uint_as_float(sign | 0x7F800000u | (man << 13));
-  if (ex == 0) {  // zero or subnormal: man * 2^-24
-    float v = (float)man * 5.9604644775390625e-8f;
-    return __uint_as_float(__float_as_uint(v) | sign);
-  }
-  return __uint_as_float(sign | ((ex + 112u) << 23) | (man << 13));
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
 // fp64 -> fp16 bits, round to nearest even, from the full 53-bit significand

@@ -39,6 +39,8 @@ struct FfnArgs {
 };
 size_t ffn_ws_bytes(int T, int k, int E, int d, int f, int format);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+// decode path for int4 experts (ffn_decode.hip); h = bf16 [P][f] scratch
+hipError_t launch_ffn_decode_w4(const FfnArgs& a, uint16_t* h, hipStream_t s);
 
 hipError_t launch_combine(const float* y, const int32_t* pair_pos,
                           const float* topk_w, int T, int k, int d, void* out,

@@ -1,8 +1,17 @@
 // Router: fp32 logits in the fixed lane-group order, top-k by wavefront
 // shuffles, renormalised softmax weights.
 // ExactMoE ("Every Expert Counts ...", Abstract): the router stays BF16 and
-// the top-k routing procedure is unchanged; the summation order below is the
-// fixed order that makes the selected expert ids reproducible bit for bit.
+// the top-k routing procedure is unchanged; the fixed summation order below
+// makes the selected expert ids reproducible bit for bit:
+//   partial l (0..15) of logit (t, e) adds x[t][i] * wr[e][i] for
+//   i = 128c + 8l + r, c ascending, r = 0..7, from +0 in fp32; the partials
+//   are combined with acc_l += acc_(l xor o) for o = 8, 4, 2, 1; the logit
+//   is acc_0 + bias[e].  bf16 * bf16 products are exact in fp32, so fma and
+//   multiply-then-add give the same sums.
+// Two launch shapes share that order: one token per 1024-thread block (64
+// lane groups, few tokens) and eight tokens per 256-thread block (16 lane
+// groups, many tokens).  Activation rows are staged in LDS; router rows are
+// streamed with up to 16 outstanding 16-byte loads per lane.
 #include <float.h>
 
 #include "kcommon.hpp"
@@ -11,9 +20,8 @@
 namespace moe {
 namespace {
 
-constexpr int kTokPerBlock = 8;   // tokens sharing each router-row load
-constexpr int kThreads = 256;     // 16 lane groups of 16
 constexpr int kInvalid = 0x7FFFFFFF;
+constexpr int kWindow = 16;  // router-row chunks in flight per lane
 
 __device__ __forceinline__ bool better(float av, int ae, float bv, int be) {
   if (ae == kInvalid) return false;
@@ -21,107 +29,160 @@ __device__ __forceinline__ bool better(float av, int ae, float bv, int be) {
   return av > bv || (av == bv && ae < be);
 }
 
-// One block: kTokPerBlock tokens x all E experts.
-// Phase 1: lane group G (16 lanes, lane l) evaluates experts G, G+16, ...;
-//   lane l accumulates elements 128c + 8l + r (c ascending, r = 0..7) for
-//   each of the block's tokens, then the xor-butterfly (8, 4, 2, 1) combines
-//   the 16 partials; lane 0 adds the bias and stores the logit in LDS.
-// Phase 2: wave w selects the top-k of tokens w and w+4 by k rounds of a
-//   wave-wide (logit desc, index asc) arg-max; the weights are the softmax
-//   over the k selected logits (equal to the renormalised full softmax).
-__global__ __launch_bounds__(kThreads) void route_kernel(
+__device__ __forceinline__ float lo_bf16(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t v) {
+  return __uint_as_float(v & 0xFFFF0000u);
+}
+
+// Top-k of one token from its E logits in LDS, by one wave: k rounds of a
+// wave-wide (logit desc, index asc) arg-max; weights = softmax over the k
+// selected logits (equal to the renormalised full softmax).
+__device__ void select_topk(const float* __restrict__ lg, int E, int k,
+                            int32_t* __restrict__ idx_out,
+                            float* __restrict__ w_out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t taken = 0;
+  float m = 0.0f, ssum = 0.0f, my_ex = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float bv = -FLT_MAX;
+    int be = kInvalid;
+    for (int i = 0; 64 * i + lane < E; ++i) {
+      const int e = 64 * i + lane;
+      if (!((taken >> i) & 1u) && better(lg[e], e, bv, be)) {
+        bv = lg[e];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oe = __shfl_xor(be, o, kWave);
+      if (better(ov, oe, bv, be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (j == 0) m = bv;
+    const float ex = expf(bv - m);
+    ssum += ex;  // rank order, identical in every lane
+    if (lane == j) {
+      my_ex = ex;
+      idx_out[j] = be;
+    }
+  }
+  if (lane < k) w_out[lane] = my_ex / ssum;
+}
+
+// Stage TB activation rows (bf16) into LDS; rows past T are zero.
+template <int TB, int NTHR>
+__device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int T,
+                                        int d, int t0, uint16_t* xs) {
+  const int n16 = TB * d / 8;  // 16-byte units
+  for (int i = threadIdx.x; i < n16; i += NTHR) {
+    const int tt = (8 * i) / d, c = 8 * i - tt * d;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (t0 + tt < T) v = *(const u32x4*)(x + (size_t)(t0 + tt) * d + c);
+    *(u32x4*)(xs + tt * d + c) = v;
+  }
+}
+
+// Logits of TB tokens (rows of xs) for the experts of this lane group; the
+// group's 16 lanes are lanes 16*(tid/16) .. +15 of one wave.
+template <int TB>
+__device__ __forceinline__ void group_logits(const uint16_t* xs, int d,
+                                             const uint16_t* __restrict__ wrow,
+                                             bool ok, float acc[TB]) {
+  const int l = threadIdx.x & 15;
+  const int nchunk = d >> 7;
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt) acc[tt] = 0.0f;
+  for (int c0 = 0; c0 < nchunk; c0 += kWindow) {
+    u32x4 wv[kWindow];
+#pragma unroll
+    for (int q = 0; q < kWindow; ++q)
+      wv[q] = (ok && c0 + q < nchunk) ? *(const u32x4*)(wrow + 128 * (c0 + q) + 8 * l)
+                                      : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < kWindow; ++q) {
+      if (c0 + q >= nchunk) break;
+      const int off = 128 * (c0 + q) + 8 * l;
+#pragma unroll
+      for (int tt = 0; tt < TB; ++tt) {
+        const u32x4 xv = *(const u32x4*)(xs + tt * d + off);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          acc[tt] = fmaf(lo_bf16(xv[p]), lo_bf16(wv[q][p]), acc[tt]);
+          acc[tt] = fmaf(hi_bf16(xv[p]), hi_bf16(wv[q][p]), acc[tt]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt) {
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) acc[tt] = acc[tt] + __shfl_xor(acc[tt], o, kWave);
+  }
+}
+
+// Many tokens: 8 per 256-thread block, 16 lane groups over the experts.
+__global__ __launch_bounds__(256) void route_tb8(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int T, int d, int E, int k,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  constexpr int TB = 8;
+  extern __shared__ float lds[];
+  float* logit_sh = lds;                               // [TB][E]
+  uint16_t* xs = (uint16_t*)(lds + TB * E);            // [TB][d]
+  const int t0 = blockIdx.x * TB;
+  stage_x<TB, 256>(x, T, d, t0, xs);
+  __syncthreads();
+  const int G = threadIdx.x >> 4, l = threadIdx.x & 15;
+  const int n_iter = (E + 15) >> 4;  // uniform trip count (shuffles inside)
+  for (int it = 0; it < n_iter; ++it) {
+    const int e = G + 16 * it;
+    const bool ok = e < E;
+    float acc[TB];
+    group_logits<TB>(xs, d, wr + (size_t)(ok ? e : 0) * d, ok, acc);
+    if (ok && l == 0) {
+      const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+      for (int tt = 0; tt < TB; ++tt) logit_sh[tt * E + e] = acc[tt] + b;
+    }
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  for (int tt = wave; tt < TB; tt += 4) {
+    const int t = t0 + tt;
+    if (t >= T) break;
+    select_topk(logit_sh + tt * E, E, k, topk_idx + (size_t)t * k,
+                topk_w + (size_t)t * k);
+  }
+}
+
+// Few tokens: one token per 1024-thread block, 64 lane groups.
+__global__ __launch_bounds__(1024) void route_tb1(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int T, int d, int E, int k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   extern __shared__ float lds[];
-  float* logit_sh = lds;                            // [kTokPerBlock][E]
-
-  const int tid = threadIdx.x;
-  const int G = tid >> 4, l = tid & 15;
-  const int t0 = blockIdx.x * kTokPerBlock;
-  const int nchunk = d >> 7;
-
-  const int n_iter = (E + 15) >> 4;  // uniform trip count for the shuffles
+  float* logit_sh = lds;                          // [E]
+  uint16_t* xs = (uint16_t*)(lds + ((E + 3) & ~3));  // [d], 16-byte aligned
+  const int t = blockIdx.x;
+  stage_x<1, 1024>(x, T, d, t, xs);
+  __syncthreads();
+  const int G = threadIdx.x >> 4, l = threadIdx.x & 15;
+  const int n_iter = (E + 63) >> 6;
   for (int it = 0; it < n_iter; ++it) {
-    const int e = G + 16 * it;
+    const int e = G + 64 * it;
     const bool ok = e < E;
-    const uint16_t* wrow = wr + (size_t)(ok ? e : 0) * d + 8 * l;
-    float acc[kTokPerBlock];
-#pragma unroll
-    for (int tt = 0; tt < kTokPerBlock; ++tt) acc[tt] = 0.0f;
-    for (int c = 0; c < nchunk; ++c) {
-      const u32x4 wv = *(const u32x4*)(wrow + 128 * c);
-      float wf[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        wf[2 * q] = __uint_as_float(wv[q] << 16);
-        wf[2 * q + 1] = __uint_as_float(wv[q] & 0xFFFF0000u);
-      }
-#pragma unroll
-      for (int tt = 0; tt < kTokPerBlock; ++tt) {
-        u32x4 xv = {0u, 0u, 0u, 0u};
-        if (t0 + tt < T)
-          xv = *(const u32x4*)(x + (size_t)(t0 + tt) * d + 128 * c + 8 * l);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          // bf16 * bf16 is exact in fp32, so fma == multiply-then-add here
-          acc[tt] = fmaf(__uint_as_float(xv[q] << 16), wf[2 * q], acc[tt]);
-          acc[tt] = fmaf(__uint_as_float(xv[q] & 0xFFFF0000u), wf[2 * q + 1],
-                         acc[tt]);
-        }
-      }
-    }
-#pragma unroll
-    for (int tt = 0; tt < kTokPerBlock; ++tt) {
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) acc[tt] = acc[tt] + __shfl_xor(acc[tt], o, kWave);
-    }
-    if (ok && l == 0) {
-      const float b = bias ? bias[e] : 0.0f;
-#pragma unroll
-      for (int tt = 0; tt < kTokPerBlock; ++tt) logit_sh[tt * E + e] = acc[tt] + b;
-    }
+    float acc[1];
+    group_logits<1>(xs, d, wr + (size_t)(ok ? e : 0) * d, ok, acc);
+    if (ok && l == 0) logit_sh[e] = acc[0] + (bias ? bias[e] : 0.0f);
   }
   __syncthreads();
-
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int tt = wave; tt < kTokPerBlock; tt += kThreads / kWave) {
-    const int t = t0 + tt;
-    if (t >= T) break;
-    const float* lg = logit_sh + tt * E;
-    uint32_t taken = 0;
-    float m = 0.0f, ssum = 0.0f, my_ex = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      float bv = -FLT_MAX;
-      int be = kInvalid;
-      for (int i = 0; 64 * i + lane < E; ++i) {
-        const int e = 64 * i + lane;
-        if (!((taken >> i) & 1u) && better(lg[e], e, bv, be)) {
-          bv = lg[e];
-          be = e;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, kWave);
-        const int oe = __shfl_xor(be, o, kWave);
-        if (better(ov, oe, bv, be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      // every lane now holds the rank-(j+1) expert (bv, be)
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      if (j == 0) m = bv;
-      const float ex = expf(bv - m);  // softmax over the selected logits
-      ssum += ex;                      // rank order, identical in all lanes
-      if (lane == j) {
-        my_ex = ex;
-        topk_idx[(size_t)t * k + j] = be;
-      }
-    }
-    if (lane < k) topk_w[(size_t)t * k + lane] = my_ex / ssum;
-  }
+  if (threadIdx.x < 64)
+    select_topk(logit_sh, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
 }
 
 }  // namespace
@@ -130,11 +191,16 @@ hipError_t launch_route(const void* x, const void* wr, const float* bias,
                         int T, int d, int E, int k, int32_t* topk_idx,
                         float* topk_w, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int blocks = (T + kTokPerBlock - 1) / kTokPerBlock;
-  const size_t lds = sizeof(float) * (size_t)kTokPerBlock * E;
-  hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(kThreads), lds, s,
-                     (const uint16_t*)x, (const uint16_t*)wr, bias, T, d, E,
-                     k, topk_idx, topk_w);
+  if (T <= 512) {
+    const size_t lds = sizeof(float) * ((E + 3) & ~3) + sizeof(uint16_t) * d;
+    hipLaunchKernelGGL(route_tb1, dim3(T), dim3(1024), lds, s, (const uint16_t*)x,
+                       (const uint16_t*)wr, bias, T, d, E, k, topk_idx, topk_w);
+  } else {
+    const size_t lds = sizeof(float) * 8 * E + sizeof(uint16_t) * 8 * d;
+    hipLaunchKernelGGL(route_tb8, dim3((T + 7) / 8), dim3(256), lds, s,
+                       (const uint16_t*)x, (const uint16_t*)wr, bias, T, d, E, k,
+                       topk_idx, topk_w);
+  }
   return hipGetLastError();
 }
 
