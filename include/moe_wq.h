@@ -108,11 +108,15 @@ const char *moe_last_error(void);
  *   wr     bf16 [E][d] (router matrix stored expert-major), 16-byte aligned.
  *   bias   fp32 [E] logit bias, or NULL.
  *   topk_idx int32 [T][k]; topk_w fp32 [T][k]  (outputs).
+ *   ws / ws_bytes: workspace of at least moe_route_ws_bytes(T, E) bytes
+ *     (small batches keep the fp32 logits there; may be 0 bytes / NULL
+ *     when the query returns 0).
  * Requires d % 128 == 0, d <= 8192, 1 <= k <= min(E, 16), E <= 512.
  * ------------------------------------------------------------------- */
+size_t moe_route_ws_bytes(int T, int E);
 int moe_route(const void *x_bf16, const void *wr_bf16, const float *bias,
               int T, int d, int E, int k, int32_t *topk_idx, float *topk_w,
-              void *stream);
+              void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------
  * moe_permute -- group the P = T*k token-expert pairs by expert.

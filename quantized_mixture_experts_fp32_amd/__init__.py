@@ -24,7 +24,8 @@ MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
 MOE_GROUP = 128
 
 # Every symbol the header declares (checked by the CPU tests).
-EXPORTS = ("moe_status_str", "moe_last_error", "moe_route", "moe_permute_ws_bytes",
+EXPORTS = ("moe_status_str", "moe_last_error", "moe_route_ws_bytes", "moe_route",
+           "moe_permute_ws_bytes",
            "moe_permute", "moe_ffn_ws_bytes", "moe_expert_ffn_wq", "moe_combine",
            "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events")
 
@@ -50,7 +51,8 @@ def load_library():
     i32, vp, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
     lib.moe_status_str.argtypes, lib.moe_status_str.restype = [i32], ctypes.c_char_p
     lib.moe_last_error.argtypes, lib.moe_last_error.restype = [], ctypes.c_char_p
-    lib.moe_route.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.moe_route_ws_bytes.argtypes, lib.moe_route_ws_bytes.restype = [i32, i32], sz
+    lib.moe_route.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.moe_permute_ws_bytes.argtypes, lib.moe_permute_ws_bytes.restype = [i32, i32, i32], sz
     lib.moe_permute.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.moe_ffn_ws_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -94,7 +96,11 @@ def _empty(shape, dtype, like):
 
 
 # ----------------------------------------------------------------- the ABI
-def moe_route(x, wr, bias, k, topk_idx=None, topk_w=None, stream=None):
+def moe_route_ws_bytes(T, E):
+    return int(load_library().moe_route_ws_bytes(T, E))
+
+
+def moe_route(x, wr, bias, k, topk_idx=None, topk_w=None, ws=None, stream=None):
     """x bf16 [T][d], wr bf16 [E][d], bias fp32 [E] or None -> (idx, w)."""
     import torch
     T, d = x.shape
@@ -103,9 +109,11 @@ def moe_route(x, wr, bias, k, topk_idx=None, topk_w=None, stream=None):
         topk_idx = _empty((T, k), torch.int32, x)
     if topk_w is None:
         topk_w = _empty((T, k), torch.float32, x)
+    if ws is None:
+        ws = _empty((max(moe_route_ws_bytes(T, E), 16),), torch.uint8, x)
     _check("moe_route", load_library().moe_route(
         _ptr(x), _ptr(wr), _ptr(bias), T, d, E, k, _ptr(topk_idx), _ptr(topk_w),
-        _stream(stream)))
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return topk_idx, topk_w
 
 
@@ -234,6 +242,8 @@ class MoeLayer:
         self.offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
         self.sorted_pair = torch.empty((P,), dtype=torch.int32, device=dev)
         self.pair_pos = torch.empty((P,), dtype=torch.int32, device=dev)
+        self.ws_route = torch.empty((max(moe_route_ws_bytes(T, E), 16),),
+                                    dtype=torch.uint8, device=dev)
         self.ws_perm = torch.empty((max(moe_permute_ws_bytes(T, k, E), 16),),
                                    dtype=torch.uint8, device=dev)
         self.ws_ffn = torch.empty((max(moe_ffn_ws_bytes(T, k, E, d, f, self.fmt), 256),),
@@ -248,7 +258,8 @@ class MoeLayer:
             self._alloc(T, x)
         gu, gus, dn, dns = weights if weights is not None else (
             self.gu, self.gus, self.dn, self.dns)
-        moe_route(x, self.wr, self.bias, self.k, self.topk_idx, self.topk_w, stream)
+        moe_route(x, self.wr, self.bias, self.k, self.topk_idx, self.topk_w,
+                  self.ws_route, stream)
         moe_permute(self.topk_idx, self.E, self.ws_perm, self.offsets,
                     self.sorted_pair, self.pair_pos, stream)
         moe_expert_ffn_wq(x, self.offsets, self.sorted_pair, self.k, self.f, gu, gus,

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmoe_wq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["abi.cpp", "route.hip", "permute.hip", "quant.hip", "ffn.hip",
-           "ffn_decode.hip", "combine.hip"]
+           "ffn_decode.hip", "ffn_prefill.hip", "combine.hip"]
 # Packed fp32 VALU instructions stay disabled in every HIP build here.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Wall", "-Wno-unused-result", "-Xclang", "-target-feature",

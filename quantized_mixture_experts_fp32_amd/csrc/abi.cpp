@@ -65,19 +65,28 @@ const char* moe_status_str(int status) {
 
 const char* moe_last_error(void) { return g_err; }
 
+size_t moe_route_ws_bytes(int T, int E) {
+  if (T < 0 || E <= 0) return 0;
+  return moe::route_ws_bytes(T, E);
+}
+
 int moe_route(const void* x_bf16, const void* wr_bf16, const float* bias,
               int T, int d, int E, int k, int32_t* topk_idx, float* topk_w,
-              void* stream) {
+              void* ws, size_t ws_bytes, void* stream) {
   int rc = check_dims(T, d, E, k);
   if (rc) return rc;
   if (T == 0) return ok();
   if (!x_bf16 || !wr_bf16 || !topk_idx || !topk_w)
     return fail(MOE_ERR_INVALID_ARG, "moe_route: null pointer");
+  const size_t need = moe::route_ws_bytes(T, E);
+  if (need && (!ws || ws_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu bytes",
+                ws ? ws_bytes : (size_t)0, need);
   if (!aligned(x_bf16, 16) || !aligned(wr_bf16, 16) || !aligned(topk_idx, 4) ||
-      !aligned(topk_w, 4) || (bias && !aligned(bias, 4)))
+      !aligned(topk_w, 4) || (bias && !aligned(bias, 4)) || (need && !aligned(ws, 16)))
     return fail(MOE_ERR_INVALID_ARG, "moe_route: misaligned pointer");
   return hip_status(moe::launch_route(x_bf16, wr_bf16, bias, T, d, E, k,
-                                      topk_idx, topk_w, (hipStream_t)stream),
+                                      topk_idx, topk_w, ws, (hipStream_t)stream),
                     "moe_route");
 }
 

@@ -419,21 +419,23 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// Workspace: [256 B header | tile list | h bf16 [P][f] | prefill scratch]
 size_t ffn_ws_bytes(int T, int k, int E, int d, int f, int format) {
-  (void)d;
   (void)format;
   const long long P = (long long)T * k;
   const size_t mt = max_tiles(P, E, 16);  // smallest tile -> most tiles
-  return 256 + align256(mt * sizeof(Tile)) + align256((size_t)P * f * 2);
+  return 256 + align256(mt * sizeof(Tile)) + align256((size_t)P * f * 2) +
+         ffn_prefill_ws_bytes(T, k, E, d, f);
 }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   const long long P = (long long)a.T * a.k;
   if (P == 0) return hipSuccess;
-  if (a.format == 0 && a.path == 1) {
-    uint16_t* h = (uint16_t*)((char*)a.ws + 256 +
-                              align256(max_tiles(P, a.E, 16) * sizeof(Tile)));
-    return launch_ffn_decode_w4(a, h, s);
+  uint16_t* h = (uint16_t*)((char*)a.ws + 256 + align256(max_tiles(P, a.E, 16) * sizeof(Tile)));
+  if (a.format == 0 && a.path == 1) return launch_ffn_decode_w4(a, h, s);
+  if (a.format == 0 && a.path == 2) {
+    void* pws = (char*)h + align256((size_t)P * a.f * 2);
+    return launch_ffn_prefill_w4(a, h, pws, s);
   }
   if (a.path == 2) return run_ffn<4>(a, s);
   return run_ffn<2>(a, s);

@@ -8,9 +8,10 @@
 
 namespace moe {
 
+size_t route_ws_bytes(int T, int E);
 hipError_t launch_route(const void* x, const void* wr, const float* bias,
                         int T, int d, int E, int k, int32_t* topk_idx,
-                        float* topk_w, hipStream_t s);
+                        float* topk_w, void* ws, hipStream_t s);
 
 size_t permute_ws_bytes(int T, int k, int E);
 hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int E,
@@ -41,6 +42,9 @@ size_t ffn_ws_bytes(int T, int k, int E, int d, int f, int format);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 // decode path for int4 experts (ffn_decode.hip); h = bf16 [P][f] scratch
 hipError_t launch_ffn_decode_w4(const FfnArgs& a, uint16_t* h, hipStream_t s);
+// prefill path for int4 experts (ffn_prefill.hip); ws: its own scratch
+size_t ffn_prefill_ws_bytes(int T, int k, int E, int d, int f);
+hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStream_t s);
 
 hipError_t launch_combine(const float* y, const int32_t* pair_pos,
                           const float* topk_w, int T, int k, int d, void* out,

@@ -8,10 +8,11 @@
 //   are combined with acc_l += acc_(l xor o) for o = 8, 4, 2, 1; the logit
 //   is acc_0 + bias[e].  bf16 * bf16 products are exact in fp32, so fma and
 //   multiply-then-add give the same sums.
-// Two launch shapes share that order: one token per 1024-thread block (64
-// lane groups, few tokens) and eight tokens per 256-thread block (16 lane
-// groups, many tokens).  Activation rows are staged in LDS; router rows are
-// streamed with up to 16 outstanding 16-byte loads per lane.
+// Two launch shapes share that order: for few tokens, (token, 16 experts)
+// blocks write logits to the workspace and a second launch selects the
+// top-k (many blocks even for one token); for many tokens, eight tokens per
+// 256-thread block with the top-k fused.  Activation rows are staged in LDS;
+// router rows are streamed with up to 16 outstanding 16-byte loads per lane.
 #include <float.h>
 
 #include "kcommon.hpp"
@@ -160,41 +161,55 @@ __global__ __launch_bounds__(256) void route_tb8(
   }
 }
 
-// Few tokens: one token per 1024-thread block, 64 lane groups.
-__global__ __launch_bounds__(1024) void route_tb1(
+// Few tokens: block (token, 16 experts) with one lane group per expert
+// writes fp32 logits to the workspace; a second launch selects the top-k.
+constexpr int kSmallT = 512;
+
+__global__ __launch_bounds__(256) void route_logits_small(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-    const float* __restrict__ bias, int T, int d, int E, int k,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
-  extern __shared__ float lds[];
-  float* logit_sh = lds;                          // [E]
-  uint16_t* xs = (uint16_t*)(lds + ((E + 3) & ~3));  // [d], 16-byte aligned
-  const int t = blockIdx.x;
-  stage_x<1, 1024>(x, T, d, t, xs);
+    const float* __restrict__ bias, int T, int d, int E,
+    float* __restrict__ logits) {
+  extern __shared__ uint16_t xs[];  // [d]
+  const int neb = (E + 15) >> 4;
+  const int t = blockIdx.x / neb, eb = blockIdx.x % neb;
+  stage_x<1, 256>(x, T, d, t, xs);
   __syncthreads();
   const int G = threadIdx.x >> 4, l = threadIdx.x & 15;
-  const int n_iter = (E + 63) >> 6;
-  for (int it = 0; it < n_iter; ++it) {
-    const int e = G + 64 * it;
-    const bool ok = e < E;
-    float acc[1];
-    group_logits<1>(xs, d, wr + (size_t)(ok ? e : 0) * d, ok, acc);
-    if (ok && l == 0) logit_sh[e] = acc[0] + (bias ? bias[e] : 0.0f);
-  }
-  __syncthreads();
-  if (threadIdx.x < 64)
-    select_topk(logit_sh, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+  const int e = 16 * eb + G;
+  const bool ok = e < E;
+  float acc[1];
+  group_logits<1>(xs, d, wr + (size_t)(ok ? e : 0) * d, ok, acc);
+  if (ok && l == 0) logits[(size_t)t * E + e] = acc[0] + (bias ? bias[e] : 0.0f);
+}
+
+__global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logits,
+                                                  int T, int E, int k,
+                                                  int32_t* __restrict__ topk_idx,
+                                                  float* __restrict__ topk_w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  select_topk(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
+              topk_w + (size_t)t * k);
 }
 
 }  // namespace
 
+size_t route_ws_bytes(int T, int E) {
+  return T <= kSmallT ? sizeof(float) * (size_t)T * E : 0;
+}
+
 hipError_t launch_route(const void* x, const void* wr, const float* bias,
                         int T, int d, int E, int k, int32_t* topk_idx,
-                        float* topk_w, hipStream_t s) {
+                        float* topk_w, void* ws, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (T <= 512) {
-    const size_t lds = sizeof(float) * ((E + 3) & ~3) + sizeof(uint16_t) * d;
-    hipLaunchKernelGGL(route_tb1, dim3(T), dim3(1024), lds, s, (const uint16_t*)x,
-                       (const uint16_t*)wr, bias, T, d, E, k, topk_idx, topk_w);
+  if (T <= kSmallT) {
+    float* logits = (float*)ws;
+    const int neb = (E + 15) / 16;
+    hipLaunchKernelGGL(route_logits_small, dim3(T * neb), dim3(256),
+                       sizeof(uint16_t) * d, s, (const uint16_t*)x, (const uint16_t*)wr,
+                       bias, T, d, E, logits);
+    hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k,
+                       topk_idx, topk_w);
   } else {
     const size_t lds = sizeof(float) * 8 * E + sizeof(uint16_t) * 8 * d;
     hipLaunchKernelGGL(route_tb8, dim3((T + 7) / 8), dim3(256), lds, s,

@@ -51,17 +51,23 @@ def err(lib):
 
 
 def test_route_validation(lib):
-    r = lib.moe_route
-    assert r(FAKE, FAKE, NULL, 4, 200, 8, 2, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
+    def r(x, w, b, T, d, E, k, i, tw, ws=FAKE, wsb=1 << 20):
+        return lib.moe_route(x, w, b, T, d, E, k, i, tw, ws, wsb, NULL)
+    assert r(FAKE, FAKE, NULL, 4, 200, 8, 2, FAKE, FAKE) == moe.MOE_ERR_UNSUPPORTED
     assert "128" in err(lib)
-    assert r(FAKE, FAKE, NULL, 4, 256, 8, 9, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID_ARG
-    assert r(FAKE, FAKE, NULL, 4, 256, 600, 2, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
-    assert r(FAKE, FAKE, NULL, 4, 256, 64, 17, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
-    assert r(NULL, FAKE, NULL, 4, 256, 8, 2, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID_ARG
-    assert r(ODD, FAKE, NULL, 4, 256, 8, 2, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID_ARG
-    assert r(FAKE, FAKE, NULL, -1, 256, 8, 2, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert r(FAKE, FAKE, NULL, 4, 256, 8, 9, FAKE, FAKE) == moe.MOE_ERR_INVALID_ARG
+    assert r(FAKE, FAKE, NULL, 4, 256, 600, 2, FAKE, FAKE) == moe.MOE_ERR_UNSUPPORTED
+    assert r(FAKE, FAKE, NULL, 4, 256, 64, 17, FAKE, FAKE) == moe.MOE_ERR_UNSUPPORTED
+    assert r(FAKE, FAKE, NULL, 4, 256 * 33, 64, 8, FAKE, FAKE) == moe.MOE_ERR_UNSUPPORTED
+    assert r(NULL, FAKE, NULL, 4, 256, 8, 2, FAKE, FAKE) == moe.MOE_ERR_INVALID_ARG
+    assert r(ODD, FAKE, NULL, 4, 256, 8, 2, FAKE, FAKE) == moe.MOE_ERR_INVALID_ARG
+    assert r(FAKE, FAKE, NULL, -1, 256, 8, 2, FAKE, FAKE) == moe.MOE_ERR_INVALID_ARG
+    need = lib.moe_route_ws_bytes(4, 8)
+    assert need >= 4 * 8 * 4
+    assert r(FAKE, FAKE, NULL, 4, 256, 8, 2, FAKE, FAKE, FAKE, need - 1) == moe.MOE_ERR_WORKSPACE
+    assert r(FAKE, FAKE, NULL, 4, 256, 8, 2, FAKE, FAKE, NULL, need) == moe.MOE_ERR_WORKSPACE
     # T = 0 is a valid no-op, even with null pointers
-    assert r(NULL, NULL, NULL, 0, 256, 8, 2, NULL, NULL, NULL) == moe.MOE_OK
+    assert r(NULL, NULL, NULL, 0, 256, 8, 2, NULL, NULL, NULL, 0) == moe.MOE_OK
 
 
 def test_permute_validation(lib):
