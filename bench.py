@@ -44,6 +44,9 @@ def parse_args():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--workloads", default="",
                     help="comma list of name filters (spaces as _) for secondary workloads")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the workloads, run one plain device-to-device copy "
+                         "of this many MiB (reference dispatch for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -242,19 +245,26 @@ def cpu_baseline(target_s, np, synth, oracle):
                       f"quantization excluded; {el:.1f} s"}
 
 
-def load_traffic(np):
-    """HBM traffic of the dominant kernel from the committed rocprofv3 counter
-    summary, valid only while the kernel source is unchanged."""
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_w4_decode_olmoe_T16.txt")
+DECODE_SRC = os.path.join(ROOT, "quantized_mixture_experts_fp32_amd", "csrc", "ffn_decode.hip")
+
+
+def load_traffic():
+    """HBM bytes per launch of the dominant kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary; None once the kernel source
+    differs from the one the counters were taken on."""
     import hashlib
-    p = os.path.join(ROOT, "profiles", "traffic_gateup_decode.json")
-    if not os.path.exists(p):
+    if not os.path.exists(TRAFFIC_FILE):
         return None
-    rec = json.load(open(p))
-    src = os.path.join(ROOT, "quantized_mixture_experts_fp32_amd", "csrc", "ffn.hip")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if rec.get("ffn_source_sha256_16") != h:
+    rec = {}
+    for ln in open(TRAFFIC_FILE):
+        if "=" in ln and not ln.lstrip().startswith("#"):
+            key, val = ln.split("=", 1)
+            rec[key.strip()] = val.strip()
+    h = hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+    if rec.get("kernel_source_sha256_16") != h:
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return int(float(rec["traffic_bytes_per_launch"]))
 
 
 def main():
@@ -275,6 +285,14 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     hip = Hip()
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     head = Workload("olmoe-decode-w4 T=16", 1, 16, args.steps)
     secondary = [
         Workload("olmoe-decode-w4 T=1", 1, 1, args.steps),
@@ -318,7 +336,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "expert gate/up (moe_expert_ffn_wq)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(np),
+                     "traffic": load_traffic(),
                      "algorithmic_bytes_per_launch": head_rec["gateup_bytes_avg"],
                      "avg_launch_us": head_rec["gateup_us"]},
         "cpu_baseline": base,
