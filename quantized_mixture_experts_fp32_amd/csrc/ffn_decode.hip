@@ -391,6 +391,170 @@ void down_w4_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
   }
 }
 
+
+// ------------------------------------------- single K slice, one token tile
+// When every wave streams the whole K range of its own 16-feature row tile
+// (KS = 1, tiles of up to 16 pairs), the four waves of a block share one
+// token tile.  The block then stages each 128-group of the tile's
+// activation rows in LDS once (one 16-byte piece per thread, permuted to
+// the conversion's K order on the way), and the waves read their B
+// fragments from there.  Compared with per-wave activation loads this cuts
+// activation registers by four, takes the permutation out of the per-wave
+// loop, and leaves the global-load counter to the codes alone, so the code
+// stream can run kDQ groups ahead of the MFMAs.  The arithmetic (operands,
+// MFMA order, scaling) is the same as in the kernels above.
+constexpr int kXRow = 136;  // bf16 per staged activation row (128 + 8 pad)
+
+template <int kDQ, int kWaves>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
+void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
+                          const int32_t* __restrict__ sorted_pair, int E, int k, int P,
+                          int d, int f, const uint8_t* __restrict__ codes,
+                          const uint16_t* __restrict__ scales, uint16_t* __restrict__ h) {
+  extern __shared__ int32_t lds_i[];
+  const int G = d >> 7, RG = f / 64;
+  int32_t* off_lds = lds_i;
+  int32_t* sp_lds = lds_i + ((E + 1 + 3) & ~3);
+  float* sc_lds = (float*)(sp_lds + ((min(P, kPairsInLds) + 3) & ~3));  // [2][G][64]
+  uint16_t* xs = (uint16_t*)(sc_lds + 2 * G * 64);                      // [2][16][kXRow]
+  const int np = stage_routing(offsets, sorted_pair, E, P, off_lds, sp_lds);
+  __syncthreads();
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int st_tok = tid >> 4, st_pc = tid & 15;  // staged row and 16-byte piece
+  const bf16x8 neg24 = bf16_splat(kBf16Neg24);
+
+  for (int w = blockIdx.x;; w += gridDim.x) {
+    TileInfo tl;
+    if (!find_tile(off_lds, E, 16, w / RG, tl)) break;
+    const int nb = (w % RG) * 64, n0 = nb + 16 * wave;
+    const size_t erow = (size_t)tl.e * 2 * f;
+    const bool st_ok = st_tok < tl.cnt;
+    const int sj = tl.r0 + (st_ok ? st_tok : 0);
+    const int sp = np ? sp_lds[sj] : sorted_pair[sj];
+    const uint16_t* xsrc = x + (size_t)(sp / k) * d + 8 * st_pc;
+    const uint8_t* cg = codes + (erow + n0 + col) * (size_t)(d >> 1) + 16 * kq;
+    const uint8_t* cu = cg + (size_t)f * (d >> 1);
+
+    u32x4 qg[kDQ], qu[kDQ], xv[kDQ];
+    auto load = [&](int g, int i) {
+      if (st_ok) xv[i] = *(const u32x4*)(xsrc + 128 * g);
+      qg[i] = *(const u32x4*)(cg + 64 * g);
+      qu[i] = *(const u32x4*)(cu + 64 * g);
+    };
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i)
+      if (i < G) load(i, i);
+    // the previous item's last barrier precedes these LDS writes; the first
+    // barrier of the group loop orders them before any read
+    stage_scales_f32(scales + (erow + nb) * G, (size_t)f, 2, 64, G, sc_lds);
+
+    f32x4 tg = {0, 0, 0, 0}, tu = {0, 0, 0, 0};
+    const int rd_tok = col < tl.cnt ? col : 0;  // padded columns re-read row 0
+    for (int g = 0; g < G; g += kDQ) {
+#pragma unroll
+      for (int i = 0; i < kDQ; ++i) {
+        const int gi = g + i;
+        if (gi >= G) break;
+        // slot gi & 1 was last read in iteration gi - 2, before the
+        // barrier of iteration gi - 1
+        uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
+        if (st_ok) *(bf16x8*)(slot + st_tok * kXRow + 8 * st_pc) = x_perm(xv[i]);
+        __syncthreads();
+        bf16x8 xp[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xp[j] = *(const bf16x8*)(slot + rd_tok * kXRow + 32 * kq + 8 * j);
+        const f32x4 sg = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
+        const f32x4 su = *(const f32x4*)(sc_lds + (G + gi) * 64 + 16 * wave + 4 * kq);
+        f32x4 seed = {0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) seed = mfma16(neg24, xp[j], seed);
+        const u32x4 a = qg[i], b = qu[i];
+        if (gi + kDQ < G) load(gi + kDQ, i);
+        tile_group(xp, seed, a, sg, tg);
+        tile_group(xp, seed, b, su, tu);
+      }
+    }
+    if (col < tl.cnt) {
+      uint32_t hb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_rne(silu_f32(tg[i]) * tu[i]);
+      uint2 pk;
+      pk.x = hb[0] | (hb[1] << 16);
+      pk.y = hb[2] | (hb[3] << 16);
+      *(uint2*)(h + (size_t)(tl.r0 + col) * f + n0 + 4 * kq) = pk;
+    }
+    __syncthreads();  // the next item rewrites the scales and the slots
+  }
+}
+
+template <int kDQ, int kWaves>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
+void down_w4_decode_lds(const uint16_t* __restrict__ h, const int32_t* __restrict__ offsets,
+                        int E, int d, int f, const uint8_t* __restrict__ codes,
+                        const uint16_t* __restrict__ scales, float* __restrict__ y) {
+  extern __shared__ int32_t lds_i[];
+  const int G = f >> 7, RG = d / 64;
+  int32_t* off_lds = lds_i;
+  float* sc_lds = (float*)(lds_i + ((E + 1 + 3) & ~3));  // [G][64]
+  uint16_t* xs = (uint16_t*)(sc_lds + G * 64);           // [2][16][kXRow]
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) off_lds[i] = offsets[i];
+  __syncthreads();
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int st_tok = tid >> 4, st_pc = tid & 15;
+  const bf16x8 neg24 = bf16_splat(kBf16Neg24);
+
+  for (int w = blockIdx.x;; w += gridDim.x) {
+    TileInfo tl;
+    if (!find_tile(off_lds, E, 16, w / RG, tl)) break;
+    const int mb = (w % RG) * 64, m0 = mb + 16 * wave;
+    const size_t erow = (size_t)tl.e * d;
+    const bool st_ok = st_tok < tl.cnt;
+    const uint16_t* hsrc = h + (size_t)(tl.r0 + (st_ok ? st_tok : 0)) * f + 8 * st_pc;
+    const uint8_t* cd = codes + (erow + m0 + col) * (size_t)(f >> 1) + 16 * kq;
+
+    u32x4 q[kDQ], hv[kDQ];
+    auto load = [&](int g, int i) {
+      if (st_ok) hv[i] = *(const u32x4*)(hsrc + 128 * g);
+      q[i] = *(const u32x4*)(cd + 64 * g);
+    };
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i)
+      if (i < G) load(i, i);
+    stage_scales_f32(scales + (erow + mb) * G, 0, 1, 64, G, sc_lds);
+
+    f32x4 acc = {0, 0, 0, 0};
+    const int rd_tok = col < tl.cnt ? col : 0;
+    for (int g = 0; g < G; g += kDQ) {
+#pragma unroll
+      for (int i = 0; i < kDQ; ++i) {
+        const int gi = g + i;
+        if (gi >= G) break;
+        uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
+        if (st_ok) *(bf16x8*)(slot + st_tok * kXRow + 8 * st_pc) = x_perm(hv[i]);
+        __syncthreads();
+        bf16x8 xp[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xp[j] = *(const bf16x8*)(slot + rd_tok * kXRow + 32 * kq + 8 * j);
+        const f32x4 sv = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
+        f32x4 seed = {0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) seed = mfma16(neg24, xp[j], seed);
+        const u32x4 a = q[i];
+        if (gi + kDQ < G) load(gi + kDQ, i);
+        tile_group(xp, seed, a, sv, acc);
+      }
+    }
+    if (col < tl.cnt) *(f32x4*)(y + (size_t)(tl.r0 + col) * d + m0 + 4 * kq) = acc;
+    __syncthreads();
+  }
+}
+
 // kDepth: 128-groups of codes + activations in flight per wave; kWaves:
 // the occupancy the register allocation is held to (measured on MI355X:
 // occupancy matters more than prefetch depth, and spilling variants lose).
@@ -430,6 +594,39 @@ void launch_decode_pair(const FfnArgs& a, uint16_t* h, long long P, hipStream_t 
   }
 }
 
+
+// Code groups in flight and occupancy of the LDS-staged kernels (measured
+// on MI355X: deeper code prefetch in gate/up costs the fourth wave).
+constexpr int kGuDQ = 2, kGuWaves = 4, kDnDQ = 4, kDnWaves = 4;
+
+void launch_decode_lds(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
+  const long long mt = (P + 15) / 16 + (P < a.E ? P : a.E);
+  const size_t off_b = sizeof(int32_t) * ((a.E + 1 + 3) & ~3);
+  const size_t xs_b = sizeof(uint16_t) * 2 * 16 * kXRow;
+  const long long cap = 256LL * 8;
+  {
+    const int G = a.d / 128;
+    const long long work = mt * (a.f / 64);
+    const int grid = (int)(work < cap ? work : cap);
+    const size_t lds = off_b + sizeof(int32_t) * ((std::min<long long>(P, kPairsInLds) + 3) & ~3) +
+                       sizeof(float) * 2 * G * 64 + xs_b;
+    if (a.ev[0]) hipEventRecord(a.ev[0], s);
+    hipLaunchKernelGGL((gateup_w4_decode_lds<kGuDQ, kGuWaves>), dim3(grid), dim3(256), lds, s,
+                       a.x, a.offsets, a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes,
+                       a.gu_scales, h);
+    if (a.ev[1]) hipEventRecord(a.ev[1], s);
+  }
+  {
+    const int G = a.f / 128;
+    const long long work = mt * (a.d / 64);
+    const int grid = (int)(work < cap ? work : cap);
+    const size_t lds = off_b + sizeof(float) * G * 64 + xs_b;
+    if (a.ev[2]) hipEventRecord(a.ev[2], s);
+    hipLaunchKernelGGL((down_w4_decode_lds<kDnDQ, kDnWaves>), dim3(grid), dim3(256), lds, s, h,
+                       a.offsets, a.E, a.d, a.f, a.dn_codes, a.dn_scales, a.y);
+    if (a.ev[3]) hipEventRecord(a.ev[3], s);
+  }
+}
 }  // namespace
 
 // Split K over 1, 2 or 4 waves so that few active experts (a single
@@ -447,7 +644,7 @@ hipError_t launch_ffn_decode_w4(const FfnArgs& a, uint16_t* h, hipStream_t s) {
   } else {
     if (KS == 4) launch_decode_pair<4, 1>(a, h, P, s);
     else if (KS == 2) launch_decode_pair<2, 1>(a, h, P, s);
-    else launch_decode_pair<1, 1>(a, h, P, s);
+    else launch_decode_lds(a, h, P, s);
   }
   return hipGetLastError();
 }

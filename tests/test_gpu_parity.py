@@ -227,6 +227,19 @@ def test_layer_ragged_tiles(path):
     check_layer(DevLayer(cfg, 100), HostLayer(cfg, 100), path)
 
 
+def test_layer_decode_single_slice_ragged():
+    # the decode kernels that stage activations in LDS (one K slice per wave,
+    # tiles of up to 16 pairs): group counts 3 (gate/up) and 13 (down) that
+    # are not multiples of the code prefetch depth, skewed routing so that
+    # some experts span several tiles with a ragged last tile
+    cfg = custom_cfg(14, d=384, E=128, k=4, f=1664, bias_sigma=2.0)
+    note("layer custom single-slice decode T=32")
+    dl, hl = DevLayer(cfg, 32), HostLayer(cfg, 32)
+    lay, _ = check_layer(dl, hl, moe.MOE_PATH_DECODE)
+    cnt = np.diff(lay.offsets.cpu().numpy())
+    assert cnt.max() > 16 and (cnt % 16 != 0).any()
+
+
 def test_layer_all_pairs_one_expert_and_empty_experts():
     cfg = custom_cfg(12, d=128, E=16, k=2, f=128, bias_sigma=30.0)
     note("layer skew: bias 30 sigma -> nearly all pairs on two experts")
