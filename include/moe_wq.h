@@ -154,12 +154,17 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E,
  * bf16 MFMA exactly and the fp16 scale multiplies each 128-group partial sum
  * in fp32.
  * Weight layouts (K = input dimension, contiguous; groups of 128 along K):
- *   MOE_FMT_W4_SYM:
- *     gate_up_codes u8 [E][2f][d/2]: rows 0..f-1 gate, f..2f-1 up; byte j of
- *       a row holds element 2j in the low nibble and 2j+1 in the high nibble,
- *       two's complement in [-7, 7].
- *     gate_up_scales fp16 [E][2f][d/128];  down_codes u8 [E][d][f/2];
- *     down_scales fp16 [E][d][f/128].
+ *   MOE_FMT_W4_SYM (codes tiled for streaming, as moe_quantize_w4 writes
+ *   them): a matrix of R rows (R = E*2f gate/up, E*d down; rows of expert e
+ *   start at e*2f resp. e*d; gate rows 0..f-1 then up rows f..2f-1 of each
+ *   expert) and K inputs is stored as u8 [R/16][K/128][16][64]: the codes of
+ *   row n, elements 128g .. 128g+127, are the 64 bytes at
+ *   (((n/16)*(K/128) + g)*16 + n%16)*64; byte j of them holds element
+ *   128g+2j in the low nibble and 128g+2j+1 in the high nibble, two's
+ *   complement in [-7, 7].  (One 16-row tile's group is 1 KiB contiguous.)
+ *     gate_up_codes: R = E*2f, K = d (E*f*d bytes);  gate_up_scales fp16
+ *     [E][2f][d/128];  down_codes: R = E*d, K = f;  down_scales fp16
+ *     [E][d][f/128].
  *   MOE_FMT_BITPLANE8 (u = 8-bit offset code, w ~ s * (u - 128)):
  *     gate_up_codes u8 [E][8][2f][d/8]: plane slab p holds bit 7-p of u
  *       (most significant first: the top b planes are slabs 0..b-1); bit i
@@ -216,8 +221,8 @@ int moe_set_ffn_events(void *gateup_begin, void *gateup_end,
  * w is fp32 [E][N][K] (K = input dimension); groups of 128 along K.
  * moe_quantize_w4 ([ExactMoE] Abstract, symmetric group-128 4-bit):
  *   s = fp16_rne(max|w| / 7) (exact quotient), q = clamp(rne(w / s), -7, 7),
- *   q = 0 when s == 0.  codes u8 [E][N][K/2] (nibble order as above),
- *   scales fp16 [E][N][K/128].
+ *   q = 0 when s == 0.  codes: E*N*K/2 bytes in the tiled int4 layout above
+ *   (R = E*N rows; requires N % 16 == 0), scales fp16 [E][N][K/128].
  * moe_quantize_bitplane8 ([PagedMoE] abstract, bitplane prefixes):
  *   s = fp16_rne(max|w| / 127), u = clamp(rne(w / s) + 128, 0, 255), u = 128
  *   when s == 0.  planes u8 [E][8][N][K/8] (layout as above), scales fp16

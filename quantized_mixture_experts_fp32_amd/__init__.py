@@ -183,7 +183,11 @@ def moe_combine(y_pairs, pair_pos, topk_w, out=None, out_dtype=MOE_OUT_BF16,
 
 
 def moe_quantize_w4(w, codes=None, scales=None, stream=None):
-    """fp32 [E][N][K] -> (codes u8 [E][N][K/2], scales fp16-bits [E][N][K/128])."""
+    """fp32 [E][N][K] -> (codes, scales fp16-bits [E][N][K/128]).
+
+    codes is a u8 tensor of shape [E][N][K/2] holding the tiled int4 layout
+    of include/moe_wq.h (per expert [N/16][K/128][16][64] bytes); N % 16 == 0.
+    """
     import torch
     E, N, K = w.shape
     if codes is None:

@@ -1,12 +1,13 @@
-// Expert SwiGLU FFN over the grouped pairs with in-kernel dequantization.
+// Expert SwiGLU FFN over the grouped pairs with in-kernel dequantization:
+// dispatch of the int4 paths (decode and prefill kernels in their own files)
+// and the kernels for bitplane-prefix experts.
 //  ExactMoE ("Every Expert Counts ...", Abstract): symmetric group-128 W4A16
 //    routed experts, executed by grouped kernels, every pair computed.
 //  PagedMoE (abstract): bitplane prefixes executed directly at the pair's
 //    bit-width, reading only the top planes the expert needs.
 //  MatMoE (abstract): floor-and-compensation dequantization of a prefix.
 //
-// Arithmetic: integer codes (int4 q in [-7,7], or the prefix value v_b in
-// [-128,127]) are exact in bf16 and enter a bf16 MFMA with bf16 activations;
+// Arithmetic (bitplane): the prefix value v_b in [-128,127] is exact in bf16 and enter a bf16 MFMA with bf16 activations;
 // each 128-element group's fp32 partial sum is multiplied by its fp16 scale
 // (exact in fp32) and added to the fp32 accumulator.  Dequantized weights
 // are therefore never rounded.  h = bf16_rne(silu(g) * u).
@@ -85,15 +86,6 @@ __global__ __launch_bounds__(1024) void ffn_prep(
 }
 
 // ---------------------------------------------------------------- weights
-// int4: the lane's 16 code bytes of one group = elements [32kq, 32kq+32)
-// of its row; dword j -> the 8 K-values of MFMA step j (natural order).
-__device__ __forceinline__ void w4_frags(const uint8_t* row, int g, int kq,
-                                         bf16x8 a[4]) {
-  const u32x4 q = *(const u32x4*)(row + 64 * g + 16 * kq);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) a[j] = w4_dword_to_bf16x8(q[j]);
-}
-
 // bitplane: one dword per plane p < maxb holds bit 7-p of the lane's 32
 // elements (bit position = element offset).  For class b the K-values are
 // v_b = (u with 8-b low bits cleared) + 2^(7-b) - 128, or u - 128 for b = 8.
@@ -123,7 +115,7 @@ __device__ __forceinline__ void bp_frags(const uint32_t pl[8], int b,
 }
 
 // -------------------------------------------------------------- gate / up
-template <int NT, bool kBP>
+template <int NT>
 __global__ __launch_bounds__(kThreads) void gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_pair,
     int k, int d, int f, const uint8_t* __restrict__ codes,
@@ -160,9 +152,9 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(
     accu[c] = f32x4{0, 0, 0, 0};
   }
 
-  // classes of bit-width present in the tile (bitplane only)
+  // classes of bit-width present in the tile
   uint32_t cls = 0;
-  if (kBP) {
+  {
 #pragma unroll
     for (int c = 0; c < NT; ++c) cls |= valid[c] ? (1u << tb[c]) : 0u;
 #pragma unroll
@@ -184,23 +176,7 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(
       pg[c] = f32x4{0, 0, 0, 0};
       pu[c] = f32x4{0, 0, 0, 0};
     }
-    if (!kBP) {
-      bf16x8 ag[4], au[4];
-      const size_t rowg = (size_t)tl.e * rows2f + n0 + col;
-      w4_frags(codes + rowg * (d >> 1), g, kq, ag);
-      w4_frags(codes + (rowg + f) * (d >> 1), g, kq, au);
-#pragma unroll
-      for (int c = 0; c < NT; ++c) {
-        if (16 * c >= tl.cnt) break;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x4 xb = {0u, 0u, 0u, 0u};
-          if (valid[c]) xb = *(const u32x4*)(xrow[c] + 128 * g + 32 * kq + 8 * j);
-          pg[c] = mfma16(ag[j], as_bf16x8(xb), pg[c]);
-          pu[c] = mfma16(au[j], as_bf16x8(xb), pu[c]);
-        }
-      }
-    } else {
+    {
       const size_t slab = rows2f * (size_t)(d >> 3);
       const uint8_t* base = codes + (size_t)tl.e * 8 * slab;
       uint32_t plg[8], plu[8];
@@ -267,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(
 }
 
 // ------------------------------------------------------------------- down
-template <int NT, bool kBP>
+template <int NT>
 __global__ __launch_bounds__(kThreads) void down_kernel(
     const uint16_t* __restrict__ h, const int32_t* __restrict__ sorted_pair,
     int k, int d, int f, const uint8_t* __restrict__ codes,
@@ -298,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(
 #pragma unroll
   for (int c = 0; c < NT; ++c) acc[c] = f32x4{0, 0, 0, 0};
   uint32_t cls = 0;
-  if (kBP) {
+  {
 #pragma unroll
     for (int c = 0; c < NT; ++c) cls |= valid[c] ? (1u << tb[c]) : 0u;
 #pragma unroll
@@ -314,20 +290,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(
     f32x4 pa[NT];
 #pragma unroll
     for (int c = 0; c < NT; ++c) pa[c] = f32x4{0, 0, 0, 0};
-    if (!kBP) {
-      bf16x8 a[4];
-      w4_frags(codes + ((size_t)tl.e * d + m0 + col) * (f >> 1), g, kq, a);
-#pragma unroll
-      for (int c = 0; c < NT; ++c) {
-        if (16 * c >= tl.cnt) break;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x4 hb = {0u, 0u, 0u, 0u};
-          if (valid[c]) hb = *(const u32x4*)(hrow[c] + 128 * g + 32 * kq + 8 * j);
-          pa[c] = mfma16(a[j], as_bf16x8(hb), pa[c]);
-        }
-      }
-    } else {
+    {
       const size_t slab = (size_t)d * (size_t)(f >> 3);
       uint32_t pl[8];
       bp_load(codes + (size_t)tl.e * 8 * slab + (size_t)(m0 + col) * (f >> 3),
@@ -389,30 +352,19 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t s) {
   int* num_tiles = (int*)ws;
   Tile* tiles = (Tile*)(ws + 256);
   uint16_t* h = (uint16_t*)(ws + 256 + align256(mt * sizeof(Tile)));
-  const bool bp = a.format == 1;
   hipLaunchKernelGGL(ffn_prep, dim3(1), dim3(1024), 0, s, a.offsets,
-                     a.sorted_pair, a.E, a.k, tok, bp ? a.bits_mode : 0,
+                     a.sorted_pair, a.E, a.k, tok, a.bits_mode,
                      a.bits, tiles, num_tiles);
   dim3 g1((unsigned)mt, a.f / 16), g2((unsigned)mt, a.d / 16);
   if (a.ev[0]) hipEventRecord(a.ev[0], s);
-  if (bp)
-    hipLaunchKernelGGL((gateup_kernel<NT, true>), g1, dim3(kThreads), 0, s,
-                       a.x, a.sorted_pair, a.k, a.d, a.f, a.gu_codes,
-                       a.gu_scales, a.bits_mode, a.bits, tiles, num_tiles, h);
-  else
-    hipLaunchKernelGGL((gateup_kernel<NT, false>), g1, dim3(kThreads), 0, s,
-                       a.x, a.sorted_pair, a.k, a.d, a.f, a.gu_codes,
-                       a.gu_scales, 0, a.bits, tiles, num_tiles, h);
+  hipLaunchKernelGGL((gateup_kernel<NT>), g1, dim3(kThreads), 0, s,
+                     a.x, a.sorted_pair, a.k, a.d, a.f, a.gu_codes,
+                     a.gu_scales, a.bits_mode, a.bits, tiles, num_tiles, h);
   if (a.ev[1]) hipEventRecord(a.ev[1], s);
   if (a.ev[2]) hipEventRecord(a.ev[2], s);
-  if (bp)
-    hipLaunchKernelGGL((down_kernel<NT, true>), g2, dim3(kThreads), 0, s, h,
-                       a.sorted_pair, a.k, a.d, a.f, a.dn_codes, a.dn_scales,
-                       a.bits_mode, a.bits, tiles, num_tiles, a.y);
-  else
-    hipLaunchKernelGGL((down_kernel<NT, false>), g2, dim3(kThreads), 0, s, h,
-                       a.sorted_pair, a.k, a.d, a.f, a.dn_codes, a.dn_scales,
-                       0, a.bits, tiles, num_tiles, a.y);
+  hipLaunchKernelGGL((down_kernel<NT>), g2, dim3(kThreads), 0, s, h,
+                     a.sorted_pair, a.k, a.d, a.f, a.dn_codes, a.dn_scales,
+                     a.bits_mode, a.bits, tiles, num_tiles, a.y);
   if (a.ev[3]) hipEventRecord(a.ev[3], s);
   return hipGetLastError();
 }
@@ -437,6 +389,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
     void* pws = (char*)h + align256((size_t)P * a.f * 2);
     return launch_ffn_prefill_w4(a, h, pws, s);
   }
+  // bitplane prefixes (int4 always resolves to one of the two paths above)
   if (a.path == 2) return run_ffn<4>(a, s);
   return run_ffn<2>(a, s);
 }

@@ -5,13 +5,18 @@
 //  once per token tile with 16-byte loads and are dequantized in registers.
 //
 // Arithmetic.  A code nibble n (two's complement q) is turned into the bf16
-// value 24 + q with one v_bitop3 (exponent of 16 plus (q+8) in the top four
-// mantissa bits); 24 + q is an exact bf16 integer.  The MFMA accumulator of
-// every 128-group starts from -24 * sum(x over the group), produced by four
-// MFMAs with a constant -24 A-operand, so the group's sum is
-// sum((24+q) x) - 24 sum(x) = sum(q x) with fp32 accumulation only.  The
+// value 136 + q with one v_bitop3 (128.0 with q + 8 in the low four
+// mantissa bits); 136 + q is an exact bf16 integer.  The MFMA accumulator of
+// every 128-group starts from -136 * sum(x over the group), produced by four
+// MFMAs with a constant -136 A-operand, so the group's sum is
+// sum((136+q) x) - 136 sum(x) = sum(q x) with fp32 accumulation only.  The
 // fp16 scale then multiplies the group sum (fp32) and the product is added to
 // the running fp32 total.  Dequantized weights are never rounded.
+//
+// Layout.  Codes are stored in 16-row tiles (see the ABI header): lane
+// (col, kq) of a wave reads bytes [16kq, 16kq + 16) of row col of its tile's
+// 128-group, so one wave-wide 16-byte load covers the tile's group, 1 KiB
+// contiguous, and consecutive groups are consecutive kilobytes.
 //
 // K order.  The conversion yields the nibbles of a dword in the order
 // 0,4,1,5,2,6,3,7; the activation fragment is permuted the same way with
@@ -32,7 +37,7 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kTileGroupBytes = 16 * 64;  // one 16-row tile x one 128-group
 
 struct TileInfo {
   int e, r0, cnt;
@@ -73,17 +78,19 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int tok,
   return false;
 }
 
-// 8 nibbles -> bf16 (24 + q) in element order 0,4,1,5,2,6,3,7.
-// bitop3 LUT 0x6A: out = B ? (x ^ D) : D, with B = nibble field (bits 3-6 of
-// each half), D = 0x41C0 per half (exponent bits of 16.0, plus the inversion
-// of the nibble's top bit that maps two's complement q to q + 8).
+// 8 nibbles -> bf16 (136 + q) in element order 0,4,1,5,2,6,3,7.
+// bitop3 LUT 0x6A: out = B ? (x ^ D) : D.  B selects bits 0-3 of each half,
+// the low mantissa bits of 128.0 (whose ulp is 1), where the nibble lands
+// unshifted for elements 0 and 4 and after shifts of 4, 8 and 12 bits for
+// the others; D = 0x4308 per half is 128.0 plus the inversion of the
+// nibble's top bit, which maps two's complement q to q + 8.
 __device__ __forceinline__ bf16x8 w4_magic(uint32_t w) {
-  const uint32_t B = 0x00780078u, D = 0x41C041C0u;
+  const uint32_t B = 0x000F000Fu, D = 0x43084308u;
   u32x4 r;
-  r[0] = __builtin_amdgcn_bitop3_b32(w << 3, B, D, 0x6A);
-  r[1] = __builtin_amdgcn_bitop3_b32(w >> 1, B, D, 0x6A);
-  r[2] = __builtin_amdgcn_bitop3_b32(w >> 5, B, D, 0x6A);
-  r[3] = __builtin_amdgcn_bitop3_b32(w >> 9, B, D, 0x6A);
+  r[0] = __builtin_amdgcn_bitop3_b32(w, B, D, 0x6A);
+  r[1] = __builtin_amdgcn_bitop3_b32(w >> 4, B, D, 0x6A);
+  r[2] = __builtin_amdgcn_bitop3_b32(w >> 8, B, D, 0x6A);
+  r[3] = __builtin_amdgcn_bitop3_b32(w >> 12, B, D, 0x6A);
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -103,7 +110,7 @@ __device__ __forceinline__ bf16x8 bf16_splat(uint32_t bits16) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-constexpr uint32_t kBf16Neg24 = 0xC1C0u;  // -24.0
+constexpr uint32_t kBf16NegOff = 0xC308u;  // -136.0, the conversion offset
 
 
 // The kernels below stage expert_offsets and (when it fits) sorted_pair in
@@ -174,7 +181,7 @@ void gateup_w4_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
   const int rt = wave / KS, ks = wave % KS;
   const int gps = (G + KS - 1) / KS;
   const int gb = ks * gps, ge = min(G, gb + gps);
-  const bf16x8 neg24 = bf16_splat(kBf16Neg24);
+  const bf16x8 negoff = bf16_splat(kBf16NegOff);
 
   for (int w = blockIdx.x;; w += gridDim.x) {
     TileInfo tl;
@@ -195,13 +202,13 @@ void gateup_w4_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
       const int p = np ? sp_lds[tl.r0 + jj] : sorted_pair[tl.r0 + jj];
       xr[c] = x + (size_t)(p / k) * d + 32 * kq;
     }
-    const uint8_t* cg = codes + (erow + n0 + col) * (size_t)(d >> 1) + 16 * kq;
+    const uint8_t* cg = codes + (erow + n0) * (size_t)(d >> 1) + 64 * col + 16 * kq;
     const uint8_t* cu = cg + (size_t)f * (d >> 1);
 
     u32x4 qg[kDepth], qu[kDepth], xv[kDepth][NT][4];
     auto load = [&](int g, u32x4& a, u32x4& b, u32x4 (&v)[NT][4]) {
-      a = *(const u32x4*)(cg + 64 * g);
-      b = *(const u32x4*)(cu + 64 * g);
+      a = *(const u32x4*)(cg + kTileGroupBytes * g);
+      b = *(const u32x4*)(cu + kTileGroupBytes * g);
 #pragma unroll
       for (int c = 0; c < NT; ++c) {
         if (c >= nch) break;
@@ -236,7 +243,7 @@ void gateup_w4_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
           for (int j = 0; j < 4; ++j) xp[j] = x_perm(xv[i][c][j]);
           f32x4 seed = {0, 0, 0, 0};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) seed = mfma16(neg24, xp[j], seed);
+          for (int j = 0; j < 4; ++j) seed = mfma16(negoff, xp[j], seed);
           tile_group(xp, seed, qg[i], sg, tg[c]);
           tile_group(xp, seed, qu[i], su, tu[c]);
         }
@@ -304,7 +311,7 @@ void down_w4_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
   const int rt = wave / KS, ks = wave % KS;
   const int gps = (G + KS - 1) / KS;
   const int gb = ks * gps, ge = min(G, gb + gps);
-  const bf16x8 neg24 = bf16_splat(kBf16Neg24);
+  const bf16x8 negoff = bf16_splat(kBf16NegOff);
 
   for (int w = blockIdx.x;; w += gridDim.x) {
     TileInfo tl;
@@ -321,11 +328,11 @@ void down_w4_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
       valid[c] = j < tl.cnt;
       hr[c] = h + (size_t)(tl.r0 + (valid[c] ? j : 0)) * f + 32 * kq;
     }
-    const uint8_t* cd = codes + (erow + m0 + col) * (size_t)(f >> 1) + 16 * kq;
+    const uint8_t* cd = codes + (erow + m0) * (size_t)(f >> 1) + 64 * col + 16 * kq;
 
     u32x4 q[kDepth], hv[kDepth][NT][4];
     auto load = [&](int g, u32x4& a, u32x4 (&v)[NT][4]) {
-      a = *(const u32x4*)(cd + 64 * g);
+      a = *(const u32x4*)(cd + kTileGroupBytes * g);
 #pragma unroll
       for (int c = 0; c < NT; ++c) {
         if (c >= nch) break;
@@ -359,7 +366,7 @@ void down_w4_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
           for (int j = 0; j < 4; ++j) hp[j] = x_perm(hv[i][c][j]);
           f32x4 seed = {0, 0, 0, 0};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) seed = mfma16(neg24, hp[j], seed);
+          for (int j = 0; j < 4; ++j) seed = mfma16(negoff, hp[j], seed);
           tile_group(hp, seed, q[i], sv, acc[c]);
         }
         if (gi + kDepth < ge) load(gi + kDepth, q[i], hv[i]);
@@ -392,6 +399,21 @@ void down_w4_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
 }
 
 
+
+// Scales of 64 rows per matrix staged as fp32 in LDS, [matrix][group][row],
+// for a 256-thread block: thread t owns row t % 64 (of matrix (t / 64) % NMAT)
+// and every (256 / (64 NMAT))-th group.
+template <int NMAT>
+__device__ __forceinline__ void stage_scales_rows64(const uint16_t* __restrict__ rows_src,
+                                                    size_t mat_stride, int G,
+                                                    float* __restrict__ dst) {
+  constexpr int kStep = 256 / (64 * NMAT);
+  const int r = threadIdx.x & 63, m = (threadIdx.x >> 6) % NMAT, g0 = (threadIdx.x >> 6) / NMAT;
+  const uint16_t* src = rows_src + ((size_t)m * mat_stride + r) * G;
+  float* d = dst + (size_t)m * G * 64 + r;
+  for (int g = g0; g < G; g += kStep) d[g * 64] = f16_bits_to_f32(src[g]);
+}
+
 // ------------------------------------------- single K slice, one token tile
 // When every wave streams the whole K range of its own 16-feature row tile
 // (KS = 1, tiles of up to 16 pairs), the four waves of a block share one
@@ -423,7 +445,7 @@ void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restr
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, kq = lane >> 4;
   const int st_tok = tid >> 4, st_pc = tid & 15;  // staged row and 16-byte piece
-  const bf16x8 neg24 = bf16_splat(kBf16Neg24);
+  const bf16x8 negoff = bf16_splat(kBf16NegOff);
 
   for (int w = blockIdx.x;; w += gridDim.x) {
     TileInfo tl;
@@ -434,21 +456,21 @@ void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restr
     const int sj = tl.r0 + (st_ok ? st_tok : 0);
     const int sp = np ? sp_lds[sj] : sorted_pair[sj];
     const uint16_t* xsrc = x + (size_t)(sp / k) * d + 8 * st_pc;
-    const uint8_t* cg = codes + (erow + n0 + col) * (size_t)(d >> 1) + 16 * kq;
+    const uint8_t* cg = codes + (erow + n0) * (size_t)(d >> 1) + 64 * col + 16 * kq;
     const uint8_t* cu = cg + (size_t)f * (d >> 1);
 
     u32x4 qg[kDQ], qu[kDQ], xv[kDQ];
     auto load = [&](int g, int i) {
       if (st_ok) xv[i] = *(const u32x4*)(xsrc + 128 * g);
-      qg[i] = *(const u32x4*)(cg + 64 * g);
-      qu[i] = *(const u32x4*)(cu + 64 * g);
+      qg[i] = *(const u32x4*)(cg + kTileGroupBytes * g);
+      qu[i] = *(const u32x4*)(cu + kTileGroupBytes * g);
     };
 #pragma unroll
     for (int i = 0; i < kDQ; ++i)
       if (i < G) load(i, i);
     // the previous item's last barrier precedes these LDS writes; the first
     // barrier of the group loop orders them before any read
-    stage_scales_f32(scales + (erow + nb) * G, (size_t)f, 2, 64, G, sc_lds);
+    stage_scales_rows64<2>(scales + (erow + nb) * G, (size_t)f, G, sc_lds);
 
     f32x4 tg = {0, 0, 0, 0}, tu = {0, 0, 0, 0};
     const int rd_tok = col < tl.cnt ? col : 0;  // padded columns re-read row 0
@@ -470,7 +492,7 @@ void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restr
         const f32x4 su = *(const f32x4*)(sc_lds + (G + gi) * 64 + 16 * wave + 4 * kq);
         f32x4 seed = {0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) seed = mfma16(neg24, xp[j], seed);
+        for (int j = 0; j < 4; ++j) seed = mfma16(negoff, xp[j], seed);
         const u32x4 a = qg[i], b = qu[i];
         if (gi + kDQ < G) load(gi + kDQ, i);
         tile_group(xp, seed, a, sg, tg);
@@ -506,7 +528,7 @@ void down_w4_decode_lds(const uint16_t* __restrict__ h, const int32_t* __restric
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, kq = lane >> 4;
   const int st_tok = tid >> 4, st_pc = tid & 15;
-  const bf16x8 neg24 = bf16_splat(kBf16Neg24);
+  const bf16x8 negoff = bf16_splat(kBf16NegOff);
 
   for (int w = blockIdx.x;; w += gridDim.x) {
     TileInfo tl;
@@ -515,17 +537,17 @@ void down_w4_decode_lds(const uint16_t* __restrict__ h, const int32_t* __restric
     const size_t erow = (size_t)tl.e * d;
     const bool st_ok = st_tok < tl.cnt;
     const uint16_t* hsrc = h + (size_t)(tl.r0 + (st_ok ? st_tok : 0)) * f + 8 * st_pc;
-    const uint8_t* cd = codes + (erow + m0 + col) * (size_t)(f >> 1) + 16 * kq;
+    const uint8_t* cd = codes + (erow + m0) * (size_t)(f >> 1) + 64 * col + 16 * kq;
 
     u32x4 q[kDQ], hv[kDQ];
     auto load = [&](int g, int i) {
       if (st_ok) hv[i] = *(const u32x4*)(hsrc + 128 * g);
-      q[i] = *(const u32x4*)(cd + 64 * g);
+      q[i] = *(const u32x4*)(cd + kTileGroupBytes * g);
     };
 #pragma unroll
     for (int i = 0; i < kDQ; ++i)
       if (i < G) load(i, i);
-    stage_scales_f32(scales + (erow + mb) * G, 0, 1, 64, G, sc_lds);
+    stage_scales_rows64<1>(scales + (erow + mb) * G, 0, G, sc_lds);
 
     f32x4 acc = {0, 0, 0, 0};
     const int rd_tok = col < tl.cnt ? col : 0;
@@ -544,7 +566,7 @@ void down_w4_decode_lds(const uint16_t* __restrict__ h, const int32_t* __restric
         const f32x4 sv = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
         f32x4 seed = {0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) seed = mfma16(neg24, xp[j], seed);
+        for (int j = 0; j < 4; ++j) seed = mfma16(negoff, xp[j], seed);
         const u32x4 a = q[i];
         if (gi + kDQ < G) load(gi + kDQ, i);
         tile_group(xp, seed, a, sv, acc);

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K]
                   const int32_t* __restrict__ sorted_pair,  // gate/up: gather
                   int k_top, int K, int N,                  // N: features per matrix
-                  const uint8_t* __restrict__ codes,        // [E][rows][K/2]
+                  const uint8_t* __restrict__ codes,        // tiled [E*rows/16][K/128][16][64]
                   const uint16_t* __restrict__ scales,      // [E][rows][K/128]
                   const uint2* __restrict__ gsum,           // [rows of act][K/128]
                   const PTile* __restrict__ tiles, const int* __restrict__ num_tiles,
@@ -132,7 +132,8 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
   const uint16_t* sb[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    cb[m] = codes + (ebase + brow[m]) * (size_t)(K >> 1) + 32 * hh;
+    const size_t row = ebase + brow[m];  // tiled codes: 16-row tiles, 1 KiB per group
+    cb[m] = codes + (row & ~(size_t)15) * (size_t)(K >> 1) + 64 * (row & 15) + 32 * hh;
     sb[m] = scales + (ebase + brow[m]) * (size_t)G;
   }
 
@@ -165,8 +166,8 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
   auto codes_load = [&](int g, u32x4 (&q)[2][2], uint32_t (&sc)[2]) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      q[m][0] = *(const u32x4*)(cb[m] + 64 * g);
-      q[m][1] = *(const u32x4*)(cb[m] + 64 * g + 16);
+      q[m][0] = *(const u32x4*)(cb[m] + 1024 * g);
+      q[m][1] = *(const u32x4*)(cb[m] + 1024 * g + 16);
       sc[m] = sb[m][g];
     }
   };

@@ -59,18 +59,6 @@ __device__ __forceinline__ uint32_t f64_to_f16_rne(double v) {
   return sign | (uint32_t)q;  // subnormal (q == 1024 encodes the min normal)
 }
 
-// Eight two's-complement nibbles (element 2j low, 2j+1 high of byte j) ->
-// eight exact bf16 values, natural element order.
-__device__ __forceinline__ bf16x8 w4_dword_to_bf16x8(uint32_t w) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int q = ((int)(w << (28 - 4 * i))) >> 28;
-    r[i] = (__bf16)(float)q;
-  }
-  return r;
-}
-
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
@@ -83,8 +71,11 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// silu(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal (about
+// 2 ulp in fp32; the product is rounded to bf16 right after).  e^-g
+// overflows to +inf for g < -88, giving g * 0 = -0.
 __device__ __forceinline__ float silu_f32(float g) {
-  return g / (1.0f + expf(-g));
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
 }  // namespace moe

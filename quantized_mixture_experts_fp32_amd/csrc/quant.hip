@@ -1,7 +1,9 @@
 // Offline quantizers (untimed packing of fp32 expert weights on the GPU).
 //  int4 (ExactMoE, "Every Expert Counts ...", Abstract: symmetric group-128
 //    four-bit): s = fp16_rne(max|w|/7), q = clamp(rne(w/s), -7, 7), q = 0 if
-//    s == 0; two nibbles per byte, element 2j low.
+//    s == 0; two nibbles per byte, element 2j low, in the tiled layout the
+//    FFN kernels stream: [rows/16][K/128][16 rows][64 bytes], so one
+//    16-row tile's 128-group is 1 KiB contiguous.
 //  bitplane8 (PagedMoE, abstract: one stored state, bitplane prefixes):
 //    s = fp16_rne(max|w|/127), u = clamp(rne(w/s) + 128, 0, 255), u = 128 if
 //    s == 0; plane slab p holds bit 7-p, bit i of a byte is element 8j + i.
@@ -39,7 +41,10 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
         r = fmin(fmax(r, -7.0), 7.0);
         q[h] = (int)r;
       }
-      codes[grp * 64 + lane] = (uint8_t)((q[0] & 0xF) | ((q[1] & 0xF) << 4));
+      const long long row = grp / G;  // over all E*N rows; N % 16 == 0
+      const long long g = grp % G;
+      codes[(((row >> 4) * G + g) * 16 + (row & 15)) * 64 + lane] =
+          (uint8_t)((q[0] & 0xF) | ((q[1] & 0xF) << 4));
     } else {
       int u[2];
       const float vv[2] = {v.x, v.y};

@@ -77,11 +77,22 @@ class HostLayer:
         return self._cache[e]
 
 
+def w4_untile(codes, N, K):
+    """The library's tiled int4 codes of one N x K matrix ([N/16][K/128][16][64]
+    bytes, include/moe_wq.h) -> the row-major [N][K/2] packing of the oracle.
+    A pure byte permutation; the nibbles are unchanged."""
+    t = np.asarray(codes, np.uint8).reshape(N // 16, K // 128, 16, 64)
+    return t.transpose(0, 2, 1, 3).reshape(N, K // 2)
+
+
 def assert_codes_equal(dev_layer, host_layer, experts):
     """Packed codes and fp16 scales of the listed experts are bit-identical."""
+    w4 = dev_layer.cfg.fmt == "w4"
     for e in experts:
         g, h = dev_layer.expert_codes(int(e)), host_layer.expert(int(e))
         for (dq, ds), (hq, hs) in zip(g, h):
+            if w4:
+                dq = w4_untile(dq, hq.shape[0], 2 * hq.shape[1])
             assert np.array_equal(dq, hq.reshape(dq.shape)), f"codes of expert {e}"
             assert np.array_equal(ds, hs.reshape(ds.shape)), f"scales of expert {e}"
 

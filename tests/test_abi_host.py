@@ -119,7 +119,9 @@ def test_combine_and_quantize_validation(lib):
     q = lib.moe_quantize_w4
     assert q(FAKE, 2, 4, 256, 64, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
     assert q(FAKE, 2, 4, 100, 128, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
-    assert q(NULL, 2, 4, 256, 128, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert q(FAKE, 2, 4, 256, 128, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED  # rows tiled by 16
+    assert "16" in err(lib)
+    assert q(NULL, 2, 16, 256, 128, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_quantize_bitplane8(FAKE, 0, 4, 256, 128, NULL, NULL, NULL) == moe.MOE_OK
 
 
@@ -128,3 +130,20 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(moe, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         moe.load_library()
+
+
+def test_w4_untile_matches_header_formula():
+    """The tests' untiling of int4 codes follows the byte-offset formula the
+    ABI header states: row n, group g -> (((n/16)*(K/128) + g)*16 + n%16)*64."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from layer_data import w4_untile
+    import numpy as np
+    N, K = 48, 384
+    tiled = np.random.default_rng(5).integers(0, 256, N * K // 2, dtype=np.uint8)
+    rm = w4_untile(tiled, N, K)
+    for n in range(N):
+        for j in range(K // 2):
+            g, o = divmod(j, 64)
+            off = (((n // 16) * (K // 128) + g) * 16 + n % 16) * 64 + o
+            assert rm[n, j] == tiled[off]

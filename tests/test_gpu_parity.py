@@ -11,7 +11,7 @@ import oracle
 import synth
 import quantized_mixture_experts_fp32_amd as moe
 from layer_data import (DEV, DevLayer, HostLayer, assert_close, assert_codes_equal,
-                        bf16_rne_bits, custom_cfg, record,
+                        bf16_rne_bits, custom_cfg, record, w4_untile,
                         stream)
 
 pytestmark = pytest.mark.gpu
@@ -65,7 +65,10 @@ def _edge_weights(rng, R, K):
 @pytest.mark.parametrize("fmt", ["w4", "bp8"])
 def test_quantize_bit_exact(fmt):
     rng = np.random.default_rng(7)
-    for (E, N, K) in [(2, 8, 256), (3, 40, 384), (1, 5, 2048)]:
+    # int4 rows are tiled by 16; bitplanes take any row count
+    shapes = ([(2, 16, 256), (3, 48, 384), (1, 32, 2048)] if fmt == "w4"
+              else [(2, 8, 256), (3, 40, 384), (1, 5, 2048)])
+    for (E, N, K) in shapes:
         note(f"quantize {fmt} E={E} N={N} K={K}")
         w = np.stack([_edge_weights(rng, N, K) for _ in range(E)])
         wd = torch.from_numpy(w).to(DEV)
@@ -78,7 +81,8 @@ def test_quantize_bit_exact(fmt):
         torch.cuda.synchronize()
         c, s = codes.cpu().numpy(), scales.cpu().numpy().view(np.uint16)
         for e in range(E):
-            assert np.array_equal(c[e], ref[e][0]), (fmt, e)
+            ce = w4_untile(c[e], N, K) if fmt == "w4" else c[e]
+            assert np.array_equal(ce, ref[e][0]), (fmt, e)
             assert np.array_equal(s[e], ref[e][1]), (fmt, e)
 
 
