@@ -12,9 +12,13 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["abi.cpp", "route.hip", "permute.hip", "quant.hip", "ffn.hip",
            "ffn_decode.hip", "ffn_prefill.hip", "combine.hip"]
 # Packed fp32 VALU instructions stay disabled in every HIP build here.
+# MFMA accumulators are allocated in ordinary VGPRs (not AGPRs): the kernels
+# rescale and convert accumulators with VALU instructions, which would
+# otherwise need a move to and from the AGPR file for every element.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Wall", "-Wno-unused-result", "-Xclang", "-target-feature",
-         "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include")]
+         "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+         "-I", os.path.join(ROOT, "include")]
 
 
 def build(verbose: bool = False) -> str:

@@ -35,18 +35,22 @@ constexpr int kThreads = 256;
 constexpr int kBT = 128;      // tokens per block tile
 constexpr int kRowB = 272;    // LDS bytes per token row: 256 + 16 padding
 constexpr int kBufB = kBT * kRowB;
+constexpr int kPfWaves = 2;   // waves per SIMD the register allocation is held to
 
 struct PTile {
   int e, r0, cnt, maxb;
 };
 
+// 8 nibbles -> bf16 (136 + q), element order 0,4,1,5,2,6,3,7 (the same
+// conversion as the decode path: q + 8 lands in the low mantissa bits of
+// 128.0, unshifted for elements 0 and 4).
 __device__ __forceinline__ bf16x8 w4_magic_pf(uint32_t w) {
-  const uint32_t B = 0x00780078u, D = 0x41C041C0u;
+  const uint32_t B = 0x000F000Fu, D = 0x43084308u;
   u32x4 r;
-  r[0] = __builtin_amdgcn_bitop3_b32(w << 3, B, D, 0x6A);
-  r[1] = __builtin_amdgcn_bitop3_b32(w >> 1, B, D, 0x6A);
-  r[2] = __builtin_amdgcn_bitop3_b32(w >> 5, B, D, 0x6A);
-  r[3] = __builtin_amdgcn_bitop3_b32(w >> 9, B, D, 0x6A);
+  r[0] = __builtin_amdgcn_bitop3_b32(w, B, D, 0x6A);
+  r[1] = __builtin_amdgcn_bitop3_b32(w >> 4, B, D, 0x6A);
+  r[2] = __builtin_amdgcn_bitop3_b32(w >> 8, B, D, 0x6A);
+  r[3] = __builtin_amdgcn_bitop3_b32(w >> 12, B, D, 0x6A);
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -92,10 +96,22 @@ __global__ __launch_bounds__(256) void group_sums(const uint16_t* __restrict__ r
 }
 
 // ------------------------------------------------------------- GEMM core
-// kGateUp: matrices m = 0 (gate rows n), 1 (up rows f + n) of one 32-feature
-// block per wave; otherwise two 32-feature blocks of one matrix.
+// One block = one tile of up to 128 grouped rows (tokens) x one feature
+// block; every wave owns all 128 tokens (four 32-token blocks) and two
+// 32-feature B blocks, i.e. eight 32x32 fp32 accumulators, so that each
+// converted code fragment feeds four MFMAs.
+//   gate/up (kGateUp): feature block fb covers features [128 fb, +128);
+//     wave w's B blocks are gate rows n = 128 fb + 32 w + c32 and the up
+//     rows N + n, so h = silu(gate) * up is formed in the lane.
+//   down: feature block fb covers [256 fb, +256); wave w's B blocks are rows
+//     256 fb + 64 w + c32 and + 32 (blocks at or past N are computed on a
+//     clamped row and not stored).
+// Pipeline per 128-group g: the block's barrier publishes the staged
+// activation tile of g; activations of g + 1 are then loaded into registers
+// while g is computed and written to the other LDS buffer afterwards; each
+// wave's codes run two groups ahead of the MFMAs.
 template <bool kGateUp>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kPfWaves, kPfWaves)))
 void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K]
                   const int32_t* __restrict__ sorted_pair,  // gate/up: gather
                   int k_top, int K, int N,                  // N: features per matrix
@@ -103,30 +119,39 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
                   const uint16_t* __restrict__ scales,      // [E][rows][K/128]
                   const uint2* __restrict__ gsum,           // [rows of act][K/128]
                   const PTile* __restrict__ tiles, const int* __restrict__ num_tiles,
+                  int nfb,                                  // feature blocks per tile
                   uint16_t* __restrict__ h_out,             // gate/up: [P][N]
                   float* __restrict__ y_out) {              // down:    [P][N]
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ uint2 xs_sum[2][kBT];  // group sums of the staged tile
 
-  if ((int)blockIdx.y >= *num_tiles) return;
-  const PTile tl = tiles[blockIdx.y];
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin by
+  // linear id, so XCD c runs tiles c, c + 8, ...; within an XCD all nfb
+  // feature blocks of a tile are consecutive and run together, and the
+  // tile's gathered activation rows are fetched into that XCD's L2 once.
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int tile = (local / nfb) * 8 + xcd, fblk = local % nfb;
+  if (tile >= *num_tiles) return;
+  const PTile tl = tiles[tile];
   const int G = K >> 7;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wt = wave >> 1, wf = wave & 1;
   const int c32 = lane & 31, hh = lane >> 5;
   const int nrows = kGateUp ? 2 * N : N;
   const size_t ebase = (size_t)tl.e * nrows;
 
-  // feature rows of this wave's two B blocks
   int brow[2];
+  bool bstore[2];
   if (kGateUp) {
-    const int n = blockIdx.x * 64 + wf * 32 + c32;
+    const int n = fblk * 128 + wave * 32 + c32;
     brow[0] = n;
     brow[1] = N + n;
+    bstore[0] = bstore[1] = true;
   } else {
-    const int n = blockIdx.x * 128 + wf * 64 + c32;
-    brow[0] = n;
-    brow[1] = n + 32;
+    const int n0 = fblk * 256 + wave * 64;
+    bstore[0] = n0 < N;
+    bstore[1] = n0 + 32 < N;
+    brow[0] = bstore[0] ? n0 + c32 : c32;
+    brow[1] = bstore[1] ? n0 + 32 + c32 : c32;
   }
   const uint8_t* cb[2];
   const uint16_t* sb[2];
@@ -134,35 +159,32 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
   for (int m = 0; m < 2; ++m) {
     const size_t row = ebase + brow[m];  // tiled codes: 16-row tiles, 1 KiB per group
     cb[m] = codes + (row & ~(size_t)15) * (size_t)(K >> 1) + 64 * (row & 15) + 32 * hh;
-    sb[m] = scales + (ebase + brow[m]) * (size_t)G;
+    sb[m] = scales + row * (size_t)G;
   }
 
   // staging assignment: thread -> (token row, half of the group)
-  const int st_row = tid >> 1, st_half = tid & 1;
+  const int st_row = tid & (kBT - 1), st_half = tid >> 7;
   const bool st_valid = st_row < tl.cnt;
   const int st_slot = tl.r0 + (st_valid ? st_row : 0);
   const long long st_src_row = kGateUp ? (long long)(sorted_pair[st_slot] / k_top) : st_slot;
   const uint16_t* st_src = act + st_src_row * K + 64 * st_half;
   const uint2* st_sum = gsum + st_src_row * G;
 
-  // Double-buffered pipeline: while group g is computed from LDS buffer
-  // g % 2, group g+1's activations and codes are loaded into registers and
-  // then written to the other buffer.
-  u32x4 stv[8];
+  // Activations are staged through registers in two halves of four
+  // 16-byte chunks each, so that only 16 registers hold them in flight.
+  u32x4 stv[4];
   uint2 st_s = {0u, 0u};
-  auto stage_load = [&](int g) {
+  auto stage_load = [&](int g, int half) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) stv[c] = *(const u32x4*)(st_src + 128 * g + 8 * c);
-    if (st_half == 0) st_s = st_sum[g];
+    for (int c = 0; c < 4; ++c) stv[c] = *(const u32x4*)(st_src + 128 * g + 32 * half + 8 * c);
+    if (half == 0 && st_half == 0) st_s = st_sum[g];
   };
-  auto stage_store = [&](int buf) {
-    uint8_t* rowp = lds + buf * kBufB + st_row * kRowB + 128 * st_half;
+  auto stage_store = [&](int buf, int half) {
+    uint8_t* rowp = lds + buf * kBufB + st_row * kRowB + 128 * st_half + 64 * half;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) *(u32x4*)(rowp + 16 * c) = perm8(stv[c]);
-    if (st_half == 0) xs_sum[buf][st_row] = st_s;
+    for (int c = 0; c < 4; ++c) *(u32x4*)(rowp + 16 * c) = perm8(stv[c]);
+    if (half == 0 && st_half == 0) xs_sum[buf][st_row] = st_s;
   };
-  u32x4 qa[2][2], qb[2][2];  // [matrix][16-byte half] codes of two groups
-  uint32_t sca[2], scb[2];
   auto codes_load = [&](int g, u32x4 (&q)[2][2], uint32_t (&sc)[2]) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -173,106 +195,121 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
   };
 
   // Running totals are kept in units of the current group's scale: before
-  // group g is added, acc *= s_prev / s_g; after the last group acc *= s.
-  // (All-zero groups, s_g == 0, contribute nothing and keep s_prev.)
-  f32x16 acc[2][2];  // [token block][matrix]
+  // group g is added, acc *= s_prev / s_g (1 when unchanged); after the last
+  // group acc *= s.  All-zero groups (s_g == 0) contribute nothing and keep
+  // s_prev.
+  f32x16 acc[4][2];  // [token block][B block]
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[t][m][i] = 0.0f;
   float s_cur[2] = {0.0f, 0.0f};
 
-  // B column of the offset MFMA: -24 in K rows 0..2 (lanes of half 0)
-  u32x4 neg24v = {0u, 0u, 0u, 0u};
+  // B column of the offset MFMA: -136 in K rows 0..2 (lanes of half 0)
+  u32x4 negv = {0u, 0u, 0u, 0u};
   if (hh == 0) {
-    neg24v[0] = 0xC1C0C1C0u;  // -24, -24
-    neg24v[1] = 0x0000C1C0u;  // -24, 0
+    negv[0] = 0xC308C308u;  // -136, -136
+    negv[1] = 0x0000C308u;  // -136, 0
   }
-  const bf16x8 negB = __builtin_bit_cast(bf16x8, neg24v);
+  const bf16x8 negB = __builtin_bit_cast(bf16x8, negv);
 
-  auto group_step = [&](int g, const u32x4 (&q)[2][2], const uint32_t (&sc)[2],
-                        u32x4 (&qn)[2][2], uint32_t (&scn)[2]) {
+  auto group_step = [&](int g, u32x4 (&q)[2][2], uint32_t (&sc)[2]) {
     const int buf = g & 1;
+    __syncthreads();  // tile g staged; every wave is done reading buffer buf ^ 1
     const bool more = g + 1 < G;
-    if (more) {
-      stage_load(g + 1);
-      codes_load(g + 1, qn, scn);
-    }
-    const uint8_t* abase = lds + buf * kBufB + (wt * 64 + c32) * kRowB + 128 * hh;
-    bf16x8 af[2][8];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2)
-        af[t][s2] = __builtin_bit_cast(bf16x8, *(const u32x4*)(abase + t * 32 * kRowB + 16 * s2));
-    bf16x8 sumA[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (hh == 0) {
-        const uint2 ss = xs_sum[buf][wt * 64 + t * 32 + c32];
-        v[0] = ss.x;
-        v[1] = ss.y;
-      }
-      sumA[t] = __builtin_bit_cast(bf16x8, v);
-    }
+    if (more) stage_load(g + 1, 0);
+    const uint8_t* abase = lds + buf * kBufB + c32 * kRowB + 128 * hh;
+    float r[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const float sg = f16_bits_to_f32(sc[m]);
-      if (sg != 0.0f && sg != s_cur[m]) {
-        const float r = (s_cur[m] == 0.0f) ? 0.0f : s_cur[m] / sg;
+      const bool upd = sg != 0.0f;
+      r[m] = upd ? ((s_cur[m] == 0.0f) ? 0.0f : s_cur[m] / sg) : 1.0f;
+      s_cur[m] = upd ? sg : s_cur[m];
+    }
+    // offset term and rescale, token block by token block
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[t][m][i] *= r;
-        s_cur[m] = sg;
+    for (int t = 0; t < 4; ++t) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (hh == 0) {
+        const uint2 ss = xs_sum[buf][t * 32 + c32];
+        v[0] = ss.x;
+        v[1] = ss.y;
       }
-      bf16x8 bfr[8];
+      const bf16x8 sumA = __builtin_bit_cast(bf16x8, v);
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) bfr[s2] = w4_magic_pf(q[m][s2 >> 2][s2 & 3]);
+      for (int m = 0; m < 2; ++m) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        acc[t][m] = mfma32(sumA[t], negB, acc[t][m]);
-#pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) acc[t][m] = mfma32(af[t][s2], bfr[s2], acc[t][m]);
+        for (int i = 0; i < 16; ++i) acc[t][m][i] *= r[m];
+        acc[t][m] = mfma32(sumA, negB, acc[t][m]);
       }
     }
-    if (more) stage_store(buf ^ 1);
-    __syncthreads();
+    bf16x8 af[2][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      af[0][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(abase + t * 32 * kRowB));
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      const int cur = s2 & 1;
+      if (s2 + 1 < 8) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          af[cur ^ 1][t] = __builtin_bit_cast(
+              bf16x8, *(const u32x4*)(abase + t * 32 * kRowB + 16 * (s2 + 1)));
+      }
+      bf16x8 bfr[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) bfr[m] = w4_magic_pf(q[m][s2 >> 2][s2 & 3]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) acc[t][m] = mfma32(af[cur][t], bfr[m], acc[t][m]);
+      if (s2 == 3 && more) {
+        stage_store(buf ^ 1, 0);
+        stage_load(g + 1, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (g + 2 < G) codes_load(g + 2, q, sc);
+    if (more) stage_store(buf ^ 1, 1);
   };
 
-  stage_load(0);
+  u32x4 qa[2][2], qb[2][2];  // [B block][16-byte half] codes of groups g, g + 1
+  uint32_t sca[2], scb[2];
   codes_load(0, qa, sca);
-  stage_store(0);
-  __syncthreads();
+  if (G > 1) codes_load(1, qb, scb);
+  stage_load(0, 0);
+  stage_store(0, 0);
+  stage_load(0, 1);
+  stage_store(0, 1);
   for (int g = 0; g < G; g += 2) {
-    group_step(g, qa, sca, qb, scb);
-    if (g + 1 < G) group_step(g + 1, qb, scb, qa, sca);
+    group_step(g, qa, sca);
+    if (g + 1 < G) group_step(g + 1, qb, scb);
   }
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[t][m][i] *= s_cur[m];
 
-  // ---- epilogue: lane owns feature brow (per matrix) for 16 token rows
+  // ---- epilogue: lane owns feature brow (per B block) for 16 token rows
   // of each token block: rows 8*(i/4) + 4*hh + i%4 of the 32-row block.
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int tok = wt * 64 + t * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+      const int tok = t * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
       if (tok >= tl.cnt) continue;
       const size_t slot = (size_t)(tl.r0 + tok);
       if (kGateUp) {
         const float hv = silu_f32(acc[t][0][i]) * acc[t][1][i];
         h_out[slot * N + brow[0]] = (uint16_t)f32_to_bf16_rne(hv);
       } else {
-        y_out[slot * N + brow[0]] = acc[t][0][i];
-        y_out[slot * N + brow[1]] = acc[t][1][i];
+        if (bstore[0]) y_out[slot * N + brow[0]] = acc[t][0][i];
+        if (bstore[1]) y_out[slot * N + brow[1]] = acc[t][1][i];
       }
     }
 }
@@ -330,9 +367,10 @@ hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStr
                        (long long)a.T, a.d, xsum);
   }
   if (a.ev[0]) hipEventRecord(a.ev[0], s);
-  hipLaunchKernelGGL((pf_w4_kernel<true>), dim3(a.f / 64, (unsigned)mt), dim3(kThreads), lds, s,
+  const unsigned mt8 = (unsigned)((mt + 7) & ~(size_t)7);
+  hipLaunchKernelGGL((pf_w4_kernel<true>), dim3(mt8 * (a.f / 128)), dim3(kThreads), lds, s,
                      a.x, a.sorted_pair, a.k, a.d, a.f, a.gu_codes, a.gu_scales, xsum, tiles,
-                     num_tiles, h, (float*)nullptr);
+                     num_tiles, a.f / 128, h, (float*)nullptr);
   if (a.ev[1]) hipEventRecord(a.ev[1], s);
   {
     const long long n = P * (a.f / 128);
@@ -340,9 +378,10 @@ hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStr
                        a.f, hsum);
   }
   if (a.ev[2]) hipEventRecord(a.ev[2], s);
-  hipLaunchKernelGGL((pf_w4_kernel<false>), dim3(a.d / 128, (unsigned)mt), dim3(kThreads), lds,
+  const int dn_fb = (a.d + 255) / 256;
+  hipLaunchKernelGGL((pf_w4_kernel<false>), dim3(mt8 * dn_fb), dim3(kThreads), lds,
                      s, h, a.sorted_pair, a.k, a.f, a.d, a.dn_codes, a.dn_scales, hsum, tiles,
-                     num_tiles, (uint16_t*)nullptr, a.y);
+                     num_tiles, dn_fb, (uint16_t*)nullptr, a.y);
   if (a.ev[3]) hipEventRecord(a.ev[3], s);
   return hipGetLastError();
 }
