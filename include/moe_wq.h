@@ -159,9 +159,11 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E,
  *   start at e*2f resp. e*d; gate rows 0..f-1 then up rows f..2f-1 of each
  *   expert) and K inputs is stored as u8 [R/16][K/128][16][64]: the codes of
  *   row n, elements 128g .. 128g+127, are the 64 bytes at
- *   (((n/16)*(K/128) + g)*16 + n%16)*64; byte j of them holds element
- *   128g+2j in the low nibble and 128g+2j+1 in the high nibble, two's
- *   complement in [-7, 7].  (One 16-row tile's group is 1 KiB contiguous.)
+ *   (((n/16)*(K/128) + g)*16 + n%16)*64, read as 16 little-endian 32-bit
+ *   words; word j holds elements 128g+8j .. +7: element 8j+2i in nibble i
+ *   (bits 4i..4i+3) and element 8j+2i+1 in nibble 4+i, for i = 0..3; each
+ *   nibble is two's complement in [-7, 7].  (One 16-row tile's group is
+ *   1 KiB contiguous.)
  *     gate_up_codes: R = E*2f, K = d (E*f*d bytes);  gate_up_scales fp16
  *     [E][2f][d/128];  down_codes: R = E*d, K = f;  down_scales fp16
  *     [E][d][f/128].

@@ -18,9 +18,10 @@
 // 128-group, so one wave-wide 16-byte load covers the tile's group, 1 KiB
 // contiguous, and consecutive groups are consecutive kilobytes.
 //
-// K order.  The conversion yields the nibbles of a dword in the order
-// 0,4,1,5,2,6,3,7; the activation fragment is permuted the same way with
-// v_perm, so A and B enumerate the same K elements.
+// K order.  Word j of a row's group holds elements 8j..8j+7 with the even
+// elements in its low half-word and the odd ones in the high half-word, so
+// the conversion yields them in natural order and activation fragments are
+// used as loaded.
 //
 // Work decomposition.  Work item = (token tile of up to 16*NT grouped
 // pairs of one expert, 4/KS row tiles of 16 output features).  Each wave
@@ -78,12 +79,13 @@ __device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int tok,
   return false;
 }
 
-// 8 nibbles -> bf16 (136 + q) in element order 0,4,1,5,2,6,3,7.
+// One code word (elements 8j..8j+7, even ones in nibbles 0-3, odd ones in
+// nibbles 4-7) -> bf16 (136 + q) of the 8 elements in order.
 // bitop3 LUT 0x6A: out = B ? (x ^ D) : D.  B selects bits 0-3 of each half,
-// the low mantissa bits of 128.0 (whose ulp is 1), where the nibble lands
-// unshifted for elements 0 and 4 and after shifts of 4, 8 and 12 bits for
-// the others; D = 0x4308 per half is 128.0 plus the inversion of the
-// nibble's top bit, which maps two's complement q to q + 8.
+// the low mantissa bits of 128.0 (whose ulp is 1): nibble m and nibble m + 4
+// (elements 2m and 2m + 1) land there after a shift by 4m; D = 0x4308 per
+// half is 128.0 plus the inversion of the nibble's top bit, which maps
+// two's complement q to q + 8.
 __device__ __forceinline__ bf16x8 w4_magic(uint32_t w) {
   const uint32_t B = 0x000F000Fu, D = 0x43084308u;
   u32x4 r;
@@ -91,16 +93,6 @@ __device__ __forceinline__ bf16x8 w4_magic(uint32_t w) {
   r[1] = __builtin_amdgcn_bitop3_b32(w >> 4, B, D, 0x6A);
   r[2] = __builtin_amdgcn_bitop3_b32(w >> 8, B, D, 0x6A);
   r[3] = __builtin_amdgcn_bitop3_b32(w >> 12, B, D, 0x6A);
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-// 8 consecutive bf16 (x0..x7 in a u32x4) -> order 0,4,1,5,2,6,3,7.
-__device__ __forceinline__ bf16x8 x_perm(u32x4 v) {
-  u32x4 r;
-  r[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
-  r[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
-  r[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
-  r[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -240,7 +232,7 @@ void gateup_w4_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
           if (c >= nch) break;
           bf16x8 xp[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) xp[j] = x_perm(xv[i][c][j]);
+          for (int j = 0; j < 4; ++j) xp[j] = __builtin_bit_cast(bf16x8, xv[i][c][j]);
           f32x4 seed = {0, 0, 0, 0};
 #pragma unroll
           for (int j = 0; j < 4; ++j) seed = mfma16(negoff, xp[j], seed);
@@ -363,7 +355,7 @@ void down_w4_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
           if (c >= nch) break;
           bf16x8 hp[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) hp[j] = x_perm(hv[i][c][j]);
+          for (int j = 0; j < 4; ++j) hp[j] = __builtin_bit_cast(bf16x8, hv[i][c][j]);
           f32x4 seed = {0, 0, 0, 0};
 #pragma unroll
           for (int j = 0; j < 4; ++j) seed = mfma16(negoff, hp[j], seed);
@@ -418,12 +410,11 @@ __device__ __forceinline__ void stage_scales_rows64(const uint16_t* __restrict__
 // When every wave streams the whole K range of its own 16-feature row tile
 // (KS = 1, tiles of up to 16 pairs), the four waves of a block share one
 // token tile.  The block then stages each 128-group of the tile's
-// activation rows in LDS once (one 16-byte piece per thread, permuted to
-// the conversion's K order on the way), and the waves read their B
-// fragments from there.  Compared with per-wave activation loads this cuts
-// activation registers by four, takes the permutation out of the per-wave
-// loop, and leaves the global-load counter to the codes alone, so the code
-// stream can run kDQ groups ahead of the MFMAs.  The arithmetic (operands,
+// activation rows in LDS once (one 16-byte piece per thread), and the waves
+// read their B fragments from there.  Compared with per-wave activation
+// loads this cuts activation registers by four and leaves the global-load
+// counter to the codes alone, so the code stream can run kDQ groups ahead
+// of the MFMAs.  The arithmetic (operands,
 // MFMA order, scaling) is the same as in the kernels above.
 constexpr int kXRow = 136;  // bf16 per staged activation row (128 + 8 pad)
 
@@ -482,7 +473,7 @@ void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restr
         // slot gi & 1 was last read in iteration gi - 2, before the
         // barrier of iteration gi - 1
         uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
-        if (st_ok) *(bf16x8*)(slot + st_tok * kXRow + 8 * st_pc) = x_perm(xv[i]);
+        if (st_ok) *(u32x4*)(slot + st_tok * kXRow + 8 * st_pc) = xv[i];
         __syncthreads();
         bf16x8 xp[4];
 #pragma unroll
@@ -557,7 +548,7 @@ void down_w4_decode_lds(const uint16_t* __restrict__ h, const int32_t* __restric
         const int gi = g + i;
         if (gi >= G) break;
         uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
-        if (st_ok) *(bf16x8*)(slot + st_tok * kXRow + 8 * st_pc) = x_perm(hv[i]);
+        if (st_ok) *(u32x4*)(slot + st_tok * kXRow + 8 * st_pc) = hv[i];
         __syncthreads();
         bf16x8 xp[4];
 #pragma unroll

@@ -7,24 +7,19 @@
 // in registers), so that each lane of a 32x32 accumulator tile owns one
 // output feature and needs one fp16 scale per 128-group.
 //
-// Arithmetic.  As in the decode path, a nibble becomes bf16(24 + q) with one
-// v_bitop3, and each group's partial sum starts from -24 * sum_k x_k: that
-// term enters as one extra MFMA per group whose A column holds the exact
-// three-part bf16 split (hi + mid + lo) of the fp32 group sum of the token's
-// activations, and whose B column holds -24.  The running fp32 total is kept
-// in units of the current group's fp16 scale: before a group with a new
-// scale is accumulated, the total is multiplied by s_prev / s_g, and after
-// the last group by the final scale, so every group's sum is weighted by its
-// own scale without a separate partial accumulator.
-// A pre-pass kernel computes the group sums (and their splits) of x per
-// token and of h per grouped pair.
+// Arithmetic.  As in the decode path, a code word becomes eight bf16
+// values 136 + q (in element order) with shifts and v_bitop3, and each
+// group's partial sum is corrected by -136 * sum_k x_k: that term enters as
+// one extra MFMA per group whose A column holds the exact three-part bf16
+// split (hi + mid + lo) of the fp32 group sum of the token's activations,
+// and whose B column holds -136.  The running fp32 total is kept in units
+// of the current group's fp16 scale: before a group is accumulated, the
+// total is multiplied by s_prev / s_g, and after the last group by the
+// final scale, so every group's sum is weighted by its own scale without a
+// separate partial accumulator.  A pre-pass kernel computes the group sums
+// (and their splits) of x per token and of h per grouped pair.
 //
-// Tiling.  Block = 4 waves = 128 tokens x 64 features (gate/up: 64 features
-// of gate and the same 64 of up).  Wave (wt, wf) owns tokens [64 wt, +64)
-// and 32 features.  Per 128-group the block stages the 128 x 128 bf16
-// activation tile in LDS (double buffered, rows padded by 16 bytes, stored in
-// the nibble order 0,4,1,5,2,6,3,7 of the conversion), while every wave
-// streams its own code rows from HBM one group ahead.
+// Tiling and pipeline: see the GEMM core below.
 #include "kcommon.hpp"
 #include "launch.hpp"
 
@@ -33,17 +28,19 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBT = 128;      // tokens per block tile
-constexpr int kRowB = 272;    // LDS bytes per token row: 256 + 16 padding
+constexpr int kRowB = 256;    // LDS bytes per staged token row (chunks swizzled)
 constexpr int kBufB = kBT * kRowB;
 constexpr int kPfWaves = 2;   // waves per SIMD the register allocation is held to
+
 
 struct PTile {
   int e, r0, cnt, maxb;
 };
 
-// 8 nibbles -> bf16 (136 + q), element order 0,4,1,5,2,6,3,7 (the same
-// conversion as the decode path: q + 8 lands in the low mantissa bits of
-// 128.0, unshifted for elements 0 and 4).
+// One code word (elements 8j..8j+7, even ones in nibbles 0-3, odd ones in
+// nibbles 4-7) -> bf16 (136 + q) of the 8 elements in order; the same
+// conversion as the decode path (q + 8 lands in the low mantissa bits of
+// 128.0).
 __device__ __forceinline__ bf16x8 w4_magic_pf(uint32_t w) {
   const uint32_t B = 0x000F000Fu, D = 0x43084308u;
   u32x4 r;
@@ -52,15 +49,6 @@ __device__ __forceinline__ bf16x8 w4_magic_pf(uint32_t w) {
   r[2] = __builtin_amdgcn_bitop3_b32(w >> 8, B, D, 0x6A);
   r[3] = __builtin_amdgcn_bitop3_b32(w >> 12, B, D, 0x6A);
   return __builtin_bit_cast(bf16x8, r);
-}
-
-__device__ __forceinline__ u32x4 perm8(u32x4 v) {
-  u32x4 r;
-  r[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);
-  r[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);
-  r[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);
-  r[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);
-  return r;
 }
 
 // ---------------------------------------------------------------- pre-pass
@@ -106,10 +94,14 @@ __global__ __launch_bounds__(256) void group_sums(const uint16_t* __restrict__ r
 //   down: feature block fb covers [256 fb, +256); wave w's B blocks are rows
 //     256 fb + 64 w + c32 and + 32 (blocks at or past N are computed on a
 //     clamped row and not stored).
-// Pipeline per 128-group g: the block's barrier publishes the staged
-// activation tile of g; activations of g + 1 are then loaded into registers
-// while g is computed and written to the other LDS buffer afterwards; each
-// wave's codes run two groups ahead of the MFMAs.
+// Pipeline: right after the block barrier that opens 128-group g, the block
+// issues the direct-to-LDS loads of group g+1's activation tile (and its
+// group sums) into the other buffer, and every wave issues its codes of
+// group g+1; all of them have the whole of group g's MFMA work to land
+// before the barrier that opens g+1 waits for them.
+// Staged tile: row t (256 bytes) holds the token's 128 activations as
+// 16-byte chunks, chunk c at position c ^ (t & 15), so that the 32 rows a
+// fragment read touches fall on distinct banks.
 template <bool kGateUp>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kPfWaves, kPfWaves)))
 void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K]
@@ -122,8 +114,12 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
                   int nfb,                                  // feature blocks per tile
                   uint16_t* __restrict__ h_out,             // gate/up: [P][N]
                   float* __restrict__ y_out) {              // down:    [P][N]
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ uint2 xs_sum[2][kBT];  // group sums of the staged tile
+  // two staging buffers as distinct objects, so that reads of one are not
+  // ordered behind the in-flight direct-to-LDS loads of the other
+  __shared__ __attribute__((aligned(16))) uint8_t abuf0[kBufB];
+  __shared__ __attribute__((aligned(16))) uint8_t abuf1[kBufB];
+  __shared__ uint2 sbuf0[kBT];
+  __shared__ uint2 sbuf1[kBT];
 
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin by
   // linear id, so XCD c runs tiles c, c + 8, ...; within an XCD all nfb
@@ -162,28 +158,37 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
     sb[m] = scales + row * (size_t)G;
   }
 
-  // staging assignment: thread -> (token row, half of the group)
-  const int st_row = tid & (kBT - 1), st_half = tid >> 7;
-  const bool st_valid = st_row < tl.cnt;
-  const int st_slot = tl.r0 + (st_valid ? st_row : 0);
-  const long long st_src_row = kGateUp ? (long long)(sorted_pair[st_slot] / k_top) : st_slot;
-  const uint16_t* st_src = act + st_src_row * K + 64 * st_half;
-  const uint2* st_sum = gsum + st_src_row * G;
-
-  // Activations are staged through registers in two halves of four
-  // 16-byte chunks each, so that only 16 registers hold them in flight.
-  u32x4 stv[4];
-  uint2 st_s = {0u, 0u};
-  auto stage_load = [&](int g, int half) {
+  // Direct-to-LDS staging: load instruction i of wave w fills rows
+  // 32 w + 4 i .. + 3 (1 KiB), lane l writing position l % 16 of row
+  // 32 w + 4 i + l / 16; it reads the row's logical chunk (l % 16) ^ (t % 16).
+  // Rows past the tile's end read the tile's first row (never stored).
+  const char* act_b = (const char*)act;
+  uint32_t srcoff[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) stv[c] = *(const u32x4*)(st_src + 128 * g + 32 * half + 8 * c);
-    if (half == 0 && st_half == 0) st_s = st_sum[g];
-  };
-  auto stage_store = [&](int buf, int half) {
-    uint8_t* rowp = lds + buf * kBufB + st_row * kRowB + 128 * st_half + 64 * half;
+  for (int i = 0; i < 8; ++i) {
+    const int t = wave * 32 + 4 * i + (lane >> 4);
+    const int slot = tl.r0 + (t < tl.cnt ? t : 0);
+    const uint32_t src_row = kGateUp ? (uint32_t)(sorted_pair[slot] / k_top) : (uint32_t)slot;
+    srcoff[i] = src_row * (uint32_t)K * 2u + 16u * (uint32_t)((lane & 15) ^ (t & 15));
+  }
+  // group sums: wave w stages tokens 32 w .. + 31, two dwords per token
+  uint32_t sumoff;
+  {
+    const int t = wave * 32 + (lane >> 1);
+    const int slot = tl.r0 + (t < tl.cnt ? t : 0);
+    const uint32_t src_row = kGateUp ? (uint32_t)(sorted_pair[slot] / k_top) : (uint32_t)slot;
+    sumoff = src_row * (uint32_t)G * 8u + 4u * (uint32_t)(lane & 1);
+  }
+  auto stage = [&](int g, uint8_t* ab, uint2* sbp) {
+    const char* gbase = act_b + 256 * g;  // uniform; per-lane 32-bit offsets
 #pragma unroll
-    for (int c = 0; c < 4; ++c) *(u32x4*)(rowp + 16 * c) = perm8(stv[c]);
-    if (half == 0 && st_half == 0) xs_sum[buf][st_row] = st_s;
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds(gbase + srcoff[i],
+                                       (__attribute__((address_space(3))) void*)(ab + (wave * 32 + 4 * i) * kRowB),
+                                       16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const char*)(gsum + g) + sumoff,
+                                     (__attribute__((address_space(3))) void*)(sbp + wave * 32),
+                                     4, 0, 0);
   };
   auto codes_load = [&](int g, u32x4 (&q)[2][2], uint32_t (&sc)[2]) {
 #pragma unroll
@@ -215,12 +220,20 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
   }
   const bf16x8 negB = __builtin_bit_cast(bf16x8, negv);
 
-  auto group_step = [&](int g, u32x4 (&q)[2][2], uint32_t (&sc)[2]) {
-    const int buf = g & 1;
-    __syncthreads();  // tile g staged; every wave is done reading buffer buf ^ 1
-    const bool more = g + 1 < G;
-    if (more) stage_load(g + 1, 0);
-    const uint8_t* abase = lds + buf * kBufB + c32 * kRowB + 128 * hh;
+  // fragment address of (token block 0, K step 0) in a staged buffer, and
+  // the chunk swizzle of K steps 1..7
+  const int x16 = c32 & 15;
+  const int rd_base = c32 * kRowB + 16 * ((8 * hh) ^ (x16 & 8));
+  const int rd_x = 16 * (x16 & 7);
+
+  auto group_step = [&](int g, const uint8_t* ab, const uint2* sbp, uint8_t* ab_next,
+                        uint2* sb_next, const u32x4 (&q)[2][2], const uint32_t (&sc)[2],
+                        u32x4 (&qn)[2][2], uint32_t (&scn)[2]) {
+    __syncthreads();  // group g staged; every wave is done with the other buffer
+    if (g + 1 < G) {
+      stage(g + 1, ab_next, sb_next);
+      codes_load(g + 1, qn, scn);
+    }
     float r[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -234,7 +247,7 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
     for (int t = 0; t < 4; ++t) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (hh == 0) {
-        const uint2 ss = xs_sum[buf][t * 32 + c32];
+        const uint2 ss = sbp[t * 32 + c32];
         v[0] = ss.x;
         v[1] = ss.y;
       }
@@ -246,18 +259,20 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
         acc[t][m] = mfma32(sumA, negB, acc[t][m]);
       }
     }
+    const uint8_t* rd = ab + rd_base;
     bf16x8 af[2][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      af[0][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(abase + t * 32 * kRowB));
+      af[0][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(rd + t * 32 * kRowB + rd_x));
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2) {
       const int cur = s2 & 1;
       if (s2 + 1 < 8) {
+        const int off = rd_x ^ (16 * (s2 + 1));
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          af[cur ^ 1][t] = __builtin_bit_cast(
-              bf16x8, *(const u32x4*)(abase + t * 32 * kRowB + 16 * (s2 + 1)));
+          af[cur ^ 1][t] =
+              __builtin_bit_cast(bf16x8, *(const u32x4*)(rd + t * 32 * kRowB + off));
       }
       bf16x8 bfr[2];
 #pragma unroll
@@ -266,27 +281,17 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int m = 0; m < 2; ++m) acc[t][m] = mfma32(af[cur][t], bfr[m], acc[t][m]);
-      if (s2 == 3 && more) {
-        stage_store(buf ^ 1, 0);
-        stage_load(g + 1, 1);
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (g + 2 < G) codes_load(g + 2, q, sc);
-    if (more) stage_store(buf ^ 1, 1);
   };
 
   u32x4 qa[2][2], qb[2][2];  // [B block][16-byte half] codes of groups g, g + 1
   uint32_t sca[2], scb[2];
   codes_load(0, qa, sca);
-  if (G > 1) codes_load(1, qb, scb);
-  stage_load(0, 0);
-  stage_store(0, 0);
-  stage_load(0, 1);
-  stage_store(0, 1);
+  stage(0, abuf0, sbuf0);
   for (int g = 0; g < G; g += 2) {
-    group_step(g, qa, sca);
-    if (g + 1 < G) group_step(g + 1, qb, scb);
+    group_step(g, abuf0, sbuf0, abuf1, sbuf1, qa, sca, qb, scb);
+    if (g + 1 < G) group_step(g + 1, abuf1, sbuf1, abuf0, sbuf0, qb, scb, qa, sca);
   }
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -358,7 +363,6 @@ hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStr
   const size_t mt = (size_t)((P + kBT - 1) / kBT + (P < a.E ? P : a.E));
   uint2* xsum = (uint2*)(w + 256 + a256(mt * sizeof(PTile)));
   uint2* hsum = (uint2*)((char*)xsum + a256((size_t)a.T * (a.d / 128) * 8));
-  const size_t lds = 2 * (size_t)kBufB;
 
   hipLaunchKernelGGL(pf_prep, dim3(1), dim3(1024), 0, s, a.offsets, a.E, tiles, num_tiles);
   {
@@ -368,7 +372,7 @@ hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStr
   }
   if (a.ev[0]) hipEventRecord(a.ev[0], s);
   const unsigned mt8 = (unsigned)((mt + 7) & ~(size_t)7);
-  hipLaunchKernelGGL((pf_w4_kernel<true>), dim3(mt8 * (a.f / 128)), dim3(kThreads), lds, s,
+  hipLaunchKernelGGL((pf_w4_kernel<true>), dim3(mt8 * (a.f / 128)), dim3(kThreads), 0, s,
                      a.x, a.sorted_pair, a.k, a.d, a.f, a.gu_codes, a.gu_scales, xsum, tiles,
                      num_tiles, a.f / 128, h, (float*)nullptr);
   if (a.ev[1]) hipEventRecord(a.ev[1], s);
@@ -379,7 +383,7 @@ hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStr
   }
   if (a.ev[2]) hipEventRecord(a.ev[2], s);
   const int dn_fb = (a.d + 255) / 256;
-  hipLaunchKernelGGL((pf_w4_kernel<false>), dim3(mt8 * dn_fb), dim3(kThreads), lds,
+  hipLaunchKernelGGL((pf_w4_kernel<false>), dim3(mt8 * dn_fb), dim3(kThreads), 0,
                      s, h, a.sorted_pair, a.k, a.f, a.d, a.dn_codes, a.dn_scales, hsum, tiles,
                      num_tiles, dn_fb, (uint16_t*)nullptr, a.y);
   if (a.ev[3]) hipEventRecord(a.ev[3], s);

@@ -1,9 +1,11 @@
 // Offline quantizers (untimed packing of fp32 expert weights on the GPU).
 //  int4 (ExactMoE, "Every Expert Counts ...", Abstract: symmetric group-128
 //    four-bit): s = fp16_rne(max|w|/7), q = clamp(rne(w/s), -7, 7), q = 0 if
-//    s == 0; two nibbles per byte, element 2j low, in the tiled layout the
-//    FFN kernels stream: [rows/16][K/128][16 rows][64 bytes], so one
-//    16-row tile's 128-group is 1 KiB contiguous.
+//    s == 0; in the tiled layout the FFN kernels stream: [rows/16][K/128]
+//    [16 rows][64 bytes], so one 16-row tile's 128-group is 1 KiB
+//    contiguous; 32-bit word j of a row's group holds elements 8j..8j+7,
+//    the even ones in nibbles 0-3 and the odd ones in nibbles 4-7, so that
+//    the kernels' nibble-to-bf16 conversion yields them in order.
 //  bitplane8 (PagedMoE, abstract: one stored state, bitplane prefixes):
 //    s = fp16_rne(max|w|/127), u = clamp(rne(w/s) + 128, 0, 255), u = 128 if
 //    s == 0; plane slab p holds bit 7-p, bit i of a byte is element 8j + i.
@@ -41,10 +43,17 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
         r = fmin(fmax(r, -7.0), 7.0);
         q[h] = (int)r;
       }
+      // elements 2*lane (even) and 2*lane+1 (odd) of the group sit in word
+      // lane/4: even elements in the low half-word, odd ones in the high
+      // half-word, at nibble lane % 4 of each half
       const long long row = grp / G;  // over all E*N rows; N % 16 == 0
       const long long g = grp % G;
-      codes[(((row >> 4) * G + g) * 16 + (row & 15)) * 64 + lane] =
-          (uint8_t)((q[0] & 0xF) | ((q[1] & 0xF) << 4));
+      uint32_t wv = ((uint32_t)(q[0] & 0xF) << (4 * (lane & 3))) |
+                    ((uint32_t)(q[1] & 0xF) << (16 + 4 * (lane & 3)));
+      wv |= __shfl_xor(wv, 1, kWave);
+      wv |= __shfl_xor(wv, 2, kWave);
+      if ((lane & 3) == 0)
+        *(uint32_t*)(codes + (((row >> 4) * G + g) * 16 + (row & 15)) * 64 + lane) = wv;
     } else {
       int u[2];
       const float vv[2] = {v.x, v.y};

@@ -77,12 +77,24 @@ class HostLayer:
         return self._cache[e]
 
 
+# nibble i of a code word holds element W4_NIBBLE_ELEMENT[i] of its 8
+W4_NIBBLE_ELEMENT = np.array([0, 2, 4, 6, 1, 3, 5, 7])
+
+
 def w4_untile(codes, N, K):
-    """The library's tiled int4 codes of one N x K matrix ([N/16][K/128][16][64]
-    bytes, include/moe_wq.h) -> the row-major [N][K/2] packing of the oracle.
-    A pure byte permutation; the nibbles are unchanged."""
+    """The library's int4 codes of one N x K matrix (include/moe_wq.h: 16-row
+    tiles [N/16][K/128][16][64] bytes; 32-bit word j of a row's group holds
+    elements 8j..8j+7, even ones in nibbles 0-3, odd ones in nibbles 4-7)
+    -> the oracle's row-major packing [N][K/2] (byte b: element 2b in the low
+    nibble, 2b+1 in the high nibble).  A pure rearrangement of nibbles."""
     t = np.asarray(codes, np.uint8).reshape(N // 16, K // 128, 16, 64)
-    return t.transpose(0, 2, 1, 3).reshape(N, K // 2)
+    t = t.transpose(0, 2, 1, 3).reshape(N, K // 8, 4).astype(np.uint32)
+    words = t[..., 0] | (t[..., 1] << 8) | (t[..., 2] << 16) | (t[..., 3] << 24)
+    elems = np.empty((N, K // 8, 8), np.uint8)
+    for i in range(8):
+        elems[:, :, W4_NIBBLE_ELEMENT[i]] = (words >> (4 * i)) & 0xF
+    elems = elems.reshape(N, K)
+    return (elems[:, 0::2] | (elems[:, 1::2] << 4)).astype(np.uint8)
 
 
 def assert_codes_equal(dev_layer, host_layer, experts):

@@ -133,8 +133,10 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
 
 
 def test_w4_untile_matches_header_formula():
-    """The tests' untiling of int4 codes follows the byte-offset formula the
-    ABI header states: row n, group g -> (((n/16)*(K/128) + g)*16 + n%16)*64."""
+    """The tests' untiling of int4 codes follows the layout the ABI header
+    states: row n, element k lives in the 32-bit word at byte offset
+    (((n/16)*(K/128) + k/128)*16 + n%16)*64 + 4*((k%128)/8), in nibble
+    e/2 for even e = k%8 and 4 + e/2 for odd e."""
     import sys
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from layer_data import w4_untile
@@ -143,7 +145,12 @@ def test_w4_untile_matches_header_formula():
     tiled = np.random.default_rng(5).integers(0, 256, N * K // 2, dtype=np.uint8)
     rm = w4_untile(tiled, N, K)
     for n in range(N):
-        for j in range(K // 2):
-            g, o = divmod(j, 64)
-            off = (((n // 16) * (K // 128) + g) * 16 + n % 16) * 64 + o
-            assert rm[n, j] == tiled[off]
+        for k in range(K):
+            g, w = divmod(k, 128)
+            off = (((n // 16) * (K // 128) + g) * 16 + n % 16) * 64 + 4 * (w // 8)
+            word = int.from_bytes(bytes(tiled[off:off + 4]), "little")
+            e = k % 8
+            nib = e // 2 if e % 2 == 0 else 4 + e // 2
+            want = (word >> (4 * nib)) & 0xF
+            got = (rm[n, k // 2] >> (4 * (k % 2))) & 0xF
+            assert got == want, (n, k)
