@@ -167,11 +167,15 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E,
  *     gate_up_codes: R = E*2f, K = d (E*f*d bytes);  gate_up_scales fp16
  *     [E][2f][d/128];  down_codes: R = E*d, K = f;  down_scales fp16
  *     [E][d][f/128].
- *   MOE_FMT_BITPLANE8 (u = 8-bit offset code, w ~ s * (u - 128)):
- *     gate_up_codes u8 [E][8][2f][d/8]: plane slab p holds bit 7-p of u
- *       (most significant first: the top b planes are slabs 0..b-1); bit i
- *       of byte (n, j) belongs to element 8j + i.
- *     down_codes u8 [E][8][d][f/8]; scales as for int4.
+ *   MOE_FMT_BITPLANE8 (u = 8-bit offset code, w ~ s * (u - 128)): a matrix
+ *   of R rows (as for int4) and K inputs is stored as u8
+ *   [R/16][K/128][8][16][16]: for 16-row tile n/16 and group g a 2 KiB
+ *   block holds the 8 planes, plane p (bit 7-p of u, most significant
+ *   first) as 16 rows x 16 bytes; bit i of byte j of row n%16 belongs to
+ *   element 128g + 8j + i.  The top b planes of every block are its first
+ *   256 b bytes: a b-bit read loads only those.
+ *     gate_up_codes: R = E*2f, K = d;  down_codes: R = E*d, K = f;
+ *     scales as for int4.
  * Bit-widths (bitplane only): bits_mode MOE_BITS_PER_PAIR (bits u8 [T*k],
  *   indexed by pair p), MOE_BITS_PER_EXPERT (bits u8 [E]) or
  *   MOE_BITS_RANK_RULE (bits NULL; requires k == 8); values in [1, 8].
@@ -227,8 +231,8 @@ int moe_set_ffn_events(void *gateup_begin, void *gateup_end,
  *   (R = E*N rows; requires N % 16 == 0), scales fp16 [E][N][K/128].
  * moe_quantize_bitplane8 ([PagedMoE] abstract, bitplane prefixes):
  *   s = fp16_rne(max|w| / 127), u = clamp(rne(w / s) + 128, 0, 255), u = 128
- *   when s == 0.  planes u8 [E][8][N][K/8] (layout as above), scales fp16
- *   [E][N][K/128].
+ *   when s == 0.  planes: E*N*K bytes in the bitplane layout above (R = E*N
+ *   rows; requires N % 16 == 0), scales fp16 [E][N][K/128].
  * Codes and scales are bit-identical to the CPU definition.  Weights with
  * max|w| above 7 * 65504 (fp16 overflow of the scale) are unsupported.
  * ------------------------------------------------------------------- */

@@ -200,7 +200,12 @@ def moe_quantize_w4(w, codes=None, scales=None, stream=None):
 
 
 def moe_quantize_bitplane8(w, planes=None, scales=None, stream=None):
-    """fp32 [E][N][K] -> (planes u8 [E][8][N][K/8], scales [E][N][K/128])."""
+    """fp32 [E][N][K] -> (planes, scales fp16-bits [E][N][K/128]).
+
+    planes is a u8 tensor of shape [E][8][N][K/8] holding the bitplane layout
+    of include/moe_wq.h (per expert [N/16][K/128][8][16][16] bytes);
+    N % 16 == 0.
+    """
     import torch
     E, N, K = w.shape
     if planes is None:

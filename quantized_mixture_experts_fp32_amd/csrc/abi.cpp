@@ -217,8 +217,8 @@ static int quantize_common(const float* w, int E, int N, int K, int group,
     return fail(MOE_ERR_INVALID_ARG, "quantize: bad size");
   if (group != MOE_GROUP) return fail(MOE_ERR_UNSUPPORTED, "group_size=%d", group);
   if (K % MOE_GROUP) return fail(MOE_ERR_UNSUPPORTED, "K=%d not a multiple of 128", K);
-  if (!bitplane && N % 16)
-    return fail(MOE_ERR_UNSUPPORTED, "quantize_w4: N=%d not a multiple of 16 (tiled rows)", N);
+  if (N % 16)
+    return fail(MOE_ERR_UNSUPPORTED, "quantize: N=%d not a multiple of 16 (tiled rows)", N);
   if ((long long)E * N == 0) return ok();
   if (!w || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "quantize: null pointer");
   if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 2))

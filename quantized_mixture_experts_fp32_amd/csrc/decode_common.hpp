@@ -1,0 +1,90 @@
+// Helpers shared by the decode-path (small batch) expert FFN kernels:
+// locating a work item's token tile from expert_offsets, staging routing
+// and group scales in LDS.
+#pragma once
+#include "kcommon.hpp"
+
+namespace moe {
+namespace dec {
+
+struct TileInfo {
+  int e, r0, cnt;
+};
+
+// Tile b of the list "every expert's slot range cut into tiles of tok
+// pairs, experts in ascending order".  Wave-cooperative (all lanes call it
+// with the same b and get the same answer); returns false past the end.
+__device__ inline bool find_tile(const int32_t* __restrict__ offsets, int E, int tok,
+                          int b, TileInfo& t) {
+  const int lane = threadIdx.x & 63;
+  int carry = 0;
+  for (int base = 0; base < E; base += 64) {
+    const int e = base + lane;
+    const int lo = (e < E) ? offsets[e] : 0;
+    const int n = (e < E) ? offsets[e + 1] - lo : 0;
+    const int c = (n + tok - 1) / tok;
+    int s = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(s, o, kWave);
+      if (lane >= o) s += v;
+    }
+    const int total = __shfl(s, 63, kWave);
+    if (b < carry + total) {
+      const uint64_t m = __ballot(carry + s > b);
+      const int L = __ffsll((unsigned long long)m) - 1;
+      const int sL = __shfl(s, L, kWave), cL = __shfl(c, L, kWave);
+      const int loL = __shfl(lo, L, kWave), nL = __shfl(n, L, kWave);
+      const int chunk = b - (carry + sL - cL);
+      t.e = base + L;
+      t.r0 = loL + chunk * tok;
+      t.cnt = min(tok, nL - chunk * tok);
+      return true;
+    }
+    carry += total;
+  }
+  return false;
+}
+
+__device__ __forceinline__ bf16x8 bf16_splat(uint32_t bits16) {
+  const uint32_t p = bits16 | (bits16 << 16);
+  u32x4 r = {p, p, p, p};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// The kernels below stage expert_offsets and (when it fits) sorted_pair in
+// LDS once per persistent block; a work item then needs one round trip to
+// HBM: all of a wave's code, scale and activation loads are issued together.
+constexpr int kPairsInLds = 4096;
+
+__device__ __forceinline__ int stage_routing(const int32_t* __restrict__ offsets,
+                                             const int32_t* __restrict__ sorted_pair,
+                                             int E, int P, int32_t* off_lds,
+                                             int32_t* sp_lds) {
+  for (int i = threadIdx.x; i <= E; i += blockDim.x) off_lds[i] = offsets[i];
+  const int np = P <= kPairsInLds ? P : 0;
+  for (int i = threadIdx.x; i < np; i += blockDim.x) sp_lds[i] = sorted_pair[i];
+  return np;
+}
+
+
+
+
+// Scales of 64 rows per matrix staged as fp32 in LDS, [matrix][group][row],
+// for a 256-thread block: thread t owns row t % 64 (of matrix (t / 64) % NMAT)
+// and every (256 / (64 NMAT))-th group.
+template <int NMAT>
+__device__ __forceinline__ void stage_scales_rows64(const uint16_t* __restrict__ rows_src,
+                                                    size_t mat_stride, int G,
+                                                    float* __restrict__ dst) {
+  constexpr int kStep = 256 / (64 * NMAT);
+  const int r = threadIdx.x & 63, m = (threadIdx.x >> 6) % NMAT, g0 = (threadIdx.x >> 6) / NMAT;
+  const uint16_t* src = rows_src + ((size_t)m * mat_stride + r) * G;
+  float* d = dst + (size_t)m * G * 64 + r;
+  for (int g = g0; g < G; g += kStep) d[g * 64] = f16_bits_to_f32(src[g]);
+}
+
+constexpr int kXRow = 136;  // bf16 per staged activation row (128 + 8 pad)
+
+}  // namespace dec
+}  // namespace moe

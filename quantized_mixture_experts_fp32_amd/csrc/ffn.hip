@@ -30,18 +30,6 @@ struct Tile {
 };
 
 // Bit-width of pair p (values outside [1, 8] are clamped into it).
-__device__ __forceinline__ int pair_bit_width(int p, int e, int k, int mode,
-                                              const uint8_t* bits) {
-  switch (mode) {
-    case 1: return min(max((int)bits[p], 1), 8);
-    case 2: return min(max((int)bits[e], 1), 8);
-    case 3: {
-      const int j = p % k;
-      return j == 0 ? 8 : (j < 4 ? 4 : 2);
-    }
-    default: return 8;
-  }
-}
 
 // One block of up to 1024 threads, one thread per expert.
 __global__ __launch_bounds__(1024) void ffn_prep(
@@ -87,15 +75,20 @@ __global__ __launch_bounds__(1024) void ffn_prep(
 
 // ---------------------------------------------------------------- weights
 // bitplane: one dword per plane p < maxb holds bit 7-p of the lane's 32
-// elements (bit position = element offset).  For class b the K-values are
-// v_b = (u with 8-b low bits cleared) + 2^(7-b) - 128, or u - 128 for b = 8.
-__device__ __forceinline__ void bp_load(const uint8_t* plane0, size_t slab,
-                                        int g, int kq, int maxb,
+// elements (bit position = element offset).  Planes are stored per 16-row
+// tile and 128-group as a 2 KiB block of 8 planes x 16 rows x 16 bytes;
+// tb = codes + (row / 16) * G * 2048 + (row % 16) * 16.  For class b the
+// K-values are v_b = (u with 8-b low bits cleared) + 2^(7-b) - 128, or
+// u - 128 for b = 8.
+__device__ __forceinline__ const uint8_t* bp_tile(const uint8_t* codes, size_t row, int G) {
+  return codes + (row >> 4) * (size_t)G * 2048 + 16 * (row & 15);
+}
+
+__device__ __forceinline__ void bp_load(const uint8_t* tb, int g, int kq, int maxb,
                                         uint32_t pl[8]) {
 #pragma unroll
   for (int p = 0; p < 8; ++p)
-    pl[p] = (p < maxb) ? *(const uint32_t*)(plane0 + p * slab + 16 * g + 4 * kq)
-                       : 0u;
+    pl[p] = (p < maxb) ? *(const uint32_t*)(tb + (size_t)g * 2048 + 256 * p + 4 * kq) : 0u;
 }
 
 __device__ __forceinline__ void bp_frags(const uint32_t pl[8], int b,
@@ -177,11 +170,9 @@ __global__ __launch_bounds__(kThreads) void gateup_kernel(
       pu[c] = f32x4{0, 0, 0, 0};
     }
     {
-      const size_t slab = rows2f * (size_t)(d >> 3);
-      const uint8_t* base = codes + (size_t)tl.e * 8 * slab;
       uint32_t plg[8], plu[8];
-      bp_load(base + (size_t)(n0 + col) * (d >> 3), slab, g, kq, tl.maxb, plg);
-      bp_load(base + (size_t)(f + n0 + col) * (d >> 3), slab, g, kq, tl.maxb, plu);
+      bp_load(bp_tile(codes, (size_t)tl.e * rows2f + n0 + col, G), g, kq, tl.maxb, plg);
+      bp_load(bp_tile(codes, (size_t)tl.e * rows2f + f + n0 + col, G), g, kq, tl.maxb, plu);
       for (int b = 1; b <= 8; ++b) {
         if (!((cls >> b) & 1u)) continue;
         bf16x8 ag[4], au[4];
@@ -291,10 +282,8 @@ __global__ __launch_bounds__(kThreads) void down_kernel(
 #pragma unroll
     for (int c = 0; c < NT; ++c) pa[c] = f32x4{0, 0, 0, 0};
     {
-      const size_t slab = (size_t)d * (size_t)(f >> 3);
       uint32_t pl[8];
-      bp_load(codes + (size_t)tl.e * 8 * slab + (size_t)(m0 + col) * (f >> 3),
-              slab, g, kq, tl.maxb, pl);
+      bp_load(bp_tile(codes, (size_t)tl.e * d + m0 + col, G), g, kq, tl.maxb, pl);
       for (int b = 1; b <= 8; ++b) {
         if (!((cls >> b) & 1u)) continue;
         bf16x8 a[4];
@@ -390,6 +379,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
     return launch_ffn_prefill_w4(a, h, pws, s);
   }
   // bitplane prefixes (int4 always resolves to one of the two paths above)
+  if (a.path == 1 && ffn_decode_bp_applies(P, a.E, a.f)) return launch_ffn_decode_bp(a, h, s);
   if (a.path == 2) return run_ffn<4>(a, s);
   return run_ffn<2>(a, s);
 }

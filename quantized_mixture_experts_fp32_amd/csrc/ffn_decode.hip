@@ -34,50 +34,13 @@
 
 #include "kcommon.hpp"
 #include "launch.hpp"
+#include "decode_common.hpp"
 
 namespace moe {
 namespace {
+using namespace dec;
 
 constexpr int kTileGroupBytes = 16 * 64;  // one 16-row tile x one 128-group
-
-struct TileInfo {
-  int e, r0, cnt;
-};
-
-// Tile b of the list "every expert's slot range cut into tiles of tok
-// pairs, experts in ascending order".  Wave-cooperative (all lanes call it
-// with the same b and get the same answer); returns false past the end.
-__device__ bool find_tile(const int32_t* __restrict__ offsets, int E, int tok,
-                          int b, TileInfo& t) {
-  const int lane = threadIdx.x & 63;
-  int carry = 0;
-  for (int base = 0; base < E; base += 64) {
-    const int e = base + lane;
-    const int lo = (e < E) ? offsets[e] : 0;
-    const int n = (e < E) ? offsets[e + 1] - lo : 0;
-    const int c = (n + tok - 1) / tok;
-    int s = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(s, o, kWave);
-      if (lane >= o) s += v;
-    }
-    const int total = __shfl(s, 63, kWave);
-    if (b < carry + total) {
-      const uint64_t m = __ballot(carry + s > b);
-      const int L = __ffsll((unsigned long long)m) - 1;
-      const int sL = __shfl(s, L, kWave), cL = __shfl(c, L, kWave);
-      const int loL = __shfl(lo, L, kWave), nL = __shfl(n, L, kWave);
-      const int chunk = b - (carry + sL - cL);
-      t.e = base + L;
-      t.r0 = loL + chunk * tok;
-      t.cnt = min(tok, nL - chunk * tok);
-      return true;
-    }
-    carry += total;
-  }
-  return false;
-}
 
 // One code word (elements 8j..8j+7, even ones in nibbles 0-3, odd ones in
 // nibbles 4-7) -> bf16 (136 + q) of the 8 elements in order.
@@ -96,31 +59,7 @@ __device__ __forceinline__ bf16x8 w4_magic(uint32_t w) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-__device__ __forceinline__ bf16x8 bf16_splat(uint32_t bits16) {
-  const uint32_t p = bits16 | (bits16 << 16);
-  u32x4 r = {p, p, p, p};
-  return __builtin_bit_cast(bf16x8, r);
-}
-
 constexpr uint32_t kBf16NegOff = 0xC308u;  // -136.0, the conversion offset
-
-
-// The kernels below stage expert_offsets and (when it fits) sorted_pair in
-// LDS once per persistent block; a work item then needs one round trip to
-// HBM: all of a wave's code, scale and activation loads are issued together.
-constexpr int kPairsInLds = 4096;
-
-__device__ __forceinline__ int stage_routing(const int32_t* __restrict__ offsets,
-                                             const int32_t* __restrict__ sorted_pair,
-                                             int E, int P, int32_t* off_lds,
-                                             int32_t* sp_lds) {
-  for (int i = threadIdx.x; i <= E; i += blockDim.x) off_lds[i] = offsets[i];
-  const int np = P <= kPairsInLds ? P : 0;
-  for (int i = threadIdx.x; i < np; i += blockDim.x) sp_lds[i] = sorted_pair[i];
-  return np;
-}
-
-
 
 
 // Scales of a work item, staged once as fp32 in LDS: [matrix][group][row].
@@ -392,20 +331,6 @@ void down_w4_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
 
 
 
-// Scales of 64 rows per matrix staged as fp32 in LDS, [matrix][group][row],
-// for a 256-thread block: thread t owns row t % 64 (of matrix (t / 64) % NMAT)
-// and every (256 / (64 NMAT))-th group.
-template <int NMAT>
-__device__ __forceinline__ void stage_scales_rows64(const uint16_t* __restrict__ rows_src,
-                                                    size_t mat_stride, int G,
-                                                    float* __restrict__ dst) {
-  constexpr int kStep = 256 / (64 * NMAT);
-  const int r = threadIdx.x & 63, m = (threadIdx.x >> 6) % NMAT, g0 = (threadIdx.x >> 6) / NMAT;
-  const uint16_t* src = rows_src + ((size_t)m * mat_stride + r) * G;
-  float* d = dst + (size_t)m * G * 64 + r;
-  for (int g = g0; g < G; g += kStep) d[g * 64] = f16_bits_to_f32(src[g]);
-}
-
 // ------------------------------------------- single K slice, one token tile
 // When every wave streams the whole K range of its own 16-feature row tile
 // (KS = 1, tiles of up to 16 pairs), the four waves of a block share one
@@ -416,8 +341,6 @@ __device__ __forceinline__ void stage_scales_rows64(const uint16_t* __restrict__
 // counter to the codes alone, so the code stream can run kDQ groups ahead
 // of the MFMAs.  The arithmetic (operands,
 // MFMA order, scaling) is the same as in the kernels above.
-constexpr int kXRow = 136;  // bf16 per staged activation row (128 + 8 pad)
-
 template <int kDQ, int kWaves>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
 void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,

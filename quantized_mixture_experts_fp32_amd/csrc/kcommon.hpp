@@ -78,4 +78,21 @@ __device__ __forceinline__ float silu_f32(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
+// Bit-width of grouped pair p (flat index t*k + rank) of expert e under a
+// bits mode: 1 per-pair array, 2 per-expert array, 3 rank rule (rank 1 ->
+// 8 bits, ranks 2-4 -> 4, ranks 5-8 -> 2), otherwise 8.  Values clamp to
+// [1, 8].
+__device__ __forceinline__ int pair_bit_width(int p, int e, int k, int mode,
+                                              const uint8_t* bits) {
+  switch (mode) {
+    case 1: return min(max((int)bits[p], 1), 8);
+    case 2: return min(max((int)bits[e], 1), 8);
+    case 3: {
+      const int j = p % k;
+      return j == 0 ? 8 : (j < 4 ? 4 : 2);
+    }
+    default: return 8;
+  }
+}
+
 }  // namespace moe

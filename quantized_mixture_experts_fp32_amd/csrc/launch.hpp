@@ -41,6 +41,10 @@ struct FfnArgs {
 size_t ffn_ws_bytes(int T, int k, int E, int d, int f, int format);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 // decode path for int4 experts (ffn_decode.hip); h = bf16 [P][f] scratch
+// Bitplane experts, small batches: true when every wave can stream a whole
+// K range (the single-slice decode kernels apply).
+bool ffn_decode_bp_applies(long long P, int E, int f);
+hipError_t launch_ffn_decode_bp(const FfnArgs& a, uint16_t* h, hipStream_t s);
 hipError_t launch_ffn_decode_w4(const FfnArgs& a, uint16_t* h, hipStream_t s);
 // prefill path for int4 experts (ffn_prefill.hip); ws: its own scratch
 size_t ffn_prefill_ws_bytes(int T, int k, int E, int d, int f);

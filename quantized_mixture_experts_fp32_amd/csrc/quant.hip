@@ -8,7 +8,9 @@
 //    the kernels' nibble-to-bf16 conversion yields them in order.
 //  bitplane8 (PagedMoE, abstract: one stored state, bitplane prefixes):
 //    s = fp16_rne(max|w|/127), u = clamp(rne(w/s) + 128, 0, 255), u = 128 if
-//    s == 0; plane slab p holds bit 7-p, bit i of a byte is element 8j + i.
+//    s == 0; per 16-row tile and 128-group a 2 KiB block holds the 8 planes
+//    (plane p = bit 7-p) of 16 rows x 16 bytes; bit i of byte j is element
+//    8j + i of the group.
 // Both quotients are evaluated in fp64, so each rounding is the rounding of
 // the exact quotient; codes and scales are bit-exact.
 #include "kcommon.hpp"
@@ -63,21 +65,19 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
         r = fmin(fmax(r, 0.0), 255.0);
         u[h] = (int)r;
       }
-      // element 2*lane and 2*lane+1 of the group; byte jj = lane/4 of the
-      // group's 16 bytes per plane, bit position 2*(lane%4) + h
-      const long long e = grp / (N * G);
-      const long long n = (grp / G) % N;
-      const int g = (int)(grp % G);
-      const long long slab = N * (long long)(K >> 3);
+      // elements 2*lane and 2*lane+1 of the group: byte lane/4 of the row's
+      // 16 bytes of each plane, bit positions 2*(lane%4) and +1; planes of a
+      // 16-row tile and group form one 2 KiB block (8 planes x 16 rows x 16)
+      const long long row = grp / G;  // over all E*N rows; N % 16 == 0
+      const long long g = grp % G;
+      uint8_t* blk = codes + ((row >> 4) * G + g) * 2048 + (row & 15) * 16 + (lane >> 2);
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
         uint32_t bits = (((u[0] >> (7 - p)) & 1) | (((u[1] >> (7 - p)) & 1) << 1))
                         << (2 * (lane & 3));
         bits |= __shfl_xor(bits, 1, kWave);
         bits |= __shfl_xor(bits, 2, kWave);
-        if ((lane & 3) == 0)
-          codes[(e * 8 + p) * slab + n * (K >> 3) + g * 16 + (lane >> 2)] =
-              (uint8_t)bits;
+        if ((lane & 3) == 0) blk[256 * p] = (uint8_t)bits;
       }
     }
   }

@@ -97,14 +97,26 @@ def w4_untile(codes, N, K):
     return (elems[:, 0::2] | (elems[:, 1::2] << 4)).astype(np.uint8)
 
 
+def bp_untile(planes, N, K):
+    """The library's bitplanes of one N x K matrix (include/moe_wq.h: per
+    16-row tile and 128-group a block of 8 planes x 16 rows x 16 bytes) ->
+    the oracle's plane-major layout [8][N][K/8].  A pure byte permutation."""
+    t = np.asarray(planes, np.uint8).reshape(N // 16, K // 128, 8, 16, 16)
+    return t.transpose(2, 0, 3, 1, 4).reshape(8, N, K // 8)
+
+
+def untile(codes, fmt, N, K):
+    return w4_untile(codes, N, K) if fmt == "w4" else bp_untile(codes, N, K)
+
+
 def assert_codes_equal(dev_layer, host_layer, experts):
     """Packed codes and fp16 scales of the listed experts are bit-identical."""
-    w4 = dev_layer.cfg.fmt == "w4"
+    fmt = dev_layer.cfg.fmt
     for e in experts:
         g, h = dev_layer.expert_codes(int(e)), host_layer.expert(int(e))
         for (dq, ds), (hq, hs) in zip(g, h):
-            if w4:
-                dq = w4_untile(dq, hq.shape[0], 2 * hq.shape[1])
+            N, K = hs.shape[0], 128 * hs.shape[1]
+            dq = untile(dq, fmt, N, K)
             assert np.array_equal(dq, hq.reshape(dq.shape)), f"codes of expert {e}"
             assert np.array_equal(ds, hs.reshape(ds.shape)), f"scales of expert {e}"
 

@@ -120,9 +120,10 @@ def test_combine_and_quantize_validation(lib):
     assert q(FAKE, 2, 4, 256, 64, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
     assert q(FAKE, 2, 4, 100, 128, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
     assert q(FAKE, 2, 4, 256, 128, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED  # rows tiled by 16
+    assert lib.moe_quantize_bitplane8(FAKE, 2, 8, 256, 128, FAKE, FAKE, NULL) == moe.MOE_ERR_UNSUPPORTED
     assert "16" in err(lib)
     assert q(NULL, 2, 16, 256, 128, FAKE, FAKE, NULL) == moe.MOE_ERR_INVALID_ARG
-    assert lib.moe_quantize_bitplane8(FAKE, 0, 4, 256, 128, NULL, NULL, NULL) == moe.MOE_OK
+    assert lib.moe_quantize_bitplane8(FAKE, 0, 16, 256, 128, NULL, NULL, NULL) == moe.MOE_OK
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
@@ -154,3 +155,22 @@ def test_w4_untile_matches_header_formula():
             want = (word >> (4 * nib)) & 0xF
             got = (rm[n, k // 2] >> (4 * (k % 2))) & 0xF
             assert got == want, (n, k)
+
+
+def test_bp_untile_matches_header_formula():
+    """The tests' untiling of bitplanes follows the ABI header: plane p of
+    row n, byte j of group g lives at ((n/16)*(K/128) + g)*2048 + 256 p +
+    16 (n%16) + j."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from layer_data import bp_untile
+    import numpy as np
+    N, K = 32, 256
+    tiled = np.random.default_rng(6).integers(0, 256, N * K, dtype=np.uint8)
+    pm = bp_untile(tiled, N, K)
+    for p in range(8):
+        for n in range(N):
+            for jj in range(K // 8):
+                g, j = divmod(jj, 16)
+                off = ((n // 16) * (K // 128) + g) * 2048 + 256 * p + 16 * (n % 16) + j
+                assert pm[p, n, jj] == tiled[off], (p, n, jj)

@@ -11,7 +11,7 @@ import oracle
 import synth
 import quantized_mixture_experts_fp32_amd as moe
 from layer_data import (DEV, DevLayer, HostLayer, assert_close, assert_codes_equal,
-                        bf16_rne_bits, custom_cfg, record, w4_untile,
+                        bf16_rne_bits, custom_cfg, record, untile,
                         stream)
 
 pytestmark = pytest.mark.gpu
@@ -65,10 +65,8 @@ def _edge_weights(rng, R, K):
 @pytest.mark.parametrize("fmt", ["w4", "bp8"])
 def test_quantize_bit_exact(fmt):
     rng = np.random.default_rng(7)
-    # int4 rows are tiled by 16; bitplanes take any row count
-    shapes = ([(2, 16, 256), (3, 48, 384), (1, 32, 2048)] if fmt == "w4"
-              else [(2, 8, 256), (3, 40, 384), (1, 5, 2048)])
-    for (E, N, K) in shapes:
+    # rows are tiled by 16
+    for (E, N, K) in [(2, 16, 256), (3, 48, 384), (1, 32, 2048)]:
         note(f"quantize {fmt} E={E} N={N} K={K}")
         w = np.stack([_edge_weights(rng, N, K) for _ in range(E)])
         wd = torch.from_numpy(w).to(DEV)
@@ -81,7 +79,7 @@ def test_quantize_bit_exact(fmt):
         torch.cuda.synchronize()
         c, s = codes.cpu().numpy(), scales.cpu().numpy().view(np.uint16)
         for e in range(E):
-            ce = w4_untile(c[e], N, K) if fmt == "w4" else c[e]
+            ce = untile(c[e], fmt, N, K)
             assert np.array_equal(ce, ref[e][0]), (fmt, e)
             assert np.array_equal(s[e], ref[e][1]), (fmt, e)
 
@@ -279,6 +277,24 @@ def test_layer_bitplane_bit_modes(mode):
     for path in PATHS:
         note(f"layer bitplane bits={mode} path={path}")
         check_layer(DevLayer(cfg, T), HostLayer(cfg, T), path, bm, bits)
+
+
+@pytest.mark.parametrize("mode", ["pair", "expert"])
+def test_layer_bitplane_single_slice_ragged(mode):
+    # the bitplane decode kernels with one K slice per wave: group counts 3
+    # (gate/up) and 13 (down) that are not multiples of the plane prefetch
+    # depth, experts spanning several tiles, every bit-width 1..8 in a tile
+    cfg = custom_cfg(15, d=384, E=128, k=4, f=1664, fmt="bp8", bias_sigma=2.0)
+    T = 32
+    rng = np.random.default_rng(12)
+    if mode == "pair":
+        bits, bm = rng.integers(1, 9, T * cfg.k).astype(np.uint8), moe.MOE_BITS_PER_PAIR
+    else:
+        bits, bm = rng.integers(1, 9, cfg.E).astype(np.uint8), moe.MOE_BITS_PER_EXPERT
+    note(f"layer bitplane single-slice T={T} bits={mode}")
+    lay, _ = check_layer(DevLayer(cfg, T), HostLayer(cfg, T), moe.MOE_PATH_DECODE, bm, bits)
+    cnt = np.diff(lay.offsets.cpu().numpy())
+    assert cnt.max() > 16
 
 
 def test_layer_zero_tokens():
