@@ -159,20 +159,32 @@ def run_workload(wl, warmup, hip, torch, np, synth, moe):
     flops_gu, flops_dn = 4.0 * P * d * f, 2.0 * P * d * f
 
     steps = wl.steps
-    ev = [[hip.event() for _ in range(4)] for _ in range(steps)]
     for i in range(warmup):
         layer.forward(xs[i % nx], out=out, path=wl.path, weights=copies[i % ncopies])
     torch.cuda.synchronize()
+
+    # pass 1, the measurement: `steps` plain layer steps between two events
     t_start, t_end = hip.event(), hip.event()
     hip.record(t_start, stream)
     wall0 = time.perf_counter()
     for i in range(steps):
-        moe.moe_set_ffn_events(*ev[i])
         layer.forward(xs[i % nx], out=out, path=wl.path, weights=copies[i % ncopies])
     hip.record(t_end, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = hip.ms(t_start, t_end)
+
+    # pass 2, the same steps again with start/stop events attached to the two
+    # expert-FFN kernel dispatches (per-kernel durations for the roofline)
+    ev = [[hip.event() for _ in range(4)] for _ in range(steps)]
+    i0, i1 = hip.event(), hip.event()
+    hip.record(i0, stream)
+    for i in range(steps):
+        moe.moe_set_ffn_events(*ev[i])
+        layer.forward(xs[i % nx], out=out, path=wl.path, weights=copies[i % ncopies])
+    hip.record(i1, stream)
+    torch.cuda.synchronize()
+    instr_ms = hip.ms(i0, i1)
     gu_ms = [hip.ms(e[0], e[1]) for e in ev]
     dn_ms = [hip.ms(e[2], e[3]) for e in ev]
     gu_b = sum(gu_bytes[i % nx] for i in range(steps))
@@ -180,14 +192,15 @@ def run_workload(wl, warmup, hip, torch, np, synth, moe):
     for e in ev:
         for h in e:
             hip.destroy(h)
-    hip.destroy(t_start)
-    hip.destroy(t_end)
+    for h in (t_start, t_end, i0, i1):
+        hip.destroy(h)
 
     ms_step = total_ms / steps
     rec = {
         "workload": wl.name, "config": cfg.name, "T": T, "d": d, "E": E, "k": k,
         "f": f, "format": "bitplane8-rank" if bp else "int4-g128",
         "ms_per_step": round(ms_step, 5), "tokens_per_s": round(T / (ms_step / 1e3), 1),
+        "ms_per_step_instrumented": round(instr_ms / steps, 5),
         "wall_s": round(wall, 3), "weight_copies": ncopies,
         "active_experts_avg": round(float(np.mean(active)), 2),
         "gateup_us": round(1e3 * float(np.mean(gu_ms)), 3),

@@ -137,6 +137,20 @@ int moe_permute(const int32_t *topk_idx, int T, int k, int E,
                 int32_t *pair_pos, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------
+ * moe_route_permute -- moe_route followed by moe_permute, with the same
+ * outputs bit for bit, in fewer launches for small batches (T <= 512: the
+ * logits kernel, then one block that selects every token's top-k and
+ * groups the pairs).  Arguments as for the two calls; ws / ws_bytes: at
+ * least moe_route_permute_ws_bytes(T, k, E).  T = 0 writes expert_offsets
+ * (all zero) and nothing else.
+ * ------------------------------------------------------------------- */
+size_t moe_route_permute_ws_bytes(int T, int k, int E);
+int moe_route_permute(const void *x_bf16, const void *wr_bf16, const float *bias,
+                      int T, int d, int E, int k, int32_t *topk_idx, float *topk_w,
+                      int32_t *expert_offsets, int32_t *sorted_pair, int32_t *pair_pos,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------
  * moe_expert_ffn_wq -- SwiGLU FFN of every grouped pair with quantized,
  * in-kernel dequantized expert weights.
  * [ExactMoE] Abstract (W4A16, grouped kernels); [PagedMoE] abstract
@@ -215,9 +229,11 @@ int moe_combine(const float *y_pairs, const int32_t *pair_pos,
  * moe_set_ffn_events -- optional timing instrumentation (no page defines
  * it; it serves throughput measurement).  Arms, for the NEXT
  * moe_expert_ffn_wq call made by the calling thread only, four hipEvent_t
- * handles (any may be NULL) that the call records on its stream
- * immediately before and after its gate/up kernel and its down kernel.
- * The events are created and owned by the caller.  Returns MOE_OK.
+ * handles (any may be NULL): the start and stop events of its gate/up
+ * kernel and of its down kernel, attached to those kernel dispatches
+ * (hipExtLaunchKernel), so that they time exactly the kernels and add no
+ * separate marker to the stream.  The events are created and owned by the
+ * caller.  Returns MOE_OK.
  * ------------------------------------------------------------------- */
 int moe_set_ffn_events(void *gateup_begin, void *gateup_end,
                        void *down_begin, void *down_end);

@@ -6,7 +6,8 @@ step of the layer runs in the library's HIP kernels.  PyTorch provides
 device memory and the current HIP stream.  There is no CPU fallback: the
 library must be built (`build.build()`) and a GPU present, or calls raise.
 
-Layer = moe_route -> moe_permute -> moe_expert_ffn_wq -> moe_combine.
+Layer = moe_route -> moe_permute -> moe_expert_ffn_wq -> moe_combine (the
+first two also as one call, moe_route_permute).
 """
 from __future__ import annotations
 
@@ -26,7 +27,8 @@ MOE_GROUP = 128
 # Every symbol the header declares (checked by the CPU tests).
 EXPORTS = ("moe_status_str", "moe_last_error", "moe_route_ws_bytes", "moe_route",
            "moe_permute_ws_bytes",
-           "moe_permute", "moe_ffn_ws_bytes", "moe_expert_ffn_wq", "moe_combine",
+           "moe_permute", "moe_route_permute_ws_bytes", "moe_route_permute",
+           "moe_ffn_ws_bytes", "moe_expert_ffn_wq", "moe_combine",
            "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events")
 
 
@@ -55,6 +57,10 @@ def load_library():
     lib.moe_route.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.moe_permute_ws_bytes.argtypes, lib.moe_permute_ws_bytes.restype = [i32, i32, i32], sz
     lib.moe_permute.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.moe_route_permute_ws_bytes.argtypes = [i32, i32, i32]
+    lib.moe_route_permute_ws_bytes.restype = sz
+    lib.moe_route_permute.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                      vp, sz, vp]
     lib.moe_ffn_ws_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.moe_ffn_ws_bytes.restype = sz
     lib.moe_expert_ffn_wq.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
@@ -63,7 +69,8 @@ def load_library():
     lib.moe_quantize_w4.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
     lib.moe_quantize_bitplane8.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
     lib.moe_set_ffn_events.argtypes = [vp, vp, vp, vp]
-    for name in ("moe_route", "moe_permute", "moe_expert_ffn_wq", "moe_combine",
+    for name in ("moe_route", "moe_permute", "moe_route_permute", "moe_expert_ffn_wq",
+                 "moe_combine",
                  "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events"):
         getattr(lib, name).restype = i32
     _lib = lib
@@ -140,6 +147,37 @@ def moe_permute(topk_idx, E, ws=None, offsets=None, sorted_pair=None,
         _ptr(topk_idx), T, k, E, _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos),
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return offsets, sorted_pair, pair_pos
+
+
+def moe_route_permute_ws_bytes(T, k, E):
+    return int(load_library().moe_route_permute_ws_bytes(T, k, E))
+
+
+def moe_route_permute(x, wr, bias, k, ws=None, topk_idx=None, topk_w=None, offsets=None,
+                      sorted_pair=None, pair_pos=None, stream=None):
+    """moe_route then moe_permute in one call -> (idx, w, offsets, sorted_pair,
+    pair_pos)."""
+    import torch
+    T, d = x.shape
+    E = wr.shape[0]
+    P = T * k
+    if topk_idx is None:
+        topk_idx = _empty((T, k), torch.int32, x)
+    if topk_w is None:
+        topk_w = _empty((T, k), torch.float32, x)
+    if offsets is None:
+        offsets = _empty((E + 1,), torch.int32, x)
+    if sorted_pair is None:
+        sorted_pair = _empty((P,), torch.int32, x)
+    if pair_pos is None:
+        pair_pos = _empty((P,), torch.int32, x)
+    if ws is None:
+        ws = _empty((max(moe_route_permute_ws_bytes(T, k, E), 16),), torch.uint8, x)
+    _check("moe_route_permute", load_library().moe_route_permute(
+        _ptr(x), _ptr(wr), _ptr(bias), T, d, E, k, _ptr(topk_idx), _ptr(topk_w),
+        _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+    return topk_idx, topk_w, offsets, sorted_pair, pair_pos
 
 
 def moe_ffn_ws_bytes(T, k, E, d, f, fmt=MOE_FMT_W4_SYM):
@@ -229,7 +267,8 @@ def moe_set_ffn_events(gateup_begin=None, gateup_end=None, down_begin=None,
 # --------------------------------------------------------- one whole layer
 class MoeLayer:
     """Resident quantized expert weights plus preallocated buffers for one
-    batch size; `forward(x)` enqueues the four ABI calls on one stream."""
+    batch size; `forward(x)` enqueues route+permute, the expert FFN and the
+    combine on one stream."""
 
     def __init__(self, wr, bias, k, f, gate_up_codes, gate_up_scales,
                  down_codes, down_scales, fmt=MOE_FMT_W4_SYM,
@@ -251,10 +290,8 @@ class MoeLayer:
         self.offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
         self.sorted_pair = torch.empty((P,), dtype=torch.int32, device=dev)
         self.pair_pos = torch.empty((P,), dtype=torch.int32, device=dev)
-        self.ws_route = torch.empty((max(moe_route_ws_bytes(T, E), 16),),
-                                    dtype=torch.uint8, device=dev)
-        self.ws_perm = torch.empty((max(moe_permute_ws_bytes(T, k, E), 16),),
-                                   dtype=torch.uint8, device=dev)
+        self.ws_rp = torch.empty((max(moe_route_permute_ws_bytes(T, k, E), 16),),
+                                 dtype=torch.uint8, device=dev)
         self.ws_ffn = torch.empty((max(moe_ffn_ws_bytes(T, k, E, d, f, self.fmt), 256),),
                                   dtype=torch.uint8, device=dev)
         self.y_pairs = torch.empty((P, d), dtype=torch.float32, device=dev)
@@ -267,10 +304,9 @@ class MoeLayer:
             self._alloc(T, x)
         gu, gus, dn, dns = weights if weights is not None else (
             self.gu, self.gus, self.dn, self.dns)
-        moe_route(x, self.wr, self.bias, self.k, self.topk_idx, self.topk_w,
-                  self.ws_route, stream)
-        moe_permute(self.topk_idx, self.E, self.ws_perm, self.offsets,
-                    self.sorted_pair, self.pair_pos, stream)
+        moe_route_permute(x, self.wr, self.bias, self.k, self.ws_rp, self.topk_idx,
+                          self.topk_w, self.offsets, self.sorted_pair, self.pair_pos,
+                          stream)
         moe_expert_ffn_wq(x, self.offsets, self.sorted_pair, self.k, self.f, gu, gus,
                           dn, dns, self.fmt, self.bits, self.bits_mode,
                           self.y_pairs, self.ws_ffn, path, stream)

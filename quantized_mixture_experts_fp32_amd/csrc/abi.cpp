@@ -117,6 +117,35 @@ int moe_permute(const int32_t* topk_idx, int T, int k, int E,
                     "moe_permute");
 }
 
+size_t moe_route_permute_ws_bytes(int T, int k, int E) {
+  if (T < 0 || k <= 0 || E <= 0) return 0;
+  return moe::route_permute_ws_bytes(T, k, E);
+}
+
+int moe_route_permute(const void* x_bf16, const void* wr_bf16, const float* bias, int T,
+                      int d, int E, int k, int32_t* topk_idx, float* topk_w,
+                      int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                      void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(T, d, E, k);
+  if (rc) return rc;
+  if (!expert_offsets) return fail(MOE_ERR_INVALID_ARG, "moe_route_permute: null offsets");
+  if (T > 0 && (!x_bf16 || !wr_bf16 || !topk_idx || !topk_w || !sorted_pair || !pair_pos))
+    return fail(MOE_ERR_INVALID_ARG, "moe_route_permute: null pointer");
+  const size_t need = moe::route_permute_ws_bytes(T, k, E);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_route_permute: workspace %zu < %zu bytes",
+                ws ? ws_bytes : (size_t)0, need);
+  if (!aligned(ws, 16) || !aligned(expert_offsets, 4) ||
+      (T > 0 && (!aligned(x_bf16, 16) || !aligned(wr_bf16, 16) || !aligned(topk_idx, 4) ||
+                 !aligned(topk_w, 4) || (bias && !aligned(bias, 4)) ||
+                 !aligned(sorted_pair, 4) || !aligned(pair_pos, 4))))
+    return fail(MOE_ERR_INVALID_ARG, "moe_route_permute: misaligned pointer");
+  return hip_status(moe::launch_route_permute(x_bf16, wr_bf16, bias, T, d, E, k, topk_idx,
+                                              topk_w, expert_offsets, sorted_pair, pair_pos,
+                                              ws, (hipStream_t)stream),
+                    "moe_route_permute");
+}
+
 size_t moe_ffn_ws_bytes(int T, int k, int E, int d, int f, int format) {
   if (T < 0 || k <= 0 || E <= 0 || d <= 0 || f <= 0) return 0;
   return moe::ffn_ws_bytes(T, k, E, d, f, format);

@@ -345,16 +345,13 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t s) {
                      a.sorted_pair, a.E, a.k, tok, a.bits_mode,
                      a.bits, tiles, num_tiles);
   dim3 g1((unsigned)mt, a.f / 16), g2((unsigned)mt, a.d / 16);
-  if (a.ev[0]) hipEventRecord(a.ev[0], s);
-  hipLaunchKernelGGL((gateup_kernel<NT>), g1, dim3(kThreads), 0, s,
-                     a.x, a.sorted_pair, a.k, a.d, a.f, a.gu_codes,
+  launch_k(gateup_kernel<NT>, g1, dim3(kThreads), 0, s, a.ev[0], a.ev[1],
+           a.x, a.sorted_pair, a.k, a.d, a.f, a.gu_codes,
                      a.gu_scales, a.bits_mode, a.bits, tiles, num_tiles, h);
-  if (a.ev[1]) hipEventRecord(a.ev[1], s);
-  if (a.ev[2]) hipEventRecord(a.ev[2], s);
-  hipLaunchKernelGGL((down_kernel<NT>), g2, dim3(kThreads), 0, s, h,
+  launch_k(down_kernel<NT>, g2, dim3(kThreads), 0, s, a.ev[2], a.ev[3],
+           h,
                      a.sorted_pair, a.k, a.d, a.f, a.dn_codes, a.dn_scales,
                      a.bits_mode, a.bits, tiles, num_tiles, a.y);
-  if (a.ev[3]) hipEventRecord(a.ev[3], s);
   return hipGetLastError();
 }
 

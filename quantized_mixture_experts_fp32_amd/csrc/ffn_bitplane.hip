@@ -330,22 +330,20 @@ hipError_t launch_ffn_decode_bp(const FfnArgs& a, uint16_t* h, hipStream_t s) {
     const int grid = (int)(work < cap ? work : cap);
     const size_t lds = off_b + sizeof(int32_t) * ((std::min<long long>(P, kPairsInLds) + 3) & ~3) +
                        sizeof(float) * 2 * G * 64 + xs_b;
-    if (a.ev[0]) hipEventRecord(a.ev[0], s);
-    hipLaunchKernelGGL((gateup_bp_decode<kBpDQ, kBpWaves>), dim3(grid), dim3(256), lds, s, a.x,
+    launch_k(gateup_bp_decode<kBpDQ, kBpWaves>, dim3(grid), dim3(256), lds, s, a.ev[0], a.ev[1],
+             a.x,
                        a.offsets, a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes,
                        a.gu_scales, a.bits_mode, a.bits, h);
-    if (a.ev[1]) hipEventRecord(a.ev[1], s);
   }
   {
     const int G = a.f / 128;
     const long long work = mt * (a.d / 64);
     const int grid = (int)(work < cap ? work : cap);
     const size_t lds = off_b + sizeof(float) * G * 64 + xs_b;
-    if (a.ev[2]) hipEventRecord(a.ev[2], s);
-    hipLaunchKernelGGL((down_bp_decode<kBpDQ, kBpWaves>), dim3(grid), dim3(256), lds, s, h,
+    launch_k(down_bp_decode<kBpDQ, kBpWaves>, dim3(grid), dim3(256), lds, s, a.ev[2], a.ev[3],
+             h,
                        a.offsets, a.sorted_pair, a.E, a.k, a.d, a.f, a.dn_codes, a.dn_scales,
                        a.bits_mode, a.bits, a.y);
-    if (a.ev[3]) hipEventRecord(a.ev[3], s);
   }
   return hipGetLastError();
 }

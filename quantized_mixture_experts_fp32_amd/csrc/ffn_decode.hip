@@ -512,21 +512,18 @@ void launch_decode_pair(const FfnArgs& a, uint16_t* h, long long P, hipStream_t 
     const int grid = (int)(work < cap ? work : cap);
     const size_t lds = off_b + sizeof(int32_t) * ((std::min<long long>(P, kPairsInLds) + 3) & ~3) +
                        sizeof(float) * 2 * G * 16 * RT + sizeof(f32x4) * 4 * NT * 2 * 64;
-    if (a.ev[0]) hipEventRecord(a.ev[0], s);
-    hipLaunchKernelGGL((gateup_w4_decode<KS, NT, gu_depth<KS, NT>(), gu_waves<KS, NT>()>), dim3(grid), dim3(256), lds, s, a.x,
-                       a.offsets, a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes,
-                       a.gu_scales, h);
-    if (a.ev[1]) hipEventRecord(a.ev[1], s);
+    launch_k(gateup_w4_decode<KS, NT, gu_depth<KS, NT>(), gu_waves<KS, NT>()>, dim3(grid),
+             dim3(256), lds, s, a.ev[0], a.ev[1], a.x, a.offsets, a.sorted_pair, a.E, a.k,
+             (int)P, a.d, a.f, a.gu_codes, a.gu_scales, h);
   }
   {
     const int G = a.f / 128;
     const long long work = mt * (a.d / (16 * RT));
     const int grid = (int)(work < cap ? work : cap);
     const size_t lds = off_b + sizeof(float) * G * 16 * RT + sizeof(f32x4) * 4 * NT * 64;
-    if (a.ev[2]) hipEventRecord(a.ev[2], s);
-    hipLaunchKernelGGL((down_w4_decode<KS, NT, dn_depth<KS, NT>(), dn_waves<KS, NT>()>), dim3(grid), dim3(256), lds, s, h,
-                       a.offsets, a.E, a.d, a.f, a.dn_codes, a.dn_scales, a.y);
-    if (a.ev[3]) hipEventRecord(a.ev[3], s);
+    launch_k(down_w4_decode<KS, NT, dn_depth<KS, NT>(), dn_waves<KS, NT>()>, dim3(grid),
+             dim3(256), lds, s, a.ev[2], a.ev[3], h, a.offsets, a.E, a.d, a.f, a.dn_codes,
+             a.dn_scales, a.y);
   }
 }
 
@@ -546,21 +543,18 @@ void launch_decode_lds(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s
     const int grid = (int)(work < cap ? work : cap);
     const size_t lds = off_b + sizeof(int32_t) * ((std::min<long long>(P, kPairsInLds) + 3) & ~3) +
                        sizeof(float) * 2 * G * 64 + xs_b;
-    if (a.ev[0]) hipEventRecord(a.ev[0], s);
-    hipLaunchKernelGGL((gateup_w4_decode_lds<kGuDQ, kGuWaves>), dim3(grid), dim3(256), lds, s,
-                       a.x, a.offsets, a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes,
+    launch_k(gateup_w4_decode_lds<kGuDQ, kGuWaves>, dim3(grid), dim3(256), lds, s, a.ev[0], a.ev[1],
+             a.x, a.offsets, a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes,
                        a.gu_scales, h);
-    if (a.ev[1]) hipEventRecord(a.ev[1], s);
   }
   {
     const int G = a.f / 128;
     const long long work = mt * (a.d / 64);
     const int grid = (int)(work < cap ? work : cap);
     const size_t lds = off_b + sizeof(float) * G * 64 + xs_b;
-    if (a.ev[2]) hipEventRecord(a.ev[2], s);
-    hipLaunchKernelGGL((down_w4_decode_lds<kDnDQ, kDnWaves>), dim3(grid), dim3(256), lds, s, h,
+    launch_k(down_w4_decode_lds<kDnDQ, kDnWaves>, dim3(grid), dim3(256), lds, s, a.ev[2], a.ev[3],
+             h,
                        a.offsets, a.E, a.d, a.f, a.dn_codes, a.dn_scales, a.y);
-    if (a.ev[3]) hipEventRecord(a.ev[3], s);
   }
 }
 }  // namespace

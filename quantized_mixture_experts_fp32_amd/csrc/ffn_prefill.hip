@@ -370,23 +370,20 @@ hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStr
     hipLaunchKernelGGL(group_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.x,
                        (long long)a.T, a.d, xsum);
   }
-  if (a.ev[0]) hipEventRecord(a.ev[0], s);
   const unsigned mt8 = (unsigned)((mt + 7) & ~(size_t)7);
-  hipLaunchKernelGGL((pf_w4_kernel<true>), dim3(mt8 * (a.f / 128)), dim3(kThreads), 0, s,
-                     a.x, a.sorted_pair, a.k, a.d, a.f, a.gu_codes, a.gu_scales, xsum, tiles,
-                     num_tiles, a.f / 128, h, (float*)nullptr);
-  if (a.ev[1]) hipEventRecord(a.ev[1], s);
+  launch_k(pf_w4_kernel<true>, dim3(mt8 * (a.f / 128)), dim3(kThreads), 0, s, a.ev[0], a.ev[1],
+           a.x, a.sorted_pair, a.k, a.d, a.f, a.gu_codes, a.gu_scales, xsum,
+           (const PTile*)tiles, (const int*)num_tiles, a.f / 128, h, (float*)nullptr);
   {
     const long long n = P * (a.f / 128);
     hipLaunchKernelGGL(group_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, h, P,
                        a.f, hsum);
   }
-  if (a.ev[2]) hipEventRecord(a.ev[2], s);
   const int dn_fb = (a.d + 255) / 256;
-  hipLaunchKernelGGL((pf_w4_kernel<false>), dim3(mt8 * dn_fb), dim3(kThreads), 0,
-                     s, h, a.sorted_pair, a.k, a.f, a.d, a.dn_codes, a.dn_scales, hsum, tiles,
-                     num_tiles, dn_fb, (uint16_t*)nullptr, a.y);
-  if (a.ev[3]) hipEventRecord(a.ev[3], s);
+  launch_k(pf_w4_kernel<false>, dim3(mt8 * dn_fb), dim3(kThreads), 0, s, a.ev[2], a.ev[3],
+           (const uint16_t*)h, a.sorted_pair, a.k, a.f, a.d, a.dn_codes, a.dn_scales,
+           (const uint2*)hsum, (const PTile*)tiles, (const int*)num_tiles, dn_fb,
+           (uint16_t*)nullptr, a.y);
   return hipGetLastError();
 }
 

@@ -3,16 +3,35 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Launch a kernel; when start/stop events are given they are attached to the
+// dispatch itself (hipExtLaunchKernel), so they time exactly this kernel and
+// put no separate marker into the stream.
+template <typename... KArgs, typename... Args>
+inline void launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
+                     hipStream_t s, hipEvent_t start, hipEvent_t stop, Args... args) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, start, stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
+
 
 size_t route_ws_bytes(int T, int E);
 hipError_t launch_route(const void* x, const void* wr, const float* bias,
                         int T, int d, int E, int k, int32_t* topk_idx,
                         float* topk_w, void* ws, hipStream_t s);
 
+size_t route_permute_ws_bytes(int T, int k, int E);
+hipError_t launch_route_permute(const void* x, const void* wr, const float* bias, int T,
+                                int d, int E, int k, int32_t* topk_idx, float* topk_w,
+                                int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                                void* ws, hipStream_t s);
 size_t permute_ws_bytes(int T, int k, int E);
 hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int E,
                           int32_t* offsets, int32_t* sorted_pair,

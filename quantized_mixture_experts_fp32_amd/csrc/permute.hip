@@ -6,6 +6,7 @@
 // (per-chunk LDS histograms, one scan block, per-chunk stable scatter).
 #include "kcommon.hpp"
 #include "launch.hpp"
+#include "permute_common.hpp"
 
 namespace moe {
 namespace {
@@ -118,78 +119,14 @@ __global__ __launch_bounds__(kThreads) void perm_scatter(
   }
 }
 
-// Small batches (P <= kSmallP): histogram, scan and stable scatter in one
-// 1024-thread block, one launch.  Same order as the three-kernel path.
-constexpr int kSmallP = 8192;
-
+// Small batches (P <= kSmallP): one 1024-thread block, one launch.
 __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ idx,
                                                    int P, int E,
                                                    int32_t* __restrict__ offsets,
                                                    int32_t* __restrict__ sorted_pair,
                                                    int32_t* __restrict__ pair_pos) {
   extern __shared__ int32_t sh[];
-  int32_t* base = sh;               // [E]: counts, then next slot per expert
-  int32_t* tot = sh + E;            // [1024] scan
-  int32_t* wave_cnt = tot + 1024;   // [16][E]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += 1024) {
-    base[e] = 0;
-    for (int w = 0; w < 16; ++w) wave_cnt[w * E + e] = 0;
-  }
-  __syncthreads();
-  for (int p = tid; p < P; p += 1024) {
-    const int e = idx[p];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&base[e], 1);
-  }
-  __syncthreads();
-  const int cnt = (tid < E) ? base[tid] : 0;
-  tot[tid] = cnt;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t v = (tid >= off) ? tot[tid - off] : 0;
-    __syncthreads();
-    tot[tid] += v;
-    __syncthreads();
-  }
-  if (tid < E) {
-    base[tid] = tot[tid] - cnt;
-    offsets[tid] = tot[tid] - cnt;
-    if (tid == E - 1) offsets[E] = tot[tid];
-  }
-  __syncthreads();
-  for (int r = 0; r < P; r += 1024) {
-    const int p = r + tid;
-    int e = (p < P) ? idx[p] : -1;
-    if ((unsigned)e >= (unsigned)E) e = -1;
-    const uint32_t key = (uint32_t)(e < 0 ? 0x3FF : e);
-    uint64_t peers = ~0ull;
-#pragma unroll
-    for (int bit = 0; bit < 10; ++bit) {
-      const bool set = (key >> bit) & 1u;
-      const uint64_t m = __ballot(set);
-      peers &= set ? m : ~m;
-    }
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int rank = __popcll(peers & below);
-    if (e >= 0 && (peers & below) == 0) wave_cnt[wave * E + e] = __popcll(peers);
-    __syncthreads();
-    if (e >= 0) {
-      int slot = base[e] + rank;
-      for (int w = 0; w < wave; ++w) slot += wave_cnt[w * E + e];
-      sorted_pair[slot] = p;
-      pair_pos[p] = slot;
-    }
-    __syncthreads();
-    for (int ee = tid; ee < E; ee += 1024) {
-      int add = 0;
-      for (int w = 0; w < 16; ++w) {
-        add += wave_cnt[w * E + ee];
-        wave_cnt[w * E + ee] = 0;
-      }
-      base[ee] += add;
-    }
-    __syncthreads();
-  }
+  permute_block(idx, P, E, offsets, sorted_pair, pair_pos, sh);
 }
 
 }  // namespace
@@ -205,7 +142,7 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int E,
                           int32_t* pair_pos, void* ws, hipStream_t s) {
   const int P = T * k;
   if (P <= kSmallP) {
-    hipLaunchKernelGGL(perm_small, dim3(1), dim3(1024), (17 * E + 1024) * sizeof(int32_t),
+    hipLaunchKernelGGL(perm_small, dim3(1), dim3(1024), permute_block_lds_bytes(E),
                        s, topk_idx, P, E, offsets, sorted_pair, pair_pos);
     return hipGetLastError();
   }

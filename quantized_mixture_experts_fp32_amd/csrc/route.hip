@@ -17,6 +17,7 @@
 
 #include "kcommon.hpp"
 #include "launch.hpp"
+#include "permute_common.hpp"
 
 namespace moe {
 namespace {
@@ -70,6 +71,78 @@ __device__ void select_topk(const float* __restrict__ lg, int E, int k,
     if (lane == j) {
       my_ex = ex;
       idx_out[j] = be;
+    }
+  }
+  if (lane < k) w_out[lane] = my_ex / ssum;
+}
+
+// The same selection with the token's logits held in registers (E <= 512,
+// up to 8 per lane), each as a 64-bit key (order-preserving logit bits,
+// inverted index): the largest key is the largest logit, ties to the lower
+// index, exactly as better() orders them.  The wave arg-max of each round
+// is four DPP steps within rows of 16 lanes and four readlanes.  Also
+// copies the ids to idx_copy (LDS).
+__device__ __forceinline__ uint32_t ordered_f32(float f) {
+  const uint32_t u = (f == 0.0f) ? 0u : __float_as_uint(f);  // -0 orders as +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unordered_f32(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_max(uint64_t v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, kCtrl, 0xF, 0xF, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, kCtrl, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max<0x141>(v);  // row_half_mirror
+  v = dpp_max<0x140>(v);  // row_mirror: every lane holds its row's maximum
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  uint64_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t k = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+    m = k > m ? k : m;
+  }
+  return m;
+}
+
+__device__ void select_topk_reg(const float* __restrict__ lg, int E, int k,
+                                int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                int32_t* __restrict__ idx_copy) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = 64 * i + lane;
+    key[i] = (e < E) ? (((uint64_t)ordered_f32(lg[e]) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
+  }
+  float m = 0.0f, ssum = 0.0f, my_ex = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t loc = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) loc = key[i] > loc ? key[i] : loc;
+    const uint64_t win = wave_max_key(loc);
+    const int be = (int)~(uint32_t)win;
+    const float bv = unordered_f32((uint32_t)(win >> 32));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (64 * i + lane == be) key[i] = 0;
+    if (j == 0) m = bv;
+    const float ex = expf(bv - m);
+    ssum += ex;  // rank order, identical in every lane
+    if (lane == j) {
+      my_ex = ex;
+      idx_out[j] = be;
+      idx_copy[j] = be;
     }
   }
   if (lane < k) w_out[lane] = my_ex / ssum;
@@ -188,8 +261,24 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logi
                                                   float* __restrict__ topk_w) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  select_topk(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
-              topk_w + (size_t)t * k);
+  select_topk_reg(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
+                  topk_w + (size_t)t * k, topk_idx + (size_t)t * k);
+}
+
+// Few tokens: top-k of every token (one wave per token, 16 waves) and the
+// grouping of the T*k pairs by expert, in one 1024-thread block.
+__global__ __launch_bounds__(1024) void route_topk_permute(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos) {
+  extern __shared__ int32_t sh[];
+  const int P = T * k;
+  int32_t* idx_lds = sh;
+  for (int t = threadIdx.x >> 6; t < T; t += 16)
+    select_topk_reg(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
+                    topk_w + (size_t)t * k, idx_lds + t * k);
+  __syncthreads();
+  permute_block(idx_lds, P, E, offsets, sorted_pair, pair_pos, sh + ((P + 3) & ~3));
 }
 
 }  // namespace
@@ -217,6 +306,35 @@ hipError_t launch_route(const void* x, const void* wr, const float* bias,
                        topk_idx, topk_w);
   }
   return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+size_t route_permute_ws_bytes(int T, int k, int E) {
+  const size_t a = route_ws_bytes(T, E), b = permute_ws_bytes(T, k, E);
+  return a > b ? a : b;
+}
+
+hipError_t launch_route_permute(const void* x, const void* wr, const float* bias, int T,
+                                int d, int E, int k, int32_t* topk_idx, float* topk_w,
+                                int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                                void* ws, hipStream_t s) {
+  if (T > 0 && T <= kSmallT) {
+    float* logits = (float*)ws;
+    const int neb = (E + 15) / 16;
+    hipLaunchKernelGGL(route_logits_small, dim3(T * neb), dim3(256), sizeof(uint16_t) * d, s,
+                       (const uint16_t*)x, (const uint16_t*)wr, bias, T, d, E, logits);
+    const int P = T * k;
+    const size_t lds = sizeof(int32_t) * ((P + 3) & ~3) + permute_block_lds_bytes(E);
+    hipLaunchKernelGGL(route_topk_permute, dim3(1), dim3(1024), lds, s, logits, T, E, k,
+                       topk_idx, topk_w, offsets, sorted_pair, pair_pos);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_route(x, wr, bias, T, d, E, k, topk_idx, topk_w, ws, s);
+  if (e != hipSuccess) return e;
+  return launch_permute(topk_idx, T, k, E, offsets, sorted_pair, pair_pos, ws, s);
 }
 
 }  // namespace moe

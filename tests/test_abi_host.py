@@ -80,6 +80,22 @@ def test_permute_validation(lib):
     assert p(FAKE, 100, 9, 8, FAKE, FAKE, FAKE, FAKE, need, NULL) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_route_permute_validation(lib):
+    rp = lib.moe_route_permute
+    need = lib.moe_route_permute_ws_bytes(4, 2, 8)
+    assert need >= max(lib.moe_route_ws_bytes(4, 8), lib.moe_permute_ws_bytes(4, 2, 8))
+    args = lambda **kw: [kw.get("x", FAKE), FAKE, NULL, kw.get("T", 4), kw.get("d", 256), 8,
+                         kw.get("k", 2), FAKE, FAKE, kw.get("off", FAKE), FAKE, FAKE,
+                         kw.get("ws", FAKE), kw.get("wsb", need), NULL]
+    assert rp(*args(d=200)) == moe.MOE_ERR_UNSUPPORTED
+    assert rp(*args(k=9)) == moe.MOE_ERR_INVALID_ARG
+    assert rp(*args(x=NULL)) == moe.MOE_ERR_INVALID_ARG
+    assert rp(*args(off=NULL)) == moe.MOE_ERR_INVALID_ARG
+    assert rp(*args(wsb=need - 1)) == moe.MOE_ERR_WORKSPACE
+    assert rp(*args(ws=NULL)) == moe.MOE_ERR_WORKSPACE
+    assert rp(*args(x=ODD)) == moe.MOE_ERR_INVALID_ARG
+
+
 def _ffn(lib, **kw):
     a = dict(x=FAKE, off=FAKE, sp=FAKE, T=4, k=2, E=8, d=256, f=512, fmt=0, group=128,
              guc=FAKE, gus=FAKE, dnc=FAKE, dns=FAKE, bits=NULL, mode=0, y=FAKE,

@@ -101,6 +101,25 @@ def test_route_bit_exact(cid, T):
     np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("cid,T", ROUTE_CASES + [(1, 512), (1, 513)])
+def test_route_permute_bit_exact(cid, T):
+    """The fused call equals the oracle's routing and grouping bit for bit
+    (both launch shapes: T <= 512 fused, larger T routed then permuted)."""
+    cfg = synth.CONFIGS[cid]
+    note(f"route+permute cfg{cid} T={T}")
+    x, wr, bias = synth.host_x(cfg, T), synth.host_router(cfg), synth.host_bias(cfg)
+    idx, w, off, sp, pp = moe.moe_route_permute(
+        t_i16(x), t_i16(wr), None if bias is None else torch.from_numpy(bias).to(DEV), cfg.k)
+    torch.cuda.synchronize()
+    _, ridx, rw = oracle.route(x, wr, bias, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
+    roff, rsp, rpp = oracle.permute(ridx, cfg.E)
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(sp.cpu().numpy(), rsp)
+    assert np.array_equal(pp.cpu().numpy(), rpp)
+
+
 def test_route_ties_and_shapes():
     rng = np.random.default_rng(3)
     cases = []
