@@ -90,8 +90,13 @@ def expert_bytes(cfg, planes=None):
 
 
 class Workload:
-    def __init__(self, name, cid, T, steps, path=0):
+    """mode: "fused" (one grouped FFN call per step), "seq-active" (one FFN
+    call per activated expert, ids read back from the routing) or "seq-all"
+    (one FFN call per expert, no read-back)."""
+
+    def __init__(self, name, cid, T, steps, path=0, mode="fused"):
         self.name, self.cid, self.T, self.steps, self.path = name, cid, T, steps, path
+        self.mode = mode
 
 
 def run_workload(wl, warmup, hip, torch, np, synth, moe):
@@ -158,21 +163,104 @@ def run_workload(wl, warmup, hip, torch, np, synth, moe):
     P = T * k
     flops_gu, flops_dn = 4.0 * P * d * f, 2.0 * P * d * f
 
+    seq_ws = torch.empty((max(moe.moe_ffn_ws_bytes(T, k, 1, d, f, fmt), 256),),
+                         dtype=torch.uint8, device=dev)
+    launches = []
+
+    bound = {}
+
+    def step(i):
+        x, wts = xs[i % nx], copies[i % ncopies]
+        if wl.mode == "fused":
+            key = (i % nx, i % ncopies)
+            if key not in bound:
+                bound[key] = layer.bind(x, out, weights=wts, path=wl.path)
+            bound[key]()
+            return
+        # the sequential baseline: same routing, same kernels, one expert FFN
+        # call per expert, then the same combine
+        moe.moe_route_permute(x, wr, bias, k, layer.ws_rp, layer.topk_idx, layer.topk_w,
+                              layer.offsets, layer.sorted_pair, layer.pair_pos)
+        experts = None
+        if wl.mode == "seq-active":
+            experts = np.nonzero(np.diff(layer.offsets.cpu().numpy()))[0]
+        launches.append(E if experts is None else len(experts))
+        moe.expert_ffn_per_expert(x, layer.offsets, layer.sorted_pair, k, f, *wts,
+                                  layer.y_pairs, seq_ws, fmt, path=wl.path,
+                                  experts=experts)
+        moe.moe_combine(layer.y_pairs, layer.pair_pos, layer.topk_w, out,
+                        moe.MOE_OUT_BF16)
+
     steps = wl.steps
+    if wl.mode == "fused":  # marshal every (batch, weight copy) pair up front
+        for i in range(min(max(steps, warmup), nx * ncopies)):
+            key = (i % nx, i % ncopies)
+            bound.setdefault(key, layer.bind(xs[key[0]], out, weights=copies[key[1]],
+                                             path=wl.path))
     for i in range(warmup):
-        layer.forward(xs[i % nx], out=out, path=wl.path, weights=copies[i % ncopies])
+        step(i)
     torch.cuda.synchronize()
 
-    # pass 1, the measurement: `steps` plain layer steps between two events
+    # pass 1, the measurement: `steps` eager layer steps (argument marshalling
+    # done up front) between two events
     t_start, t_end = hip.event(), hip.event()
     hip.record(t_start, stream)
     wall0 = time.perf_counter()
     for i in range(steps):
-        layer.forward(xs[i % nx], out=out, path=wl.path, weights=copies[i % ncopies])
+        step(i)
     hip.record(t_end, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = hip.ms(t_start, t_end)
+    # the same steps replayed from HIP graphs (one per batch / weight-copy
+    # pair), reported beside the eager rate
+    graph_ms = None
+    if wl.mode == "fused":
+        graphs = {key: layer.capture(xs[key[0]], out, weights=copies[key[1]], path=wl.path)
+                  for key in bound}
+        for i in range(warmup):
+            graphs[(i % nx, i % ncopies)].replay()
+        torch.cuda.synchronize()
+        hip.record(t_start, stream)
+        for i in range(steps):
+            graphs[(i % nx, i % ncopies)].replay()
+        hip.record(t_end, stream)
+        torch.cuda.synchronize()
+        graph_ms = hip.ms(t_start, t_end) / steps
+        del graphs
+    if wl.mode != "fused":
+        hip.destroy(t_start)
+        hip.destroy(t_end)
+        # pass 2: kernel durations of every per-expert call (attached events)
+        kern_us = []
+        for i in range(steps):
+            x, wts = xs[i % nx], copies[i % ncopies]
+            moe.moe_route_permute(x, wr, bias, k, layer.ws_rp, layer.topk_idx,
+                                  layer.topk_w, layer.offsets, layer.sorted_pair,
+                                  layer.pair_pos)
+            experts = (np.nonzero(np.diff(layer.offsets.cpu().numpy()))[0]
+                       if wl.mode == "seq-active" else range(E))
+            ev = [[hip.event() for _ in range(4)] for _ in experts]
+            moe.expert_ffn_per_expert(x, layer.offsets, layer.sorted_pair, k, f, *wts,
+                                      layer.y_pairs, seq_ws, fmt, path=wl.path,
+                                      experts=experts, events=ev)
+            torch.cuda.synchronize()
+            kern_us.append(1e3 * sum(hip.ms(e[0], e[1]) + hip.ms(e[2], e[3]) for e in ev))
+            for e in ev:
+                for h in e:
+                    hip.destroy(h)
+        ms_step = total_ms / steps
+        rec = {"workload": wl.name, "config": cfg.name, "T": T, "d": d, "E": E, "k": k,
+               "f": f, "format": "int4-g128", "mode": wl.mode,
+               "ms_per_step": round(ms_step, 5),
+               "tokens_per_s": round(T / (ms_step / 1e3), 1),
+               "wall_s": round(wall, 3), "weight_copies": ncopies,
+               "ffn_calls_per_step": round(float(np.mean(launches[-steps:])), 2),
+               "ffn_kernel_us_per_step": round(float(np.mean(kern_us)), 2),
+               "active_experts_avg": round(float(np.mean(active)), 2)}
+        del copies, layer, xs
+        torch.cuda.empty_cache()
+        return rec
 
     # pass 2, the same steps again with start/stop events attached to the two
     # expert-FFN kernel dispatches (per-kernel durations for the roofline)
@@ -201,6 +289,7 @@ def run_workload(wl, warmup, hip, torch, np, synth, moe):
         "f": f, "format": "bitplane8-rank" if bp else "int4-g128",
         "ms_per_step": round(ms_step, 5), "tokens_per_s": round(T / (ms_step / 1e3), 1),
         "ms_per_step_instrumented": round(instr_ms / steps, 5),
+        "graph_replay_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "wall_s": round(wall, 3), "weight_copies": ncopies,
         "active_experts_avg": round(float(np.mean(active)), 2),
         "gateup_us": round(1e3 * float(np.mean(gu_ms)), 3),
@@ -311,6 +400,10 @@ def main():
         Workload("olmoe-decode-w4 T=1", 1, 1, args.steps),
         Workload("olmoe-decode-w4 T=4", 1, 4, args.steps),
         Workload("olmoe-decode-w4 T=8", 1, 8, args.steps),
+        Workload("olmoe-sequential-w4 T=16", 1, 16, max(10, args.steps // 4),
+                 mode="seq-active"),
+        Workload("olmoe-sequential-all-w4 T=16", 1, 16, max(10, args.steps // 4),
+                 mode="seq-all"),
         Workload("olmoe-bitplane-decode T=16", 3, 16, args.steps),
         Workload("e256-w4 T=1", 4, 1, args.steps),
         Workload("e256-w4 T=64", 4, 64, args.steps),
@@ -327,6 +420,14 @@ def main():
         for wl in secondary:
             others.append(run_workload(wl, max(2, args.warmup // 4), hip, torch, np,
                                        synth, moe))
+    for r in others:
+        if r.get("mode", "fused") != "fused" and r["T"] == head.T and r["config"] == \
+                head_rec["config"]:
+            r["fused_ms_per_step"] = head_rec["ms_per_step"]
+            r["fused_speedup"] = round(r["ms_per_step"] / head_rec["ms_per_step"], 3)
+            fk = head_rec["gateup_us"] + head_rec["down_us"]
+            r["fused_ffn_kernel_us_per_step"] = round(fk, 2)
+            r["fused_kernel_speedup"] = round(r["ffn_kernel_us_per_step"] / fk, 3)
     base = None
     if not args.no_cpu_baseline:
         import oracle

@@ -72,7 +72,7 @@ extern "C" {
 #define MOE_OUT_BF16 0 /* layer output as bf16 (round to nearest even)     */
 #define MOE_OUT_F32 1  /* layer output as fp32 (same sum, before rounding)  */
 
-#define MOE_PATH_AUTO 0    /* pick the FFN kernels from T*k and E          */
+#define MOE_PATH_AUTO 0    /* DECODE if T*k <= 8*E or T <= 16, else PREFILL */
 #define MOE_PATH_DECODE 1  /* weight-streaming kernels (small batches)     */
 #define MOE_PATH_PREFILL 2 /* LDS-tiled grouped MFMA kernels               */
 
@@ -196,6 +196,12 @@ int moe_route_permute(const void *x_bf16, const void *wr_bf16, const float *bias
  *   The int4 format takes MOE_BITS_NONE and bits NULL.
  * Other arguments:
  *   x bf16 [T][d]; expert_offsets, sorted_pair as from moe_permute.
+ *   E counts the experts whose weights this call receives (E may be below
+ *     k).  Slot positions in expert_offsets are absolute, so experts
+ *     [e0, e0+E) of a larger grouping are run by passing expert_offsets + e0
+ *     and each weight/scale pointer advanced by e0 experts (and bits + e0
+ *     for MOE_BITS_PER_EXPERT); y_pairs rows of the other experts are left
+ *     untouched.
  *   y_pairs fp32 [T*k][d] in grouped (slot) order (output).
  *   ws / ws_bytes: at least moe_ffn_ws_bytes(T, k, E, d, f, format).
  *   path_hint: MOE_PATH_AUTO / _DECODE / _PREFILL (all give results within

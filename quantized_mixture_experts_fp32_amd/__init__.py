@@ -205,6 +205,49 @@ def moe_expert_ffn_wq(x, expert_offsets, sorted_pair, k, f, gate_up_codes,
     return y_pairs
 
 
+def expert_ffn_per_expert(x, expert_offsets, sorted_pair, k, f, gate_up_codes,
+                          gate_up_scales, down_codes, down_scales, y_pairs, ws,
+                          fmt=MOE_FMT_W4_SYM, bits=None, bits_mode=MOE_BITS_NONE,
+                          path=MOE_PATH_DECODE, stream=None, experts=None, events=None):
+    """The sequential baseline of ExactMoE's ablation ("Every Expert Counts
+    ...", Abstract: fused grouped execution against one launch per expert):
+    the same expert FFN computed by one moe_expert_ffn_wq call per expert.
+    Call e sees a one-expert problem whose expert_offsets are the pointer
+    expert_offsets + e (so its slot range is [offsets[e], offsets[e+1]) of
+    the shared sorted_pair / y_pairs) and whose weights are expert e's
+    slices.  experts: the expert ids to launch (the activated ones, which
+    the caller reads from the routing); None launches every expert, and
+    those without pairs exit at once.  Writes the y_pairs rows of the
+    launched experts like the grouped call.  ws must hold
+    moe_ffn_ws_bytes(T, k, 1, d, f, fmt) bytes.  events: optional list with
+    one 4-tuple of hipEvent_t handles per launched expert, armed with
+    moe_set_ffn_events before that expert's call."""
+    T, d = x.shape
+    E = expert_offsets.numel() - 1
+    lib = load_library()
+    vp = ctypes.c_void_p
+    esz = lambda t: (t.numel() // t.shape[0]) * t.element_size()
+    gu_b, gus_b, dn_b, dns_b = (esz(gate_up_codes), esz(gate_up_scales),
+                                esz(down_codes), esz(down_scales))
+    wsb, st = ws.numel() * ws.element_size(), _stream(stream)
+    for i, e in enumerate(range(E) if experts is None else experts):
+        e = int(e)
+        if events is not None:
+            moe_set_ffn_events(*events[i])
+        if not 0 <= e < E:
+            raise ValueError(f"expert id {e} outside [0, {E})")
+        # a per-expert bit-width array is indexed by the (one) local expert
+        b = None if bits is None else vp(
+            bits.data_ptr() + (e if bits_mode == MOE_BITS_PER_EXPERT else 0))
+        _check("moe_expert_ffn_wq", lib.moe_expert_ffn_wq(
+            _ptr(x), vp(expert_offsets.data_ptr() + 4 * e), _ptr(sorted_pair), T, k, 1, d,
+            f, fmt, MOE_GROUP, vp(gate_up_codes.data_ptr() + e * gu_b),
+            vp(gate_up_scales.data_ptr() + e * gus_b), vp(down_codes.data_ptr() + e * dn_b),
+            vp(down_scales.data_ptr() + e * dns_b), b, bits_mode, _ptr(y_pairs),
+            _ptr(ws), wsb, path, st))
+    return y_pairs
+
+
 def moe_combine(y_pairs, pair_pos, topk_w, out=None, out_dtype=MOE_OUT_BF16,
                 stream=None):
     """Layer output [T][d] (bf16 bits in an int16 tensor, or fp32)."""
@@ -312,3 +355,58 @@ class MoeLayer:
                           self.y_pairs, self.ws_ffn, path, stream)
         return moe_combine(self.y_pairs, self.pair_pos, self.topk_w, out, out_dtype,
                            stream)
+
+    def bind(self, x, out, weights=None, path=MOE_PATH_AUTO, out_dtype=MOE_OUT_BF16,
+             stream=None):
+        """A step with every argument marshalled once: returns a callable that
+        enqueues the same three ABI calls as forward(x, out, ...) for these
+        fixed buffers (x, out and the weights must stay alive and in place).
+        For decode loops, where converting arguments on every call would cost
+        as much host time as the kernels take on the GPU."""
+        T = x.shape[0]
+        if self._T != T:
+            self._alloc(T, x)
+        gu, gus, dn, dns = weights if weights is not None else (
+            self.gu, self.gus, self.dn, self.dns)
+        lib = load_library()
+        E, k, d, f = self.E, self.k, self.d, self.f
+        st = _stream(stream)
+        rp_args = (_ptr(x), _ptr(self.wr), _ptr(self.bias), T, d, E, k, _ptr(self.topk_idx),
+                   _ptr(self.topk_w), _ptr(self.offsets), _ptr(self.sorted_pair),
+                   _ptr(self.pair_pos), _ptr(self.ws_rp),
+                   self.ws_rp.numel() * self.ws_rp.element_size(), st)
+        ffn_args = (_ptr(x), _ptr(self.offsets), _ptr(self.sorted_pair), T, k, E, d, f,
+                    self.fmt, MOE_GROUP, _ptr(gu), _ptr(gus), _ptr(dn), _ptr(dns),
+                    _ptr(self.bits), self.bits_mode, _ptr(self.y_pairs), _ptr(self.ws_ffn),
+                    self.ws_ffn.numel() * self.ws_ffn.element_size(), path, st)
+        cb_args = (_ptr(self.y_pairs), _ptr(self.pair_pos), _ptr(self.topk_w), T, k, d,
+                   _ptr(out), out_dtype, st)
+        rp, ffn, cb = lib.moe_route_permute, lib.moe_expert_ffn_wq, lib.moe_combine
+
+        def step():
+            rc = rp(*rp_args)
+            if rc:
+                _check("moe_route_permute", rc)
+            rc = ffn(*ffn_args)
+            if rc:
+                _check("moe_expert_ffn_wq", rc)
+            rc = cb(*cb_args)
+            if rc:
+                _check("moe_combine", rc)
+            return out
+
+        return step
+
+    def capture(self, x, out, weights=None, path=MOE_PATH_AUTO, out_dtype=MOE_OUT_BF16):
+        """One step for these fixed buffers recorded as a HIP graph (torch's
+        CUDAGraph object; replay() re-runs the five kernels with one host
+        call).  The library records only kernel launches (no memset or
+        copy nodes) and allocates nothing, so replays are self-contained."""
+        import torch
+        T = x.shape[0]
+        if self._T != T:
+            self._alloc(T, x)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):  # binds to the capture stream
+            self.bind(x, out, weights, path, out_dtype)()
+        return g

@@ -33,11 +33,13 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-int check_dims(int T, int d, int E, int k) {
+// k <= E holds for routing; the expert FFN may receive a slice of the
+// experts (fewer than k of them), so it skips that check.
+int check_dims(int T, int d, int E, int k, bool k_le_E = true) {
   if (T < 0 || d <= 0 || E <= 0 || k <= 0)
     return fail(MOE_ERR_INVALID_ARG, "negative or zero size (T=%d d=%d E=%d k=%d)",
                 T, d, E, k);
-  if (k > E) return fail(MOE_ERR_INVALID_ARG, "k=%d > E=%d", k, E);
+  if (k_le_E && k > E) return fail(MOE_ERR_INVALID_ARG, "k=%d > E=%d", k, E);
   if (E > MOE_MAX_EXPERTS)
     return fail(MOE_ERR_UNSUPPORTED, "E=%d > %d", E, MOE_MAX_EXPERTS);
   if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k=%d > %d", k, MOE_MAX_TOPK);
@@ -160,7 +162,7 @@ int moe_expert_ffn_wq(const void* x_bf16, const int32_t* expert_offsets,
                       const uint16_t* down_scales_f16, const uint8_t* bits,
                       int bits_mode, float* y_pairs, void* ws, size_t ws_bytes,
                       int path_hint, void* stream) {
-  int rc = check_dims(T, d, E, k);
+  int rc = check_dims(T, d, E, k, false);
   if (rc) return rc;
   if (f <= 0) return fail(MOE_ERR_INVALID_ARG, "f=%d", f);
   if (f % MOE_GROUP) return fail(MOE_ERR_UNSUPPORTED, "f=%d not a multiple of 128", f);
@@ -200,7 +202,10 @@ int moe_expert_ffn_wq(const void* x_bf16, const int32_t* expert_offsets,
     return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_wq: workspace not 256-byte aligned");
   const long long P = (long long)T * k;
   int path = path_hint;
-  if (path == MOE_PATH_AUTO) path = (P <= 8LL * E) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+  // weight streaming while experts receive few pairs on average; an expert
+  // receives at most T pairs (one per token), so T <= 16 always streams
+  if (path == MOE_PATH_AUTO)
+    path = (P <= 8LL * E || T <= 16) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
   moe::FfnArgs a{(const uint16_t*)x_bf16, expert_offsets, sorted_pair, T, k, E,
                  d, f, format, gate_up_codes, gate_up_scales_f16, down_codes,
                  down_scales_f16, bits, bits_mode, y_pairs, ws, path,

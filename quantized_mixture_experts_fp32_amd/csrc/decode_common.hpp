@@ -84,6 +84,55 @@ __device__ __forceinline__ void stage_scales_rows64(const uint16_t* __restrict__
   for (int g = g0; g < G; g += kStep) d[g * 64] = f16_bits_to_f32(src[g]);
 }
 
+// The same staging in two phases for G % 8 == 0 and 16-byte aligned scale
+// rows: fetch() issues one 16-byte load (8 consecutive groups of one row)
+// per chunk, kSC chunks per thread, before the code loads; store() converts
+// and writes them to LDS after those loads are issued, so the scales share
+// their round trip instead of queueing before it.  Chunk c covers row c % 64
+// of matrix c / (64 G/8), groups 8 ((c / 64) % (G/8)) + 0..7; threads past
+// the last chunk take chunk c mod total and store the same values to the same
+// places as its owner (an unconditional store keeps the fetch where it is).
+template <int NMAT, int kSC>
+struct ScaleStage {
+  u32x4 v[kSC];
+  int c0;
+  __device__ __forceinline__ void fetch(const uint16_t* __restrict__ rows_src,
+                                        size_t mat_stride, int G) {
+    const int cpr = G >> 3, total = NMAT * 64 * cpr;
+    c0 = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kSC; ++i) {
+      int c = c0 + 256 * i;
+      c = c < total ? c : c % total;
+      const int r = c & 63, m = (c >> 6) / cpr, cc = (c >> 6) % cpr;
+      v[i] = *(const u32x4*)(rows_src + ((size_t)m * mat_stride + r) * G + 8 * cc);
+    }
+  }
+  __device__ __forceinline__ void store(int G, float* __restrict__ dst) const {
+    const int cpr = G >> 3, total = NMAT * 64 * cpr;
+#pragma unroll
+    for (int i = 0; i < kSC; ++i) {
+      int c = c0 + 256 * i;
+      c = c < total ? c : c % total;
+      const int r = c & 63, m = (c >> 6) / cpr, cc = (c >> 6) % cpr;
+      float* d = dst + ((size_t)m * G + 8 * cc) * 64 + r;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        d[(2 * q) * 64] = f16_bits_to_f32(v[i][q] & 0xFFFFu);
+        d[(2 * q + 1) * 64] = f16_bits_to_f32(v[i][q] >> 16);
+      }
+    }
+  }
+};
+
+// kSC for a staging of NMAT matrices x 64 rows x G groups (0: G % 8 != 0 or
+// unaligned scales, use stage_scales_rows64).
+inline int scale_chunks(int nmat, int G, const void* scales) {
+  if (G % 8 || ((uintptr_t)scales & 15)) return 0;
+  const int per = (nmat * 64 * (G / 8) + 255) / 256;
+  return per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 0;
+}
+
 constexpr int kXRow = 136;  // bf16 per staged activation row (128 + 8 pad)
 
 }  // namespace dec

@@ -341,7 +341,12 @@ void down_w4_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
 // counter to the codes alone, so the code stream can run kDQ groups ahead
 // of the MFMAs.  The arithmetic (operands,
 // MFMA order, scaling) is the same as in the kernels above.
-template <int kDQ, int kWaves>
+// The group loop keeps every global load unconditional (addresses of rows
+// past the tile, and of groups past the end, are clamped to valid ones) and
+// refills every slot in its steady state without a branch, so the compiler's
+// wait before each use counts exactly the loads issued after it: kDQ groups
+// stay in flight across the loop edge.
+template <int kDQ, int kWaves, int kSC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
 void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
                           const int32_t* __restrict__ sorted_pair, int E, int k, int P,
@@ -366,53 +371,75 @@ void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restr
     if (!find_tile(off_lds, E, 16, w / RG, tl)) break;
     const int nb = (w % RG) * 64, n0 = nb + 16 * wave;
     const size_t erow = (size_t)tl.e * 2 * f;
-    const bool st_ok = st_tok < tl.cnt;
-    const int sj = tl.r0 + (st_ok ? st_tok : 0);
+    // rows past the tile stage a copy of its first row (never stored)
+    const int sj = tl.r0 + (st_tok < tl.cnt ? st_tok : 0);
     const int sp = np ? sp_lds[sj] : sorted_pair[sj];
+    // take the routing value here, before any weight load is issued: a wait
+    // for it after those loads would also wait for them
+    asm volatile("" ::"v"(sp) : "memory");
     const uint16_t* xsrc = x + (size_t)(sp / k) * d + 8 * st_pc;
     const uint8_t* cg = codes + (erow + n0) * (size_t)(d >> 1) + 64 * col + 16 * kq;
     const uint8_t* cu = cg + (size_t)f * (d >> 1);
 
     u32x4 qg[kDQ], qu[kDQ], xv[kDQ];
     auto load = [&](int g, int i) {
-      if (st_ok) xv[i] = *(const u32x4*)(xsrc + 128 * g);
+      xv[i] = *(const u32x4*)(xsrc + 128 * g);
       qg[i] = *(const u32x4*)(cg + kTileGroupBytes * g);
       qu[i] = *(const u32x4*)(cu + kTileGroupBytes * g);
     };
-#pragma unroll
-    for (int i = 0; i < kDQ; ++i)
-      if (i < G) load(i, i);
     // the previous item's last barrier precedes these LDS writes; the first
     // barrier of the group loop orders them before any read
-    stage_scales_rows64<2>(scales + (erow + nb) * G, (size_t)f, G, sc_lds);
+    ScaleStage<2, kSC ? kSC : 1> sst;
+    if (kSC) sst.fetch(scales + (erow + nb) * G, (size_t)f, G);
+    __builtin_amdgcn_sched_barrier(0);  // scales first: their wait skips the codes
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i) load(i < G ? i : G - 1, i);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kSC)
+      sst.store(G, sc_lds);
+    else
+      stage_scales_rows64<2>(scales + (erow + nb) * G, (size_t)f, G, sc_lds);
 
     f32x4 tg = {0, 0, 0, 0}, tu = {0, 0, 0, 0};
-    const int rd_tok = col < tl.cnt ? col : 0;  // padded columns re-read row 0
-    for (int g = 0; g < G; g += kDQ) {
+    auto step = [&](int gi, int i) {
+      // slot gi & 1 was last read in step gi - 2, before the barrier of step gi - 1
+      uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
+      *(u32x4*)(slot + st_tok * kXRow + 8 * st_pc) = xv[i];
+      __syncthreads();
+      bf16x8 xp[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xp[j] = *(const bf16x8*)(slot + col * kXRow + 32 * kq + 8 * j);
+      const f32x4 sg = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
+      const f32x4 su = *(const f32x4*)(sc_lds + (G + gi) * 64 + 16 * wave + 4 * kq);
+      f32x4 seed = {0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) seed = mfma16(negoff, xp[j], seed);
+      tile_group(xp, seed, qg[i], sg, tg);
+      tile_group(xp, seed, qu[i], su, tu);
+    };
+    // steady state: slot i is refilled right after its codes are used (the
+    // new loads reuse its registers: no copy, hence no wait, at the edge)
+    int g = 0;
+    for (; g + 2 * kDQ <= G; g += kDQ) {
 #pragma unroll
       for (int i = 0; i < kDQ; ++i) {
-        const int gi = g + i;
-        if (gi >= G) break;
-        // slot gi & 1 was last read in iteration gi - 2, before the
-        // barrier of iteration gi - 1
-        uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
-        if (st_ok) *(u32x4*)(slot + st_tok * kXRow + 8 * st_pc) = xv[i];
-        __syncthreads();
-        bf16x8 xp[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          xp[j] = *(const bf16x8*)(slot + rd_tok * kXRow + 32 * kq + 8 * j);
-        const f32x4 sg = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
-        const f32x4 su = *(const f32x4*)(sc_lds + (G + gi) * 64 + 16 * wave + 4 * kq);
-        f32x4 seed = {0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) seed = mfma16(negoff, xp[j], seed);
-        const u32x4 a = qg[i], b = qu[i];
-        if (gi + kDQ < G) load(gi + kDQ, i);
-        tile_group(xp, seed, a, sg, tg);
-        tile_group(xp, seed, b, su, tu);
+        step(g + i, i);
+        load(g + i + kDQ, i);
+        // keep the refill ahead of the next step's waits
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // the last (fewer than 2 kDQ) groups
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i) {
+      if (g + i >= G) break;
+      step(g + i, i);
+      if (g + i + kDQ < G) load(g + i + kDQ, i);
+    }
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i)
+      if (g + kDQ + i < G) step(g + kDQ + i, i);
+
     if (col < tl.cnt) {
       uint32_t hb[4];
 #pragma unroll
@@ -426,7 +453,7 @@ void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restr
   }
 }
 
-template <int kDQ, int kWaves>
+template <int kDQ, int kWaves, int kSC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
 void down_w4_decode_lds(const uint16_t* __restrict__ h, const int32_t* __restrict__ offsets,
                         int E, int d, int f, const uint8_t* __restrict__ codes,
@@ -449,43 +476,59 @@ void down_w4_decode_lds(const uint16_t* __restrict__ h, const int32_t* __restric
     if (!find_tile(off_lds, E, 16, w / RG, tl)) break;
     const int mb = (w % RG) * 64, m0 = mb + 16 * wave;
     const size_t erow = (size_t)tl.e * d;
-    const bool st_ok = st_tok < tl.cnt;
-    const uint16_t* hsrc = h + (size_t)(tl.r0 + (st_ok ? st_tok : 0)) * f + 8 * st_pc;
+    const uint16_t* hsrc = h + (size_t)(tl.r0 + (st_tok < tl.cnt ? st_tok : 0)) * f + 8 * st_pc;
     const uint8_t* cd = codes + (erow + m0) * (size_t)(f >> 1) + 64 * col + 16 * kq;
 
     u32x4 q[kDQ], hv[kDQ];
     auto load = [&](int g, int i) {
-      if (st_ok) hv[i] = *(const u32x4*)(hsrc + 128 * g);
+      hv[i] = *(const u32x4*)(hsrc + 128 * g);
       q[i] = *(const u32x4*)(cd + kTileGroupBytes * g);
     };
+    ScaleStage<1, kSC ? kSC : 1> sst;
+    if (kSC) sst.fetch(scales + (erow + mb) * G, 0, G);
+    __builtin_amdgcn_sched_barrier(0);  // scales first: their wait skips the codes
 #pragma unroll
-    for (int i = 0; i < kDQ; ++i)
-      if (i < G) load(i, i);
-    stage_scales_rows64<1>(scales + (erow + mb) * G, 0, G, sc_lds);
+    for (int i = 0; i < kDQ; ++i) load(i < G ? i : G - 1, i);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kSC)
+      sst.store(G, sc_lds);
+    else
+      stage_scales_rows64<1>(scales + (erow + mb) * G, 0, G, sc_lds);
 
     f32x4 acc = {0, 0, 0, 0};
-    const int rd_tok = col < tl.cnt ? col : 0;
-    for (int g = 0; g < G; g += kDQ) {
+    auto step = [&](int gi, int i) {
+      uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
+      *(u32x4*)(slot + st_tok * kXRow + 8 * st_pc) = hv[i];
+      __syncthreads();
+      bf16x8 xp[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xp[j] = *(const bf16x8*)(slot + col * kXRow + 32 * kq + 8 * j);
+      const f32x4 sv = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
+      f32x4 seed = {0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) seed = mfma16(negoff, xp[j], seed);
+      tile_group(xp, seed, q[i], sv, acc);
+    };
+    int g = 0;
+    for (; g + 2 * kDQ <= G; g += kDQ) {
 #pragma unroll
       for (int i = 0; i < kDQ; ++i) {
-        const int gi = g + i;
-        if (gi >= G) break;
-        uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
-        if (st_ok) *(u32x4*)(slot + st_tok * kXRow + 8 * st_pc) = hv[i];
-        __syncthreads();
-        bf16x8 xp[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          xp[j] = *(const bf16x8*)(slot + rd_tok * kXRow + 32 * kq + 8 * j);
-        const f32x4 sv = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
-        f32x4 seed = {0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) seed = mfma16(negoff, xp[j], seed);
-        const u32x4 a = q[i];
-        if (gi + kDQ < G) load(gi + kDQ, i);
-        tile_group(xp, seed, a, sv, acc);
+        step(g + i, i);
+        load(g + i + kDQ, i);
+        // keep the refill ahead of the next step's waits
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i) {
+      if (g + i >= G) break;
+      step(g + i, i);
+      if (g + i + kDQ < G) load(g + i + kDQ, i);
+    }
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i)
+      if (g + kDQ + i < G) step(g + kDQ + i, i);
+
     if (col < tl.cnt) *(f32x4*)(y + (size_t)(tl.r0 + col) * d + m0 + 4 * kq) = acc;
     __syncthreads();
   }
@@ -543,18 +586,26 @@ void launch_decode_lds(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s
     const int grid = (int)(work < cap ? work : cap);
     const size_t lds = off_b + sizeof(int32_t) * ((std::min<long long>(P, kPairsInLds) + 3) & ~3) +
                        sizeof(float) * 2 * G * 64 + xs_b;
-    launch_k(gateup_w4_decode_lds<kGuDQ, kGuWaves>, dim3(grid), dim3(256), lds, s, a.ev[0], a.ev[1],
-             a.x, a.offsets, a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes,
-                       a.gu_scales, h);
+    const int sc = scale_chunks(2, G, a.gu_scales);
+    auto kern = sc == 1   ? gateup_w4_decode_lds<kGuDQ, kGuWaves, 1>
+                : sc == 2 ? gateup_w4_decode_lds<kGuDQ, kGuWaves, 2>
+                : sc == 4 ? gateup_w4_decode_lds<kGuDQ, kGuWaves, 4>
+                          : gateup_w4_decode_lds<kGuDQ, kGuWaves, 0>;
+    launch_k(kern, dim3(grid), dim3(256), lds, s, a.ev[0], a.ev[1], a.x, a.offsets,
+             a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes, a.gu_scales, h);
   }
   {
     const int G = a.f / 128;
     const long long work = mt * (a.d / 64);
     const int grid = (int)(work < cap ? work : cap);
     const size_t lds = off_b + sizeof(float) * G * 64 + xs_b;
-    launch_k(down_w4_decode_lds<kDnDQ, kDnWaves>, dim3(grid), dim3(256), lds, s, a.ev[2], a.ev[3],
-             h,
-                       a.offsets, a.E, a.d, a.f, a.dn_codes, a.dn_scales, a.y);
+    const int sc = scale_chunks(1, G, a.dn_scales);
+    auto kern = sc == 1   ? down_w4_decode_lds<kDnDQ, kDnWaves, 1>
+                : sc == 2 ? down_w4_decode_lds<kDnDQ, kDnWaves, 2>
+                : sc == 4 ? down_w4_decode_lds<kDnDQ, kDnWaves, 4>
+                          : down_w4_decode_lds<kDnDQ, kDnWaves, 0>;
+    launch_k(kern, dim3(grid), dim3(256), lds, s, a.ev[2], a.ev[3], h, a.offsets, a.E, a.d,
+             a.f, a.dn_codes, a.dn_scales, a.y);
   }
 }
 }  // namespace

@@ -148,6 +148,60 @@ __device__ void select_topk_reg(const float* __restrict__ lg, int E, int k,
   if (lane < k) w_out[lane] = my_ex / ssum;
 }
 
+// The same selection for E <= 64 (one logit per lane) by rank instead of k
+// arg-max rounds: a lane's rank is the number of the token's keys above its
+// own, counted against the wave's keys in LDS; ranks are distinct because
+// the keys are, so lanes of rank < k are the top-k in rank order.  The
+// weights use the same fp32 steps as above: m is the rank-0 logit, the
+// exponentials are summed in rank order from 0.  wl is this wave's
+// kTopkLds bytes of LDS.
+constexpr int kTopkLds = 64 * 8 + 32 * 4;
+
+__device__ __forceinline__ void select_topk_rank64(const float* __restrict__ lg, int E, int k,
+                                                   int32_t* __restrict__ idx_out,
+                                                   float* __restrict__ w_out,
+                                                   int32_t* __restrict__ idx_copy,
+                                                   char* wl) {
+  uint64_t* keys = (uint64_t*)wl;          // [64]
+  float* val = (float*)(wl + 64 * 8);      // [16] logit of rank r
+  float* exb = val + 16;                   // [16] exponential of rank r
+  const int lane = threadIdx.x & 63;
+  const bool ok = lane < E;
+  const uint64_t key =
+      ok ? (((uint64_t)ordered_f32(lg[lane]) << 32) | (uint32_t)~(uint32_t)lane) : 0ull;
+  keys[lane] = key;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int rank = 0;
+  for (int j = 0; j < E; j += 2) {  // E is even or the last pad key is 0
+    const u64x2 kv = *(const u64x2*)(keys + j);
+    rank += (kv[0] > key) + (kv[1] > key);
+  }
+  const bool sel = ok && rank < k;
+  const float v = unordered_f32((uint32_t)(key >> 32));
+  if (sel) val[rank] = v;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float ex = expf(v - val[0]);
+  if (sel) exb[rank] = ex;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float ssum = 0.0f;
+  for (int r = 0; r < k; ++r) ssum += exb[r];  // rank order
+  if (sel) {
+    idx_out[rank] = lane;
+    idx_copy[rank] = lane;
+    w_out[rank] = ex / ssum;
+  }
+  // the next token's writes to this wave's LDS come after every read above
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Stage TB activation rows (bf16) into LDS; rows past T are zero.
 template <int TB, int NTHR>
 __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int T,
@@ -259,10 +313,16 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logi
                                                   int T, int E, int k,
                                                   int32_t* __restrict__ topk_idx,
                                                   float* __restrict__ topk_w) {
+  __shared__ __align__(16) char wl[4][kTopkLds];
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  select_topk_reg(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
-                  topk_w + (size_t)t * k, topk_idx + (size_t)t * k);
+  if (E <= 64)
+    select_topk_rank64(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
+                       topk_w + (size_t)t * k, topk_idx + (size_t)t * k,
+                       wl[threadIdx.x >> 6]);
+  else
+    select_topk_reg(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
+                    topk_w + (size_t)t * k, topk_idx + (size_t)t * k);
 }
 
 // Few tokens: top-k of every token (one wave per token, 16 waves) and the
@@ -272,11 +332,17 @@ __global__ __launch_bounds__(1024) void route_topk_permute(
     float* __restrict__ topk_w, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos) {
   extern __shared__ int32_t sh[];
+  __shared__ __align__(16) char wl[16][kTopkLds];
   const int P = T * k;
   int32_t* idx_lds = sh;
-  for (int t = threadIdx.x >> 6; t < T; t += 16)
-    select_topk_reg(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
-                    topk_w + (size_t)t * k, idx_lds + t * k);
+  for (int t = threadIdx.x >> 6; t < T; t += 16) {
+    if (E <= 64)
+      select_topk_rank64(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
+                         topk_w + (size_t)t * k, idx_lds + t * k, wl[threadIdx.x >> 6]);
+    else
+      select_topk_reg(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
+                      topk_w + (size_t)t * k, idx_lds + t * k);
+  }
   __syncthreads();
   permute_block(idx_lds, P, E, offsets, sorted_pair, pair_pos, sh + ((P + 3) & ~3));
 }

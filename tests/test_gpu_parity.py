@@ -277,6 +277,54 @@ def test_layer_cfg1_decode(T):
     check_layer(DevLayer(cfg, T), HostLayer(cfg, T), moe.MOE_PATH_AUTO)
 
 
+@pytest.mark.parametrize("T", [1, 16])
+def test_layer_cfg1_sequential_per_expert(T):
+    """One launch per expert over the same routed pairs gives the fused result."""
+    note(f"layer cfg1 sequential per-expert T={T}")
+    cfg = synth.CONFIGS[1]
+    dl, hl = DevLayer(cfg, T), HostLayer(cfg, T)
+    lay, _, _ = run_layer(dl, moe.MOE_PATH_DECODE)
+    E, d = lay.E, lay.d
+    fmt = moe.MOE_FMT_W4_SYM
+    ws = torch.empty((max(moe.moe_ffn_ws_bytes(T, cfg.k, 1, d, cfg.f, fmt), 256),),
+                     dtype=torch.uint8, device=DEV)
+    ref = oracle.layer(hl.x, hl.wr, hl.bias, cfg.k, cfg.f, hl.expert, cfg.fmt,
+                       moe.MOE_BITS_NONE, None)
+    active = np.nonzero(np.diff(lay.offsets.cpu().numpy()))[0]
+    for experts in (None, active):      # every expert, then the activated ones
+        y = torch.full_like(lay.y_pairs, float("nan"))
+        moe.expert_ffn_per_expert(dl.x, lay.offsets, lay.sorted_pair, cfg.k, cfg.f,
+                                  dl.guc, dl.gus, dl.dnc, dl.dns, y, ws, fmt,
+                                  path=moe.MOE_PATH_DECODE, experts=experts)
+        o = moe.moe_combine(y, lay.pair_pos, lay.topk_w, out_dtype=moe.MOE_OUT_F32)
+        torch.cuda.synchronize()
+        assert_close(y.cpu().numpy(), ref["y_pairs"], "y_pairs sequential")
+        assert_close(o.cpu().numpy(), ref["o"], "out sequential")
+
+
+def test_layer_graph_replay_matches_eager():
+    """Graph-replayed steps equal eager steps bit for bit, replay after
+    replay, with eager work and synchronizations between the replays."""
+    note("layer cfg1 T=16 graph replay")
+    cfg = synth.CONFIGS[1]
+    dl_a, dl_b = DevLayer(cfg, 16, step=0), DevLayer(cfg, 16, step=1)
+    lay = dl_a.layer()
+    out_g = torch.empty((16, cfg.d), dtype=torch.bfloat16, device=DEV)
+    g = lay.capture(dl_a.x, out_g)
+    torch.cuda.synchronize()
+    ref_a = lay.forward(dl_a.x, out_dtype=moe.MOE_OUT_BF16).clone()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out_g.fill_(0)
+        eager_b = lay.forward(dl_b.x, out_dtype=moe.MOE_OUT_BF16).clone()  # eager work between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, ref_a), f"replay {rep}"
+        assert not torch.equal(eager_b, ref_a)
+    del g  # the eager result itself is checked against the oracle elsewhere
+
+
 def test_layer_cfg3_bitplane_rank_rule():
     note("layer cfg3 T=16 bitplane rank rule")
     cfg = synth.CONFIGS[3]
