@@ -232,6 +232,36 @@ int moe_combine(const float *y_pairs, const int32_t *pair_pos,
                 int out_dtype, void *stream);
 
 /* ---------------------------------------------------------------------
+ * moe_layer_forward_wq -- one routed-expert MoE layer step in one call:
+ * the composition moe_route_permute -> moe_expert_ffn_wq -> moe_combine
+ * with the same arguments, producing the same outputs bit for bit
+ * (topk_idx, topk_w, expert_offsets, sorted_pair, pair_pos, y_pairs, out).
+ * [ExactMoE] Abstract: unchanged top-k routing, every selected expert
+ * executed by grouped kernels, outputs combined.
+ * When the decode path applies to an int4 layer with T <= 16 and
+ * 2 T k >= E, the grouping is computed inside the expert gate/up kernel
+ * (expert-major work items; no separate permute launch); otherwise the
+ * three steps run as listed.
+ * ws / ws_bytes: at least moe_layer_ws_bytes(T, k, E, d, f, format),
+ *   256-byte aligned, caller-owned, no contents carried between calls.
+ * Every argument is checked as by the three entry points before anything
+ * is enqueued; error codes as there.  Timing events armed with
+ * moe_set_ffn_events apply to its gate/up and down kernels.
+ * ------------------------------------------------------------------- */
+size_t moe_layer_ws_bytes(int T, int k, int E, int d, int f, int format);
+int moe_layer_forward_wq(const void *x_bf16, const void *wr_bf16, const float *bias,
+                         int T, int d, int E, int k, int f, int format,
+                         int group_size, const uint8_t *gate_up_codes,
+                         const uint16_t *gate_up_scales_f16,
+                         const uint8_t *down_codes,
+                         const uint16_t *down_scales_f16, const uint8_t *bits,
+                         int bits_mode, int32_t *topk_idx, float *topk_w,
+                         int32_t *expert_offsets, int32_t *sorted_pair,
+                         int32_t *pair_pos, float *y_pairs, void *out,
+                         int out_dtype, void *ws, size_t ws_bytes, int path_hint,
+                         void *stream);
+
+/* ---------------------------------------------------------------------
  * moe_set_ffn_events -- optional timing instrumentation (no page defines
  * it; it serves throughput measurement).  Arms, for the NEXT
  * moe_expert_ffn_wq call made by the calling thread only, four hipEvent_t

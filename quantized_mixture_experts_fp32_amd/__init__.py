@@ -29,7 +29,8 @@ EXPORTS = ("moe_status_str", "moe_last_error", "moe_route_ws_bytes", "moe_route"
            "moe_permute_ws_bytes",
            "moe_permute", "moe_route_permute_ws_bytes", "moe_route_permute",
            "moe_ffn_ws_bytes", "moe_expert_ffn_wq", "moe_combine",
-           "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events")
+           "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events",
+           "moe_layer_ws_bytes", "moe_layer_forward_wq")
 
 
 class MoeError(RuntimeError):
@@ -69,8 +70,13 @@ def load_library():
     lib.moe_quantize_w4.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
     lib.moe_quantize_bitplane8.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp]
     lib.moe_set_ffn_events.argtypes = [vp, vp, vp, vp]
+    lib.moe_layer_ws_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.moe_layer_ws_bytes.restype = sz
+    lib.moe_layer_forward_wq.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                         vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                         vp, i32, vp, sz, i32, vp]
     for name in ("moe_route", "moe_permute", "moe_route_permute", "moe_expert_ffn_wq",
-                 "moe_combine",
+                 "moe_combine", "moe_layer_forward_wq",
                  "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events"):
         getattr(lib, name).restype = i32
     _lib = lib
@@ -248,6 +254,28 @@ def expert_ffn_per_expert(x, expert_offsets, sorted_pair, k, f, gate_up_codes,
     return y_pairs
 
 
+def moe_layer_ws_bytes(T, k, E, d, f, fmt=MOE_FMT_W4_SYM):
+    return int(load_library().moe_layer_ws_bytes(T, k, E, d, f, fmt))
+
+
+def moe_layer_forward(x, wr, bias, k, f, gate_up_codes, gate_up_scales, down_codes,
+                      down_scales, topk_idx, topk_w, offsets, sorted_pair, pair_pos,
+                      y_pairs, out, ws, fmt=MOE_FMT_W4_SYM, bits=None,
+                      bits_mode=MOE_BITS_NONE, out_dtype=MOE_OUT_BF16,
+                      path=MOE_PATH_AUTO, stream=None):
+    """moe_route_permute -> moe_expert_ffn_wq -> moe_combine in one ABI call
+    (same outputs); every output buffer is caller-provided."""
+    T, d = x.shape
+    E = wr.shape[0]
+    _check("moe_layer_forward_wq", load_library().moe_layer_forward_wq(
+        _ptr(x), _ptr(wr), _ptr(bias), T, d, E, k, f, fmt, MOE_GROUP, _ptr(gate_up_codes),
+        _ptr(gate_up_scales), _ptr(down_codes), _ptr(down_scales), _ptr(bits), bits_mode,
+        _ptr(topk_idx), _ptr(topk_w), _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos),
+        _ptr(y_pairs), _ptr(out), out_dtype, _ptr(ws), ws.numel() * ws.element_size(),
+        path, _stream(stream)))
+    return out
+
+
 def moe_combine(y_pairs, pair_pos, topk_w, out=None, out_dtype=MOE_OUT_BF16,
                 stream=None):
     """Layer output [T][d] (bf16 bits in an int16 tensor, or fp32)."""
@@ -337,11 +365,32 @@ class MoeLayer:
                                  dtype=torch.uint8, device=dev)
         self.ws_ffn = torch.empty((max(moe_ffn_ws_bytes(T, k, E, d, f, self.fmt), 256),),
                                   dtype=torch.uint8, device=dev)
+        self.ws_layer = torch.empty((max(moe_layer_ws_bytes(T, k, E, d, f, self.fmt), 256),),
+                                    dtype=torch.uint8, device=dev)
         self.y_pairs = torch.empty((P, d), dtype=torch.float32, device=dev)
         self._T = T
 
     def forward(self, x, out=None, out_dtype=MOE_OUT_BF16, path=MOE_PATH_AUTO,
                 stream=None, weights=None):
+        """One layer step through moe_layer_forward_wq."""
+        import torch
+        T = x.shape[0]
+        if self._T != T:
+            self._alloc(T, x)
+        gu, gus, dn, dns = weights if weights is not None else (
+            self.gu, self.gus, self.dn, self.dns)
+        if out is None:
+            out = _empty((T, self.d), torch.bfloat16 if out_dtype == MOE_OUT_BF16
+                         else torch.float32, x)
+        return moe_layer_forward(x, self.wr, self.bias, self.k, self.f, gu, gus, dn, dns,
+                                 self.topk_idx, self.topk_w, self.offsets, self.sorted_pair,
+                                 self.pair_pos, self.y_pairs, out, self.ws_layer, self.fmt,
+                                 self.bits, self.bits_mode, out_dtype, path, stream)
+
+    def forward_steps(self, x, out=None, out_dtype=MOE_OUT_BF16, path=MOE_PATH_AUTO,
+                      stream=None, weights=None):
+        """The same step as moe_route_permute, moe_expert_ffn_wq and
+        moe_combine calls (the composition the layer entry point equals)."""
         T = x.shape[0]
         if self._T != T:
             self._alloc(T, x)
@@ -359,8 +408,8 @@ class MoeLayer:
     def bind(self, x, out, weights=None, path=MOE_PATH_AUTO, out_dtype=MOE_OUT_BF16,
              stream=None):
         """A step with every argument marshalled once: returns a callable that
-        enqueues the same three ABI calls as forward(x, out, ...) for these
-        fixed buffers (x, out and the weights must stay alive and in place).
+        enqueues the same ABI call as forward(x, out, ...) for these fixed
+        buffers (x, out and the weights must stay alive and in place).
         For decode loops, where converting arguments on every call would cost
         as much host time as the kernels take on the GPU."""
         T = x.shape[0]
@@ -368,31 +417,19 @@ class MoeLayer:
             self._alloc(T, x)
         gu, gus, dn, dns = weights if weights is not None else (
             self.gu, self.gus, self.dn, self.dns)
-        lib = load_library()
         E, k, d, f = self.E, self.k, self.d, self.f
-        st = _stream(stream)
-        rp_args = (_ptr(x), _ptr(self.wr), _ptr(self.bias), T, d, E, k, _ptr(self.topk_idx),
-                   _ptr(self.topk_w), _ptr(self.offsets), _ptr(self.sorted_pair),
-                   _ptr(self.pair_pos), _ptr(self.ws_rp),
-                   self.ws_rp.numel() * self.ws_rp.element_size(), st)
-        ffn_args = (_ptr(x), _ptr(self.offsets), _ptr(self.sorted_pair), T, k, E, d, f,
-                    self.fmt, MOE_GROUP, _ptr(gu), _ptr(gus), _ptr(dn), _ptr(dns),
-                    _ptr(self.bits), self.bits_mode, _ptr(self.y_pairs), _ptr(self.ws_ffn),
-                    self.ws_ffn.numel() * self.ws_ffn.element_size(), path, st)
-        cb_args = (_ptr(self.y_pairs), _ptr(self.pair_pos), _ptr(self.topk_w), T, k, d,
-                   _ptr(out), out_dtype, st)
-        rp, ffn, cb = lib.moe_route_permute, lib.moe_expert_ffn_wq, lib.moe_combine
+        args = (_ptr(x), _ptr(self.wr), _ptr(self.bias), T, d, E, k, f, self.fmt, MOE_GROUP,
+                _ptr(gu), _ptr(gus), _ptr(dn), _ptr(dns), _ptr(self.bits), self.bits_mode,
+                _ptr(self.topk_idx), _ptr(self.topk_w), _ptr(self.offsets),
+                _ptr(self.sorted_pair), _ptr(self.pair_pos), _ptr(self.y_pairs), _ptr(out),
+                out_dtype, _ptr(self.ws_layer),
+                self.ws_layer.numel() * self.ws_layer.element_size(), path, _stream(stream))
+        fn = load_library().moe_layer_forward_wq
 
         def step():
-            rc = rp(*rp_args)
+            rc = fn(*args)
             if rc:
-                _check("moe_route_permute", rc)
-            rc = ffn(*ffn_args)
-            if rc:
-                _check("moe_expert_ffn_wq", rc)
-            rc = cb(*cb_args)
-            if rc:
-                _check("moe_combine", rc)
+                _check("moe_layer_forward_wq", rc)
             return out
 
         return step

@@ -124,10 +124,10 @@ size_t moe_route_permute_ws_bytes(int T, int k, int E) {
   return moe::route_permute_ws_bytes(T, k, E);
 }
 
-int moe_route_permute(const void* x_bf16, const void* wr_bf16, const float* bias, int T,
-                      int d, int E, int k, int32_t* topk_idx, float* topk_w,
-                      int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
-                      void* ws, size_t ws_bytes, void* stream) {
+static int route_permute_check(const void* x_bf16, const void* wr_bf16, const float* bias,
+                               int T, int d, int E, int k, int32_t* topk_idx, float* topk_w,
+                               int32_t* expert_offsets, int32_t* sorted_pair,
+                               int32_t* pair_pos, void* ws, size_t ws_bytes) {
   int rc = check_dims(T, d, E, k);
   if (rc) return rc;
   if (!expert_offsets) return fail(MOE_ERR_INVALID_ARG, "moe_route_permute: null offsets");
@@ -142,6 +142,16 @@ int moe_route_permute(const void* x_bf16, const void* wr_bf16, const float* bias
                  !aligned(topk_w, 4) || (bias && !aligned(bias, 4)) ||
                  !aligned(sorted_pair, 4) || !aligned(pair_pos, 4))))
     return fail(MOE_ERR_INVALID_ARG, "moe_route_permute: misaligned pointer");
+  return MOE_OK;
+}
+
+int moe_route_permute(const void* x_bf16, const void* wr_bf16, const float* bias, int T,
+                      int d, int E, int k, int32_t* topk_idx, float* topk_w,
+                      int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                      void* ws, size_t ws_bytes, void* stream) {
+  int rc = route_permute_check(x_bf16, wr_bf16, bias, T, d, E, k, topk_idx, topk_w,
+                               expert_offsets, sorted_pair, pair_pos, ws, ws_bytes);
+  if (rc) return rc;
   return hip_status(moe::launch_route_permute(x_bf16, wr_bf16, bias, T, d, E, k, topk_idx,
                                               topk_w, expert_offsets, sorted_pair, pair_pos,
                                               ws, (hipStream_t)stream),
@@ -153,15 +163,13 @@ size_t moe_ffn_ws_bytes(int T, int k, int E, int d, int f, int format) {
   return moe::ffn_ws_bytes(T, k, E, d, f, format);
 }
 
-int moe_expert_ffn_wq(const void* x_bf16, const int32_t* expert_offsets,
-                      const int32_t* sorted_pair, int T, int k, int E, int d,
-                      int f, int format, int group_size,
-                      const uint8_t* gate_up_codes,
-                      const uint16_t* gate_up_scales_f16,
-                      const uint8_t* down_codes,
-                      const uint16_t* down_scales_f16, const uint8_t* bits,
-                      int bits_mode, float* y_pairs, void* ws, size_t ws_bytes,
-                      int path_hint, void* stream) {
+// Checks of moe_expert_ffn_wq; *path receives the resolved path.
+static int ffn_check(const void* x_bf16, const int32_t* expert_offsets,
+                     const int32_t* sorted_pair, int T, int k, int E, int d, int f,
+                     int format, int group_size, const uint8_t* gate_up_codes,
+                     const uint16_t* gate_up_scales_f16, const uint8_t* down_codes,
+                     const uint16_t* down_scales_f16, const uint8_t* bits, int bits_mode,
+                     float* y_pairs, void* ws, size_t ws_bytes, int path_hint, int* path) {
   int rc = check_dims(T, d, E, k, false);
   if (rc) return rc;
   if (f <= 0) return fail(MOE_ERR_INVALID_ARG, "f=%d", f);
@@ -201,11 +209,28 @@ int moe_expert_ffn_wq(const void* x_bf16, const int32_t* expert_offsets,
   if (!aligned(ws, 256))
     return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_wq: workspace not 256-byte aligned");
   const long long P = (long long)T * k;
-  int path = path_hint;
+  *path = path_hint;
   // weight streaming while experts receive few pairs on average; an expert
   // receives at most T pairs (one per token), so T <= 16 always streams
-  if (path == MOE_PATH_AUTO)
-    path = (P <= 8LL * E || T <= 16) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+  if (*path == MOE_PATH_AUTO)
+    *path = (P <= 8LL * E || T <= 16) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+  return MOE_OK;
+}
+
+int moe_expert_ffn_wq(const void* x_bf16, const int32_t* expert_offsets,
+                      const int32_t* sorted_pair, int T, int k, int E, int d,
+                      int f, int format, int group_size,
+                      const uint8_t* gate_up_codes,
+                      const uint16_t* gate_up_scales_f16,
+                      const uint8_t* down_codes,
+                      const uint16_t* down_scales_f16, const uint8_t* bits,
+                      int bits_mode, float* y_pairs, void* ws, size_t ws_bytes,
+                      int path_hint, void* stream) {
+  int path = 0;
+  int rc = ffn_check(x_bf16, expert_offsets, sorted_pair, T, k, E, d, f, format, group_size,
+                     gate_up_codes, gate_up_scales_f16, down_codes, down_scales_f16, bits,
+                     bits_mode, y_pairs, ws, ws_bytes, path_hint, &path);
+  if (rc || T == 0) return rc;
   moe::FfnArgs a{(const uint16_t*)x_bf16, expert_offsets, sorted_pair, T, k, E,
                  d, f, format, gate_up_codes, gate_up_scales_f16, down_codes,
                  down_scales_f16, bits, bits_mode, y_pairs, ws, path,
@@ -223,9 +248,8 @@ int moe_set_ffn_events(void* gateup_begin, void* gateup_end, void* down_begin,
   return ok();
 }
 
-int moe_combine(const float* y_pairs, const int32_t* pair_pos,
-                const float* topk_w, int T, int k, int d, void* out,
-                int out_dtype, void* stream) {
+static int combine_check(const float* y_pairs, const int32_t* pair_pos, const float* topk_w,
+                         int T, int k, int d, void* out, int out_dtype) {
   if (T < 0 || k <= 0 || d <= 0)
     return fail(MOE_ERR_INVALID_ARG, "moe_combine: bad size");
   if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k=%d > %d", k, MOE_MAX_TOPK);
@@ -238,6 +262,14 @@ int moe_combine(const float* y_pairs, const int32_t* pair_pos,
   if (!aligned(y_pairs, 16) || !aligned(out, 16) || !aligned(pair_pos, 4) ||
       !aligned(topk_w, 4))
     return fail(MOE_ERR_INVALID_ARG, "moe_combine: misaligned pointer");
+  return MOE_OK;
+}
+
+int moe_combine(const float* y_pairs, const int32_t* pair_pos,
+                const float* topk_w, int T, int k, int d, void* out,
+                int out_dtype, void* stream) {
+  int rc = combine_check(y_pairs, pair_pos, topk_w, T, k, d, out, out_dtype);
+  if (rc || T == 0) return rc;
   return hip_status(moe::launch_combine(y_pairs, pair_pos, topk_w, T, k, d, out,
                                         out_dtype == MOE_OUT_F32,
                                         (hipStream_t)stream),
@@ -273,3 +305,66 @@ int moe_quantize_bitplane8(const float* w, int E, int N, int K, int group_size,
 }
 
 }  // extern "C"
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t moe_layer_ws_bytes(int T, int k, int E, int d, int f, int format) {
+  if (T < 0 || k <= 0 || E <= 0 || d <= 0 || f <= 0) return 0;
+  const size_t ffn = moe::ffn_ws_bytes(T, k, E, d, f, format);
+  const size_t em = moe::em_h_bytes(E, f);
+  return align256(moe::route_permute_ws_bytes(T, k, E)) + (ffn > em ? ffn : em);
+}
+
+int moe_layer_forward_wq(const void* x_bf16, const void* wr_bf16, const float* bias, int T,
+                         int d, int E, int k, int f, int format, int group_size,
+                         const uint8_t* gate_up_codes, const uint16_t* gate_up_scales_f16,
+                         const uint8_t* down_codes, const uint16_t* down_scales_f16,
+                         const uint8_t* bits, int bits_mode, int32_t* topk_idx,
+                         float* topk_w, int32_t* expert_offsets, int32_t* sorted_pair,
+                         int32_t* pair_pos, float* y_pairs, void* out, int out_dtype,
+                         void* ws, size_t ws_bytes, int path_hint, void* stream) {
+  const size_t need = moe_layer_ws_bytes(T, k, E, d, f, format);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_layer_forward_wq: workspace %zu < %zu bytes",
+                ws ? ws_bytes : (size_t)0, need);
+  if (!aligned(ws, 256))
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_wq: workspace not 256-byte aligned");
+  const size_t rp_b = align256(moe::route_permute_ws_bytes(T, k, E));
+  void* ws_ffn = (char*)ws + rp_b;
+  int path = 0;
+  int rc = route_permute_check(x_bf16, wr_bf16, bias, T, d, E, k, topk_idx, topk_w,
+                               expert_offsets, sorted_pair, pair_pos, ws, rp_b);
+  if (!rc)
+    rc = ffn_check(x_bf16, expert_offsets, sorted_pair, T, k, E, d, f, format, group_size,
+                   gate_up_codes, gate_up_scales_f16, down_codes, down_scales_f16, bits,
+                   bits_mode, y_pairs, ws_ffn, ws_bytes - rp_b, path_hint, &path);
+  if (!rc) rc = combine_check(y_pairs, pair_pos, topk_w, T, k, d, out, out_dtype);
+  if (rc) return rc;
+  const hipStream_t s = (hipStream_t)stream;
+  if (T == 0)  // no tokens: expert_offsets becomes all zero, as from moe_route_permute
+    return hip_status(moe::launch_route_permute(x_bf16, wr_bf16, bias, 0, d, E, k, topk_idx,
+                                                topk_w, expert_offsets, sorted_pair,
+                                                pair_pos, ws, s),
+                      "moe_layer_forward_wq");
+  moe::FfnArgs a{(const uint16_t*)x_bf16, expert_offsets, sorted_pair, T, k, E,
+                 d, f, format, gate_up_codes, gate_up_scales_f16, down_codes,
+                 down_scales_f16, bits, bits_mode, y_pairs, ws_ffn, path,
+                 {g_ffn_ev[0], g_ffn_ev[1], g_ffn_ev[2], g_ffn_ev[3]}};
+  for (auto& ev : g_ffn_ev) ev = nullptr;  // one-shot
+  hipError_t e;
+  if (path == MOE_PATH_DECODE && moe::em_applies(T, k, E, d, f, format)) {
+    // routing only; the grouping comes out of the expert-major gate/up kernel
+    e = moe::launch_route(x_bf16, wr_bf16, bias, T, d, E, k, topk_idx, topk_w, ws, s);
+    if (e == hipSuccess)
+      e = moe::launch_ffn_decode_em(a, topk_idx, expert_offsets, sorted_pair, pair_pos,
+                                    (uint16_t*)ws_ffn, s);
+  } else {
+    e = moe::launch_route_permute(x_bf16, wr_bf16, bias, T, d, E, k, topk_idx, topk_w,
+                                  expert_offsets, sorted_pair, pair_pos, ws, s);
+    if (e == hipSuccess) e = moe::launch_ffn(a, s);
+  }
+  if (e == hipSuccess)
+    e = moe::launch_combine(y_pairs, pair_pos, topk_w, T, k, d, out, out_dtype == MOE_OUT_F32,
+                            s);
+  return hip_status(e, "moe_layer_forward_wq");
+}

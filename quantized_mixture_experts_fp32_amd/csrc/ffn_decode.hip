@@ -608,6 +608,230 @@ void launch_decode_lds(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s
              a.f, a.dn_codes, a.dn_scales, a.y);
   }
 }
+// ------------------------------------ expert-major, at most 16 tokens
+// With at most 16 tokens every expert receives at most 16 pairs (a token's
+// k experts are distinct), so each expert needs one token tile and a work
+// item (expert e, 64 features) follows from blockIdx alone.  The gate/up
+// block issues its first scale, code and activation loads (the rows of all
+// T tokens) together with topk_idx and derives the grouping itself: ballots
+// over the T*k pairs give expert e's slot range [r0, r0 + cnt) (pairs
+// ordered by expert, then by pair index: the counting sort of the permute
+// step) and the pair of each of its columns.  Block (e, 0) stores expert
+// e's part of expert_offsets, sorted_pair and pair_pos.  h is kept per
+// expert, [E][16][f] bf16, so the down block loads its rows without waiting
+// for the grouping; its slot range comes from expert_offsets, loaded beside
+// its first code loads.  Per group, operands and MFMA order are those of
+// the LDS-staged kernels above (the same fp32 results).
+constexpr int kEmMaxT = 16;
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & 63;
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+template <int kDQ, int kWaves, int kSC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
+void gateup_w4_em(const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
+                  int T, int k, int E, int d, int f, const uint8_t* __restrict__ codes,
+                  const uint16_t* __restrict__ scales, uint16_t* __restrict__ hE,
+                  int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
+                  int32_t* __restrict__ pair_pos) {
+  extern __shared__ int32_t lds_i[];
+  __shared__ int32_t wcnt[4][2];
+  __shared__ int32_t colpair[kEmMaxT];
+  const int G = d >> 7, RG = f / 64, P = T * k;
+  float* sc_lds = (float*)lds_i;                    // [2][G][64]
+  uint16_t* xs = (uint16_t*)(sc_lds + 2 * G * 64);  // [2][16][kXRow]
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int st_tok = tid >> 4, st_pc = tid & 15;  // staged token row and 16-byte piece
+  const bf16x8 negoff = bf16_splat(kBf16NegOff);
+  const int e = blockIdx.x / RG, rg = blockIdx.x % RG;
+  const int nb = rg * 64, n0 = nb + 16 * wave;
+  const size_t erow = (size_t)e * 2 * f;
+
+  // t = 0: every pair's expert, then scales, codes and activations
+  const int pe = tid < P ? topk_idx[tid] : -1;
+  const uint16_t* xsrc = x + (size_t)(st_tok < T ? st_tok : 0) * d + 8 * st_pc;
+  const uint8_t* cg = codes + (erow + n0) * (size_t)(d >> 1) + 64 * col + 16 * kq;
+  const uint8_t* cu = cg + (size_t)f * (d >> 1);
+  u32x4 qg[kDQ], qu[kDQ], xv[kDQ];
+  auto load = [&](int g, int i) {
+    xv[i] = *(const u32x4*)(xsrc + 128 * g);
+    qg[i] = *(const u32x4*)(cg + kTileGroupBytes * g);
+    qu[i] = *(const u32x4*)(cu + kTileGroupBytes * g);
+  };
+  ScaleStage<2, kSC ? kSC : 1> sst;
+  if (kSC) sst.fetch(scales + (erow + nb) * G, (size_t)f, G);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kDQ; ++i) load(i < G ? i : G - 1, i);
+  __builtin_amdgcn_sched_barrier(0);
+  if (kSC)
+    sst.store(G, sc_lds);
+  else
+    stage_scales_rows64<2>(scales + (erow + nb) * G, (size_t)f, G, sc_lds);
+
+  // the grouping of the pairs, as far as expert e is concerned
+  const bool mine = pe == e;
+  const bool below = (unsigned)pe < (unsigned)E && pe < e;
+  const uint64_t bm = __ballot(mine), bb = __ballot(below);
+  if (lane == 0) {
+    wcnt[wave][0] = __popcll(bm);
+    wcnt[wave][1] = __popcll(bb);
+  }
+  __syncthreads();
+  int cnt = 0, r0 = 0, rank = __popcll(bm & lanemask_lt());
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    cnt += wcnt[w][0];
+    r0 += wcnt[w][1];
+    rank += w < wave ? wcnt[w][0] : 0;
+  }
+  if (mine && rank < kEmMaxT) colpair[rank] = tid;
+  if (rg == 0) {
+    if (mine) {
+      sorted_pair[r0 + rank] = tid;
+      pair_pos[tid] = r0 + rank;
+    }
+    if (tid == 0) {
+      offsets[e] = r0;
+      if (e == E - 1) offsets[E] = r0 + cnt;
+    }
+  }
+  __syncthreads();
+  if (cnt == 0) return;  // block-uniform
+  const int ncol = cnt < kEmMaxT ? cnt : kEmMaxT;
+  const int xrow = colpair[col < ncol ? col : 0] / k;  // staged row of column col
+
+  f32x4 tg = {0, 0, 0, 0}, tu = {0, 0, 0, 0};
+  auto step = [&](int gi, int i) {
+    // slot gi & 1 was last read in step gi - 2, before the barrier of step gi - 1
+    uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
+    *(u32x4*)(slot + st_tok * kXRow + 8 * st_pc) = xv[i];
+    __syncthreads();
+    bf16x8 xp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xp[j] = *(const bf16x8*)(slot + xrow * kXRow + 32 * kq + 8 * j);
+    const f32x4 sg = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
+    const f32x4 su = *(const f32x4*)(sc_lds + (G + gi) * 64 + 16 * wave + 4 * kq);
+    f32x4 seed = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) seed = mfma16(negoff, xp[j], seed);
+    tile_group(xp, seed, qg[i], sg, tg);
+    tile_group(xp, seed, qu[i], su, tu);
+  };
+  // the first groups' loads were issued at the start (their one wait at the
+  // loop entry covers loads issued together); each slot is refilled after use
+  int g = 0;
+  for (; g + 2 * kDQ <= G; g += kDQ) {
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i) {
+      step(g + i, i);
+      load(g + i + kDQ, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kDQ; ++i) {
+    if (g + i >= G) break;
+    step(g + i, i);
+    if (g + i + kDQ < G) load(g + i + kDQ, i);
+  }
+#pragma unroll
+  for (int i = 0; i < kDQ; ++i)
+    if (g + kDQ + i < G) step(g + kDQ + i, i);
+
+  if (col < ncol) {
+    uint32_t hb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_rne(silu_f32(tg[i]) * tu[i]);
+    uint2 pk;
+    pk.x = hb[0] | (hb[1] << 16);
+    pk.y = hb[2] | (hb[3] << 16);
+    *(uint2*)(hE + ((size_t)e * kEmMaxT + col) * f + n0 + 4 * kq) = pk;
+  }
+}
+
+template <int kDQ, int kWaves, int kSC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
+void down_w4_em(const uint16_t* __restrict__ hE, const int32_t* __restrict__ offsets,
+                int E, int d, int f, const uint8_t* __restrict__ codes,
+                const uint16_t* __restrict__ scales, float* __restrict__ y) {
+  extern __shared__ int32_t lds_i[];
+  const int G = f >> 7, RG = d / 64;
+  float* sc_lds = (float*)lds_i;                // [G][64]
+  uint16_t* xs = (uint16_t*)(sc_lds + G * 64);  // [2][16][kXRow]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int st_tok = tid >> 4, st_pc = tid & 15;
+  const bf16x8 negoff = bf16_splat(kBf16NegOff);
+  const int e = blockIdx.x / RG, rg = blockIdx.x % RG;
+  const int mb = rg * 64, m0 = mb + 16 * wave;
+  const size_t erow = (size_t)e * d;
+
+  // t = 0: the slot range, scales, codes and all 16 rows of h (rows past the
+  // expert's count hold stale values that feed only unstored columns)
+  const int lo = offsets[e], hi = offsets[e + 1];
+  const uint16_t* hsrc = hE + ((size_t)e * kEmMaxT + st_tok) * f + 8 * st_pc;
+  const uint8_t* cd = codes + (erow + m0) * (size_t)(f >> 1) + 64 * col + 16 * kq;
+  u32x4 q[kDQ], hv[kDQ];
+  auto load = [&](int g, int i) {
+    hv[i] = *(const u32x4*)(hsrc + 128 * g);
+    q[i] = *(const u32x4*)(cd + kTileGroupBytes * g);
+  };
+  ScaleStage<1, kSC ? kSC : 1> sst;
+  if (kSC) sst.fetch(scales + (erow + mb) * G, 0, G);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kDQ; ++i) load(i < G ? i : G - 1, i);
+  __builtin_amdgcn_sched_barrier(0);
+  if (kSC)
+    sst.store(G, sc_lds);
+  else
+    stage_scales_rows64<1>(scales + (erow + mb) * G, 0, G, sc_lds);
+  const int cnt = hi - lo;
+  if (cnt <= 0) return;  // block-uniform
+  const int ncol = cnt < kEmMaxT ? cnt : kEmMaxT;
+
+  f32x4 acc = {0, 0, 0, 0};
+  auto step = [&](int gi, int i) {
+    uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
+    *(u32x4*)(slot + st_tok * kXRow + 8 * st_pc) = hv[i];
+    __syncthreads();
+    bf16x8 xp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xp[j] = *(const bf16x8*)(slot + col * kXRow + 32 * kq + 8 * j);
+    const f32x4 sv = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
+    f32x4 seed = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) seed = mfma16(negoff, xp[j], seed);
+    tile_group(xp, seed, q[i], sv, acc);
+  };
+  // the first groups' loads were issued at the start (their one wait at the
+  // loop entry covers loads issued together); each slot is refilled after use
+  int g = 0;
+  for (; g + 2 * kDQ <= G; g += kDQ) {
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i) {
+      step(g + i, i);
+      load(g + i + kDQ, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kDQ; ++i) {
+    if (g + i >= G) break;
+    step(g + i, i);
+    if (g + i + kDQ < G) load(g + i + kDQ, i);
+  }
+#pragma unroll
+  for (int i = 0; i < kDQ; ++i)
+    if (g + kDQ + i < G) step(g + kDQ + i, i);
+  if (col < ncol) *(f32x4*)(y + (size_t)(lo + col) * d + m0 + 4 * kq) = acc;
+}
+
 }  // namespace
 
 // Split K over 1, 2 or 4 waves so that few active experts (a single
@@ -626,6 +850,47 @@ hipError_t launch_ffn_decode_w4(const FfnArgs& a, uint16_t* h, hipStream_t s) {
     if (KS == 4) launch_decode_pair<4, 1>(a, h, P, s);
     else if (KS == 2) launch_decode_pair<2, 1>(a, h, P, s);
     else launch_decode_lds(a, h, P, s);
+  }
+  return hipGetLastError();
+}
+
+// Expert-major decode of at most 16 tokens (int4): gate/up also produces the
+// grouping (expert_offsets, sorted_pair, pair_pos) from topk_idx; hE is the
+// per-expert h scratch of em_h_bytes(E, f) bytes.
+size_t em_h_bytes(int E, int f) { return (size_t)E * kEmMaxT * f * sizeof(uint16_t); }
+
+// Every expert's blocks issue their first loads before knowing whether the
+// expert has pairs, so the path needs most experts active: 2 T k >= E.
+bool em_applies(int T, int k, int E, int d, int f, int format) {
+  return format == 0 && T >= 1 && T <= kEmMaxT && 2LL * T * k >= E && d % 128 == 0 &&
+         f % 128 == 0;
+}
+
+hipError_t launch_ffn_decode_em(const FfnArgs& a, const int32_t* topk_idx, int32_t* offsets,
+                                int32_t* sorted_pair, int32_t* pair_pos, uint16_t* hE,
+                                hipStream_t s) {
+  {
+    const int G = a.d / 128;
+    const size_t lds = sizeof(float) * 2 * G * 64 + sizeof(uint16_t) * 2 * 16 * kXRow;
+    const int sc = scale_chunks(2, G, a.gu_scales);
+    auto kern = sc == 1   ? gateup_w4_em<kGuDQ, kGuWaves, 1>
+                : sc == 2 ? gateup_w4_em<kGuDQ, kGuWaves, 2>
+                : sc == 4 ? gateup_w4_em<kGuDQ, kGuWaves, 4>
+                          : gateup_w4_em<kGuDQ, kGuWaves, 0>;
+    launch_k(kern, dim3(a.E * (a.f / 64)), dim3(256), lds, s, a.ev[0], a.ev[1], a.x, topk_idx,
+             a.T, a.k, a.E, a.d, a.f, a.gu_codes, a.gu_scales, hE, offsets, sorted_pair,
+             pair_pos);
+  }
+  {
+    const int G = a.f / 128;
+    const size_t lds = sizeof(float) * G * 64 + sizeof(uint16_t) * 2 * 16 * kXRow;
+    const int sc = scale_chunks(1, G, a.dn_scales);
+    auto kern = sc == 1   ? down_w4_em<kDnDQ, kDnWaves, 1>
+                : sc == 2 ? down_w4_em<kDnDQ, kDnWaves, 2>
+                : sc == 4 ? down_w4_em<kDnDQ, kDnWaves, 4>
+                          : down_w4_em<kDnDQ, kDnWaves, 0>;
+    launch_k(kern, dim3(a.E * (a.d / 64)), dim3(256), lds, s, a.ev[2], a.ev[3], hE, offsets,
+             a.E, a.d, a.f, a.dn_codes, a.dn_scales, a.y);
   }
   return hipGetLastError();
 }

@@ -69,6 +69,14 @@ hipError_t launch_ffn_decode_w4(const FfnArgs& a, uint16_t* h, hipStream_t s);
 size_t ffn_prefill_ws_bytes(int T, int k, int E, int d, int f);
 hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStream_t s);
 
+// expert-major decode of at most 16 tokens, int4 (ffn_decode.hip): the
+// grouping comes out of its gate/up kernel; hE: em_h_bytes(E, f) of scratch
+size_t em_h_bytes(int E, int f);
+bool em_applies(int T, int k, int E, int d, int f, int format);
+hipError_t launch_ffn_decode_em(const FfnArgs& a, const int32_t* topk_idx, int32_t* offsets,
+                                int32_t* sorted_pair, int32_t* pair_pos, uint16_t* hE,
+                                hipStream_t s);
+
 hipError_t launch_combine(const float* y, const int32_t* pair_pos,
                           const float* topk_w, int T, int k, int d, void* out,
                           int out_f32, hipStream_t s);

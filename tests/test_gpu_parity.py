@@ -302,6 +302,52 @@ def test_layer_cfg1_sequential_per_expert(T):
         assert_close(o.cpu().numpy(), ref["o"], "out sequential")
 
 
+# (config, T, whether the three-call composition runs the same decode kernel
+# arithmetic, so that y_pairs and out must agree bit for bit)
+LAYER_ENTRY_CASES = [
+    (synth.CONFIGS[1], 16, True),
+    (synth.CONFIGS[1], 1, False),
+    (synth.CONFIGS[1], 4, False),
+    (custom_cfg(20, 256, 8, 2, 256), 16, False),            # up to 16 pairs per expert
+    (custom_cfg(21, 384, 20, 3, 640, bias_sigma=1.0), 13, False),  # G = 3, ragged
+    (synth.CONFIGS[1], 17, True),                            # composition path
+]
+
+
+@pytest.mark.parametrize("case", range(len(LAYER_ENTRY_CASES)))
+def test_layer_entry_matches_composition(case):
+    """moe_layer_forward_wq equals moe_route_permute -> moe_expert_ffn_wq ->
+    moe_combine: routing outputs bit for bit, y_pairs / out within the
+    oracle's bar (bit for bit where the same kernels run)."""
+    cfg, T, same_kernels = LAYER_ENTRY_CASES[case]
+    note(f"layer entry {cfg.name} d={cfg.d} E={cfg.E} k={cfg.k} f={cfg.f} T={T}")
+    dl, hl = DevLayer(cfg, T), HostLayer(cfg, T)
+    lay = dl.layer()
+    outs = []
+    for fwd in (lay.forward, lay.forward_steps):
+        o = fwd(dl.x, out_dtype=moe.MOE_OUT_F32).clone()
+        torch.cuda.synchronize()
+        outs.append(dict(o=o, y=lay.y_pairs.clone(), idx=lay.topk_idx.clone(),
+                         w=lay.topk_w.clone(), off=lay.offsets.clone(),
+                         sp=lay.sorted_pair.clone(), pp=lay.pair_pos.clone()))
+        lay.y_pairs.fill_(float("nan"))
+        lay.offsets.fill_(-1)
+        lay.sorted_pair.fill_(-1)
+        lay.pair_pos.fill_(-1)
+    a, b = outs
+    for key in ("idx", "w", "off", "sp", "pp"):
+        assert torch.equal(a[key], b[key]), key
+    ref = oracle.layer(hl.x, hl.wr, hl.bias, cfg.k, cfg.f, hl.expert, cfg.fmt,
+                       moe.MOE_BITS_NONE, None)
+    assert np.array_equal(a["off"].cpu().numpy(), ref["expert_offsets"])
+    assert np.array_equal(a["sp"].cpu().numpy(), ref["sorted_pair"])
+    assert_close(a["y"].cpu().numpy(), ref["y_pairs"], "y_pairs layer entry")
+    assert_close(a["o"].cpu().numpy(), ref["o"], "out layer entry")
+    if same_kernels:
+        assert torch.equal(a["y"], b["y"])
+        assert torch.equal(a["o"], b["o"])
+
+
 def test_layer_graph_replay_matches_eager():
     """Graph-replayed steps equal eager steps bit for bit, replay after
     replay, with eager work and synchronizations between the replays."""
