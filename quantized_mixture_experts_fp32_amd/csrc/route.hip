@@ -325,6 +325,41 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logi
                     topk_w + (size_t)t * k, topk_idx + (size_t)t * k);
 }
 
+// Very few tokens: one 1024-thread block per token computes all E logits
+// (64 lane groups, one expert each per pass, same order as above) into LDS
+// and selects the token's top-k there: one launch, no logits round trip.
+constexpr int kTokenBlockT = 16;
+
+__global__ __launch_bounds__(1024) void route_token_block(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int T, int d, int E, int k,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  extern __shared__ float lds[];
+  float* lg = lds;                                            // [E]
+  char* wl = (char*)(lds + ((E + 3) & ~3));                   // kTopkLds
+  uint16_t* xs = (uint16_t*)(wl + kTopkLds);                  // [d]
+  const int t = blockIdx.x;
+  stage_x<1, 1024>(x, T, d, t, xs);
+  __syncthreads();
+  const int G = threadIdx.x >> 4, l = threadIdx.x & 15;
+  for (int e0 = 0; e0 < E; e0 += 64) {  // uniform trip count (shuffles inside)
+    const int e = e0 + G;
+    const bool ok = e < E;
+    float acc[1];
+    group_logits<1>(xs, d, wr + (size_t)(ok ? e : 0) * d, ok, acc);
+    if (ok && l == 0) lg[e] = acc[0] + (bias ? bias[e] : 0.0f);
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    if (E <= 64)
+      select_topk_rank64(lg, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k,
+                         topk_idx + (size_t)t * k, wl);
+    else
+      select_topk_reg(lg, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k,
+                      topk_idx + (size_t)t * k);
+  }
+}
+
 // Few tokens: top-k of every token (one wave per token, 16 waves) and the
 // grouping of the T*k pairs by expert, in one 1024-thread block.
 __global__ __launch_bounds__(1024) void route_topk_permute(
@@ -357,7 +392,11 @@ hipError_t launch_route(const void* x, const void* wr, const float* bias,
                         int T, int d, int E, int k, int32_t* topk_idx,
                         float* topk_w, void* ws, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (T <= kSmallT) {
+  if (T <= kTokenBlockT) {
+    const size_t lds = sizeof(float) * ((E + 3) & ~3) + kTopkLds + sizeof(uint16_t) * d;
+    hipLaunchKernelGGL(route_token_block, dim3(T), dim3(1024), lds, s, (const uint16_t*)x,
+                       (const uint16_t*)wr, bias, T, d, E, k, topk_idx, topk_w);
+  } else if (T <= kSmallT) {
     float* logits = (float*)ws;
     const int neb = (E + 15) / 16;
     hipLaunchKernelGGL(route_logits_small, dim3(T * neb), dim3(256),
