@@ -347,7 +347,7 @@ def cpu_baseline(target_s, np, synth, oracle):
                       f"quantization excluded; {el:.1f} s"}
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_w4_decode_olmoe_T16.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_w4_em_olmoe_T16.txt")
 DECODE_SRC = os.path.join(ROOT, "quantized_mixture_experts_fp32_amd", "csrc", "ffn_decode.hip")
 
 
@@ -447,7 +447,7 @@ def main():
                    "weights": "int4-g128 codes + fp16 scales",
                    "weight_copies_rotated": head_rec["weight_copies"],
                    "token_batches_rotated": 16},
-        "roofline": {"bound": "hbm", "kernel": "expert gate/up (moe_expert_ffn_wq)",
+        "roofline": {"bound": "hbm", "kernel": "expert gate/up (gateup_w4_em, moe_layer_forward_wq)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(),
