@@ -42,6 +42,8 @@ def _load():
             "oracle_pair_bits": [i32, i32, i32, vp, i32, vp, vp],
             "oracle_expert_ffn": [vp, i32, i32, i32, vp, vp, vp, vp],
             "oracle_combine": [vp, vp, vp, i32, i32, i32, vp, vp],
+            "oracle_bp_distortion": [vp, vp, vp, vp, i32, i32, vp],
+            "oracle_allocate_bits": [vp, vp, i32, i32, i32, i32, i32, i64, vp, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -246,3 +248,36 @@ def layer(x, wr, bias, k, f, get_expert, fmt="w4", bits_mode=BITS_NONE,
     return dict(logits=logits, topk_idx=idx, topk_w=w, expert_offsets=off,
                 sorted_pair=sp, pair_pos=pp, pair_bits=pb, y_pairs=y, o=o,
                 out=out)
+
+
+# ------------------------------------------------------- read-budget allocator
+def bp_distortion(gu_planes, gu_scales, dn_planes, dn_scales, d, f):
+    """Weight-space distortion [8] of one expert at prefix widths 1..8 (planes
+    in the oracle's slab layout [8][R][K/8])."""
+    out = np.zeros(8, np.float64)
+    args = [np.ascontiguousarray(a) for a in (gu_planes, gu_scales, dn_planes, dn_scales)]
+    _ok(_load().oracle_bp_distortion(*[_p(a) for a in args], d, f, _p(out)),
+        "bp_distortion")
+    return out
+
+
+def bp_read_bytes(d, f, b):
+    """Bytes one expert reads at prefix width b (planes plus fp16 scales)."""
+    return b * 3 * d * f // 8 + 3 * d * f // 64
+
+
+def allocate_bits(dist, counts, d, f, bmin, bmax, budget):
+    """-> (bits [E] u8, lambda, read) of the read-budget bisection."""
+    dist = np.ascontiguousarray(dist, np.float64)
+    counts = np.ascontiguousarray(counts, np.int32)
+    E = dist.shape[0]
+    bits = np.zeros(E, np.uint8)
+    lam = ctypes.c_double()
+    rd = ctypes.c_int64()
+    _ok(_load().oracle_allocate_bits(_p(dist), _p(counts), E, d, f, bmin, bmax,
+                                     int(budget), _p(bits),
+                                     ctypes.cast(ctypes.pointer(lam), ctypes.c_void_p),
+                                     ctypes.cast(ctypes.pointer(rd), ctypes.c_void_p)),
+        "allocate_bits")
+    return bits, lam.value, rd.value
+

@@ -415,3 +415,137 @@ int oracle_combine(const double *y_pairs, const int32_t *pair_pos,
     }
   return 0;
 }
+
+/* Read-side bit allocation (DuoRate, "Two-Rate Per-Expert Precision
+ * Allocation for Mixture-of-Experts Serving": the routing-weighted read rate
+ * sum_e f_e R(M_e); a Lagrangian relaxation whose per-expert minimizer does
+ * not depend on f_e; selection by one evaluation per expert and a bisection
+ * on the multiplier to meet a read budget).  The distortion is taken in
+ * weight space from the stored codes (no calibration data), and the
+ * precisions are the prefixes of the bitplane codes (PagedMoE, abstract;
+ * MatMoE, abstract: floor-and-compensation).
+ *
+ * Distortion of one expert at prefix width b (1..8): the squared error of
+ * its b-bit prefix weights against its 8-bit weights, over gate/up ([2f][d])
+ * and down ([d][f]).  Per element, v_b - v_8 = 2^(7-b) - (u mod 2^(8-b)),
+ * an integer; per 128-group the squared differences sum to an exact integer
+ * I; the group contributes (s*s)*I (s*s exact in fp64, one rounding).  The
+ * sum order is fixed: groups ascending within a row from +0 (a row partial),
+ * then the row partials of gate/up rows 0..2f-1 followed by down rows
+ * 0..d-1, from +0.  Planes are the oracle's slab layout [8][R][K/8]. */
+static double bp_row_distortion(const uint8_t *planes, int64_t slab, int64_t r,
+                                int K, const uint16_t *scales, int b) {
+  int G = K / 128;
+  double acc = 0.0;
+  for (int g = 0; g < G; ++g) {
+    int64_t I = 0;
+    for (int i = 128 * g; i < 128 * (g + 1); ++i) {
+      int u = 0;
+      for (int p = 0; p < 8; ++p)
+        u |= ((planes[p * slab + r * (K / 8) + i / 8] >> (i % 8)) & 1) << (7 - p);
+      int64_t diff = (b == 8) ? 0 : (1 << (7 - b)) - (u & ((1 << (8 - b)) - 1));
+      I += diff * diff;
+    }
+    double s = oracle_f16_to_f64(scales[r * G + g]);
+    acc = acc + (s * s) * (double)I;
+  }
+  return acc;
+}
+
+int oracle_bp_distortion(const uint8_t *gu_planes, const uint16_t *gu_scales,
+                         const uint8_t *dn_planes, const uint16_t *dn_scales,
+                         int d, int f, double *dist) {
+  if (d <= 0 || f <= 0 || d % 128 || f % 128) return -1;
+  if (!gu_planes || !gu_scales || !dn_planes || !dn_scales || !dist) return -1;
+  int64_t gu_slab = (int64_t)2 * f * (d / 8), dn_slab = (int64_t)d * (f / 8);
+  for (int b = 1; b <= 8; ++b) {
+    double tot = 0.0;
+    for (int64_t r = 0; r < 2 * (int64_t)f; ++r)
+      tot = tot + bp_row_distortion(gu_planes, gu_slab, r, d, gu_scales, b);
+    for (int64_t r = 0; r < d; ++r)
+      tot = tot + bp_row_distortion(dn_planes, dn_slab, r, f, dn_scales, b);
+    dist[b - 1] = tot;
+  }
+  return 0;
+}
+
+/* Bytes read for one expert at prefix width b: b planes of gate/up and down
+ * (3df/8 bytes each) plus the fp16 scales (3df/64 bytes). */
+static int64_t bp_read_bytes(int d, int f, int b) {
+  return (int64_t)b * 3 * d * f / 8 + (int64_t)3 * d * f / 64;
+}
+
+/* The per-expert Lagrangian choice: b in [bmin, bmax] minimizing
+ * D_e(b) + lambda * R(b), evaluated as fma(lambda, R(b), D_e(b)); ties go to
+ * the larger b.  The routing count of the expert does not enter. */
+static int alloc_choose(const double *dist_e, int bmin, int bmax, int d, int f,
+                        double lambda) {
+  int best = bmax;
+  double key = fma(lambda, (double)bp_read_bytes(d, f, bmax), dist_e[bmax - 1]);
+  for (int b = bmax - 1; b >= bmin; --b) {
+    double kb = fma(lambda, (double)bp_read_bytes(d, f, b), dist_e[b - 1]);
+    if (kb < key) {
+      key = kb;
+      best = b;
+    }
+  }
+  return best;
+}
+
+/* Read rate at a multiplier: sum_e counts_e * R(b_e(lambda)), exact. */
+static int64_t alloc_read(const double *dist, const int32_t *counts, int E, int bmin,
+                          int bmax, int d, int f, double lambda) {
+  int64_t tot = 0;
+  for (int e = 0; e < E; ++e)
+    tot += (int64_t)counts[e] *
+           bp_read_bytes(d, f, alloc_choose(dist + 8 * e, bmin, bmax, d, f, lambda));
+  return tot;
+}
+
+/* Bisection on the multiplier.  lambda = 0 when the widest choice already
+ * meets the budget.  Otherwise hi starts at 1 and doubles (at most 2^1023)
+ * until its read meets the budget; then 64 halvings of [lo, hi] keep read(hi)
+ * within the budget and read(lo) above it; the result is b_e(hi).  When even
+ * the narrowest choice exceeds the budget every expert gets bmin (the
+ * returned read then exceeds the budget). */
+int oracle_allocate_bits(const double *dist, const int32_t *counts, int E, int d,
+                         int f, int bmin, int bmax, int64_t budget, uint8_t *bits,
+                         double *lambda_out, int64_t *read_out) {
+  if (E <= 0 || d <= 0 || f <= 0 || bmin < 1 || bmax > 8 || bmin > bmax) return -1;
+  if (!dist || !counts || !bits) return -1;
+  for (int e = 0; e < E; ++e)
+    if (counts[e] < 0) return -1;
+  double lambda = 0.0;
+  if (alloc_read(dist, counts, E, bmin, bmax, d, f, 0.0) > budget) {
+    double lo = 0.0, hi = 1.0;
+    int n = 0;
+    while (alloc_read(dist, counts, E, bmin, bmax, d, f, hi) > budget && n < 1023) {
+      lo = hi;
+      hi = hi * 2.0;
+      ++n;
+    }
+    if (alloc_read(dist, counts, E, bmin, bmax, d, f, hi) > budget) {
+      hi = INFINITY;
+    } else {
+      for (int it = 0; it < 64; ++it) {
+        double mid = 0.5 * (lo + hi);
+        if (alloc_read(dist, counts, E, bmin, bmax, d, f, mid) <= budget)
+          hi = mid;
+        else
+          lo = mid;
+      }
+    }
+    lambda = hi;
+  }
+  for (int e = 0; e < E; ++e)
+    bits[e] = (uint8_t)(isinf(lambda) ? bmin
+                                      : alloc_choose(dist + 8 * e, bmin, bmax, d, f, lambda));
+  if (lambda_out) *lambda_out = lambda;
+  if (read_out) {
+    int64_t tot = 0;
+    for (int e = 0; e < E; ++e) tot += (int64_t)counts[e] * bp_read_bytes(d, f, bits[e]);
+    *read_out = tot;
+  }
+  return 0;
+}
+

@@ -56,6 +56,16 @@ int oracle_dequant_w4(const uint8_t *codes, const uint16_t *scales_f16,
                       int64_t R, int K, double *w);
 int oracle_dequant_bp(const uint8_t *planes, const uint16_t *scales_f16,
                       int64_t R, int K, int bits, double *w);
+/* Weight-space distortion of one bitplane expert at prefix widths 1..8
+ * (dist[8]), fixed fp64 summation order (see oracle.c). */
+int oracle_bp_distortion(const uint8_t *gu_planes, const uint16_t *gu_scales,
+                         const uint8_t *dn_planes, const uint16_t *dn_scales,
+                         int d, int f, double *dist);
+/* Read-budget bit allocation: per-expert Lagrangian choice, bisection on the
+ * multiplier (see oracle.c).  dist [E][8], counts [E] routing counts. */
+int oracle_allocate_bits(const double *dist, const int32_t *counts, int E, int d,
+                         int f, int bmin, int bmax, int64_t budget, uint8_t *bits,
+                         double *lambda_out, int64_t *read_out);
 /* Bit-width of every pair [T*k] from a bits mode (see oracle.c). */
 int oracle_pair_bits(int T, int k, int E, const int32_t *topk_idx,
                      int bits_mode, const uint8_t *bits, uint8_t *pair_bits);

@@ -289,6 +289,111 @@ def test_bitplane_prefix_properties(rng):
         assert np.all(np.abs(w - deq) <= s * (2 ** (7 - b) + 0.5))
 
 
+# ---------------------------------------------------- read-budget allocator
+def _bp_expert(rng, d, f):
+    gu = rng.normal(0, 0.14, (2 * f, d)).astype(np.float32)
+    dn = rng.normal(0, 0.14, (d, f)).astype(np.float32)
+    return oracle.quantize_bp8(gu) + oracle.quantize_bp8(dn)
+
+
+def test_bp_distortion_is_prefix_error_energy(rng):
+    """D(b) equals the summed squared difference between the b-bit and the
+    8-bit dequantized weights (brute force through dequant_bp, another sum
+    order), and D(8) = 0."""
+    d, f = 256, 128
+    gp, gs, dp, ds = _bp_expert(rng, d, f)
+    dist = oracle.bp_distortion(gp, gs, dp, ds, d, f)
+    assert dist[7] == 0.0
+    for b in range(1, 8):
+        ref = 0.0
+        for planes, scales in ((gp, gs), (dp, ds)):
+            diff = oracle.dequant_bp(planes, scales, b) - oracle.dequant_bp(planes, scales, 8)
+            ref += float(np.sum(diff * diff))
+        assert abs(dist[b - 1] - ref) <= 1e-12 * ref, b
+    assert np.all(np.diff(dist) < 0)  # each extra plane halves the step
+
+
+def test_bp_distortion_closed_form_zero_codes():
+    """All codes u = 0: every element's prefix error is 2^(7-b), so
+    D(b) = sum over groups of s^2 * 128 * 4^(7-b), exactly."""
+    d, f = 128, 128
+    gp = np.zeros((8, 2 * f, d // 8), np.uint8)
+    dp = np.zeros((8, d, f // 8), np.uint8)
+    gs = np.full((2 * f, 1), oracle.f64_to_f16(0.5), np.uint16)
+    ds = np.full((d, 1), oracle.f64_to_f16(0.25), np.uint16)
+    dist = oracle.bp_distortion(gp, gs, dp, ds, d, f)
+    for b in range(1, 9):
+        e = 4.0 ** (7 - b) if b < 8 else 0.0
+        assert dist[b - 1] == 128 * e * (2 * f * 0.25 + d * 0.0625), b
+
+
+def _rand_dist(rng, E):
+    # decreasing in b, roughly halving per plane, with per-expert spread
+    base = rng.uniform(0.5, 2.0, (E, 1)) * 4.0 ** (8 - np.arange(1, 9))[None, :]
+    dist = base * rng.uniform(0.7, 1.3, (E, 8))
+    dist[:, 7] = 0.0
+    return np.sort(dist, axis=1)[:, ::-1].copy()
+
+
+def test_allocate_bits_is_budget_optimal_brute_force(rng):
+    """Everett: the Lagrangian choice is optimal for its own read level; no
+    assignment reading no more has a lower routing-weighted distortion
+    (exhaustive over 3 experts x widths 1..8)."""
+    import itertools
+    d, f, E = 128, 128, 3
+    R = np.array([oracle.bp_read_bytes(d, f, b) for b in range(1, 9)], np.int64)
+    for trial in range(6):
+        dist = _rand_dist(rng, E)
+        counts = rng.integers(0, 5, E).astype(np.int32)
+        counts[0] = max(counts[0], 1)
+        full = int(np.sum(counts * R[7]))
+        budget = int(rng.uniform(0.3, 1.0) * full)
+        bits, lam, read = oracle.allocate_bits(dist, counts, d, f, 1, 8, budget)
+        assert read == int(np.sum(counts * R[bits.astype(int) - 1]))
+        if read <= budget:
+            obj = float(np.sum(counts * dist[np.arange(E), bits.astype(int) - 1]))
+            for a in itertools.product(range(8), repeat=E):
+                a = np.array(a)
+                if np.sum(counts * R[a]) <= read:
+                    assert np.sum(counts * dist[np.arange(E), a]) >= obj * (1 - 1e-12), (trial, a)
+        else:
+            assert np.all(bits == 1)
+
+
+def test_allocate_bits_budget_extremes(rng):
+    d, f, E = 256, 256, 5
+    dist = _rand_dist(rng, E)
+    counts = np.array([3, 0, 1, 7, 2], np.int32)
+    R = [oracle.bp_read_bytes(d, f, b) for b in range(1, 9)]
+    hi = int(np.sum(counts)) * R[6]
+    bits, lam, read = oracle.allocate_bits(dist, counts, d, f, 2, 7, hi)
+    assert np.all(bits == 7) and lam == 0.0 and read == hi
+    lo = int(np.sum(counts)) * R[1]
+    bits, lam, read = oracle.allocate_bits(dist, counts, d, f, 2, 7, lo)
+    assert np.all(bits == 2) and read == lo
+    bits, lam, read = oracle.allocate_bits(dist, counts, d, f, 2, 7, lo - 1)
+    assert np.all(bits == 2) and math.isinf(lam) and read == lo
+
+
+def test_allocate_bits_frequency_cancels_and_monotone(rng):
+    """Scaling every routing count and the budget by one factor leaves every
+    decision unchanged (the frequency cancels from the per-expert choice),
+    and a larger budget never narrows any expert."""
+    d, f, E = 256, 128, 16
+    dist = _rand_dist(rng, E)
+    counts = rng.integers(1, 9, E).astype(np.int32)
+    R8 = oracle.bp_read_bytes(d, f, 8)
+    prev = None
+    for frac in np.linspace(0.3, 1.0, 8):
+        budget = int(frac * int(np.sum(counts)) * R8)
+        bits, _, _ = oracle.allocate_bits(dist, counts, d, f, 1, 8, budget)
+        bits3, _, _ = oracle.allocate_bits(dist, 3 * counts, d, f, 1, 8, 3 * budget)
+        assert np.array_equal(bits, bits3)
+        if prev is not None:
+            assert np.all(bits >= prev)
+        prev = bits
+
+
 def test_pair_bits_modes():
     idx = np.tile(np.arange(8, dtype=np.int32), (3, 1))
     pb = oracle.pair_bits(idx, 8, oracle.BITS_RANK_RULE)
