@@ -92,11 +92,14 @@ def expert_bytes(cfg, planes=None):
 class Workload:
     """mode: "fused" (one grouped FFN call per step), "seq-active" (one FFN
     call per activated expert, ids read back from the routing) or "seq-all"
-    (one FFN call per expert, no read-back)."""
+    (one FFN call per expert, no read-back).  budget_bits (bitplane layers):
+    per-expert widths from the read-budget allocator at that many bits per
+    weight on average over the routing counts of the workload's batches,
+    instead of the rank rule."""
 
-    def __init__(self, name, cid, T, steps, path=0, mode="fused"):
+    def __init__(self, name, cid, T, steps, path=0, mode="fused", budget_bits=None):
         self.name, self.cid, self.T, self.steps, self.path = name, cid, T, steps, path
-        self.mode = mode
+        self.mode, self.budget_bits = mode, budget_bits
 
 
 def run_workload(wl, warmup, hip, torch, np, synth, moe):
@@ -138,6 +141,45 @@ def run_workload(wl, warmup, hip, torch, np, synth, moe):
     bmode = moe.MOE_BITS_RANK_RULE if (bp and cfg.bits_rule == "rank") else moe.MOE_BITS_NONE
     layer = moe.MoeLayer(wr, bias, k, f, *copies[0], fmt, bmode, None)
     out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    alloc = None
+    if bp and wl.budget_bits is not None:
+        # offline distortion table, routing counts of the workload's batches,
+        # then the allocator kernel (each timed on its own, outside the steps)
+        ev = [hip.event() for _ in range(4)]
+        hip.record(ev[0], stream)
+        dist = moe.moe_bp_distortion(gu[0], gu[1], dn[0], dn[1], d, f)
+        hip.record(ev[1], stream)
+        counts = torch.zeros((E,), dtype=torch.int32, device=dev)
+        for x in xs:
+            layer.forward(x, out=out, path=wl.path)
+            counts += torch.diff(layer.offsets).to(torch.int32)
+        lo_b = expert_bytes(cfg, int(wl.budget_bits))
+        hi_b = expert_bytes(cfg, int(wl.budget_bits) + 1)
+        frac = wl.budget_bits - int(wl.budget_bits)
+        per = (1 - frac) * (lo_b[0] + lo_b[1]) + frac * (hi_b[0] + hi_b[1])
+        budget = int(int(counts.sum().item()) * per)
+        for _ in range(3):
+            bits_t, lam_t, read_t = moe.moe_allocate_bits(dist, counts, d, f, 2, 8, budget)
+        hip.record(ev[2], stream)
+        bits_t, lam_t, read_t = moe.moe_allocate_bits(dist, counts, d, f, 2, 8, budget)
+        hip.record(ev[3], stream)
+        torch.cuda.synchronize()
+        bits_np = bits_t.cpu().numpy()
+        dist_np = dist.cpu().numpy()
+        cnt_np = counts.cpu().numpy()
+        uni = int(wl.budget_bits)
+        alloc = {"budget_bits_per_weight": wl.budget_bits, "budget_bytes": budget,
+                 "read_bytes": int(read_t.cpu()[0]), "lambda": float(lam_t.cpu()[0]),
+                 "bits_histogram": {int(b): int((bits_np == b).sum()) for b in np.unique(bits_np)},
+                 "distortion_table_ms": round(hip.ms(ev[0], ev[1]), 3),
+                 "allocator_us": round(1e3 * hip.ms(ev[2], ev[3]), 2),
+                 "weighted_distortion_allocated": float(np.sum(cnt_np * dist_np[np.arange(E), bits_np - 1])),
+                 "weighted_distortion_uniform_%d" % uni: float(np.sum(cnt_np * dist_np[:, uni - 1])),
+                 "weighted_distortion_uniform_%d" % (uni + 1): float(np.sum(cnt_np * dist_np[:, uni]))}
+        for h in ev:
+            hip.destroy(h)
+        layer = moe.MoeLayer(wr, bias, k, f, *copies[0], fmt, moe.MOE_BITS_PER_EXPERT, bits_t)
+        bmode = moe.MOE_BITS_PER_EXPERT
 
     # algorithmic work of each x batch (routing is re-run here, untimed)
     gu_bytes, dn_bytes, active = [], [], []
@@ -151,7 +193,8 @@ def run_workload(wl, warmup, hip, torch, np, synth, moe):
             rank_bits = np.array([8, 4, 4, 4, 2, 2, 2, 2])[:k]
             gsum = dsum = 0
             for e in experts:
-                mb = int(rank_bits[np.nonzero(idx == e)[1]].max())
+                mb = (int(bits_np[e]) if alloc is not None
+                      else int(rank_bits[np.nonzero(idx == e)[1]].max()))
                 g1, d1 = expert_bytes(cfg, mb)
                 gsum, dsum = gsum + g1, dsum + d1
             gu_bytes.append(gsum)
@@ -286,7 +329,7 @@ def run_workload(wl, warmup, hip, torch, np, synth, moe):
     ms_step = total_ms / steps
     rec = {
         "workload": wl.name, "config": cfg.name, "T": T, "d": d, "E": E, "k": k,
-        "f": f, "format": "bitplane8-rank" if bp else "int4-g128",
+        "f": f, "format": ("bitplane8-allocated" if alloc else "bitplane8-rank") if bp else "int4-g128",
         "ms_per_step": round(ms_step, 5), "tokens_per_s": round(T / (ms_step / 1e3), 1),
         "ms_per_step_instrumented": round(instr_ms / steps, 5),
         "graph_replay_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
@@ -301,6 +344,8 @@ def run_workload(wl, warmup, hip, torch, np, synth, moe):
         "gateup_TFLOPs": round(flops_gu * steps / (sum(gu_ms) * 1e-3) / 1e12, 2),
         "down_TFLOPs": round(flops_dn * steps / (sum(dn_ms) * 1e-3) / 1e12, 2),
     }
+    if alloc:
+        rec["allocation"] = alloc
     rec["ffn_mfma_util_pct"] = round(100 * (flops_gu + flops_dn) * steps /
                                      ((sum(gu_ms) + sum(dn_ms)) * 1e-3) / 1e12 /
                                      MFMA_BF16_PEAK_TFS, 2)
@@ -405,6 +450,7 @@ def main():
         Workload("olmoe-sequential-all-w4 T=16", 1, 16, max(10, args.steps // 4),
                  mode="seq-all"),
         Workload("olmoe-bitplane-decode T=16", 3, 16, args.steps),
+        Workload("olmoe-bitplane-budget4.5 T=16", 3, 16, args.steps, budget_bits=4.5),
         Workload("e256-w4 T=1", 4, 1, args.steps),
         Workload("e256-w4 T=64", 4, 64, args.steps),
         Workload("olmoe-prefill-w4 T=4096", 2, 4096, max(5, args.steps // 10)),

@@ -262,6 +262,53 @@ int moe_layer_forward_wq(const void *x_bf16, const void *wr_bf16, const float *b
                          void *stream);
 
 /* ---------------------------------------------------------------------
+ * moe_bp_distortion -- weight-space distortion of bitplane experts, the
+ * offline half of read-budget bit allocation.
+ * [DuoRate] "Two-Rate Per-Expert Precision Allocation for Mixture-of-Experts
+ * Serving": a distortion table is computed once, offline, per expert and
+ * precision; [PagedMoE] abstract and [MatMoE] abstract: the precisions are
+ * prefixes of one stored code with floor-and-compensation.
+ *   dist[e][b-1], b = 1..8 (fp64, device, [E][8]) = sum over the expert's
+ *   gate/up and down weights of (s * (v_b(u) - v_8(u)))^2, where
+ *   v_b(u) - v_8(u) = 2^(7-b) - (u mod 2^(8-b)) and s is the group's fp16
+ *   scale.  Order: per 128-group the integer sum I of squared prefix errors;
+ *   row partial = groups in ascending order from +0 of fp64 (s*s)*I; total =
+ *   row partials of gate/up rows 0..2f-1 then down rows 0..d-1 from +0; every
+ *   product and sum rounded separately (reproducible bit for bit).
+ * Planes and scales: as written by moe_quantize_bitplane8 for [E][2f][d]
+ * (gate rows then up rows) and [E][d][f].  ws: moe_bp_distortion_ws_bytes
+ * (8-byte aligned).  Requires d % 128 == 0, f % 128 == 0, E <= 512.
+ * ------------------------------------------------------------------- */
+size_t moe_bp_distortion_ws_bytes(int E, int d, int f);
+int moe_bp_distortion(const uint8_t *gate_up_planes,
+                      const uint16_t *gate_up_scales_f16,
+                      const uint8_t *down_planes, const uint16_t *down_scales_f16,
+                      int E, int d, int f, double *dist, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------
+ * moe_allocate_bits -- per-expert prefix width under a read budget, the
+ * online half.
+ * [DuoRate]: read rate sum_e f_e R(b_e); in the Lagrangian relaxation the
+ * routing frequency cancels from each expert's decision, which is
+ *   b_e(lambda) = argmin_{b_min <= b <= b_max} fma(lambda, R(b), dist[e][b-1])
+ * (ties to the larger b), with R(b) = b*3df/8 + 3df/64 bytes read (planes
+ * plus scales); a bisection on lambda meets the budget:
+ *   read(lambda) = sum_e counts[e] * R(b_e(lambda)) (exact int64);
+ *   lambda = 0 if read(0) <= budget_bytes; otherwise hi = 1, doubled (at
+ *   most 1023 times) until read(hi) <= budget, then 64 halvings of [lo, hi]
+ *   (mid = 0.5*(lo+hi)); the result is b_e(hi).  If even b_min everywhere
+ *   exceeds the budget, lambda = +inf and every expert gets b_min.
+ * counts: int32 [E] routing counts of a profiling window (>= 0).  bits: u8
+ * [E] output, usable as MOE_BITS_PER_EXPERT.  lambda (fp64) and read_bytes
+ * (int64): optional device outputs (NULL to skip); a read above the budget
+ * signals an infeasible budget.  One 512-thread block; device pointers.
+ * ------------------------------------------------------------------- */
+int moe_allocate_bits(const double *dist, const int32_t *counts, int E, int d, int f,
+                      int b_min, int b_max, int64_t budget_bytes, uint8_t *bits,
+                      double *lambda, int64_t *read_bytes, void *stream);
+
+/* ---------------------------------------------------------------------
  * moe_set_ffn_events -- optional timing instrumentation (no page defines
  * it; it serves throughput measurement).  Arms, for the NEXT
  * moe_expert_ffn_wq call made by the calling thread only, four hipEvent_t

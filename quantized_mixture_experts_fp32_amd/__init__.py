@@ -30,7 +30,8 @@ EXPORTS = ("moe_status_str", "moe_last_error", "moe_route_ws_bytes", "moe_route"
            "moe_permute", "moe_route_permute_ws_bytes", "moe_route_permute",
            "moe_ffn_ws_bytes", "moe_expert_ffn_wq", "moe_combine",
            "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events",
-           "moe_layer_ws_bytes", "moe_layer_forward_wq")
+           "moe_layer_ws_bytes", "moe_layer_forward_wq", "moe_bp_distortion_ws_bytes",
+           "moe_bp_distortion", "moe_allocate_bits")
 
 
 class MoeError(RuntimeError):
@@ -75,8 +76,14 @@ def load_library():
     lib.moe_layer_forward_wq.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                          vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
                                          vp, i32, vp, sz, i32, vp]
+    lib.moe_bp_distortion_ws_bytes.argtypes = [i32, i32, i32]
+    lib.moe_bp_distortion_ws_bytes.restype = sz
+    lib.moe_bp_distortion.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
+    lib.moe_allocate_bits.argtypes = [vp, vp, i32, i32, i32, i32, i32, ctypes.c_int64, vp,
+                                      vp, vp, vp]
     for name in ("moe_route", "moe_permute", "moe_route_permute", "moe_expert_ffn_wq",
-                 "moe_combine", "moe_layer_forward_wq",
+                 "moe_combine", "moe_layer_forward_wq", "moe_bp_distortion",
+                 "moe_allocate_bits",
                  "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events"):
         getattr(lib, name).restype = i32
     _lib = lib
@@ -274,6 +281,42 @@ def moe_layer_forward(x, wr, bias, k, f, gate_up_codes, gate_up_scales, down_cod
         _ptr(y_pairs), _ptr(out), out_dtype, _ptr(ws), ws.numel() * ws.element_size(),
         path, _stream(stream)))
     return out
+
+
+def moe_bp_distortion(gate_up_planes, gate_up_scales, down_planes, down_scales, d, f,
+                      dist=None, ws=None, stream=None):
+    """Weight-space distortion [E][8] (fp64) of bitplane experts at prefix
+    widths 1..8 (the offline table of the read-budget allocator)."""
+    import torch
+    E = gate_up_planes.shape[0]
+    if dist is None:
+        dist = torch.empty((E, 8), dtype=torch.float64, device=gate_up_planes.device)
+    if ws is None:
+        ws = torch.empty((int(load_library().moe_bp_distortion_ws_bytes(E, d, f)),),
+                         dtype=torch.uint8, device=gate_up_planes.device)
+    _check("moe_bp_distortion", load_library().moe_bp_distortion(
+        _ptr(gate_up_planes), _ptr(gate_up_scales), _ptr(down_planes), _ptr(down_scales),
+        E, d, f, _ptr(dist), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return dist
+
+
+def moe_allocate_bits(dist, counts, d, f, b_min, b_max, budget_bytes, bits=None,
+                      lam=None, read=None, stream=None):
+    """Per-expert prefix widths [E] (u8) under a routing-weighted read
+    budget -> (bits, lambda [1] fp64, read [1] int64), all on the device."""
+    import torch
+    E = dist.shape[0]
+    dev = dist.device
+    if bits is None:
+        bits = torch.empty((E,), dtype=torch.uint8, device=dev)
+    if lam is None:
+        lam = torch.empty((1,), dtype=torch.float64, device=dev)
+    if read is None:
+        read = torch.empty((1,), dtype=torch.int64, device=dev)
+    _check("moe_allocate_bits", load_library().moe_allocate_bits(
+        _ptr(dist), _ptr(counts), E, d, f, b_min, b_max, int(budget_bytes), _ptr(bits),
+        _ptr(lam), _ptr(read), _stream(stream)))
+    return bits, lam, read
 
 
 def moe_combine(y_pairs, pair_pos, topk_w, out=None, out_dtype=MOE_OUT_BF16,

@@ -368,3 +368,51 @@ int moe_layer_forward_wq(const void* x_bf16, const void* wr_bf16, const float* b
                             s);
   return hip_status(e, "moe_layer_forward_wq");
 }
+
+size_t moe_bp_distortion_ws_bytes(int E, int d, int f) {
+  if (E <= 0 || d <= 0 || f <= 0) return 0;
+  return moe::bp_distortion_ws_bytes(E, d, f);
+}
+
+int moe_bp_distortion(const uint8_t* gate_up_planes, const uint16_t* gate_up_scales_f16,
+                      const uint8_t* down_planes, const uint16_t* down_scales_f16, int E,
+                      int d, int f, double* dist, void* ws, size_t ws_bytes, void* stream) {
+  if (E <= 0 || d <= 0 || f <= 0) return fail(MOE_ERR_INVALID_ARG, "moe_bp_distortion: bad size");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E=%d > %d", E, MOE_MAX_EXPERTS);
+  if (d % MOE_GROUP || f % MOE_GROUP)
+    return fail(MOE_ERR_UNSUPPORTED, "d=%d, f=%d must be multiples of 128", d, f);
+  if (!gate_up_planes || !gate_up_scales_f16 || !down_planes || !down_scales_f16 || !dist)
+    return fail(MOE_ERR_INVALID_ARG, "moe_bp_distortion: null pointer");
+  if (!aligned(gate_up_planes, 16) || !aligned(down_planes, 16) || !aligned(dist, 8) ||
+      !aligned(gate_up_scales_f16, 2) || !aligned(down_scales_f16, 2))
+    return fail(MOE_ERR_INVALID_ARG, "moe_bp_distortion: misaligned pointer");
+  const size_t need = moe::bp_distortion_ws_bytes(E, d, f);
+  if (!ws || ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_bp_distortion: workspace %zu < %zu bytes",
+                ws ? ws_bytes : (size_t)0, need);
+  if (!aligned(ws, 8)) return fail(MOE_ERR_INVALID_ARG, "moe_bp_distortion: misaligned workspace");
+  return hip_status(moe::launch_bp_distortion(gate_up_planes, gate_up_scales_f16, down_planes,
+                                              down_scales_f16, E, d, f, dist, ws,
+                                              (hipStream_t)stream),
+                    "moe_bp_distortion");
+}
+
+int moe_allocate_bits(const double* dist, const int32_t* counts, int E, int d, int f,
+                      int b_min, int b_max, int64_t budget_bytes, uint8_t* bits,
+                      double* lambda, int64_t* read_bytes, void* stream) {
+  if (E <= 0 || d <= 0 || f <= 0) return fail(MOE_ERR_INVALID_ARG, "moe_allocate_bits: bad size");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E=%d > %d", E, MOE_MAX_EXPERTS);
+  if (d % MOE_GROUP || f % MOE_GROUP)
+    return fail(MOE_ERR_UNSUPPORTED, "d=%d, f=%d must be multiples of 128", d, f);
+  if (b_min < 1 || b_max > 8 || b_min > b_max)
+    return fail(MOE_ERR_INVALID_ARG, "bit range [%d, %d] outside 1..8", b_min, b_max);
+  if (!dist || !counts || !bits)
+    return fail(MOE_ERR_INVALID_ARG, "moe_allocate_bits: null pointer");
+  if (!aligned(dist, 8) || !aligned(counts, 4) || (lambda && !aligned(lambda, 8)) ||
+      (read_bytes && !aligned(read_bytes, 8)))
+    return fail(MOE_ERR_INVALID_ARG, "moe_allocate_bits: misaligned pointer");
+  return hip_status(moe::launch_allocate_bits(dist, counts, E, d, f, b_min, b_max, budget_bytes,
+                                              bits, lambda, read_bytes, (hipStream_t)stream),
+                    "moe_allocate_bits");
+}
+

@@ -77,6 +77,15 @@ hipError_t launch_ffn_decode_em(const FfnArgs& a, const int32_t* topk_idx, int32
                                 int32_t* sorted_pair, int32_t* pair_pos, uint16_t* hE,
                                 hipStream_t s);
 
+// read-budget bit allocation (alloc.hip)
+size_t bp_distortion_ws_bytes(int E, int d, int f);
+hipError_t launch_bp_distortion(const uint8_t* gu_planes, const uint16_t* gu_scales,
+                                const uint8_t* dn_planes, const uint16_t* dn_scales, int E,
+                                int d, int f, double* dist, void* ws, hipStream_t s);
+hipError_t launch_allocate_bits(const double* dist, const int32_t* counts, int E, int d, int f,
+                                int bmin, int bmax, int64_t budget, uint8_t* bits,
+                                double* lambda, int64_t* read, hipStream_t s);
+
 hipError_t launch_combine(const float* y, const int32_t* pair_pos,
                           const float* topk_w, int T, int k, int d, void* out,
                           int out_f32, hipStream_t s);

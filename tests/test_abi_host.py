@@ -142,6 +142,24 @@ def test_combine_and_quantize_validation(lib):
     assert lib.moe_quantize_bitplane8(FAKE, 0, 16, 256, 128, NULL, NULL, NULL) == moe.MOE_OK
 
 
+def test_allocator_validation(lib):
+    ws = lib.moe_bp_distortion_ws_bytes(4, 256, 128)
+    assert ws == 8 * 8 * 4 * (2 * 128 + 256)
+    dz = lib.moe_bp_distortion
+    assert dz(FAKE, FAKE, FAKE, FAKE, 4, 200, 128, FAKE, FAKE, ws, NULL) == moe.MOE_ERR_UNSUPPORTED
+    assert dz(FAKE, FAKE, FAKE, FAKE, 0, 256, 128, FAKE, FAKE, ws, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert dz(FAKE, FAKE, NULL, FAKE, 4, 256, 128, FAKE, FAKE, ws, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert dz(FAKE, FAKE, FAKE, FAKE, 4, 256, 128, FAKE, FAKE, ws - 1, NULL) == moe.MOE_ERR_WORKSPACE
+    assert dz(ODD, FAKE, FAKE, FAKE, 4, 256, 128, FAKE, FAKE, ws, NULL) == moe.MOE_ERR_INVALID_ARG
+    al = lib.moe_allocate_bits
+    assert al(FAKE, FAKE, 4, 256, 128, 0, 8, 10, FAKE, NULL, NULL, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert al(FAKE, FAKE, 4, 256, 128, 5, 4, 10, FAKE, NULL, NULL, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert al(FAKE, FAKE, 4, 256, 128, 1, 9, 10, FAKE, NULL, NULL, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert al(FAKE, FAKE, 513, 256, 128, 1, 8, 10, FAKE, NULL, NULL, NULL) == moe.MOE_ERR_UNSUPPORTED
+    assert al(FAKE, NULL, 4, 256, 128, 1, 8, 10, FAKE, NULL, NULL, NULL) == moe.MOE_ERR_INVALID_ARG
+    assert al(FAKE, FAKE, 4, 256, 128, 1, 8, 10, FAKE, ODD, NULL, NULL) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(moe, "_lib", None)

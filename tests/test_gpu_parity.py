@@ -474,3 +474,76 @@ def test_layer_full_size_sampled(cid, T, path):
         assert_close(o32[t], o, f"out t={t}")
         assert np.array_equal(o16[t], bf16_rne_bits(o32[t]))
 
+
+# ------------------------------------------------------ read-budget allocator
+def _host_bp_expert(hl, e):
+    """The oracle's bitplane matrices (planes, scales) of expert e."""
+    (gp, gs), (dp, ds) = hl.expert(e)
+    return gp, gs, dp, ds
+
+
+@pytest.mark.parametrize("cid", [13, 3])
+def test_bp_distortion_bit_exact(cid):
+    """The distortion table equals the oracle's bit for bit (same fp64 order)."""
+    cfg = (custom_cfg(13, d=256, E=6, k=4, f=256, fmt="bp8", bias_sigma=0.5) if cid == 13
+           else synth.CONFIGS[3])
+    note(f"bp distortion {cfg.name}")
+    dl, hl = DevLayer(cfg, 1), HostLayer(cfg, 1)
+    dist = moe.moe_bp_distortion(dl.guc, dl.gus, dl.dnc, dl.dns, cfg.d, cfg.f)
+    torch.cuda.synchronize()
+    got = dist.cpu().numpy()
+    for e in ([0, cfg.E // 2, cfg.E - 1] if cfg.E > 8 else range(cfg.E)):
+        ref = oracle.bp_distortion(*_host_bp_expert(hl, e), cfg.d, cfg.f)
+        assert np.array_equal(got[e], ref), e
+
+
+def test_allocate_bits_bit_exact():
+    """Bits, multiplier and read equal the oracle's, over budgets from
+    infeasible to unconstrained, with zero counts and narrowed ranges."""
+    rng = np.random.default_rng(11)
+    d, f = 2048, 1024
+    for E in (1, 7, 64, 300):
+        base = rng.uniform(0.5, 2.0, (E, 1)) * 4.0 ** (8 - np.arange(1, 9))[None, :]
+        dist = np.sort(base * rng.uniform(0.7, 1.3, (E, 8)), axis=1)[:, ::-1].copy()
+        dist[:, 7] = 0.0
+        counts = rng.integers(0, 40, E).astype(np.int32)
+        dd, cd = torch.from_numpy(dist).to(DEV), torch.from_numpy(counts).to(DEV)
+        tot = int(counts.sum())
+        for bmin, bmax in ((1, 8), (2, 6)):
+            R = [oracle.bp_read_bytes(d, f, b) for b in (bmin, bmax)]
+            for budget in (tot * R[0] - 1, tot * R[0], (tot * (R[0] + R[1])) // 2,
+                           int(0.8 * tot * R[1]), tot * R[1]):
+                note(f"allocate E={E} b=[{bmin},{bmax}] budget={budget}")
+                bits, lam, read = moe.moe_allocate_bits(dd, cd, d, f, bmin, bmax, budget)
+                torch.cuda.synchronize()
+                rb, rl, rr = oracle.allocate_bits(dist, counts, d, f, bmin, bmax, budget)
+                assert np.array_equal(bits.cpu().numpy(), rb)
+                gl = float(lam.cpu()[0])
+                assert gl == rl or (np.isinf(gl) and np.isinf(rl))
+                assert int(read.cpu()[0]) == rr
+
+
+def test_layer_with_allocated_bits():
+    """Distortion and allocation on the GPU from the routing counts of a
+    profiling batch, then a decode step at those per-expert widths, against
+    the oracle's layer at the same widths."""
+    cfg = synth.CONFIGS[3]
+    note("layer with allocated bits cfg3")
+    prof = DevLayer(cfg, 64, step=7)
+    lay = prof.layer(moe.MOE_BITS_RANK_RULE)
+    lay.forward(prof.x)
+    counts = torch.diff(lay.offsets).to(torch.int32)
+    dist = moe.moe_bp_distortion(prof.guc, prof.gus, prof.dnc, prof.dns, cfg.d, cfg.f)
+    # halfway between 4 and 5 bits per weight on average: the synthetic experts
+    # have similar distortion curves, so they split between widths 4 and 5 by
+    # their marginal gain
+    tot = int(counts.sum().item())
+    budget = tot * (oracle.bp_read_bytes(cfg.d, cfg.f, 4) + oracle.bp_read_bytes(cfg.d, cfg.f, 5)) // 2
+    bits, lam, read = moe.moe_allocate_bits(dist, counts, cfg.d, cfg.f, 2, 8, budget)
+    torch.cuda.synchronize()
+    assert int(read.cpu()[0]) <= budget
+    b_np = bits.cpu().numpy()
+    assert set(b_np.tolist()) == {4, 5}
+    dl, hl = DevLayer(cfg, 16), HostLayer(cfg, 16)
+    check_layer(dl, hl, moe.MOE_PATH_AUTO, moe.MOE_BITS_PER_EXPERT, b_np)
+
