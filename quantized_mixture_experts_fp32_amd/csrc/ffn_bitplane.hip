@@ -100,15 +100,15 @@ __device__ __forceinline__ ColWeights col_weights(int b) {
 
 // One group of one 16-row matrix tile: sum over planes p < nb of the
 // weighted chains, plus c_b X, times the group scale, into acc.
+template <int NB>
 __device__ __forceinline__ void bp_group(const bf16x8 (&xf)[4], const f32x4 seed, const f32x4 dx,
-                                         const uint32_t (&pw)[8], int nb, const ColWeights& cw,
+                                         const uint32_t (&pw)[NB], const ColWeights& cw,
                                          const f32x4 sv, f32x4& acc) {
   f32x4 comb;
 #pragma unroll
   for (int i = 0; i < 4; ++i) comb[i] = cw.cb * dx[i];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    if (p >= nb) break;
+  for (int p = 0; p < NB; ++p) {
     bf16x8 a[4];
     bp_frags(pw[p], a);
     f32x4 d = seed;
@@ -116,6 +116,7 @@ __device__ __forceinline__ void bp_group(const bf16x8 (&xf)[4], const f32x4 seed
     for (int j = 0; j < 4; ++j) d = mfma16(a[j], xf[j], d);
 #pragma unroll
     for (int i = 0; i < 4; ++i) comb[i] = fmaf(cw.wp[p], d[i], comb[i]);
+    __builtin_amdgcn_sched_barrier(0);  // one plane's fragments live at a time
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = fmaf(sv[i], comb[i], acc[i]);
@@ -145,7 +146,81 @@ __device__ __forceinline__ int tile_bits(const int32_t* __restrict__ sp, int r0,
 }
 
 // ------------------------------------------------------------- gate / up
-template <int kDQ, int kWaves>
+// One work item reading the NB planes of its tile's largest bit-width (NB is
+// a compile-time constant, chosen per item by a block-uniform switch, so
+// every load of the group loop is unconditional).  The loop refills each
+// slot right after its use in a branch-free steady state: the compiler's
+// waits then count exactly the loads issued after the one needed, and kDQ
+// groups stay in flight across the loop edge.  Scales are fetched before
+// the plane words and written to LDS after them.  Rows past the tile stage a
+// copy of its first row (they feed only unstored columns).
+template <int NB, int kDQ, int kSC>
+__device__ __forceinline__ void bp_gu_item(const uint16_t* __restrict__ xsrc,
+                                           const uint8_t* __restrict__ pg,
+                                           const uint8_t* __restrict__ pu, int G,
+                                           const uint16_t* __restrict__ sc_src, size_t f,
+                                           float* sc_lds, uint16_t* xs, const ColWeights& cw,
+                                           f32x4& tg, f32x4& tu) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int st_tok = tid >> 4, st_pc = tid & 15;
+  uint32_t wg[kDQ][NB], wu[kDQ][NB];
+  u32x4 xv[kDQ];
+  auto load = [&](int g, int i) {
+    xv[i] = *(const u32x4*)(xsrc + 128 * g);
+#pragma unroll
+    for (int p = 0; p < NB; ++p) {
+      wg[i][p] = *(const uint32_t*)(pg + (size_t)g * kBlockBytes + 256 * p);
+      wu[i][p] = *(const uint32_t*)(pu + (size_t)g * kBlockBytes + 256 * p);
+    }
+  };
+  ScaleStage<2, kSC ? kSC : 1> sst;
+  if (kSC) sst.fetch(sc_src, f, G);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kDQ; ++i) load(i < G ? i : G - 1, i);
+  __builtin_amdgcn_sched_barrier(0);
+  if (kSC)
+    sst.store(G, sc_lds);
+  else
+    stage_scales_rows64<2>(sc_src, f, G, sc_lds);
+  auto step = [&](int gi, int i) {
+    // slot gi & 1 was last read in step gi - 2, before the barrier of step gi - 1
+    uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
+    bp_stage8(slot + st_tok * kXRow, 8 * st_pc, xv[i]);
+    __syncthreads();
+    bf16x8 xf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xf[j] = *(const bf16x8*)(slot + col * kXRow + 8 * (kq * 4 + j));
+    const f32x4 sg = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
+    const f32x4 su = *(const f32x4*)(sc_lds + (G + gi) * 64 + 16 * wave + 4 * kq);
+    f32x4 seed, dx;
+    bp_seeds(xf, seed, dx);
+    bp_group<NB>(xf, seed, dx, wg[i], cw, sg, tg);
+    bp_group<NB>(xf, seed, dx, wu[i], cw, su, tu);
+  };
+  int g = 0;
+  for (; g + 2 * kDQ <= G; g += kDQ) {
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i) {
+      step(g + i, i);
+      __builtin_amdgcn_sched_barrier(0);  // the slot's words are consumed first
+      load(g + i + kDQ, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kDQ; ++i) {
+    if (g + i >= G) break;
+    step(g + i, i);
+    if (g + i + kDQ < G) load(g + i + kDQ, i);
+  }
+#pragma unroll
+  for (int i = 0; i < kDQ; ++i)
+    if (g + kDQ + i < G) step(g + kDQ + i, i);
+}
+
+template <int kDQ, int kWaves, int kSC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
 void gateup_bp_decode(const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
                       const int32_t* __restrict__ sorted_pair, int E, int k, int P, int d,
@@ -173,52 +248,26 @@ void gateup_bp_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
     int maxb;
     const int b = tile_bits(spp, tl.r0, tl.cnt, col, tl.e, k, bits_mode, bits, maxb);
     const ColWeights cw = col_weights(b);
-    const bool st_ok = st_tok < tl.cnt;
-    const int sj = tl.r0 + (st_ok ? st_tok : 0);
-    const uint16_t* xsrc = x + (size_t)(spp[sj] / k) * d + 8 * st_pc;
+    const int sj = tl.r0 + (st_tok < tl.cnt ? st_tok : 0);
+    const int sp = spp[sj];
+    asm volatile("" ::"v"(sp) : "memory");  // routing value taken before any plane load
+    const uint16_t* xsrc = x + (size_t)(sp / k) * d + 8 * st_pc;
     // plane words: tiles of 16 rows; row n0 + col of gate, f + n0 + col of up
     const size_t rg = (size_t)tl.e * 2 * f + n0, ru = rg + f;
     const uint8_t* pg = planes + (rg >> 4) * (size_t)G * kBlockBytes + 16 * col + 4 * kq;
     const uint8_t* pu = planes + (ru >> 4) * (size_t)G * kBlockBytes + 16 * col + 4 * kq;
-
-    uint32_t wg[kDQ][8], wu[kDQ][8];
-    u32x4 xv[kDQ];
-    auto load = [&](int g, int i) {
-      if (st_ok) xv[i] = *(const u32x4*)(xsrc + 128 * g);
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        if (p >= maxb) break;
-        wg[i][p] = *(const uint32_t*)(pg + (size_t)g * kBlockBytes + 256 * p);
-        wu[i][p] = *(const uint32_t*)(pu + (size_t)g * kBlockBytes + 256 * p);
-      }
-    };
-#pragma unroll
-    for (int i = 0; i < kDQ; ++i)
-      if (i < G) load(i, i);
-    stage_scales_rows64<2>(scales + ((size_t)tl.e * 2 * f + nb) * G, (size_t)f, G, sc_lds);
-
+    const uint16_t* sc_src = scales + ((size_t)tl.e * 2 * f + nb) * G;
     f32x4 tg = {0, 0, 0, 0}, tu = {0, 0, 0, 0};
-    const int rd_tok = col < tl.cnt ? col : 0;
-    for (int g = 0; g < G; g += kDQ) {
-#pragma unroll
-      for (int i = 0; i < kDQ; ++i) {
-        const int gi = g + i;
-        if (gi >= G) break;
-        uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
-        if (st_ok) bp_stage8(slot + st_tok * kXRow, 8 * st_pc, xv[i]);
-        __syncthreads();
-        bf16x8 xf[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          xf[j] = *(const bf16x8*)(slot + rd_tok * kXRow + 8 * (kq * 4 + j));
-        const f32x4 sg = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
-        const f32x4 su = *(const f32x4*)(sc_lds + (G + gi) * 64 + 16 * wave + 4 * kq);
-        f32x4 seed, dx;
-        bp_seeds(xf, seed, dx);
-        bp_group(xf, seed, dx, wg[i], maxb, cw, sg, tg);
-        bp_group(xf, seed, dx, wu[i], maxb, cw, su, tu);
-        if (gi + kDQ < G) load(gi + kDQ, i);
-      }
+    switch (maxb) {  // block-uniform
+#define BP_GU_CASE(N) \
+  case N:             \
+    bp_gu_item<N, kDQ, kSC>(xsrc, pg, pu, G, sc_src, (size_t)f, sc_lds, xs, cw, tg, tu); \
+    break;
+      BP_GU_CASE(1) BP_GU_CASE(2) BP_GU_CASE(3) BP_GU_CASE(4)
+      BP_GU_CASE(5) BP_GU_CASE(6) BP_GU_CASE(7)
+      default:
+        bp_gu_item<8, kDQ, kSC>(xsrc, pg, pu, G, sc_src, (size_t)f, sc_lds, xs, cw, tg, tu);
+#undef BP_GU_CASE
     }
     if (col < tl.cnt) {
       uint32_t hb[4];
@@ -234,7 +283,66 @@ void gateup_bp_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
 }
 
 // ------------------------------------------------------------------ down
-template <int kDQ, int kWaves>
+template <int NB, int kDQ, int kSC>
+__device__ __forceinline__ void bp_dn_item(const uint16_t* __restrict__ hsrc,
+                                           const uint8_t* __restrict__ pd, int G,
+                                           const uint16_t* __restrict__ sc_src, float* sc_lds,
+                                           uint16_t* xs, const ColWeights& cw, f32x4& acc) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int st_tok = tid >> 4, st_pc = tid & 15;
+  uint32_t wd[kDQ][NB];
+  u32x4 hv[kDQ];
+  auto load = [&](int g, int i) {
+    hv[i] = *(const u32x4*)(hsrc + 128 * g);
+#pragma unroll
+    for (int p = 0; p < NB; ++p)
+      wd[i][p] = *(const uint32_t*)(pd + (size_t)g * kBlockBytes + 256 * p);
+  };
+  ScaleStage<1, kSC ? kSC : 1> sst;
+  if (kSC) sst.fetch(sc_src, 0, G);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kDQ; ++i) load(i < G ? i : G - 1, i);
+  __builtin_amdgcn_sched_barrier(0);
+  if (kSC)
+    sst.store(G, sc_lds);
+  else
+    stage_scales_rows64<1>(sc_src, 0, G, sc_lds);
+  auto step = [&](int gi, int i) {
+    uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
+    bp_stage8(slot + st_tok * kXRow, 8 * st_pc, hv[i]);
+    __syncthreads();
+    bf16x8 xf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xf[j] = *(const bf16x8*)(slot + col * kXRow + 8 * (kq * 4 + j));
+    const f32x4 sv = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
+    f32x4 seed, dx;
+    bp_seeds(xf, seed, dx);
+    bp_group<NB>(xf, seed, dx, wd[i], cw, sv, acc);
+  };
+  int g = 0;
+  for (; g + 2 * kDQ <= G; g += kDQ) {
+#pragma unroll
+    for (int i = 0; i < kDQ; ++i) {
+      step(g + i, i);
+      __builtin_amdgcn_sched_barrier(0);  // the slot's words are consumed first
+      load(g + i + kDQ, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kDQ; ++i) {
+    if (g + i >= G) break;
+    step(g + i, i);
+    if (g + i + kDQ < G) load(g + i + kDQ, i);
+  }
+#pragma unroll
+  for (int i = 0; i < kDQ; ++i)
+    if (g + kDQ + i < G) step(g + kDQ + i, i);
+}
+
+template <int kDQ, int kWaves, int kSC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
 void down_bp_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ offsets,
                     const int32_t* __restrict__ sorted_pair, int E, int k, int d, int f,
@@ -259,57 +367,31 @@ void down_bp_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
     int maxb;
     const int b = tile_bits(sorted_pair, tl.r0, tl.cnt, col, tl.e, k, bits_mode, bits, maxb);
     const ColWeights cw = col_weights(b);
-    const bool st_ok = st_tok < tl.cnt;
-    const uint16_t* hsrc = h + (size_t)(tl.r0 + (st_ok ? st_tok : 0)) * f + 8 * st_pc;
+    const uint16_t* hsrc = h + (size_t)(tl.r0 + (st_tok < tl.cnt ? st_tok : 0)) * f + 8 * st_pc;
     const size_t rd0 = (size_t)tl.e * d + m0;
     const uint8_t* pd = planes + (rd0 >> 4) * (size_t)G * kBlockBytes + 16 * col + 4 * kq;
-
-    uint32_t wd[kDQ][8];
-    u32x4 hv[kDQ];
-    auto load = [&](int g, int i) {
-      if (st_ok) hv[i] = *(const u32x4*)(hsrc + 128 * g);
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        if (p >= maxb) break;
-        wd[i][p] = *(const uint32_t*)(pd + (size_t)g * kBlockBytes + 256 * p);
-      }
-    };
-#pragma unroll
-    for (int i = 0; i < kDQ; ++i)
-      if (i < G) load(i, i);
-    stage_scales_rows64<1>(scales + ((size_t)tl.e * d + mb) * G, 0, G, sc_lds);
-
+    const uint16_t* sc_src = scales + ((size_t)tl.e * d + mb) * G;
     f32x4 acc = {0, 0, 0, 0};
-    const int rd_tok = col < tl.cnt ? col : 0;
-    for (int g = 0; g < G; g += kDQ) {
-#pragma unroll
-      for (int i = 0; i < kDQ; ++i) {
-        const int gi = g + i;
-        if (gi >= G) break;
-        uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
-        if (st_ok) bp_stage8(slot + st_tok * kXRow, 8 * st_pc, hv[i]);
-        __syncthreads();
-        bf16x8 xf[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          xf[j] = *(const bf16x8*)(slot + rd_tok * kXRow + 8 * (kq * 4 + j));
-        const f32x4 sv = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
-        f32x4 seed, dx;
-        bp_seeds(xf, seed, dx);
-        bp_group(xf, seed, dx, wd[i], maxb, cw, sv, acc);
-        if (gi + kDQ < G) load(gi + kDQ, i);
-      }
+    switch (maxb) {  // block-uniform
+#define BP_DN_CASE(N) \
+  case N:             \
+    bp_dn_item<N, kDQ, kSC>(hsrc, pd, G, sc_src, sc_lds, xs, cw, acc); \
+    break;
+      BP_DN_CASE(1) BP_DN_CASE(2) BP_DN_CASE(3) BP_DN_CASE(4)
+      BP_DN_CASE(5) BP_DN_CASE(6) BP_DN_CASE(7)
+      default:
+        bp_dn_item<8, kDQ, kSC>(hsrc, pd, G, sc_src, sc_lds, xs, cw, acc);
+#undef BP_DN_CASE
     }
     if (col < tl.cnt) *(f32x4*)(y + (size_t)(tl.r0 + col) * d + m0 + 4 * kq) = acc;
     __syncthreads();
   }
 }
 
-#ifndef BP_DQ
-#define BP_DQ 2
-#define BP_WAVES 3
-#endif
-constexpr int kBpDQ = BP_DQ, kBpWaves = BP_WAVES;
+// Plane-word groups in flight and occupancy (measured on MI355X): gate/up
+// holds two matrices' words per group and fits one group ahead at three
+// waves per SIMD; down keeps two groups ahead at two waves.
+constexpr int kBpGuDQ = 1, kBpGuWaves = 3, kBpDnDQ = 2, kBpDnWaves = 2;
 
 }  // namespace
 
@@ -330,20 +412,28 @@ hipError_t launch_ffn_decode_bp(const FfnArgs& a, uint16_t* h, hipStream_t s) {
     const int grid = (int)(work < cap ? work : cap);
     const size_t lds = off_b + sizeof(int32_t) * ((std::min<long long>(P, kPairsInLds) + 3) & ~3) +
                        sizeof(float) * 2 * G * 64 + xs_b;
-    launch_k(gateup_bp_decode<kBpDQ, kBpWaves>, dim3(grid), dim3(256), lds, s, a.ev[0], a.ev[1],
-             a.x,
-                       a.offsets, a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes,
-                       a.gu_scales, a.bits_mode, a.bits, h);
+    const int sc = scale_chunks(2, G, a.gu_scales);
+    auto kern = sc == 1   ? gateup_bp_decode<kBpGuDQ, kBpGuWaves, 1>
+                : sc == 2 ? gateup_bp_decode<kBpGuDQ, kBpGuWaves, 2>
+                : sc == 4 ? gateup_bp_decode<kBpGuDQ, kBpGuWaves, 4>
+                          : gateup_bp_decode<kBpGuDQ, kBpGuWaves, 0>;
+    launch_k(kern, dim3(grid), dim3(256), lds, s, a.ev[0], a.ev[1], a.x, a.offsets,
+             a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes, a.gu_scales, a.bits_mode,
+             a.bits, h);
   }
   {
     const int G = a.f / 128;
     const long long work = mt * (a.d / 64);
     const int grid = (int)(work < cap ? work : cap);
     const size_t lds = off_b + sizeof(float) * G * 64 + xs_b;
-    launch_k(down_bp_decode<kBpDQ, kBpWaves>, dim3(grid), dim3(256), lds, s, a.ev[2], a.ev[3],
-             h,
-                       a.offsets, a.sorted_pair, a.E, a.k, a.d, a.f, a.dn_codes, a.dn_scales,
-                       a.bits_mode, a.bits, a.y);
+    const int sc = scale_chunks(1, G, a.dn_scales);
+    auto kern = sc == 1   ? down_bp_decode<kBpDnDQ, kBpDnWaves, 1>
+                : sc == 2 ? down_bp_decode<kBpDnDQ, kBpDnWaves, 2>
+                : sc == 4 ? down_bp_decode<kBpDnDQ, kBpDnWaves, 4>
+                          : down_bp_decode<kBpDnDQ, kBpDnWaves, 0>;
+    launch_k(kern, dim3(grid), dim3(256), lds, s, a.ev[2], a.ev[3], h, a.offsets,
+             a.sorted_pair, a.E, a.k, a.d, a.f, a.dn_codes, a.dn_scales, a.bits_mode, a.bits,
+             a.y);
   }
   return hipGetLastError();
 }
