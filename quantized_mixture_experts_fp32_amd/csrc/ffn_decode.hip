@@ -629,26 +629,32 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-template <int kDQ, int kWaves, int kSC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
+// kW waves per block (4 or 8), one 16-feature row tile each: blocks of 16 kW
+// features; every group of four waves stages the whole activation tile
+// (waves 4-7 write the same values to the same places as waves 0-3).
+template <int kDQ, int kWaves, int kSC, int kW>
+__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
 void gateup_w4_em(const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
                   int T, int k, int E, int d, int f, const uint8_t* __restrict__ codes,
                   const uint16_t* __restrict__ scales, uint16_t* __restrict__ hE,
                   int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
                   int32_t* __restrict__ pair_pos) {
+  constexpr int kRows = 16 * kW, kMat = kW / 4;  // 64-row scale chunks per matrix
   extern __shared__ int32_t lds_i[];
-  __shared__ int32_t wcnt[4][2];
+  __shared__ int32_t wcnt[kW][2];
   __shared__ int32_t colpair[kEmMaxT];
-  const int G = d >> 7, RG = f / 64, P = T * k;
-  float* sc_lds = (float*)lds_i;                    // [2][G][64]
-  uint16_t* xs = (uint16_t*)(sc_lds + 2 * G * 64);  // [2][16][kXRow]
+  const int G = d >> 7, RG = f / kRows, P = T * k;
+  float* sc_lds = (float*)lds_i;                          // [gate, up][kMat][G][64]
+  uint16_t* xs = (uint16_t*)(sc_lds + 2 * kMat * G * 64);  // [2][16][kXRow]
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, kq = lane >> 4;
-  const int st_tok = tid >> 4, st_pc = tid & 15;  // staged token row and 16-byte piece
+  const int st_tok = (tid >> 4) & 15, st_pc = tid & 15;  // staged token row, 16-byte piece
   const bf16x8 negoff = bf16_splat(kBf16NegOff);
   const int e = blockIdx.x / RG, rg = blockIdx.x % RG;
-  const int nb = rg * 64, n0 = nb + 16 * wave;
+  const int nb = rg * kRows, n0 = nb + 16 * wave;
+  const int sc_g = ((wave >> 2) * G) * 64 + 16 * (wave & 3) + 4 * kq;  // gate scale slot
+  const int sc_u = sc_g + kMat * G * 64;                              // up scale slot
   const size_t erow = (size_t)e * 2 * f;
 
   // t = 0: every pair's expert, then scales, codes and activations
@@ -662,16 +668,26 @@ void gateup_w4_em(const uint16_t* __restrict__ x, const int32_t* __restrict__ to
     qg[i] = *(const u32x4*)(cg + kTileGroupBytes * g);
     qu[i] = *(const u32x4*)(cu + kTileGroupBytes * g);
   };
-  ScaleStage<2, kSC ? kSC : 1> sst;
-  if (kSC) sst.fetch(scales + (erow + nb) * G, (size_t)f, G);
+  // scales: 4 waves take gate and up as two 64-row matrices; 8 waves take
+  // gate then up as pairs of 64-row chunks
+  const uint16_t* sc_src = scales + (erow + nb) * G;
+  const size_t sc_stride = kW == 4 ? (size_t)f : 64;
+  ScaleStage<2, kSC ? kSC : 1> sst, sst2;
+  if (kSC) {
+    sst.fetch(sc_src, sc_stride, G);
+    if (kW == 8) sst2.fetch(sc_src + (size_t)f * G, 64, G);
+  }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < kDQ; ++i) load(i < G ? i : G - 1, i);
   __builtin_amdgcn_sched_barrier(0);
-  if (kSC)
+  if (kSC) {
     sst.store(G, sc_lds);
-  else
-    stage_scales_rows64<2>(scales + (erow + nb) * G, (size_t)f, G, sc_lds);
+    if (kW == 8) sst2.store(G, sc_lds + 2 * G * 64);
+  } else if (tid < 256) {
+    stage_scales_rows64<2>(sc_src, sc_stride, G, sc_lds);
+    if (kW == 8) stage_scales_rows64<2>(sc_src + (size_t)f * G, 64, G, sc_lds + 2 * G * 64);
+  }
 
   // the grouping of the pairs, as far as expert e is concerned
   const bool mine = pe == e;
@@ -684,7 +700,7 @@ void gateup_w4_em(const uint16_t* __restrict__ x, const int32_t* __restrict__ to
   __syncthreads();
   int cnt = 0, r0 = 0, rank = __popcll(bm & lanemask_lt());
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < kW; ++w) {
     cnt += wcnt[w][0];
     r0 += wcnt[w][1];
     rank += w < wave ? wcnt[w][0] : 0;
@@ -714,8 +730,8 @@ void gateup_w4_em(const uint16_t* __restrict__ x, const int32_t* __restrict__ to
     bf16x8 xp[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) xp[j] = *(const bf16x8*)(slot + xrow * kXRow + 32 * kq + 8 * j);
-    const f32x4 sg = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
-    const f32x4 su = *(const f32x4*)(sc_lds + (G + gi) * 64 + 16 * wave + 4 * kq);
+    const f32x4 sg = *(const f32x4*)(sc_lds + sc_g + gi * 64);
+    const f32x4 su = *(const f32x4*)(sc_lds + sc_u + gi * 64);
     f32x4 seed = {0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < 4; ++j) seed = mfma16(negoff, xp[j], seed);
@@ -870,14 +886,15 @@ hipError_t launch_ffn_decode_em(const FfnArgs& a, const int32_t* topk_idx, int32
                                 int32_t* sorted_pair, int32_t* pair_pos, uint16_t* hE,
                                 hipStream_t s) {
   {
+    // 8-wave blocks of 128 features (f % 128 == 0 always holds here)
     const int G = a.d / 128;
-    const size_t lds = sizeof(float) * 2 * G * 64 + sizeof(uint16_t) * 2 * 16 * kXRow;
+    const size_t lds = sizeof(float) * 4 * G * 64 + sizeof(uint16_t) * 2 * 16 * kXRow;
     const int sc = scale_chunks(2, G, a.gu_scales);
-    auto kern = sc == 1   ? gateup_w4_em<kGuDQ, kGuWaves, 1>
-                : sc == 2 ? gateup_w4_em<kGuDQ, kGuWaves, 2>
-                : sc == 4 ? gateup_w4_em<kGuDQ, kGuWaves, 4>
-                          : gateup_w4_em<kGuDQ, kGuWaves, 0>;
-    launch_k(kern, dim3(a.E * (a.f / 64)), dim3(256), lds, s, a.ev[0], a.ev[1], a.x, topk_idx,
+    auto kern = sc == 1   ? gateup_w4_em<kGuDQ, kGuWaves, 1, 8>
+                : sc == 2 ? gateup_w4_em<kGuDQ, kGuWaves, 2, 8>
+                : sc == 4 ? gateup_w4_em<kGuDQ, kGuWaves, 4, 8>
+                          : gateup_w4_em<kGuDQ, kGuWaves, 0, 8>;
+    launch_k(kern, dim3(a.E * (a.f / 128)), dim3(512), lds, s, a.ev[0], a.ev[1], a.x, topk_idx,
              a.T, a.k, a.E, a.d, a.f, a.gu_codes, a.gu_scales, hE, offsets, sorted_pair,
              pair_pos);
   }
