@@ -182,7 +182,7 @@ def run_workload(wl, warmup, hip, torch, np, synth, moe):
         bmode = moe.MOE_BITS_PER_EXPERT
 
     # algorithmic work of each x batch (routing is re-run here, untimed)
-    gu_bytes, dn_bytes, active = [], [], []
+    gu_bytes, dn_bytes, active, indep = [], [], [], []
     for x in xs:
         layer.forward(x, out=out, path=wl.path)
         torch.cuda.synchronize()
@@ -191,14 +191,18 @@ def run_workload(wl, warmup, hip, torch, np, synth, moe):
         active.append(len(experts))
         if bp:
             rank_bits = np.array([8, 4, 4, 4, 2, 2, 2, 2])[:k]
-            gsum = dsum = 0
+            gsum = dsum = isum = 0
             for e in experts:
-                mb = (int(bits_np[e]) if alloc is not None
-                      else int(rank_bits[np.nonzero(idx == e)[1]].max()))
-                g1, d1 = expert_bytes(cfg, mb)
+                widths = ({int(bits_np[e])} if alloc is not None
+                          else set(rank_bits[np.nonzero(idx == e)[1]].tolist()))
+                g1, d1 = expert_bytes(cfg, max(widths))
                 gsum, dsum = gsum + g1, dsum + d1
+                # a design keeping each precision as its own object reads one
+                # object per distinct (expert, width) (PagedMoE, abstract)
+                isum += sum(sum(expert_bytes(cfg, b)) for b in widths)
             gu_bytes.append(gsum)
             dn_bytes.append(dsum)
+            indep.append(isum)
         else:
             g1, d1 = expert_bytes(cfg)
             gu_bytes.append(len(experts) * g1)
@@ -346,6 +350,9 @@ def run_workload(wl, warmup, hip, torch, np, synth, moe):
     }
     if alloc:
         rec["allocation"] = alloc
+    if indep:
+        rec["prefix_bytes_avg"] = int(np.mean([g + dd for g, dd in zip(gu_bytes, dn_bytes)]))
+        rec["independent_objects_bytes_avg"] = int(np.mean(indep))
     rec["ffn_mfma_util_pct"] = round(100 * (flops_gu + flops_dn) * steps /
                                      ((sum(gu_ms) + sum(dn_ms)) * 1e-3) / 1e12 /
                                      MFMA_BF16_PEAK_TFS, 2)
@@ -451,6 +458,7 @@ def main():
                  mode="seq-all"),
         Workload("olmoe-bitplane-decode T=16", 3, 16, args.steps),
         Workload("olmoe-bitplane-budget4.5 T=16", 3, 16, args.steps, budget_bits=4.5),
+        Workload("olmoe-bitplane-prefill T=4096", 3, 4096, max(5, args.steps // 10), path=2),
         Workload("e256-w4 T=1", 4, 1, args.steps),
         Workload("e256-w4 T=64", 4, 64, args.steps),
         Workload("olmoe-prefill-w4 T=4096", 2, 4096, max(5, args.steps // 10)),

@@ -377,7 +377,10 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   }
   // bitplane prefixes (int4 always resolves to one of the two paths above)
   if (a.path == 1 && ffn_decode_bp_applies(P, a.E, a.f)) return launch_ffn_decode_bp(a, h, s);
-  if (a.path == 2) return run_ffn<4>(a, s);
+  if (a.path == 2) {
+    void* pws = (char*)h + align256((size_t)P * a.f * 2);
+    return launch_ffn_prefill_bp(a, h, pws, s);
+  }
   return run_ffn<2>(a, s);
 }
 

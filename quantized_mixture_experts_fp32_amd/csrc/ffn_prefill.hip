@@ -7,16 +7,20 @@
 // in registers), so that each lane of a 32x32 accumulator tile owns one
 // output feature and needs one fp16 scale per 128-group.
 //
-// Arithmetic.  As in the decode path, a code word becomes eight bf16
-// values 136 + q (in element order) with shifts and v_bitop3, and each
-// group's partial sum is corrected by -136 * sum_k x_k: that term enters as
-// one extra MFMA per group whose A column holds the exact three-part bf16
-// split (hi + mid + lo) of the fp32 group sum of the token's activations,
-// and whose B column holds -136.  The running fp32 total is kept in units
-// of the current group's fp16 scale: before a group is accumulated, the
-// total is multiplied by s_prev / s_g, and after the last group by the
-// final scale, so every group's sum is weighted by its own scale without a
-// separate partial accumulator.  A pre-pass kernel computes the group sums
+// Arithmetic.  A code word becomes eight bf16 values 192 + 8 q (in element
+// order) with shifts and v_bitop3: the code, sign bit flipped, lands in the
+// top four mantissa bits of 128.0, so that the MFMA sums x * (192 + 8 q)
+// and each group's partial sum is corrected by -192 * sum_k x_k.  (Codes in
+// the top mantissa bits keep the exact part of every MFMA partial sum small
+// next to its signal: the offset is 24 code steps, not the 136 of codes in
+// the low bits, so fp32 rounding of the partial sums costs about 6x less.)
+// The correction enters as one extra MFMA per group whose A column holds
+// the exact three-part bf16 split (hi + mid + lo) of the fp32 group sum of
+// the token's activations, and whose B column holds -192.  The running fp32
+// total is kept in units of the current group's fp16 scale / 8: before a
+// group is accumulated, the total is multiplied by s_prev / s_g, and after
+// the last group by the final scale, so every group's sum is weighted by its
+// own scale without a separate partial accumulator.  A pre-pass kernel computes the group sums
 // (and their splits) of x per token and of h per grouped pair.
 //
 // Tiling and pipeline: see the GEMM core below.
@@ -37,17 +41,18 @@ struct PTile {
   int e, r0, cnt, maxb;
 };
 
-// One code word (elements 8j..8j+7, even ones in nibbles 0-3, odd ones in
-// nibbles 4-7) -> bf16 (136 + q) of the 8 elements in order; the same
-// conversion as the decode path (q + 8 lands in the low mantissa bits of
-// 128.0).
-__device__ __forceinline__ bf16x8 w4_magic_pf(uint32_t w) {
-  const uint32_t B = 0x000F000Fu, D = 0x43084308u;
+// One code word (elements 8j..8j+7, element 2i in nibble i, 2i+1 in
+// nibble 4+i) -> eight bf16 in element order: nibble c goes to mantissa
+// bits 3..6 and is XORed into D there.  D = 0x4340 (192.0): two's
+// complement codes q -> 192 + 8 q.  D = 0x4300 (128.0): unsigned nibbles
+// c -> 128 + 8 c; D = 0x4500 (2048.0): 16 (128 + 8 c).
+__device__ __forceinline__ bf16x8 w4_top(uint32_t w, uint32_t D) {
+  const uint32_t B = 0x00780078u;
   u32x4 r;
-  r[0] = __builtin_amdgcn_bitop3_b32(w, B, D, 0x6A);
-  r[1] = __builtin_amdgcn_bitop3_b32(w >> 4, B, D, 0x6A);
-  r[2] = __builtin_amdgcn_bitop3_b32(w >> 8, B, D, 0x6A);
-  r[3] = __builtin_amdgcn_bitop3_b32(w >> 12, B, D, 0x6A);
+  r[0] = __builtin_amdgcn_bitop3_b32(w << 3, B, D, 0x6A);
+  r[1] = __builtin_amdgcn_bitop3_b32(w >> 1, B, D, 0x6A);
+  r[2] = __builtin_amdgcn_bitop3_b32(w >> 5, B, D, 0x6A);
+  r[3] = __builtin_amdgcn_bitop3_b32(w >> 9, B, D, 0x6A);
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -179,13 +184,19 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
     const uint32_t src_row = kGateUp ? (uint32_t)(sorted_pair[slot] / k_top) : (uint32_t)slot;
     sumoff = src_row * (uint32_t)G * 8u + 4u * (uint32_t)(lane & 1);
   }
+  // (the empty asm hides the offsets' loop invariance, so that the loads
+  // keep the uniform-base + 32-bit offset form instead of eight hoisted
+  // 64-bit addresses held across the loop)
   auto stage = [&](int g, uint8_t* ab, uint2* sbp) {
     const char* gbase = act_b + 256 * g;  // uniform; per-lane 32-bit offsets
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(gbase + srcoff[i],
+    for (int i = 0; i < 8; ++i) {
+      uint32_t o = srcoff[i];
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(gbase + o,
                                        (__attribute__((address_space(3))) void*)(ab + (wave * 32 + 4 * i) * kRowB),
                                        16, 0, 0);
+    }
     __builtin_amdgcn_global_load_lds((const char*)(gsum + g) + sumoff,
                                      (__attribute__((address_space(3))) void*)(sbp + wave * 32),
                                      4, 0, 0);
@@ -199,9 +210,9 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
     }
   };
 
-  // Running totals are kept in units of the current group's scale: before
-  // group g is added, acc *= s_prev / s_g (1 when unchanged); after the last
-  // group acc *= s.  All-zero groups (s_g == 0) contribute nothing and keep
+  // Running totals are kept in units of the current group's scale / 8:
+  // before group g is added, acc *= s_prev / s_g (1 when unchanged); after
+  // the last group acc *= s / 8.  All-zero groups (s_g == 0) contribute nothing and keep
   // s_prev.
   f32x16 acc[4][2];  // [token block][B block]
 #pragma unroll
@@ -212,11 +223,11 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
       for (int i = 0; i < 16; ++i) acc[t][m][i] = 0.0f;
   float s_cur[2] = {0.0f, 0.0f};
 
-  // B column of the offset MFMA: -136 in K rows 0..2 (lanes of half 0)
+  // B column of the offset MFMA: -192 in K rows 0..2 (lanes of half 0)
   u32x4 negv = {0u, 0u, 0u, 0u};
   if (hh == 0) {
-    negv[0] = 0xC308C308u;  // -136, -136
-    negv[1] = 0x0000C308u;  // -136, 0
+    negv[0] = 0xC340C340u;  // -192, -192
+    negv[1] = 0x0000C340u;  // -192, 0
   }
   const bf16x8 negB = __builtin_bit_cast(bf16x8, negv);
 
@@ -237,7 +248,7 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
     float r[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const float sg = f16_bits_to_f32(sc[m]);
+      const float sg = 0.125f * f16_bits_to_f32(sc[m]);
       const bool upd = sg != 0.0f;
       r[m] = upd ? ((s_cur[m] == 0.0f) ? 0.0f : s_cur[m] / sg) : 1.0f;
       s_cur[m] = upd ? sg : s_cur[m];
@@ -276,7 +287,7 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
       }
       bf16x8 bfr[2];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) bfr[m] = w4_magic_pf(q[m][s2 >> 2][s2 & 3]);
+      for (int m = 0; m < 2; ++m) bfr[m] = w4_top(q[m][s2 >> 2][s2 & 3], 0x43404340u);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -344,14 +355,428 @@ __global__ __launch_bounds__(1024) void pf_prep(const int32_t* __restrict__ offs
   if (e == 1023) *num_tiles = sc[1023];
 }
 
+// ============================================ bitplane experts, prefill
+// PagedMoE (abstract): a pair at width b runs the b-plane prefix of its
+// expert directly.  MatMoE (abstract): the b-bit prefix of the 8-bit code u
+// dequantizes to v_b(u) = (u with its 8 - b low bits cleared) + 2^(7-b) - 128
+// for b < 8, and u - 128 for b = 8.  With planes P0 (most significant) ..
+// P7 and unsigned nibbles placed by w4_top (nibble c -> 128 + 8 c):
+//   b <= 4: one pass over the nibble (P0, .., P(b-1), zeros), code
+//     C = 128 + 2^(7-b) t for the top b bits t, and v_b = 2 (C - 192 +
+//     2^(6-b));
+//   b > 4: two passes, (P0..P3) converted to 16 C0 and (P4..P7, planes at or
+//     past b read as 0) to C1, and 8 v_b = 16 C0 + C1 - 3200 + 8 c_b with
+//     c_b = 2^(7-b) for b < 8 and 0 for b = 8.
+// So a tile of width b runs the int4 pipeline once or twice over the same
+// staged activations, with the group scale times 2 (b <= 4) or 1/8 (b > 4)
+// and the constant terms in the one offset MFMA of the group: K rows 0..2
+// carry the split group sum against -192 + 2^(6-b) (or -3200), rows 3..5
+// the same sum against 0 (or 8 c_b).  Every code sits in the top mantissa
+// bits, so the exact part of an MFMA partial sum stays within a few times
+// its signal at every width (with codes in the low mantissa bits a 1-bit
+// prefix would carry 270 times its signal).
+// Codes come from plane words by an in-register bit transpose: four source
+// bytes (nibble bits 0..3 of eight elements) become one int4-ordered code
+// word with four delta swaps.  Tiles hold pairs of one expert and one width
+// (an expert's slots are listed by width, then slot, in `bslot`), so the
+// codes of a tile serve all of its token rows.
+
+// Four source bytes (byte k = nibble bit k of elements 0..7, bit i of a byte
+// = element i) -> one int4 code word (element 2i in nibble i, 2i+1 in 4+i).
+__device__ __forceinline__ uint32_t nib_transpose(uint32_t x) {
+  uint32_t t;
+  t = ((x >> 1) ^ x) & 0x22222222u;  x ^= t ^ (t << 1);
+  t = ((x >> 3) ^ x) & 0x0A0A0A0Au;  x ^= t ^ (t << 3);
+  t = ((x >> 7) ^ x) & 0x00AA00AAu;  x ^= t ^ (t << 7);
+  t = ((x >> 14) ^ x) & 0x0000CCCCu; x ^= t ^ (t << 14);
+  return x;
+}
+
+// Pairs of one expert grouped by width: counts per (expert, width) by
+// ballots over each expert's slots, width-ordered slot lists (stable), and
+// the 128-pair tiles of every (expert, width).  One 1024-thread block.
+__global__ __launch_bounds__(1024) void bp_pf_prep(const int32_t* __restrict__ offsets,
+                                                   const int32_t* __restrict__ sorted_pair,
+                                                   int E, int k, int mode,
+                                                   const uint8_t* __restrict__ bits,
+                                                   int32_t* __restrict__ bslot,
+                                                   PTile* __restrict__ tiles,
+                                                   int* __restrict__ num_tiles) {
+  extern __shared__ int32_t lds[];
+  int32_t* cnt = lds;              // [E][8]
+  int32_t* sbase = lds + 8 * E;    // [E][8] first bslot index of (e, width)
+  int32_t* tbase = lds + 16 * E;   // [E][8] first tile of (e, width)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  for (int e = wave; e < E; e += 16) {
+    const int lo = offsets[e], n = offsets[e + 1] - lo;
+    int c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const int i = i0 + lane;
+      const int b = i < n ? pair_bit_width(sorted_pair[lo + i], e, k, mode, bits) : 0;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) c[w] += __popcll(__ballot(b == w + 1));
+    }
+    if (lane < 8) {
+      int v = c[0];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) v = lane == w ? c[w] : v;
+      cnt[8 * e + lane] = v;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tiles_run = 0;
+    for (int e = 0; e < E; ++e) {
+      int s = offsets[e];
+      for (int w = 0; w < 8; ++w) {
+        sbase[8 * e + w] = s;
+        tbase[8 * e + w] = tiles_run;
+        s += cnt[8 * e + w];
+        tiles_run += (cnt[8 * e + w] + kBT - 1) / kBT;
+      }
+    }
+    *num_tiles = tiles_run;
+  }
+  __syncthreads();
+  for (int e = wave; e < E; e += 16) {
+    const int lo = offsets[e], n = offsets[e + 1] - lo;
+    int run[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const int i = i0 + lane;
+      const int b = i < n ? pair_bit_width(sorted_pair[lo + i], e, k, mode, bits) : 0;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const uint64_t m = __ballot(b == w + 1);
+        if (b == w + 1) bslot[sbase[8 * e + w] + run[w] + __popcll(m & below)] = lo + i;
+        run[w] += __popcll(m);
+      }
+    }
+    for (int w = lane; w < 8; w += 64) {
+      const int nw = cnt[8 * e + w];
+      for (int c2 = 0; c2 * kBT < nw; ++c2)
+        tiles[tbase[8 * e + w] + c2] =
+            PTile{e, sbase[8 * e + w] + c2 * kBT, min(kBT, nw - c2 * kBT), w + 1};
+    }
+  }
+}
+
+template <bool kGateUp>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kPfWaves, kPfWaves)))
+void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K]
+                  const int32_t* __restrict__ sorted_pair,  // gate/up: gather
+                  const int32_t* __restrict__ bslot,        // tile rows -> slots
+                  int k_top, int K, int N,
+                  const uint8_t* __restrict__ planes,       // [E*rows/16][K/128][8][16][16]
+                  const uint16_t* __restrict__ scales,      // [E][rows][K/128]
+                  const uint2* __restrict__ gsum,           // [rows of act][K/128]
+                  const PTile* __restrict__ tiles, const int* __restrict__ num_tiles, int nfb,
+                  uint16_t* __restrict__ h_out, float* __restrict__ y_out) {
+  __shared__ __attribute__((aligned(16))) uint8_t abuf0[kBufB];
+  __shared__ __attribute__((aligned(16))) uint8_t abuf1[kBufB];
+  __shared__ uint2 sbuf0[kBT];
+  __shared__ uint2 sbuf1[kBT];
+
+  // same XCD-aware tile order as the int4 kernel
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int tile = (local / nfb) * 8 + xcd, fblk = local % nfb;
+  if (tile >= *num_tiles) return;
+  const PTile tl = tiles[tile];
+  const int nb = tl.maxb;  // the tile's width, 1..8
+  const int G = K >> 7;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c32 = lane & 31, hh = lane >> 5;
+  const int nrows = kGateUp ? 2 * N : N;
+  const size_t ebase = (size_t)tl.e * nrows;
+
+  int brow[2];
+  bool bstore[2];
+  if (kGateUp) {
+    const int n = fblk * 128 + wave * 32 + c32;
+    brow[0] = n;
+    brow[1] = N + n;
+    bstore[0] = bstore[1] = true;
+  } else {
+    const int n0 = fblk * 256 + wave * 64;
+    bstore[0] = n0 < N;
+    bstore[1] = n0 + 32 < N;
+    brow[0] = bstore[0] ? n0 + c32 : c32;
+    brow[1] = bstore[1] ? n0 + 32 + c32 : c32;
+  }
+  // lane half hh reads bytes 8 hh .. 8 hh + 7 of its row's 16 bytes per
+  // plane: elements 64 hh .. 64 hh + 63 of the group, the int4 lane split.
+  // Addresses are a uniform base (expert, group, plane) plus a 32-bit lane
+  // offset within the expert (its nrows * K bytes).
+  const uint8_t* pe = planes + ebase * (size_t)K;  // 2 KiB blocks: 16 rows x 8 planes per group
+  const uint16_t* se = scales + ebase * (size_t)G;
+  uint32_t lo_p[2], lo_s[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    lo_p[m] = (uint32_t)(brow[m] >> 4) * (uint32_t)G * 2048u + 16u * (uint32_t)(brow[m] & 15) +
+              8u * (uint32_t)hh;
+    lo_s[m] = (uint32_t)brow[m] * (uint32_t)G;
+  }
+
+  const char* act_b = (const char*)act;
+  uint32_t srcoff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = wave * 32 + 4 * i + (lane >> 4);
+    const int slot = bslot[tl.r0 + (t < tl.cnt ? t : 0)];
+    const uint32_t src_row = kGateUp ? (uint32_t)(sorted_pair[slot] / k_top) : (uint32_t)slot;
+    srcoff[i] = src_row * (uint32_t)K * 2u + 16u * (uint32_t)((lane & 15) ^ (t & 15));
+  }
+  uint32_t sumoff;
+  {
+    const int t = wave * 32 + (lane >> 1);
+    const int slot = bslot[tl.r0 + (t < tl.cnt ? t : 0)];
+    const uint32_t src_row = kGateUp ? (uint32_t)(sorted_pair[slot] / k_top) : (uint32_t)slot;
+    sumoff = src_row * (uint32_t)G * 8u + 4u * (uint32_t)(lane & 1);
+  }
+  // (empty asm: as in the int4 kernel)
+  auto stage = [&](int g, uint8_t* ab, uint2* sbp) {
+    const char* gbase = act_b + 256 * g;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t o = srcoff[i];
+      asm volatile("" : "+v"(o));
+      __builtin_amdgcn_global_load_lds(gbase + o,
+                                       (__attribute__((address_space(3))) void*)(ab + (wave * 32 + 4 * i) * kRowB),
+                                       16, 0, 0);
+    }
+    __builtin_amdgcn_global_load_lds((const char*)(gsum + g) + sumoff,
+                                     (__attribute__((address_space(3))) void*)(sbp + wave * 32),
+                                     4, 0, 0);
+  };
+
+  // A pass reads four plane words per B block: nibble bit kb of pass j is
+  // plane 4 j + 3 - kb, at byte offset poff[j][kb] of the group's 2 KiB
+  // block; planes at or past the width read the last present one and are
+  // masked to zero (keep[j] holds 0xFF in the bytes kept).
+  uint32_t poff[2][4], keep[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int p = 4 * j + 3 - kb;
+      poff[j][kb] = 256u * (uint32_t)min(p, nb - 1);
+      keep[j] |= p < nb ? 0xFFu << (8 * kb) : 0u;
+    }
+  auto unit_load = [&](int g, int pass, uint2 (&U)[2][4]) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        uint32_t o = lo_p[m];
+        asm volatile("" : "+v"(o));  // keep the uniform-base + offset form
+        U[m][kb] = *(const uint2*)(pe + ((size_t)g * 2048 + poff[pass][kb]) + o);
+      }
+  };
+  // zero the absent planes of a pass (keep mask uniform per pass)
+  auto unit_fix = [&](uint2 (&U)[2][4], uint32_t kp) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint32_t km = (kp >> (8 * kb)) & 0xFFu ? 0xFFFFFFFFu : 0u;
+        U[m][kb].x &= km;
+        U[m][kb].y &= km;
+      }
+  };
+  auto code_word = [&](const uint2 (&S)[4], int s2) {
+    const int sh = 8 * (s2 & 3);
+    uint32_t x = 0;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint32_t w = (s2 < 4) ? S[kb].x : S[kb].y;
+      x |= ((w >> sh) & 0xFFu) << (8 * kb);
+    }
+    return nib_transpose(x);
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[t][m][i] = 0.0f;
+  float s_cur[2] = {0.0f, 0.0f};
+
+  // group scale multiplier and the offset MFMA's B column (all constants
+  // are exact in bf16)
+  const float smul = nb > 4 ? 0.125f : 2.0f;
+  uint32_t hi3, lo3;  // bf16 constants of K rows 0..2 and 3..5
+  if (nb > 4) {
+    hi3 = f32_to_bf16_rne(-3200.0f);
+    lo3 = f32_to_bf16_rne((float)(nb == 8 ? 0 : 8 << (7 - nb)));
+  } else {
+    hi3 = f32_to_bf16_rne((float)(-192 + (1 << (6 - nb))));
+    lo3 = 0u;
+  }
+  u32x4 offv = {0u, 0u, 0u, 0u};
+  if (hh == 0) {
+    offv[0] = hi3 | (hi3 << 16);
+    offv[1] = hi3 | (lo3 << 16);
+    offv[2] = lo3 | (lo3 << 16);
+  }
+  const bf16x8 offB = __builtin_bit_cast(bf16x8, offv);
+  const uint32_t D0 = nb > 4 ? 0x45004500u : 0x43004300u;
+
+  const int x16 = c32 & 15;
+  const int rd_base = c32 * kRowB + 16 * ((8 * hh) ^ (x16 & 8));
+  const int rd_x = 16 * (x16 & 7);
+
+  // rescale to group g's scale and add its offset term
+  auto group_head = [&](const uint2* sbp, const uint32_t (&sc)[2]) {
+    float r[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const float sg = smul * f16_bits_to_f32(sc[m]);
+      const bool upd = sg != 0.0f;
+      r[m] = upd ? ((s_cur[m] == 0.0f) ? 0.0f : s_cur[m] / sg) : 1.0f;
+      s_cur[m] = upd ? sg : s_cur[m];
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (hh == 0) {
+        const uint2 ss = sbp[t * 32 + c32];  // {hi | mid << 16, lo}
+        v[0] = ss.x;
+        v[1] = ss.y | (ss.x << 16);          // lo, hi
+        v[2] = (ss.x >> 16) | (ss.y << 16);  // mid, lo
+      }
+      const bf16x8 sumA = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][m][i] *= r[m];
+        acc[t][m] = mfma32(sumA, offB, acc[t][m]);
+      }
+    }
+  };
+  auto run_pass = [&](const uint8_t* ab, const uint2 (&U)[2][4], uint32_t D) {
+    const uint8_t* rd = ab + rd_base;
+    bf16x8 af[2][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      af[0][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(rd + t * 32 * kRowB + rd_x));
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      const int cur = s2 & 1;
+      if (s2 + 1 < 8) {
+        const int off = rd_x ^ (16 * (s2 + 1));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          af[cur ^ 1][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(rd + t * 32 * kRowB + off));
+      }
+      bf16x8 bfr[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) bfr[m] = w4_top(code_word(U[m], s2), D);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) acc[t][m] = mfma32(af[cur][t], bfr[m], acc[t][m]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto scales_load = [&](int g, uint32_t (&sc)[2]) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      uint32_t o = lo_s[m];
+      asm volatile("" : "+v"(o));
+      sc[m] = (se + g)[o];
+    }
+  };
+
+  if (nb > 4) {
+    // two passes per group: UA = planes 0..3 of group g (loaded one group
+    // ahead), UB = planes 4..7 (loaded at the group's start)
+    uint2 UA[2][4], UB[2][4];
+    uint32_t sc[2];
+    unit_load(0, 0, UA);
+    scales_load(0, sc);
+    stage(0, abuf0, sbuf0);
+    auto gstep = [&](int g, uint8_t* ab, uint2* sbp, uint8_t* ab_next, uint2* sb_next) {
+      __syncthreads();
+      if (g + 1 < G) stage(g + 1, ab_next, sb_next);
+      unit_load(g, 1, UB);
+      group_head(sbp, sc);
+      unit_fix(UA, keep[0]);
+      run_pass(ab, UA, D0);
+      if (g + 1 < G) {
+        unit_load(g + 1, 0, UA);
+        scales_load(g + 1, sc);
+      }
+      unit_fix(UB, keep[1]);
+      run_pass(ab, UB, 0x43004300u);
+    };
+    for (int g = 0; g < G; g += 2) {
+      gstep(g, abuf0, sbuf0, abuf1, sbuf1);
+      if (g + 1 < G) gstep(g + 1, abuf1, sbuf1, abuf0, sbuf0);
+    }
+  } else {
+    uint2 UA[2][4], UB[2][4];
+    uint32_t sca[2], scb[2];
+    unit_load(0, 0, UA);
+    scales_load(0, sca);
+    stage(0, abuf0, sbuf0);
+    auto gstep = [&](int g, uint8_t* ab, uint2* sbp, uint8_t* ab_next, uint2* sb_next,
+                     uint2 (&U)[2][4], const uint32_t (&sc)[2], uint2 (&Un)[2][4],
+                     uint32_t (&scn)[2]) {
+      __syncthreads();
+      if (g + 1 < G) {
+        stage(g + 1, ab_next, sb_next);
+        unit_load(g + 1, 0, Un);
+        scales_load(g + 1, scn);
+      }
+      group_head(sbp, sc);
+      unit_fix(U, keep[0]);
+      run_pass(ab, U, D0);
+    };
+    for (int g = 0; g < G; g += 2) {
+      gstep(g, abuf0, sbuf0, abuf1, sbuf1, UA, sca, UB, scb);
+      if (g + 1 < G) gstep(g + 1, abuf1, sbuf1, abuf0, sbuf0, UB, scb, UA, sca);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[t][m][i] *= s_cur[m];
+
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tok = t * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+      if (tok >= tl.cnt) continue;
+      const size_t slot = (size_t)bslot[tl.r0 + tok];
+      if (kGateUp) {
+        const float hv = silu_f32(acc[t][0][i]) * acc[t][1][i];
+        h_out[slot * N + brow[0]] = (uint16_t)f32_to_bf16_rne(hv);
+      } else {
+        if (bstore[0]) y_out[slot * N + brow[0]] = acc[t][0][i];
+        if (bstore[1]) y_out[slot * N + brow[1]] = acc[t][1][i];
+      }
+    }
+}
+
 }  // namespace
+
+// Tiles: at most one partial tile per (expert, width) beyond P / 128.
+static size_t pf_max_tiles(long long P, int E) {
+  const long long nonempty = P < 8LL * E ? P : 8LL * E;
+  return (size_t)((P + kBT - 1) / kBT + nonempty);
+}
 
 size_t ffn_prefill_ws_bytes(int T, int k, int E, int d, int f) {
   const long long P = (long long)T * k;
-  const size_t tiles = (size_t)((P + kBT - 1) / kBT + (P < E ? P : E));
+  const size_t tiles = pf_max_tiles(P, E);
   auto a256 = [](size_t v) { return (v + 255) & ~(size_t)255; };
   return 256 + a256(tiles * sizeof(PTile)) + a256((size_t)T * (d / 128) * 8) +
-         a256((size_t)P * (f / 128) * 8);
+         a256((size_t)P * (f / 128) * 8) + a256((size_t)P * sizeof(int32_t));
 }
 
 hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStream_t s) {
@@ -361,7 +786,7 @@ hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStr
   int* num_tiles = (int*)w;
   PTile* tiles = (PTile*)(w + 256);
   const size_t mt = (size_t)((P + kBT - 1) / kBT + (P < a.E ? P : a.E));
-  uint2* xsum = (uint2*)(w + 256 + a256(mt * sizeof(PTile)));
+  uint2* xsum = (uint2*)(w + 256 + a256(pf_max_tiles(P, a.E) * sizeof(PTile)));
   uint2* hsum = (uint2*)((char*)xsum + a256((size_t)a.T * (a.d / 128) * 8));
 
   hipLaunchKernelGGL(pf_prep, dim3(1), dim3(1024), 0, s, a.offsets, a.E, tiles, num_tiles);
@@ -383,6 +808,44 @@ hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStr
   launch_k(pf_w4_kernel<false>, dim3(mt8 * dn_fb), dim3(kThreads), 0, s, a.ev[2], a.ev[3],
            (const uint16_t*)h, a.sorted_pair, a.k, a.f, a.d, a.dn_codes, a.dn_scales,
            (const uint2*)hsum, (const PTile*)tiles, (const int*)num_tiles, dn_fb,
+           (uint16_t*)nullptr, a.y);
+  return hipGetLastError();
+}
+
+// Bitplane experts, prefill: tiles of one expert and one width (bp_pf_prep),
+// then the same two GEMM launches with plane words in place of codes.
+hipError_t launch_ffn_prefill_bp(const FfnArgs& a, uint16_t* h, void* ws, hipStream_t s) {
+  const long long P = (long long)a.T * a.k;
+  auto a256 = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  char* w = (char*)ws;
+  int* num_tiles = (int*)w;
+  PTile* tiles = (PTile*)(w + 256);
+  const size_t mt = pf_max_tiles(P, a.E);
+  uint2* xsum = (uint2*)(w + 256 + a256(mt * sizeof(PTile)));
+  uint2* hsum = (uint2*)((char*)xsum + a256((size_t)a.T * (a.d / 128) * 8));
+  int32_t* bslot = (int32_t*)((char*)hsum + a256((size_t)P * (a.f / 128) * 8));
+
+  hipLaunchKernelGGL(bp_pf_prep, dim3(1), dim3(1024), sizeof(int32_t) * 24 * a.E, s, a.offsets,
+                     a.sorted_pair, a.E, a.k, a.bits_mode, a.bits, bslot, tiles, num_tiles);
+  {
+    const long long n = (long long)a.T * (a.d / 128);
+    hipLaunchKernelGGL(group_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.x,
+                       (long long)a.T, a.d, xsum);
+  }
+  const unsigned mt8 = (unsigned)((mt + 7) & ~(size_t)7);
+  launch_k(pf_bp_kernel<true>, dim3(mt8 * (a.f / 128)), dim3(kThreads), 0, s, a.ev[0], a.ev[1],
+           a.x, a.sorted_pair, (const int32_t*)bslot, a.k, a.d, a.f, a.gu_codes, a.gu_scales,
+           (const uint2*)xsum, (const PTile*)tiles, (const int*)num_tiles, a.f / 128, h,
+           (float*)nullptr);
+  {
+    const long long n = P * (a.f / 128);
+    hipLaunchKernelGGL(group_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, h, P,
+                       a.f, hsum);
+  }
+  const int dn_fb = (a.d + 255) / 256;
+  launch_k(pf_bp_kernel<false>, dim3(mt8 * dn_fb), dim3(kThreads), 0, s, a.ev[2], a.ev[3],
+           (const uint16_t*)h, a.sorted_pair, (const int32_t*)bslot, a.k, a.f, a.d, a.dn_codes,
+           a.dn_scales, (const uint2*)hsum, (const PTile*)tiles, (const int*)num_tiles, dn_fb,
            (uint16_t*)nullptr, a.y);
   return hipGetLastError();
 }

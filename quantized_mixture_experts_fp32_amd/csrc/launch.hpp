@@ -68,6 +68,8 @@ hipError_t launch_ffn_decode_w4(const FfnArgs& a, uint16_t* h, hipStream_t s);
 // prefill path for int4 experts (ffn_prefill.hip); ws: its own scratch
 size_t ffn_prefill_ws_bytes(int T, int k, int E, int d, int f);
 hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStream_t s);
+// prefill path for bitplane experts (ffn_prefill.hip), same workspace
+hipError_t launch_ffn_prefill_bp(const FfnArgs& a, uint16_t* h, void* ws, hipStream_t s);
 
 // expert-major decode of at most 16 tokens, int4 (ffn_decode.hip): the
 // grouping comes out of its gate/up kernel; hE: em_h_bytes(E, f) of scratch

@@ -410,6 +410,33 @@ def test_layer_bitplane_single_slice_ragged(mode):
     assert cnt.max() > 16
 
 
+@pytest.mark.parametrize("mode", ["pair", "expert", "rank"])
+def test_layer_bitplane_prefill_width_tiles(mode):
+    # the bitplane prefill kernels: an expert's pairs regrouped by width,
+    # several 128-pair tiles per (expert, width) with ragged tails, widths
+    # 1..8 (one and two 4-bit passes), f not a power of two
+    cfg = custom_cfg(17, d=256, E=4, k=2, f=384, fmt="bp8", bias_sigma=0.3)
+    rng = np.random.default_rng(17)
+    if mode == "pair":
+        T = 2048
+        bits, bm = rng.integers(1, 9, T * cfg.k).astype(np.uint8), moe.MOE_BITS_PER_PAIR
+    elif mode == "expert":
+        T = 700
+        bits, bm = np.array([8, 5, 4, 1], np.uint8), moe.MOE_BITS_PER_EXPERT
+    else:  # the rank rule is defined for k = 8
+        cfg = custom_cfg(18, d=256, E=10, k=8, f=384, fmt="bp8", bias_sigma=0.3)
+        T, bits, bm = 400, None, moe.MOE_BITS_RANK_RULE
+    note(f"layer bitplane prefill T={T} bits={mode}")
+    hl = HostLayer(cfg, T)
+    lay, _ = check_layer(DevLayer(cfg, T), hl, moe.MOE_PATH_PREFILL, bm, bits)
+    _, ridx, _ = oracle.route(hl.x, hl.wr, hl.bias, cfg.k)
+    pb = oracle.pair_bits(ridx, cfg.E, bm, bits)
+    off = lay.offsets.cpu().numpy()
+    sp = lay.sorted_pair.cpu().numpy()
+    per = [np.bincount(pb[sp[off[e]:off[e + 1]]], minlength=9) for e in range(cfg.E)]
+    assert max(int(c.max()) for c in per) > 128  # some (expert, width) spans 2+ tiles
+
+
 def test_layer_zero_tokens():
     cfg = synth.CONFIGS[0]
     dl = DevLayer(cfg, 0)
@@ -433,20 +460,23 @@ def test_layer_deterministic():
 
 
 # ----------------------------------------- full-size configs, sampled outputs
-FULL = [(2, 4096, moe.MOE_PATH_AUTO), (4, 1, moe.MOE_PATH_AUTO),
-        (4, 64, moe.MOE_PATH_AUTO), (4, 8192, moe.MOE_PATH_AUTO)]
+FULL = [(2, 4096, moe.MOE_PATH_AUTO, moe.MOE_BITS_NONE),
+        (3, 4096, moe.MOE_PATH_AUTO, moe.MOE_BITS_RANK_RULE),
+        (4, 1, moe.MOE_PATH_AUTO, moe.MOE_BITS_NONE),
+        (4, 64, moe.MOE_PATH_AUTO, moe.MOE_BITS_NONE),
+        (4, 8192, moe.MOE_PATH_AUTO, moe.MOE_BITS_NONE)]
 
 
-@pytest.mark.parametrize("cid,T,path", FULL)
-def test_layer_full_size_sampled(cid, T, path):
+@pytest.mark.parametrize("cid,T,path,bits_mode", FULL)
+def test_layer_full_size_sampled(cid, T, path, bits_mode):
     """Full-size layer in the benchmark's launch configuration: routing and
     grouping bit-exact over every token; codes of every touched expert
     bit-exact; outputs of sampled tokens against the oracle."""
     cfg = synth.CONFIGS[cid]
-    note(f"full-size cfg{cid} T={T}: device setup")
+    note(f"full-size cfg{cid} T={T} bits_mode={bits_mode}: device setup")
     dl = DevLayer(cfg, T)
     hl = HostLayer(cfg, T)
-    lay, o32, o16 = run_layer(dl, path)
+    lay, o32, o16 = run_layer(dl, path, bits_mode)
     note("  routing + grouping vs oracle")
     _, ridx, rw = oracle.route(hl.x, hl.wr, hl.bias, cfg.k)
     idx = lay.topk_idx.cpu().numpy()
@@ -461,14 +491,19 @@ def test_layer_full_size_sampled(cid, T, path):
     toks = sorted({0, T - 1, T // 2, int(rsp[roff[hot]]) // cfg.k})[:4]
     note(f"  sampled tokens {toks} (hottest expert {hot} has {cnt[hot]} pairs)")
     y = lay.y_pairs.cpu().numpy()
+    pb = oracle.pair_bits(ridx, cfg.E, bits_mode) if cfg.fmt == "bp8" else None
     for t in toks:
         experts = ridx[t]
         assert_codes_equal(dl, hl, experts)
         o = np.zeros(cfg.d)
         for j, e in enumerate(experts):
             (gq, gs), (dq, ds) = hl.expert(int(e))
-            _, yy = oracle.expert_ffn(hl.x[t:t + 1], oracle.dequant_w4(gq, gs),
-                                      oracle.dequant_w4(dq, ds))
+            if pb is None:
+                wg, wd = oracle.dequant_w4(gq, gs), oracle.dequant_w4(dq, ds)
+            else:
+                b = int(pb[t * cfg.k + j])
+                wg, wd = oracle.dequant_bp(gq, gs, b), oracle.dequant_bp(dq, ds, b)
+            _, yy = oracle.expert_ffn(hl.x[t:t + 1], wg, wd)
             assert_close(y[rpp[t * cfg.k + j]], yy[0], f"y t={t} e={e}")
             o += rw[t, j] * yy[0]
         assert_close(o32[t], o, f"out t={t}")
