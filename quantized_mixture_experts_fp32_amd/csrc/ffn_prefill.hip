@@ -376,20 +376,36 @@ __global__ __launch_bounds__(1024) void pf_prep(const int32_t* __restrict__ offs
 // its signal at every width (with codes in the low mantissa bits a 1-bit
 // prefix would carry 270 times its signal).
 // Codes come from plane words by an in-register bit transpose: four source
-// bytes (nibble bits 0..3 of eight elements) become one int4-ordered code
-// word with four delta swaps.  Tiles hold pairs of one expert and one width
+// bytes (nibble bits 0..3 of eight elements, bit i = element i) become one
+// code word with two delta swaps, which w4_top_bp expands to eight bf16.  Tiles hold pairs of one expert and one width
 // (an expert's slots are listed by width, then slot, in `bslot`), so the
 // codes of a tile serve all of its token rows.
 
-// Four source bytes (byte k = nibble bit k of elements 0..7, bit i of a byte
-// = element i) -> one int4 code word (element 2i in nibble i, 2i+1 in 4+i).
-__device__ __forceinline__ uint32_t nib_transpose(uint32_t x) {
+// Code word of eight elements from the 32-bit word x whose byte b holds
+// nibble bit (0, 2, 1, 3)[b] of elements 0..7 (bit i = element i): with
+// the bits of x indexed by (byte b1 b0, element e2 e1 e0), the two delta
+// swaps exchange index bits 0 <-> 4 and 1 <-> 3, which leaves element e's
+// nibble (bit k at 4 n + k) at nibble n = 4 e0 + 2 e1 + e2.
+__device__ __forceinline__ uint32_t nib_transpose2(uint32_t x) {
   uint32_t t;
-  t = ((x >> 1) ^ x) & 0x22222222u;  x ^= t ^ (t << 1);
-  t = ((x >> 3) ^ x) & 0x0A0A0A0Au;  x ^= t ^ (t << 3);
-  t = ((x >> 7) ^ x) & 0x00AA00AAu;  x ^= t ^ (t << 7);
-  t = ((x >> 14) ^ x) & 0x0000CCCCu; x ^= t ^ (t << 14);
+  t = __builtin_amdgcn_bitop3_b32(x >> 15, x, 0x0000AAAAu, 0x28);  // (a ^ b) & c
+  x = __builtin_amdgcn_bitop3_b32(x, t, t << 15, 0x96);            // a ^ b ^ c
+  t = __builtin_amdgcn_bitop3_b32(x >> 6, x, 0x00CC00CCu, 0x28);
+  x = __builtin_amdgcn_bitop3_b32(x, t, t << 6, 0x96);
   return x;
+}
+
+// nib_transpose2's word -> eight bf16 in element order (elements 2j, 2j+1
+// sit in nibbles n, n + 4 with n = 0, 2, 1, 3 for j = 0..3); the nibble goes
+// to mantissa bits 3..6 of D, as w4_top.
+__device__ __forceinline__ bf16x8 w4_top_bp(uint32_t w, uint32_t D) {
+  const uint32_t B = 0x00780078u;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_bitop3_b32(w << 3, B, D, 0x6A);
+  r[1] = __builtin_amdgcn_bitop3_b32(w >> 5, B, D, 0x6A);
+  r[2] = __builtin_amdgcn_bitop3_b32(w >> 1, B, D, 0x6A);
+  r[3] = __builtin_amdgcn_bitop3_b32(w >> 9, B, D, 0x6A);
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 // Pairs of one expert grouped by width: counts per (expert, width) by
@@ -583,15 +599,12 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
         U[m][kb].y &= km;
       }
   };
+  // step s2's word: byte b = byte s2 of the source of nibble bit (0, 2,
+  // 1, 3)[b]
   auto code_word = [&](const uint2 (&S)[4], int s2) {
     const int sh = 8 * (s2 & 3);
-    uint32_t x = 0;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const uint32_t w = (s2 < 4) ? S[kb].x : S[kb].y;
-      x |= ((w >> sh) & 0xFFu) << (8 * kb);
-    }
-    return nib_transpose(x);
+    auto byte = [&](int kb) { return (((s2 < 4) ? S[kb].x : S[kb].y) >> sh) & 0xFFu; };
+    return nib_transpose2(byte(0) | (byte(2) << 8) | (byte(1) << 16) | (byte(3) << 24));
   };
 
   f32x16 acc[4][2];
@@ -672,7 +685,7 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
       }
       bf16x8 bfr[2];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) bfr[m] = w4_top(code_word(U[m], s2), D);
+      for (int m = 0; m < 2; ++m) bfr[m] = w4_top_bp(code_word(U[m], s2), D);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
