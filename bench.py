@@ -97,9 +97,82 @@ class Workload:
     weight on average over the routing counts of the workload's batches,
     instead of the rank rule."""
 
-    def __init__(self, name, cid, T, steps, path=0, mode="fused", budget_bits=None):
+    def __init__(self, name, cid, T, steps, path=0, mode="fused", budget_bits=None,
+                 slots=None):
         self.name, self.cid, self.T, self.steps, self.path = name, cid, T, steps, path
-        self.mode, self.budget_bits = mode, budget_bits
+        self.mode, self.budget_bits, self.slots = mode, budget_bits, slots
+
+
+def run_cache_workload(wl, warmup, hip, torch, np, synth, moe):
+    """Layer steps with the expert bank in pinned host memory behind
+    `wl.slots` HBM slots (moe_cache_forward): each step routes a fresh batch,
+    copies the experts (bitplane: the planes) it is missing, then computes.
+    The step time includes the host round trip of the routing result and the
+    host-to-device copies."""
+    cfg = synth.CONFIGS[wl.cid]
+    T, d, E, k, f = wl.T, cfg.d, cfg.E, cfg.k, cfg.f
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    bp = cfg.fmt == "bp8"
+    quant = moe.moe_quantize_bitplane8 if bp else moe.moe_quantize_w4
+    w = torch.empty((E, 2 * f, d), dtype=torch.float32, device=dev)
+    synth.dev_fill_weight(cfg, synth.T_W_GATE_UP, w.data_ptr(), stream)
+    gu = quant(w)
+    del w
+    w = torch.empty((E, d, f), dtype=torch.float32, device=dev)
+    synth.dev_fill_weight(cfg, synth.T_W_DOWN, w.data_ptr(), stream)
+    dn = quant(w)
+    del w
+    wr = torch.empty((E, d), dtype=torch.int16, device=dev)
+    synth.dev_fill_router(cfg, wr.data_ptr(), stream)
+    bias = None
+    if cfg.bias_sigma is not None:
+        bias = torch.empty((E,), dtype=torch.float32, device=dev)
+        synth.dev_fill_bias(cfg, bias.data_ptr(), stream)
+    nx = 16
+    xs = []
+    for i in range(nx):
+        x = torch.empty((T, d), dtype=torch.int16, device=dev)
+        synth.dev_fill_x(cfg, x.data_ptr(), T, stream, step=i)
+        xs.append(x)
+    fmt = moe.MOE_FMT_BITPLANE8 if bp else moe.MOE_FMT_W4_SYM
+    bmode = moe.MOE_BITS_RANK_RULE if bp else moe.MOE_BITS_NONE
+    cache = moe.ExpertCache(wr, bias, k, f, gu[0], gu[1], dn[0], dn[1], fmt, wl.slots)
+    del gu, dn
+    out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    for i in range(warmup):
+        cache.forward(xs[i % nx], out=out, bits_mode=bmode)
+    torch.cuda.synchronize()
+    st0 = cache.stats()
+    t_start, t_end = hip.event(), hip.event()
+    hip.record(t_start, stream)
+    wall0 = time.perf_counter()
+    for i in range(wl.steps):
+        cache.forward(xs[(warmup + i) % nx], out=out, bits_mode=bmode)
+    hip.record(t_end, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = hip.ms(t_start, t_end) / wl.steps
+    hip.destroy(t_start)
+    hip.destroy(t_end)
+    st = {key: v - st0[key] for key, v in cache.stats().items()}
+    n = max(st["steps"], 1)
+    routed = st["hits"] + st["loads_full"]
+    rec = {"workload": wl.name, "config": cfg.name, "T": T, "d": d, "E": E, "k": k, "f": f,
+           "format": "bitplane8-rank" if bp else "int4-g128", "slots": wl.slots,
+           "ms_per_step": round(ms, 5), "tokens_per_s": round(T / (ms * 1e-3), 1),
+           "wall_ms_per_step": round(1e3 * wall / wl.steps, 5),
+           "hit_rate": round(st["hits"] / max(routed, 1), 4),
+           "experts_routed_per_step": round(routed / n, 2),
+           "experts_loaded_per_step": round(st["loads_full"] / n, 2),
+           "experts_extended_per_step": round(st["loads_partial"] / n, 2),
+           "h2d_MB_per_step": round(st["bytes"] / n / 1e6, 3),
+           "h2d_GBps_of_step_time": round(st["bytes"] / n / (ms * 1e-3) / 1e9, 2),
+           "ffn_chunks_per_step": round(st["chunks"] / n, 2),
+           "note": "bank in pinned host memory; step time includes the routing "
+                   "read-back and the host-to-device copies"}
+    cache.close()
+    return rec
 
 
 def run_workload(wl, warmup, hip, torch, np, synth, moe):
@@ -459,6 +532,16 @@ def main():
         Workload("olmoe-bitplane-decode T=16", 3, 16, args.steps),
         Workload("olmoe-bitplane-budget4.5 T=16", 3, 16, args.steps, budget_bits=4.5),
         Workload("olmoe-bitplane-prefill T=4096", 3, 4096, max(5, args.steps // 10), path=2),
+        Workload("olmoe-cache64-w4 T=16", 1, 16, max(20, args.steps // 4), mode="cache",
+                 slots=64),
+        Workload("olmoe-cache32-w4 T=16", 1, 16, max(20, args.steps // 4), mode="cache",
+                 slots=32),
+        Workload("olmoe-cache16-w4 T=16", 1, 16, max(20, args.steps // 4), mode="cache",
+                 slots=16),
+        Workload("olmoe-bitplane-cache64 T=16", 3, 16, max(20, args.steps // 4), mode="cache",
+                 slots=64),
+        Workload("olmoe-bitplane-cache16 T=16", 3, 16, max(20, args.steps // 4), mode="cache",
+                 slots=16),
         Workload("e256-w4 T=1", 4, 1, args.steps),
         Workload("e256-w4 T=64", 4, 64, args.steps),
         Workload("olmoe-prefill-w4 T=4096", 2, 4096, max(5, args.steps // 10)),
@@ -472,8 +555,8 @@ def main():
     others = []
     if not args.only_headline:
         for wl in secondary:
-            others.append(run_workload(wl, max(2, args.warmup // 4), hip, torch, np,
-                                       synth, moe))
+            run = run_cache_workload if wl.mode == "cache" else run_workload
+            others.append(run(wl, max(2, args.warmup // 4), hip, torch, np, synth, moe))
     for r in others:
         if r.get("mode", "fused") != "fused" and r["T"] == head.T and r["config"] == \
                 head_rec["config"]:

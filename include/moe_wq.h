@@ -322,6 +322,70 @@ int moe_set_ffn_events(void *gateup_begin, void *gateup_end,
                        void *down_begin, void *down_end);
 
 /* ---------------------------------------------------------------------
+ * HBM expert slot cache.  [ExactMoE] Abstract: the routed-expert bank sits
+ * in pinned host memory in front of a device-side expert cache; [PagedMoE]
+ * abstract: per-step precision is chosen from routing before any transfer,
+ * and a step fetches only the bitplanes it is missing.
+ *
+ * moe_cache_create -- a cache of `slots` device slots (2 <= slots <= E) over
+ * a bank of E experts of the given format.
+ *   host_*: the whole bank, in the layouts above ([E] experts), in PINNED
+ *     host memory (hipHostMalloc; checked, MOE_ERR_INVALID_ARG otherwise).
+ *   slot_*: device arrays of `slots` experts in the same per-expert layout.
+ *   Both stay owned by the caller and must outlive the cache.  The cache
+ *   itself (host state, one copy stream, its events and two small pinned
+ *   staging buffers) is allocated here and freed by moe_cache_destroy.
+ * moe_cache_forward -- one MoE layer step (as moe_layer_forward_wq: routing,
+ *   grouping, expert FFN, combine) with the experts read from the slots:
+ *   routes on `stream`, copies the per-expert request back and WAITS for it
+ *   (the one host synchronisation of a step), assigns slots, issues the
+ *   host-to-device copies of missing experts (bitplane: missing plane
+ *   ranges of resident experts, whole prefixes of new ones) on the copy
+ *   stream, and runs the FFN on `stream` after them.  Resident experts keep
+ *   their slot; new ones take empty slots, then the least recently used.
+ *   When a step routes to more experts than there are slots, the FFN runs in
+ *   chunks: chunk 0 on all slots, then slot halves in turn, copies of the
+ *   next chunk overlapping the FFN of the current one.
+ *   Outputs: topk_idx, topk_w (as moe_route), pair_pos [T*k] and y_pairs
+ *   [T*k][d] fp32 (grouped order of this step's internal grouping; pair p's
+ *   output row is y_pairs[pair_pos[p]]), out [T][d] as moe_combine.
+ *   ws: moe_cache_ws_bytes(cache, T, k) bytes, 256-byte aligned.  Calls
+ *   that share a cache must not overlap (one stream, one thread at a time).
+ * moe_cache_stats -- int64[6]: steps, expert hits, experts loaded whole,
+ *   experts extended by missing planes, bytes copied, FFN chunks.
+ * moe_cache_slots -- the resident expert (-1: empty) and plane count of each
+ *   slot (host arrays [slots]).
+ * moe_cache_reset -- forget every resident expert and the statistics.
+ * moe_cache_plan -- the slot assignment of one step alone, on host state
+ *   (no device work; for checking the policy): slot_expert/slot_bits/
+ *   slot_last [slots] in/out, need [E] (widest prefix per routed expert,
+ *   int4: 8; 0 = not routed).  Outputs vmap [E] (virtual expert id, -1),
+ *   chunks [n][4] = {first virtual id, count, first slot, FFN chunk the
+ *   copies wait for or -1}, loads [n][6] = {expert, slot, first plane, end
+ *   plane, chunk, scales copied}, V = number of virtual experts.
+ * ------------------------------------------------------------------- */
+typedef struct moe_cache moe_cache;
+int moe_cache_create(int E, int d, int f, int format, int slots,
+                     const uint8_t *host_gate_up_codes, const uint16_t *host_gate_up_scales_f16,
+                     const uint8_t *host_down_codes, const uint16_t *host_down_scales_f16,
+                     uint8_t *slot_gate_up_codes, uint16_t *slot_gate_up_scales_f16,
+                     uint8_t *slot_down_codes, uint16_t *slot_down_scales_f16,
+                     moe_cache **cache);
+void moe_cache_destroy(moe_cache *cache);
+size_t moe_cache_ws_bytes(const moe_cache *cache, int T, int k);
+int moe_cache_forward(moe_cache *cache, const void *x_bf16, const void *wr_bf16,
+                      const float *bias, int T, int k, const uint8_t *bits, int bits_mode,
+                      int32_t *topk_idx, float *topk_w, int32_t *pair_pos, float *y_pairs,
+                      void *out, int out_dtype, void *ws, size_t ws_bytes, void *stream);
+int moe_cache_stats(const moe_cache *cache, int64_t *stats6);
+int moe_cache_slots(const moe_cache *cache, int32_t *slot_expert, int32_t *slot_bits);
+int moe_cache_reset(moe_cache *cache);
+int moe_cache_plan(int E, int slots, int format, int32_t *slot_expert, int32_t *slot_bits,
+                   int64_t *slot_last, int64_t step, const int32_t *need, int32_t *vmap,
+                   int32_t *chunks, int max_chunks, int *n_chunks, int32_t *loads,
+                   int max_loads, int *n_loads, int *V);
+
+/* ---------------------------------------------------------------------
  * Offline quantizers (untimed packing of fp32 expert weights on the GPU).
  * w is fp32 [E][N][K] (K = input dimension); groups of 128 along K.
  * moe_quantize_w4 ([ExactMoE] Abstract, symmetric group-128 4-bit):

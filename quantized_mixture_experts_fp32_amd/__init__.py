@@ -31,7 +31,9 @@ EXPORTS = ("moe_status_str", "moe_last_error", "moe_route_ws_bytes", "moe_route"
            "moe_ffn_ws_bytes", "moe_expert_ffn_wq", "moe_combine",
            "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events",
            "moe_layer_ws_bytes", "moe_layer_forward_wq", "moe_bp_distortion_ws_bytes",
-           "moe_bp_distortion", "moe_allocate_bits")
+           "moe_bp_distortion", "moe_allocate_bits", "moe_cache_create", "moe_cache_destroy",
+           "moe_cache_ws_bytes", "moe_cache_forward", "moe_cache_stats", "moe_cache_slots",
+           "moe_cache_reset", "moe_cache_plan")
 
 
 class MoeError(RuntimeError):
@@ -81,9 +83,21 @@ def load_library():
     lib.moe_bp_distortion.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
     lib.moe_allocate_bits.argtypes = [vp, vp, i32, i32, i32, i32, i32, ctypes.c_int64, vp,
                                       vp, vp, vp]
+    lib.moe_cache_create.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     vp]
+    lib.moe_cache_destroy.argtypes, lib.moe_cache_destroy.restype = [vp], None
+    lib.moe_cache_ws_bytes.argtypes, lib.moe_cache_ws_bytes.restype = [vp, i32, i32], sz
+    lib.moe_cache_forward.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, vp, vp,
+                                      i32, vp, sz, vp]
+    lib.moe_cache_stats.argtypes = [vp, vp]
+    lib.moe_cache_slots.argtypes = [vp, vp, vp]
+    lib.moe_cache_reset.argtypes = [vp]
+    lib.moe_cache_plan.argtypes = [i32, i32, i32, vp, vp, vp, ctypes.c_int64, vp, vp, vp, i32,
+                                   vp, vp, i32, vp, vp]
     for name in ("moe_route", "moe_permute", "moe_route_permute", "moe_expert_ffn_wq",
                  "moe_combine", "moe_layer_forward_wq", "moe_bp_distortion",
-                 "moe_allocate_bits",
+                 "moe_allocate_bits", "moe_cache_create", "moe_cache_forward",
+                 "moe_cache_stats", "moe_cache_slots", "moe_cache_reset", "moe_cache_plan",
                  "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events"):
         getattr(lib, name).restype = i32
     _lib = lib
@@ -376,6 +390,116 @@ def moe_set_ffn_events(gateup_begin=None, gateup_end=None, down_begin=None,
         return None if e is None else ctypes.c_void_p(e)
     _check("moe_set_ffn_events", load_library().moe_set_ffn_events(
         h(gateup_begin), h(gateup_end), h(down_begin), h(down_end)))
+
+
+# ------------------------------------------------------ expert slot cache
+def _np_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def moe_cache_plan(E, slots, fmt, slot_expert, slot_bits, slot_last, step, need):
+    """One step's slot assignment on host state (no device work).  The slot
+    arrays (numpy int32/int32/int64 [slots]) are updated in place; returns
+    dict(vmap [E], chunks [n][4], loads [n][6], V)."""
+    import numpy as np
+    for a, dt in ((slot_expert, np.int32), (slot_bits, np.int32), (slot_last, np.int64)):
+        if a.dtype != dt or not a.flags.c_contiguous or a.shape != (slots,):
+            raise ValueError("slot arrays: contiguous int32, int32, int64 of length slots")
+    need = np.ascontiguousarray(need, np.int32)
+    vmap = np.zeros(E, np.int32)
+    max_chunks = 2 + 2 * E // max(slots // 2, 1)
+    chunks = np.zeros((max_chunks, 4), np.int32)
+    loads = np.zeros((2 * E + 1, 6), np.int32)
+    nc, nl, V = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    ref = lambda v: ctypes.cast(ctypes.pointer(v), ctypes.c_void_p)  # noqa: E731
+    _check("moe_cache_plan", load_library().moe_cache_plan(
+        E, slots, fmt, _np_ptr(slot_expert), _np_ptr(slot_bits), _np_ptr(slot_last),
+        int(step), _np_ptr(need), _np_ptr(vmap), _np_ptr(chunks), max_chunks, ref(nc),
+        _np_ptr(loads), loads.shape[0], ref(nl), ref(V)))
+    return dict(vmap=vmap, chunks=chunks[:nc.value].copy(), loads=loads[:nl.value].copy(),
+                V=V.value)
+
+
+class ExpertCache:
+    """Expert bank in pinned host memory behind `slots` device slots
+    (moe_cache_*): forward(x) runs one layer step, copying the experts (or
+    bitplanes) it is missing into the slots first."""
+
+    def __init__(self, wr, bias, k, f, gate_up_codes, gate_up_scales, down_codes,
+                 down_scales, fmt, slots):
+        import torch
+        self.wr, self.bias, self.k, self.f, self.fmt, self.slots = wr, bias, k, f, fmt, slots
+        self.E, self.d = wr.shape
+        dev = wr.device
+        # the whole bank, pinned host memory (the cache's backing store)
+        self.host = [t.detach().to("cpu").contiguous().pin_memory()
+                     for t in (gate_up_codes, gate_up_scales, down_codes, down_scales)]
+        self.dev = [torch.empty((slots,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev)
+                    for t in self.host]
+        h = ctypes.c_void_p()
+        _check("moe_cache_create", load_library().moe_cache_create(
+            self.E, self.d, f, fmt, slots, *[_ptr(t) for t in self.host],
+            *[_ptr(t) for t in self.dev], ctypes.cast(ctypes.pointer(h), ctypes.c_void_p)))
+        self.handle = h
+        self._T = None
+
+    def _alloc(self, T, like):
+        import torch
+        k, d = self.k, self.d
+        dev = like.device
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.pair_pos = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        self.y_pairs = torch.empty((T * k, d), dtype=torch.float32, device=dev)
+        nb = int(load_library().moe_cache_ws_bytes(self.handle, T, k))
+        self.ws = torch.empty((max(nb, 256),), dtype=torch.uint8, device=dev)
+        self._T = T
+
+    def forward(self, x, out=None, out_dtype=MOE_OUT_BF16, bits=None,
+                bits_mode=MOE_BITS_NONE, stream=None):
+        import torch
+        T = x.shape[0]
+        if self._T != T:
+            self._alloc(T, x)
+        if out is None:
+            out = _empty((T, self.d), torch.bfloat16 if out_dtype == MOE_OUT_BF16
+                         else torch.float32, x)
+        _check("moe_cache_forward", load_library().moe_cache_forward(
+            self.handle, _ptr(x), _ptr(self.wr), _ptr(self.bias), T, self.k, _ptr(bits),
+            bits_mode, _ptr(self.topk_idx), _ptr(self.topk_w), _ptr(self.pair_pos),
+            _ptr(self.y_pairs), _ptr(out), out_dtype, _ptr(self.ws),
+            self.ws.numel(), _stream(stream)))
+        return out
+
+    def stats(self):
+        import numpy as np
+        a = np.zeros(6, np.int64)
+        _check("moe_cache_stats", load_library().moe_cache_stats(self.handle, _np_ptr(a)))
+        keys = ("steps", "hits", "loads_full", "loads_partial", "bytes", "chunks")
+        return {k: int(v) for k, v in zip(keys, a)}
+
+    def resident(self):
+        """(expert [slots], planes [slots]) of each slot; -1 = empty."""
+        import numpy as np
+        e = np.zeros(self.slots, np.int32)
+        b = np.zeros(self.slots, np.int32)
+        _check("moe_cache_slots", load_library().moe_cache_slots(self.handle, _np_ptr(e),
+                                                                _np_ptr(b)))
+        return e, b
+
+    def reset(self):
+        _check("moe_cache_reset", load_library().moe_cache_reset(self.handle))
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            load_library().moe_cache_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # --------------------------------------------------------- one whole layer

@@ -11,7 +11,7 @@ LIB = os.path.join(HERE, "libmoe_wq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["abi.cpp", "route.hip", "permute.hip", "quant.hip", "ffn.hip",
            "ffn_decode.hip", "ffn_bitplane.hip", "ffn_prefill.hip",
-           "combine.hip", "alloc.hip"]
+           "combine.hip", "alloc.hip", "cache.hip", "cache.cpp"]
 # Packed fp32 VALU instructions stay disabled in every HIP build here.
 # MFMA accumulators are allocated in ordinary VGPRs (not AGPRs): the kernels
 # rescale and convert accumulators with VALU instructions, which would

@@ -52,6 +52,16 @@ int check_dims(int T, int d, int E, int k, bool k_le_E = true) {
 
 }  // namespace
 
+namespace moe {
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+}  // namespace moe
+
 extern "C" {
 
 const char* moe_status_str(int status) {

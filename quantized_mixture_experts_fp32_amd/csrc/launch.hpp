@@ -88,6 +88,17 @@ hipError_t launch_allocate_bits(const double* dist, const int32_t* counts, int E
                                 int bmin, int bmax, int64_t budget, uint8_t* bits,
                                 double* lambda, int64_t* read, hipStream_t s);
 
+// status code + message of the calling thread's last error (abi.cpp)
+int set_error(int code, const char* fmt, ...);
+
+// expert slot cache (cache.hip): need_cnt = [need[E] | cnt[E]] int32
+hipError_t launch_cache_need(const int32_t* topk_idx, int P, int k, int E, int format,
+                             int bits_mode, const uint8_t* bits, int32_t* need_cnt,
+                             hipStream_t s);
+hipError_t launch_cache_remap(const int32_t* topk_idx, int P, int E, const int32_t* vmap,
+                              int32_t* vidx, const uint8_t* bits_e, uint8_t* bits_v,
+                              hipStream_t s);
+
 hipError_t launch_combine(const float* y, const int32_t* pair_pos,
                           const float* topk_w, int T, int k, int d, void* out,
                           int out_f32, hipStream_t s);

@@ -48,6 +48,14 @@ class DevLayer:
         del w
         torch.cuda.synchronize()
 
+    @staticmethod
+    def x_only(cfg, T, step):
+        """The activations of step `step` alone (weights unchanged)."""
+        x = torch.empty((T, cfg.d), dtype=torch.int16, device=DEV)
+        if T:
+            synth.dev_fill_x(cfg, x.data_ptr(), T, stream(), step=step)
+        return x
+
     def layer(self, bits_mode=moe.MOE_BITS_NONE, bits=None):
         fmt = moe.MOE_FMT_W4_SYM if self.cfg.fmt == "w4" else moe.MOE_FMT_BITPLANE8
         return moe.MoeLayer(self.wr, self.bias, self.cfg.k, self.cfg.f, self.guc,
