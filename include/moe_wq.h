@@ -333,15 +333,17 @@ int moe_set_ffn_events(void *gateup_begin, void *gateup_end,
  *     host memory (hipHostMalloc; checked, MOE_ERR_INVALID_ARG otherwise).
  *   slot_*: device arrays of `slots` experts in the same per-expert layout.
  *   Both stay owned by the caller and must outlive the cache.  The cache
- *   itself (host state, one copy stream, its events and two small pinned
- *   staging buffers) is allocated here and freed by moe_cache_destroy.
+ *   itself (host state, four copy streams, their events, small pinned
+ *   staging buffers, and a device copy of all E experts' scales -- 1/32 of
+ *   an int4 bank -- from which slots take their scales) is allocated here
+ *   and freed by moe_cache_destroy.
  * moe_cache_forward -- one MoE layer step (as moe_layer_forward_wq: routing,
  *   grouping, expert FFN, combine) with the experts read from the slots:
  *   routes on `stream`, copies the per-expert request back and WAITS for it
  *   (the one host synchronisation of a step), assigns slots, issues the
  *   host-to-device copies of missing experts (bitplane: missing plane
  *   ranges of resident experts, whole prefixes of new ones) on the copy
- *   stream, and runs the FFN on `stream` after them.  Resident experts keep
+ *   streams, and runs the FFN on `stream` after them.  Resident experts keep
  *   their slot; new ones take empty slots, then the least recently used.
  *   When a step routes to more experts than there are slots, the FFN runs in
  *   chunks: chunk 0 on all slots, then slot halves in turn, copies of the
@@ -352,7 +354,8 @@ int moe_set_ffn_events(void *gateup_begin, void *gateup_end,
  *   ws: moe_cache_ws_bytes(cache, T, k) bytes, 256-byte aligned.  Calls
  *   that share a cache must not overlap (one stream, one thread at a time).
  * moe_cache_stats -- int64[6]: steps, expert hits, experts loaded whole,
- *   experts extended by missing planes, bytes copied, FFN chunks.
+ *   experts extended by missing planes, bytes copied from the host, FFN
+ *   chunks.
  * moe_cache_slots -- the resident expert (-1: empty) and plane count of each
  *   slot (host arrays [slots]).
  * moe_cache_reset -- forget every resident expert and the statistics.

@@ -145,10 +145,16 @@ struct moe_cache {
   uint16_t* s_dns = nullptr;
   size_t gu_b = 0, gus_b = 0, dn_b = 0, dns_b = 0;  // bytes per expert
   int Vmax = 0;
-  hipStream_t copy = nullptr;
-  std::vector<hipEvent_t> copy_done, ffn_done;
-  int32_t* host_need = nullptr;  // pinned [2E]: need | cnt
-  int32_t* host_vmap = nullptr;  // pinned [E]
+  static constexpr int kCopyStreams = 4;  // copy engines fed in parallel
+  hipStream_t copy[kCopyStreams] = {};
+  std::vector<hipEvent_t> copy_done;  // [chunk][stream]
+  std::vector<hipEvent_t> ffn_done;   // [chunk]
+  int32_t* host_need = nullptr;   // pinned [2E]: need | cnt
+  int32_t* host_vmap = nullptr;   // pinned [E]
+  int32_t* host_items = nullptr;  // pinned [E][2]: (expert, slot) needing scales
+  std::vector<int> item_begin;    // per chunk, into host_items
+  uint8_t* d_gus = nullptr;       // device-resident scale bank [E] (1/32 of
+  uint8_t* d_dns = nullptr;       // the int4 bank): slots take theirs by gather
   moe::CachePlan plan;
   int64_t step = 0;
   int64_t stats[6] = {0, 0, 0, 0, 0, 0};  // steps, hits, full loads, partial loads, bytes, chunks
@@ -169,11 +175,12 @@ bool pinned_host(const void* p) {
 
 size_t a256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Workspace: route | need_cnt [2E] | vmap [E] | vidx [P] | bits_v [Vmax] |
-// offsets [Vmax + 1] | sorted_pair [P] | permute | ffn (or em scratch)
+// Workspace: route | need_cnt [2E] | vmap [E] | items [E][2] | vidx [P] |
+// bits_v [Vmax] | offsets [Vmax + 1] | sorted_pair [P] | permute | ffn (or
+// em scratch)
 struct CacheWs {
   void* route;
-  int32_t *need_cnt, *vmap, *vidx, *offsets, *sorted_pair;
+  int32_t *need_cnt, *vmap, *items, *vidx, *offsets, *sorted_pair;
   uint8_t* bits_v;
   void* perm;
   void* ffn;
@@ -193,6 +200,7 @@ CacheWs cache_ws(const moe_cache* c, int T, int k, char* base) {
   w.route = take(moe::route_ws_bytes(T, E) + 16);
   w.need_cnt = (int32_t*)take(sizeof(int32_t) * 2 * E);
   w.vmap = (int32_t*)take(sizeof(int32_t) * E);
+  w.items = (int32_t*)take(sizeof(int32_t) * 2 * E);
   w.vidx = (int32_t*)take(sizeof(int32_t) * (P + 1));
   w.bits_v = (uint8_t*)take(V + 1);
   w.offsets = (int32_t*)take(sizeof(int32_t) * (V + 1));
@@ -256,15 +264,24 @@ int moe_cache_create(int E, int d, int f, int format, int slots,
   c->dns_b = (size_t)d * (f / MOE_GROUP) * 2;
   c->Vmax = moe::max_virtual(E, slots);
   const int max_chunks = 1 + (c->Vmax - slots) / (slots / 2) + 1;
-  hipError_t e = hipStreamCreateWithFlags(&c->copy, hipStreamNonBlocking);
-  c->copy_done.assign(max_chunks, nullptr);
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < moe_cache::kCopyStreams && e == hipSuccess; ++i)
+    e = hipStreamCreateWithFlags(&c->copy[i], hipStreamNonBlocking);
+  c->copy_done.assign((size_t)max_chunks * moe_cache::kCopyStreams, nullptr);
   c->ffn_done.assign(max_chunks, nullptr);
-  for (int i = 0; i < max_chunks && e == hipSuccess; ++i) {
-    e = hipEventCreateWithFlags(&c->copy_done[i], hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ffn_done[i], hipEventDisableTiming);
-  }
+  for (auto& ev : c->copy_done)
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+  for (auto& ev : c->ffn_done)
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
   if (e == hipSuccess) e = hipHostMalloc((void**)&c->host_need, sizeof(int32_t) * 2 * E);
   if (e == hipSuccess) e = hipHostMalloc((void**)&c->host_vmap, sizeof(int32_t) * E);
+  if (e == hipSuccess) e = hipHostMalloc((void**)&c->host_items, sizeof(int32_t) * 2 * E);
+  if (e == hipSuccess) e = hipMalloc((void**)&c->d_gus, (size_t)E * c->gus_b);
+  if (e == hipSuccess) e = hipMalloc((void**)&c->d_dns, (size_t)E * c->dns_b);
+  if (e == hipSuccess)
+    e = hipMemcpy(c->d_gus, c->h_gus, (size_t)E * c->gus_b, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(c->d_dns, c->h_dns, (size_t)E * c->dns_b, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     moe_cache_destroy(c);
     return moe::set_error(MOE_ERR_HIP, "moe_cache_create: %s", hipGetErrorString(e));
@@ -275,14 +292,19 @@ int moe_cache_create(int E, int d, int f, int format, int slots,
 
 void moe_cache_destroy(moe_cache* c) {
   if (!c) return;
-  if (c->copy) (void)hipStreamSynchronize(c->copy);
+  for (auto st : c->copy)
+    if (st) (void)hipStreamSynchronize(st);
   for (auto ev : c->copy_done)
     if (ev) (void)hipEventDestroy(ev);
   for (auto ev : c->ffn_done)
     if (ev) (void)hipEventDestroy(ev);
-  if (c->copy) (void)hipStreamDestroy(c->copy);
+  for (auto st : c->copy)
+    if (st) (void)hipStreamDestroy(st);
   if (c->host_need) (void)hipHostFree(c->host_need);
   if (c->host_vmap) (void)hipHostFree(c->host_vmap);
+  if (c->host_items) (void)hipHostFree(c->host_items);
+  if (c->d_gus) (void)hipFree(c->d_gus);
+  if (c->d_dns) (void)hipFree(c->d_dns);
   delete c;
 }
 
@@ -382,46 +404,80 @@ int moe_cache_plan(int E, int slots, int format, int32_t* slot_expert, int32_t* 
 
 namespace {
 
-// Copies of one load on the copy stream: whole int4 experts, or the plane
-// range [p0, p1) of each 2 KiB bitplane block (a strided 2-D copy).
-hipError_t enqueue_load(moe_cache* c, const moe::CacheLoad& l, int64_t* bytes) {
-  const size_t e = (size_t)l.e, s = (size_t)l.slot;
+// Copies of a run of n loads (experts e.., slots s.., the same plane range)
+// on copy stream `st`: whole int4 experts, or the plane range [p0, p1) of
+// every 2 KiB bitplane block (a strided 2-D copy).  Scales come from the
+// device-resident scale bank (cache_scale_gather on the compute stream).
+hipError_t enqueue_run(moe_cache* c, const moe::CacheLoad& l, int n, hipStream_t st,
+                       int64_t* bytes) {
+  const size_t e = (size_t)l.e, s = (size_t)l.slot, m = (size_t)n;
   hipError_t r = hipSuccess;
-  auto copy = [&](void* dst, const void* src, size_t n) {
-    if (r == hipSuccess) r = hipMemcpyAsync(dst, src, n, hipMemcpyHostToDevice, c->copy);
-    *bytes += (int64_t)n;
+  auto copy = [&](void* dst, const void* src, size_t len) {
+    if (r == hipSuccess) r = hipMemcpyAsync(dst, src, len, hipMemcpyHostToDevice, st);
+    *bytes += (int64_t)len;
   };
   if (c->format == MOE_FMT_W4_SYM) {
-    copy(c->s_gu + s * c->gu_b, c->h_gu + e * c->gu_b, c->gu_b);
-    copy(c->s_dn + s * c->dn_b, c->h_dn + e * c->dn_b, c->dn_b);
-  } else {
+    copy(c->s_gu + s * c->gu_b, c->h_gu + e * c->gu_b, m * c->gu_b);
+    copy(c->s_dn + s * c->dn_b, c->h_dn + e * c->dn_b, m * c->dn_b);
+  } else if (l.p1 > l.p0) {
     const size_t w = (size_t)256 * (l.p1 - l.p0), off = (size_t)256 * l.p0;
-    const size_t gu_blocks = c->gu_b / 2048, dn_blocks = c->dn_b / 2048;
     auto copy2d = [&](uint8_t* dst, const uint8_t* src, size_t blocks) {
+      if (w == 2048) {  // all eight planes: the blocks are contiguous
+        copy(dst, src, 2048 * blocks);
+        return;
+      }
       if (r == hipSuccess)
         r = hipMemcpy2DAsync(dst + off, 2048, src + off, 2048, w, blocks, hipMemcpyHostToDevice,
-                             c->copy);
+                             st);
       *bytes += (int64_t)(w * blocks);
     };
-    if (l.p1 > l.p0) {
-      copy2d(c->s_gu + s * c->gu_b, c->h_gu + e * c->gu_b, gu_blocks);
-      copy2d(c->s_dn + s * c->dn_b, c->h_dn + e * c->dn_b, dn_blocks);
-    }
-  }
-  if (l.scales) {
-    copy((char*)c->s_gus + s * c->gus_b, (const char*)c->h_gus + e * c->gus_b, c->gus_b);
-    copy((char*)c->s_dns + s * c->dns_b, (const char*)c->h_dns + e * c->dns_b, c->dns_b);
+    copy2d(c->s_gu + s * c->gu_b, c->h_gu + e * c->gu_b, m * (c->gu_b / 2048));
+    copy2d(c->s_dn + s * c->dn_b, c->h_dn + e * c->dn_b, m * (c->dn_b / 2048));
   }
   return r;
 }
 
+// The loads of one chunk: runs of up to kMaxRun consecutive experts into
+// consecutive slots become single copies, spread over the copy streams (the
+// least loaded first); each stream first waits for the FFN chunk that last
+// used the slots, and records the chunk's copy_done event.  (Measured with
+// 16 and 32 slots: one stream or four, whole runs or runs of 1-2 experts
+// all move 33-41 GB/s; short runs over four streams were at the top.)
+constexpr int kMaxRun = 2;
+
 hipError_t enqueue_chunk_loads(moe_cache* c, int chunk) {
   const auto& ch = c->plan.chunks[chunk];
+  constexpr int NS = moe_cache::kCopyStreams;
   hipError_t r = hipSuccess;
-  if (ch.wait >= 0) r = hipStreamWaitEvent(c->copy, c->ffn_done[ch.wait], 0);
+  std::vector<const moe::CacheLoad*> ls;
   for (const auto& l : c->plan.loads)
-    if (l.chunk == chunk && r == hipSuccess) r = enqueue_load(c, l, &c->stats[4]);
-  if (r == hipSuccess) r = hipEventRecord(c->copy_done[chunk], c->copy);
+    if (l.chunk == chunk) ls.push_back(&l);
+  for (int i = 0; i < NS && r == hipSuccess; ++i)
+    if (ch.wait >= 0) r = hipStreamWaitEvent(c->copy[i], c->ffn_done[ch.wait], 0);
+  int64_t load[NS] = {};
+  for (size_t i = 0; i < ls.size() && r == hipSuccess;) {
+    size_t j = i + 1;
+    while (j < ls.size() && (int)(j - i) < kMaxRun && ls[j]->e == ls[j - 1]->e + 1 &&
+           ls[j]->slot == ls[j - 1]->slot + 1 && ls[j]->p0 == ls[i]->p0 &&
+           ls[j]->p1 == ls[i]->p1)
+      ++j;
+    const int st = (int)(std::min_element(load, load + NS) - load);
+    int64_t b = 0;
+    r = enqueue_run(c, *ls[i], (int)(j - i), c->copy[st], &b);
+    load[st] += b;
+    c->stats[4] += b;
+    i = j;
+  }
+  for (int i = 0; i < NS && r == hipSuccess; ++i)
+    r = hipEventRecord(c->copy_done[(size_t)chunk * NS + i], c->copy[i]);
+  return r;
+}
+
+// The compute stream waits for every copy stream's part of a chunk.
+hipError_t wait_chunk_loads(moe_cache* c, int chunk, hipStream_t s) {
+  hipError_t r = hipSuccess;
+  for (int i = 0; i < moe_cache::kCopyStreams && r == hipSuccess; ++i)
+    r = hipStreamWaitEvent(s, c->copy_done[(size_t)chunk * moe_cache::kCopyStreams + i], 0);
   return r;
 }
 
@@ -482,13 +538,31 @@ extern "C" int moe_cache_forward(moe_cache* c, const void* x_bf16, const void* w
     c->stats[3] += pl.loads_partial;
     c->stats[5] += (int64_t)pl.chunks.size();
     std::memcpy(c->host_vmap, pl.vmap.data(), sizeof(int32_t) * E);
+    // experts new to their slots, chunk by chunk: their scales are gathered
+    // from the resident scale bank right before the chunk's FFN
+    const int nch_all = (int)pl.chunks.size();
+    c->item_begin.assign(nch_all + 1, 0);
+    int ni = 0;
+    for (int ci = 0; ci < nch_all; ++ci) {
+      c->item_begin[ci] = ni;
+      for (const auto& l : pl.loads)
+        if (l.chunk == ci && l.scales) {
+          c->host_items[2 * ni] = l.e;
+          c->host_items[2 * ni + 1] = l.slot;
+          ++ni;
+        }
+    }
+    c->item_begin[nch_all] = ni;
     r = hipMemcpyAsync(w.vmap, c->host_vmap, sizeof(int32_t) * E, hipMemcpyHostToDevice, s);
+    if (r == hipSuccess && ni > 0)
+      r = hipMemcpyAsync(w.items, c->host_items, sizeof(int32_t) * 2 * ni,
+                         hipMemcpyHostToDevice, s);
     const bool per_expert = bits_mode == MOE_BITS_PER_EXPERT;
     if (r == hipSuccess)
       r = moe::launch_cache_remap(topk_idx, (int)P, E, w.vmap, w.vidx, per_expert ? bits : nullptr,
                                   per_expert ? w.bits_v : nullptr, s);
     if (r == hipSuccess) r = enqueue_chunk_loads(c, 0);
-    if (r == hipSuccess) r = hipStreamWaitEvent(s, c->copy_done[0], 0);
+    if (r == hipSuccess) r = wait_chunk_loads(c, 0, s);
     if (r != hipSuccess) goto hip_error;
 
     const int nch = (int)pl.chunks.size();
@@ -513,6 +587,11 @@ extern "C" int moe_cache_forward(moe_cache* c, const void* x_bf16, const void* w
       }
       return n;
     };
+    auto gather_scales = [&](int ci) {
+      const int i0 = c->item_begin[ci], n = c->item_begin[ci + 1] - i0;
+      return moe::launch_cache_scale_gather(w.items + 2 * i0, n, c->d_gus, c->d_dns, c->s_gus,
+                                            c->s_dns, c->gus_b, c->dns_b, s);
+    };
     auto path_of = [&](int ci) {
       const long long pc = chunk_pairs(ci);
       return (pc <= 8LL * pl.chunks[ci].n || T <= 16) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
@@ -521,13 +600,16 @@ extern "C" int moe_cache_forward(moe_cache* c, const void* x_bf16, const void* w
         moe::em_applies(T, k, c->st.S, d, f, c->format)) {
       // expert-major decode over the slots: grouping inside its gate/up
       moe::FfnArgs a = ffn_args(0, MOE_PATH_DECODE);
-      r = moe::launch_ffn_decode_em(a, w.vidx, w.offsets, w.sorted_pair, pair_pos,
-                                    (uint16_t*)w.ffn, s);
+      r = gather_scales(0);
+      if (r == hipSuccess)
+        r = moe::launch_ffn_decode_em(a, w.vidx, w.offsets, w.sorted_pair, pair_pos,
+                                      (uint16_t*)w.ffn, s);
     } else {
       r = moe::launch_permute(w.vidx, T, k, pl.V, w.offsets, w.sorted_pair, pair_pos, w.perm,
                               s);
       for (int ci = 0; ci < nch && r == hipSuccess; ++ci) {
-        if (ci > 0) r = hipStreamWaitEvent(s, c->copy_done[ci], 0);
+        if (ci > 0) r = wait_chunk_loads(c, ci, s);
+        if (r == hipSuccess) r = gather_scales(ci);
         if (r == hipSuccess) r = moe::launch_ffn(ffn_args(ci, path_of(ci)), s);
         if (r == hipSuccess) r = hipEventRecord(c->ffn_done[ci], s);
         // loads that follow this chunk's FFN: chunks 1 and 2 after chunk 0,

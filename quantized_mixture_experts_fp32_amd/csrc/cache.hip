@@ -55,7 +55,32 @@ __global__ __launch_bounds__(256) void cache_remap_kernel(const int32_t* __restr
   }
 }
 
+// Scales of experts new to their slots, from the device-resident scale
+// bank: item i = (expert, slot); block (i, part) copies a 1/8 share of the
+// expert's gate/up and down scales in 16-byte words.
+__global__ __launch_bounds__(256) void cache_scale_gather_kernel(
+    const int32_t* __restrict__ items, const uint4* __restrict__ bank_gu,
+    const uint4* __restrict__ bank_dn, uint4* __restrict__ slot_gu, uint4* __restrict__ slot_dn,
+    int gu_words, int dn_words) {
+  const int e = items[2 * blockIdx.x], s = items[2 * blockIdx.x + 1];
+  const int part = blockIdx.y, nparts = gridDim.y;
+  for (int i = part * 256 + threadIdx.x; i < gu_words; i += nparts * 256)
+    slot_gu[(size_t)s * gu_words + i] = bank_gu[(size_t)e * gu_words + i];
+  for (int i = part * 256 + threadIdx.x; i < dn_words; i += nparts * 256)
+    slot_dn[(size_t)s * dn_words + i] = bank_dn[(size_t)e * dn_words + i];
+}
+
 }  // namespace
+
+hipError_t launch_cache_scale_gather(const int32_t* items, int n, const void* bank_gu,
+                                     const void* bank_dn, void* slot_gu, void* slot_dn,
+                                     size_t gu_bytes, size_t dn_bytes, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(cache_scale_gather_kernel, dim3(n, 8), dim3(256), 0, s, items,
+                     (const uint4*)bank_gu, (const uint4*)bank_dn, (uint4*)slot_gu,
+                     (uint4*)slot_dn, (int)(gu_bytes / 16), (int)(dn_bytes / 16));
+  return hipGetLastError();
+}
 
 hipError_t launch_cache_need(const int32_t* topk_idx, int P, int k, int E, int format,
                              int bits_mode, const uint8_t* bits, int32_t* need_cnt,

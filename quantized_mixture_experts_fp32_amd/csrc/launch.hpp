@@ -95,6 +95,10 @@ int set_error(int code, const char* fmt, ...);
 hipError_t launch_cache_need(const int32_t* topk_idx, int P, int k, int E, int format,
                              int bits_mode, const uint8_t* bits, int32_t* need_cnt,
                              hipStream_t s);
+// items [n][2] = (expert, slot); scale bytes per expert multiples of 16
+hipError_t launch_cache_scale_gather(const int32_t* items, int n, const void* bank_gu,
+                                     const void* bank_dn, void* slot_gu, void* slot_dn,
+                                     size_t gu_bytes, size_t dn_bytes, hipStream_t s);
 hipError_t launch_cache_remap(const int32_t* topk_idx, int P, int E, const int32_t* vmap,
                               int32_t* vidx, const uint8_t* bits_e, uint8_t* bits_v,
                               hipStream_t s);
