@@ -574,6 +574,11 @@ void launch_decode_pair(const FfnArgs& a, uint16_t* h, long long P, hipStream_t 
 // Code groups in flight and occupancy of the LDS-staged kernels (measured
 // on MI355X: deeper code prefetch in gate/up costs the fourth wave).
 constexpr int kGuDQ = 2, kGuWaves = 4, kDnDQ = 4, kDnWaves = 4;
+// row tiles per wave of the expert-major down kernel: one h staging per
+// group serves four row tiles (measured at the OLMoE decode shape: 16.7 us
+// with one, 14.5 with two, 14.1 with four, 18.5 with eight; one group of
+// codes in flight per row tile, deeper was slower)
+constexpr int kDnRT = 4;
 
 void launch_decode_lds(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
   const long long mt = (P + 15) / 16 + (P < a.E ? P : a.E);
@@ -770,35 +775,43 @@ void gateup_w4_em(const uint16_t* __restrict__ x, const int32_t* __restrict__ to
   }
 }
 
-template <int kDQ, int kWaves, int kSC>
+// Down, expert-major: block = (expert e, 64 kRT features); wave w owns the
+// row tiles 64 r + 16 w (r < kRT) of the block, so one staging of h per
+// group (and one seed) serves kRT row tiles of codes.
+template <int kDQ, int kWaves, int kSC, int kRT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
 void down_w4_em(const uint16_t* __restrict__ hE, const int32_t* __restrict__ offsets,
                 int E, int d, int f, const uint8_t* __restrict__ codes,
                 const uint16_t* __restrict__ scales, float* __restrict__ y) {
   extern __shared__ int32_t lds_i[];
-  const int G = f >> 7, RG = d / 64;
-  float* sc_lds = (float*)lds_i;                // [G][64]
-  uint16_t* xs = (uint16_t*)(sc_lds + G * 64);  // [2][16][kXRow]
+  constexpr int kRows = 64 * kRT;
+  const int G = f >> 7, RG = d / kRows;
+  float* sc_lds = (float*)lds_i;                      // [kRT][G][64]
+  uint16_t* xs = (uint16_t*)(sc_lds + kRT * G * 64);  // [2][16][kXRow]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, kq = lane >> 4;
   const int st_tok = tid >> 4, st_pc = tid & 15;
   const bf16x8 negoff = bf16_splat(kBf16NegOff);
   const int e = blockIdx.x / RG, rg = blockIdx.x % RG;
-  const int mb = rg * 64, m0 = mb + 16 * wave;
+  const int mb = rg * kRows;
   const size_t erow = (size_t)e * d;
 
   // t = 0: the slot range, scales, codes and all 16 rows of h (rows past the
   // expert's count hold stale values that feed only unstored columns)
   const int lo = offsets[e], hi = offsets[e + 1];
   const uint16_t* hsrc = hE + ((size_t)e * kEmMaxT + st_tok) * f + 8 * st_pc;
-  const uint8_t* cd = codes + (erow + m0) * (size_t)(f >> 1) + 64 * col + 16 * kq;
-  u32x4 q[kDQ], hv[kDQ];
+  const uint8_t* cd[kRT];
+#pragma unroll
+  for (int r = 0; r < kRT; ++r)
+    cd[r] = codes + (erow + mb + 64 * r + 16 * wave) * (size_t)(f >> 1) + 64 * col + 16 * kq;
+  u32x4 q[kDQ][kRT], hv[kDQ];
   auto load = [&](int g, int i) {
     hv[i] = *(const u32x4*)(hsrc + 128 * g);
-    q[i] = *(const u32x4*)(cd + kTileGroupBytes * g);
+#pragma unroll
+    for (int r = 0; r < kRT; ++r) q[i][r] = *(const u32x4*)(cd[r] + kTileGroupBytes * g);
   };
-  ScaleStage<1, kSC ? kSC : 1> sst;
-  if (kSC) sst.fetch(scales + (erow + mb) * G, 0, G);
+  ScaleStage<kRT, kSC ? kSC : 1> sst;
+  if (kSC) sst.fetch(scales + (erow + mb) * G, 64, G);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < kDQ; ++i) load(i < G ? i : G - 1, i);
@@ -806,12 +819,14 @@ void down_w4_em(const uint16_t* __restrict__ hE, const int32_t* __restrict__ off
   if (kSC)
     sst.store(G, sc_lds);
   else
-    stage_scales_rows64<1>(scales + (erow + mb) * G, 0, G, sc_lds);
+    stage_scales_rows64<kRT>(scales + (erow + mb) * G, 64, G, sc_lds);
   const int cnt = hi - lo;
   if (cnt <= 0) return;  // block-uniform
   const int ncol = cnt < kEmMaxT ? cnt : kEmMaxT;
 
-  f32x4 acc = {0, 0, 0, 0};
+  f32x4 acc[kRT];
+#pragma unroll
+  for (int r = 0; r < kRT; ++r) acc[r] = f32x4{0, 0, 0, 0};
   auto step = [&](int gi, int i) {
     uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
     *(u32x4*)(slot + st_tok * kXRow + 8 * st_pc) = hv[i];
@@ -819,11 +834,14 @@ void down_w4_em(const uint16_t* __restrict__ hE, const int32_t* __restrict__ off
     bf16x8 xp[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) xp[j] = *(const bf16x8*)(slot + col * kXRow + 32 * kq + 8 * j);
-    const f32x4 sv = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
     f32x4 seed = {0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < 4; ++j) seed = mfma16(negoff, xp[j], seed);
-    tile_group(xp, seed, q[i], sv, acc);
+#pragma unroll
+    for (int r = 0; r < kRT; ++r) {
+      const f32x4 sv = *(const f32x4*)(sc_lds + (r * G + gi) * 64 + 16 * wave + 4 * kq);
+      tile_group(xp, seed, q[i][r], sv, acc[r]);
+    }
   };
   // the first groups' loads were issued at the start (their one wait at the
   // loop entry covers loads issued together); each slot is refilled after use
@@ -845,7 +863,11 @@ void down_w4_em(const uint16_t* __restrict__ hE, const int32_t* __restrict__ off
 #pragma unroll
   for (int i = 0; i < kDQ; ++i)
     if (g + kDQ + i < G) step(g + kDQ + i, i);
-  if (col < ncol) *(f32x4*)(y + (size_t)(lo + col) * d + m0 + 4 * kq) = acc;
+  if (col < ncol) {
+#pragma unroll
+    for (int r = 0; r < kRT; ++r)
+      *(f32x4*)(y + (size_t)(lo + col) * d + mb + 64 * r + 16 * wave + 4 * kq) = acc[r];
+  }
 }
 
 }  // namespace
@@ -899,15 +921,28 @@ hipError_t launch_ffn_decode_em(const FfnArgs& a, const int32_t* topk_idx, int32
              pair_pos);
   }
   {
+    // kDnRT row tiles per wave when d allows (d % 128 == 0 always holds)
+    constexpr int RT = kDnRT;
+    const int rt = a.d % (64 * RT) == 0 ? RT : 1;
     const int G = a.f / 128;
-    const size_t lds = sizeof(float) * G * 64 + sizeof(uint16_t) * 2 * 16 * kXRow;
-    const int sc = scale_chunks(1, G, a.dn_scales);
-    auto kern = sc == 1   ? down_w4_em<kDnDQ, kDnWaves, 1>
-                : sc == 2 ? down_w4_em<kDnDQ, kDnWaves, 2>
-                : sc == 4 ? down_w4_em<kDnDQ, kDnWaves, 4>
-                          : down_w4_em<kDnDQ, kDnWaves, 0>;
-    launch_k(kern, dim3(a.E * (a.d / 64)), dim3(256), lds, s, a.ev[2], a.ev[3], hE, offsets,
-             a.E, a.d, a.f, a.dn_codes, a.dn_scales, a.y);
+    const size_t lds = sizeof(float) * rt * G * 64 + sizeof(uint16_t) * 2 * 16 * kXRow;
+    const int sc = scale_chunks(rt, G, a.dn_scales);
+    if (rt == RT) {
+      constexpr int DQ = kDnDQ / RT > 0 ? kDnDQ / RT : 1;  // same bytes in flight per wave
+      auto kern = sc == 1   ? down_w4_em<DQ, kDnWaves, 1, RT>
+                  : sc == 2 ? down_w4_em<DQ, kDnWaves, 2, RT>
+                  : sc == 4 ? down_w4_em<DQ, kDnWaves, 4, RT>
+                            : down_w4_em<DQ, kDnWaves, 0, RT>;
+      launch_k(kern, dim3(a.E * (a.d / (64 * RT))), dim3(256), lds, s, a.ev[2], a.ev[3], hE,
+               offsets, a.E, a.d, a.f, a.dn_codes, a.dn_scales, a.y);
+    } else {
+      auto kern = sc == 1   ? down_w4_em<kDnDQ, kDnWaves, 1, 1>
+                  : sc == 2 ? down_w4_em<kDnDQ, kDnWaves, 2, 1>
+                  : sc == 4 ? down_w4_em<kDnDQ, kDnWaves, 4, 1>
+                            : down_w4_em<kDnDQ, kDnWaves, 0, 1>;
+      launch_k(kern, dim3(a.E * (a.d / 64)), dim3(256), lds, s, a.ev[2], a.ev[3], hE, offsets,
+               a.E, a.d, a.f, a.dn_codes, a.dn_scales, a.y);
+    }
   }
   return hipGetLastError();
 }
