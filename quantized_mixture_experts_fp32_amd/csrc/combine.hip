@@ -10,7 +10,9 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <bool kF32Out>
+// K > 0: top-k fixed at compile time (all K slots, weights and rows are
+// loaded together: two round trips); K = 0: any k, one rank at a time.
+template <bool kF32Out, int K>
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const float* __restrict__ y, const int32_t* __restrict__ pair_pos,
     const float* __restrict__ topk_w, int k, int d, void* __restrict__ out) {
@@ -19,12 +21,30 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
   const int m = ((blockIdx.x % nch) * kThreads + threadIdx.x) * 4;
   if (m >= d) return;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = 0; j < k; ++j) {
-    const int64_t slot = pair_pos[(int64_t)t * k + j];
-    const float w = topk_w[(int64_t)t * k + j];
-    const f32x4 v = *(const f32x4*)(y + slot * d + m);
+  if (K > 0) {
+    int64_t slot[K > 0 ? K : 1];
+    float w[K > 0 ? K : 1];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = fmaf(w, v[q], acc[q]);
+    for (int j = 0; j < K; ++j) {
+      slot[j] = pair_pos[(int64_t)t * K + j];
+      w[j] = topk_w[(int64_t)t * K + j];
+    }
+    f32x4 v[K > 0 ? K : 1];
+#pragma unroll
+    for (int j = 0; j < K; ++j) v[j] = *(const f32x4*)(y + slot[j] * d + m);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fmaf(w[j], v[j][q], acc[q]);
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const int64_t slot = pair_pos[(int64_t)t * k + j];
+      const float w = topk_w[(int64_t)t * k + j];
+      const f32x4 v = *(const f32x4*)(y + slot * d + m);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fmaf(w, v[q], acc[q]);
+    }
   }
   if (kF32Out) {
     *(f32x4*)((float*)out + (int64_t)t * d + m) = acc;
@@ -43,12 +63,9 @@ hipError_t launch_combine(const float* y, const int32_t* pair_pos,
                           int out_f32, hipStream_t s) {
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)T * ((d / 4 + kThreads - 1) / kThreads));
-  if (out_f32)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(kThreads), 0, s, y,
-                       pair_pos, topk_w, k, d, out);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(kThreads), 0, s, y,
-                       pair_pos, topk_w, k, d, out);
+  auto kern = out_f32 ? (k == 8 ? combine_kernel<true, 8> : combine_kernel<true, 0>)
+                      : (k == 8 ? combine_kernel<false, 8> : combine_kernel<false, 0>);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, y, pair_pos, topk_w, k, d, out);
   return hipGetLastError();
 }
 
