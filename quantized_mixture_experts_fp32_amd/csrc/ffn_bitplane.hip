@@ -391,7 +391,7 @@ void down_bp_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
 // Plane-word groups in flight and occupancy (measured on MI355X): gate/up
 // holds two matrices' words per group and fits one group ahead at three
 // waves per SIMD; down keeps two groups ahead at two waves.
-constexpr int kBpGuDQ = 1, kBpGuWaves = 3, kBpDnDQ = 2, kBpDnWaves = 2;
+constexpr int kBpGuDQ = 2, kBpGuWaves = 2, kBpDnDQ = 2, kBpDnWaves = 2;
 
 }  // namespace
 
