@@ -668,12 +668,18 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
       }
     }
   };
+  // The B fragments of K step s2 + 1 are converted in the same scheduling
+  // region as the MFMAs of step s2 (independent work the VALU does while
+  // the matrix core runs).
   auto run_pass = [&](const uint8_t* ab, const uint2 (&U)[2][4], uint32_t D) {
     const uint8_t* rd = ab + rd_base;
     bf16x8 af[2][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       af[0][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(rd + t * 32 * kRowB + rd_x));
+    bf16x8 bfr[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) bfr[0][m] = w4_top_bp(code_word(U[m], 0), D);
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2) {
       const int cur = s2 & 1;
@@ -683,13 +689,14 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
         for (int t = 0; t < 4; ++t)
           af[cur ^ 1][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(rd + t * 32 * kRowB + off));
       }
-      bf16x8 bfr[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) bfr[m] = w4_top_bp(code_word(U[m], s2), D);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int m = 0; m < 2; ++m) acc[t][m] = mfma32(af[cur][t], bfr[m], acc[t][m]);
+        for (int m = 0; m < 2; ++m) acc[t][m] = mfma32(af[cur][t], bfr[cur][m], acc[t][m]);
+      if (s2 + 1 < 8) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) bfr[cur ^ 1][m] = w4_top_bp(code_word(U[m], s2 + 1), D);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
