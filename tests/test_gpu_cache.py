@@ -133,6 +133,30 @@ def test_cache_full_size_decode_matches_resident_layer(slots):
     cache.close()
 
 
+@pytest.mark.parametrize("fmt", ["w4", "bp8"])
+def test_cache_prefill_chunks(fmt):
+    # a batch large enough for the prefill kernels, routed to more experts
+    # than there are slots: every chunk runs the grouped MFMA path on its
+    # slice of the slots
+    cfg = custom_cfg(25, d=256, E=8, k=2, f=256, fmt=fmt, bias_sigma=0.5)
+    T = 300
+    dl = DevLayer(cfg, T)
+    cache = make_cache(dl, 4)
+    rng = np.random.default_rng(25)
+    hl = None
+    for step in range(2):
+        note(f"cache prefill {fmt} step={step}")
+        if fmt == "w4":
+            hl = check_step(cache, cfg, T, step, hl_w=hl)
+        else:
+            bits = rng.integers(1, 9, T * cfg.k).astype(np.uint8)
+            hl = check_step(cache, cfg, T, step, moe.MOE_BITS_PER_PAIR, bits, hl_w=hl)
+    st = cache.stats()
+    note(f"  stats {st}")
+    assert st["chunks"] >= 2 * 3  # chunk 0 and at least two streamed chunks per step
+    cache.close()
+
+
 def test_cache_rejects_unpinned_bank():
     cfg = custom_cfg(24, d=256, E=4, k=2, f=256)
     dl = DevLayer(cfg, 1)
