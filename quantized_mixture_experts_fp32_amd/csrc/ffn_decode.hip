@@ -543,33 +543,37 @@ template <int KS, int NT> constexpr int dn_depth() { return NT == 1 ? 2 : 1; }
 template <int KS, int NT> constexpr int dn_waves() { return NT == 1 ? 4 : 2; }
 
 template <int KS, int NT>
-void launch_decode_pair(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
+void launch_gu_pair(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
   constexpr int RT = 4 / KS;
   const int tok = 16 * NT;
   const long long mt = (P + tok - 1) / tok + (P < a.E ? P : a.E);
   const size_t off_b = sizeof(int32_t) * ((a.E + 1 + 3) & ~3);
   const long long cap = 256LL * 8;
-  {
-    const int G = a.d / 128;
-    const long long work = mt * (a.f / (16 * RT));
-    const int grid = (int)(work < cap ? work : cap);
-    const size_t lds = off_b + sizeof(int32_t) * ((std::min<long long>(P, kPairsInLds) + 3) & ~3) +
-                       sizeof(float) * 2 * G * 16 * RT + sizeof(f32x4) * 4 * NT * 2 * 64;
-    launch_k(gateup_w4_decode<KS, NT, gu_depth<KS, NT>(), gu_waves<KS, NT>()>, dim3(grid),
-             dim3(256), lds, s, a.ev[0], a.ev[1], a.x, a.offsets, a.sorted_pair, a.E, a.k,
-             (int)P, a.d, a.f, a.gu_codes, a.gu_scales, h);
-  }
-  {
-    const int G = a.f / 128;
-    const long long work = mt * (a.d / (16 * RT));
-    const int grid = (int)(work < cap ? work : cap);
-    const size_t lds = off_b + sizeof(float) * G * 16 * RT + sizeof(f32x4) * 4 * NT * 64;
-    launch_k(down_w4_decode<KS, NT, dn_depth<KS, NT>(), dn_waves<KS, NT>()>, dim3(grid),
-             dim3(256), lds, s, a.ev[2], a.ev[3], h, a.offsets, a.E, a.d, a.f, a.dn_codes,
-             a.dn_scales, a.y);
-  }
+  const int G = a.d / 128;
+  const long long work = mt * (a.f / (16 * RT));
+  const int grid = (int)(work < cap ? work : cap);
+  const size_t lds = off_b + sizeof(int32_t) * ((std::min<long long>(P, kPairsInLds) + 3) & ~3) +
+                     sizeof(float) * 2 * G * 16 * RT + sizeof(f32x4) * 4 * NT * 2 * 64;
+  launch_k(gateup_w4_decode<KS, NT, gu_depth<KS, NT>(), gu_waves<KS, NT>()>, dim3(grid),
+           dim3(256), lds, s, a.ev[0], a.ev[1], a.x, a.offsets, a.sorted_pair, a.E, a.k,
+           (int)P, a.d, a.f, a.gu_codes, a.gu_scales, h);
 }
 
+template <int KS, int NT>
+void launch_dn_pair(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
+  constexpr int RT = 4 / KS;
+  const int tok = 16 * NT;
+  const long long mt = (P + tok - 1) / tok + (P < a.E ? P : a.E);
+  const size_t off_b = sizeof(int32_t) * ((a.E + 1 + 3) & ~3);
+  const long long cap = 256LL * 8;
+  const int G = a.f / 128;
+  const long long work = mt * (a.d / (16 * RT));
+  const int grid = (int)(work < cap ? work : cap);
+  const size_t lds = off_b + sizeof(float) * G * 16 * RT + sizeof(f32x4) * 4 * NT * 64;
+  launch_k(down_w4_decode<KS, NT, dn_depth<KS, NT>(), dn_waves<KS, NT>()>, dim3(grid),
+           dim3(256), lds, s, a.ev[2], a.ev[3], h, a.offsets, a.E, a.d, a.f, a.dn_codes,
+           a.dn_scales, a.y);
+}
 
 // Code groups in flight and occupancy of the LDS-staged kernels (measured
 // on MI355X: deeper code prefetch in gate/up costs the fourth wave).
@@ -580,7 +584,7 @@ constexpr int kGuDQ = 2, kGuWaves = 4, kDnDQ = 4, kDnWaves = 4;
 // codes in flight per row tile, deeper was slower)
 constexpr int kDnRT = 4;
 
-void launch_decode_lds(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
+void launch_gu_lds(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
   const long long mt = (P + 15) / 16 + (P < a.E ? P : a.E);
   const size_t off_b = sizeof(int32_t) * ((a.E + 1 + 3) & ~3);
   const size_t xs_b = sizeof(uint16_t) * 2 * 16 * kXRow;
@@ -599,6 +603,13 @@ void launch_decode_lds(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s
     launch_k(kern, dim3(grid), dim3(256), lds, s, a.ev[0], a.ev[1], a.x, a.offsets,
              a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes, a.gu_scales, h);
   }
+}
+
+void launch_dn_lds(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
+  const long long mt = (P + 15) / 16 + (P < a.E ? P : a.E);
+  const size_t off_b = sizeof(int32_t) * ((a.E + 1 + 3) & ~3);
+  const size_t xs_b = sizeof(uint16_t) * 2 * 16 * kXRow;
+  const long long cap = 256LL * 8;
   {
     const int G = a.f / 128;
     const long long work = mt * (a.d / 64);
@@ -879,17 +890,30 @@ void down_w4_em(const uint16_t* __restrict__ hE, const int32_t* __restrict__ off
 hipError_t launch_ffn_decode_w4(const FfnArgs& a, uint16_t* h, hipStream_t s) {
   const long long P = (long long)a.T * a.k;
   const long long active = P < a.E ? P : a.E;
-  const long long row_tiles = active * (a.f / 16);
-  const int KS = row_tiles < 2048 ? 4 : (row_tiles < 4096 ? 2 : 1);
+  // K split per kernel from its own row-tile count (gate/up: f rows per
+  // matrix; down: d rows).  Down, whose K (= f) is the shorter one, runs
+  // one K slice per wave from 1024 row tiles up (measured: E = 256, T = 1
+  // down 18.4 us with four slices, 14.6 with two, 11.5 with one); gate/up
+  // keeps the split (forcing one or two slices at T = 1 was slower).
+  auto ks_of = [](long long row_tiles) { return row_tiles < 2048 ? 4 : (row_tiles < 4096 ? 2 : 1); };
+  const int KSg = ks_of(active * (a.f / 16));
+  const long long rt_d = active * (a.d / 16);
+  const int KSd = rt_d < 1024 ? ks_of(rt_d) : 1;
   const bool nt2 = P > 2LL * a.E;
   if (nt2) {
-    if (KS == 4) launch_decode_pair<4, 2>(a, h, P, s);
-    else if (KS == 2) launch_decode_pair<2, 2>(a, h, P, s);
-    else launch_decode_pair<1, 2>(a, h, P, s);
+    if (KSg == 4) launch_gu_pair<4, 2>(a, h, P, s);
+    else if (KSg == 2) launch_gu_pair<2, 2>(a, h, P, s);
+    else launch_gu_pair<1, 2>(a, h, P, s);
+    if (KSd == 4) launch_dn_pair<4, 2>(a, h, P, s);
+    else if (KSd == 2) launch_dn_pair<2, 2>(a, h, P, s);
+    else launch_dn_pair<1, 2>(a, h, P, s);
   } else {
-    if (KS == 4) launch_decode_pair<4, 1>(a, h, P, s);
-    else if (KS == 2) launch_decode_pair<2, 1>(a, h, P, s);
-    else launch_decode_lds(a, h, P, s);
+    if (KSg == 4) launch_gu_pair<4, 1>(a, h, P, s);
+    else if (KSg == 2) launch_gu_pair<2, 1>(a, h, P, s);
+    else launch_gu_lds(a, h, P, s);
+    if (KSd == 4) launch_dn_pair<4, 1>(a, h, P, s);
+    else if (KSd == 2) launch_dn_pair<2, 1>(a, h, P, s);
+    else launch_dn_lds(a, h, P, s);
   }
   return hipGetLastError();
 }
