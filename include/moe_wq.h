@@ -359,6 +359,10 @@ int moe_set_ffn_events(void *gateup_begin, void *gateup_end,
  * moe_cache_slots -- the resident expert (-1: empty) and plane count of each
  *   slot (host arrays [slots]).
  * moe_cache_reset -- forget every resident expert and the statistics.
+ * moe_cache_destroy -- waits for the last step's work, then frees the
+ *   cache's own resources (never the caller's bank or slots).
+ * A moe_cache_forward that fails with MOE_ERR_HIP leaves the cache with
+ *   every slot empty.
  * moe_cache_plan -- the slot assignment of one step alone, on host state
  *   (no device work; for checking the policy): slot_expert/slot_bits/
  *   slot_last [slots] in/out, need [E] (widest prefix per routed expert,

@@ -149,6 +149,7 @@ struct moe_cache {
   hipStream_t copy[kCopyStreams] = {};
   std::vector<hipEvent_t> copy_done;  // [chunk][stream]
   std::vector<hipEvent_t> ffn_done;   // [chunk]
+  hipEvent_t last = nullptr;          // end of the last step on its stream
   int32_t* host_need = nullptr;   // pinned [2E]: need | cnt
   int32_t* host_vmap = nullptr;   // pinned [E]
   int32_t* host_items = nullptr;  // pinned [E][2]: (expert, slot) needing scales
@@ -273,6 +274,7 @@ int moe_cache_create(int E, int d, int f, int format, int slots,
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
   for (auto& ev : c->ffn_done)
     if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->last, hipEventDisableTiming);
   if (e == hipSuccess) e = hipHostMalloc((void**)&c->host_need, sizeof(int32_t) * 2 * E);
   if (e == hipSuccess) e = hipHostMalloc((void**)&c->host_vmap, sizeof(int32_t) * E);
   if (e == hipSuccess) e = hipHostMalloc((void**)&c->host_items, sizeof(int32_t) * 2 * E);
@@ -292,8 +294,12 @@ int moe_cache_create(int E, int d, int f, int format, int slots,
 
 void moe_cache_destroy(moe_cache* c) {
   if (!c) return;
+  // the last step's kernels read the scale bank and its uploads read the
+  // pinned staging buffers: let them finish before anything is freed
+  if (c->last) (void)hipEventSynchronize(c->last);
   for (auto st : c->copy)
     if (st) (void)hipStreamSynchronize(st);
+  if (c->last) (void)hipEventDestroy(c->last);
   for (auto ev : c->copy_done)
     if (ev) (void)hipEventDestroy(ev);
   for (auto ev : c->ffn_done)
@@ -622,7 +628,10 @@ extern "C" int moe_cache_forward(moe_cache* c, const void* x_bf16, const void* w
   if (r == hipSuccess)
     r = moe::launch_combine(y_pairs, pair_pos, topk_w, T, k, d, out, out_dtype == MOE_OUT_F32,
                             s);
+  if (r == hipSuccess) r = hipEventRecord(c->last, s);
   if (r == hipSuccess) return moe::set_error(MOE_OK, "%s", "");
 hip_error:
+  // the slot table may name copies that never ran: start from empty slots
+  c->st.reset();
   return moe::set_error(MOE_ERR_HIP, "moe_cache_forward: %s", hipGetErrorString(r));
 }
