@@ -363,11 +363,21 @@ int moe_layer_forward_wq(const void* x_bf16, const void* wr_bf16, const float* b
   for (auto& ev : g_ffn_ev) ev = nullptr;  // one-shot
   hipError_t e;
   if (path == MOE_PATH_DECODE && moe::em_applies(T, k, E, d, f, format)) {
-    // routing only; the grouping comes out of the expert-major gate/up kernel
-    e = moe::launch_route(x_bf16, wr_bf16, bias, T, d, E, k, topk_idx, topk_w, ws, s);
-    if (e == hipSuccess)
-      e = moe::launch_ffn_decode_em(a, topk_idx, expert_offsets, sorted_pair, pair_pos,
-                                    (uint16_t*)ws_ffn, s);
+    // the grouping comes out of the expert-major kernels; for E <= 64 they
+    // take the routing (and select the top-k) from logits that the routing
+    // launch spreads over (token, 16 experts) blocks
+    if (moe::em_selects_topk(T, k, E)) {
+      float* logits = (float*)ws;  // route_ws_bytes(T, E) <= rp_b
+      e = moe::launch_route_logits(x_bf16, wr_bf16, bias, T, d, E, logits, s);
+      if (e == hipSuccess)
+        e = moe::launch_ffn_decode_em(a, nullptr, expert_offsets, sorted_pair, pair_pos,
+                                      (uint16_t*)ws_ffn, s, logits, topk_idx, topk_w);
+    } else {
+      e = moe::launch_route(x_bf16, wr_bf16, bias, T, d, E, k, topk_idx, topk_w, ws, s);
+      if (e == hipSuccess)
+        e = moe::launch_ffn_decode_em(a, topk_idx, expert_offsets, sorted_pair, pair_pos,
+                                      (uint16_t*)ws_ffn, s);
+    }
   } else {
     e = moe::launch_route_permute(x_bf16, wr_bf16, bias, T, d, E, k, topk_idx, topk_w,
                                   expert_offsets, sorted_pair, pair_pos, ws, s);

@@ -31,9 +31,11 @@
 // grid stride and decode their tile from expert_offsets staged in LDS (no
 // separate preparation launch).
 #include <algorithm>
+#include <type_traits>
 
 #include "kcommon.hpp"
 #include "launch.hpp"
+#include "route_common.hpp"
 #include "decode_common.hpp"
 
 namespace moe {
@@ -638,6 +640,14 @@ void launch_dn_lds(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
 // for the grouping; its slot range comes from expert_offsets, loaded beside
 // its first code loads.  Per group, operands and MFMA order are those of
 // the LDS-staged kernels above (the same fp32 results).
+// With kLg (E <= 64, k <= 16) the block takes the router logits [T][E]
+// instead of topk_idx: e's rank among each token's logits says whether the
+// token chose e (rank < k) and at which place (the pair t k + rank), which
+// is all the block's columns need.  The grouping is finished by the down
+// kernel from the per-expert counts and pair lists that the (e, 0) blocks
+// store; block b < T also selects token b's top-k (one wave, while its first
+// loads are in flight) and stores topk_idx and topk_w.  The routing launch
+// thus only computes logits, over many more blocks than one per token.
 constexpr int kEmMaxT = 16;
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -648,13 +658,17 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 // kW waves per block (4 or 8), one 16-feature row tile each: blocks of 16 kW
 // features; every group of four waves stages the whole activation tile
 // (waves 4-7 write the same values to the same places as waves 0-3).
-template <int kDQ, int kWaves, int kSC, int kW>
+template <int kDQ, int kWaves, int kSC, int kW, bool kLg>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
 void gateup_w4_em(const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
                   int T, int k, int E, int d, int f, const uint8_t* __restrict__ codes,
                   const uint16_t* __restrict__ scales, uint16_t* __restrict__ hE,
                   int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
-                  int32_t* __restrict__ pair_pos) {
+                  int32_t* __restrict__ pair_pos, const float* __restrict__ logits,
+                  int32_t* __restrict__ em_cnt, int32_t* __restrict__ em_list,
+                  int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+  static_assert(!kLg || kEmMaxT % kW == 0, "tokens per wave");
+  constexpr int kTokW = kLg ? kEmMaxT / kW : 1;  // tokens whose top-k a wave selects
   constexpr int kRows = 16 * kW, kMat = kW / 4;  // 64-row scale chunks per matrix
   extern __shared__ int32_t lds_i[];
   __shared__ int32_t wcnt[kW][2];
@@ -673,8 +687,19 @@ void gateup_w4_em(const uint16_t* __restrict__ x, const int32_t* __restrict__ to
   const int sc_u = sc_g + kMat * G * 64;                              // up scale slot
   const size_t erow = (size_t)e * 2 * f;
 
-  // t = 0: every pair's expert, then scales, codes and activations
-  const int pe = tid < P ? topk_idx[tid] : -1;
+  // t = 0: every pair's expert (or this wave's tokens' logits), then
+  // scales, codes and activations
+  int pe = -1;
+  float lgv[kTokW];
+  if constexpr (kLg) {
+#pragma unroll
+    for (int j = 0; j < kTokW; ++j) {
+      const int t = wave + kW * j;
+      lgv[j] = (t < T && lane < E) ? logits[(size_t)t * E + lane] : 0.0f;
+    }
+  } else {
+    pe = tid < P ? topk_idx[tid] : -1;
+  }
   const uint16_t* xsrc = x + (size_t)(st_tok < T ? st_tok : 0) * d + 8 * st_pc;
   const uint8_t* cg = codes + (erow + n0) * (size_t)(d >> 1) + 64 * col + 16 * kq;
   const uint8_t* cu = cg + (size_t)f * (d >> 1);
@@ -707,37 +732,66 @@ void gateup_w4_em(const uint16_t* __restrict__ x, const int32_t* __restrict__ to
       stage_scales_rows64<kStageMat>(sc_src + (size_t)f * G, 64, G, sc_lds + kMat * G * 64);
   }
 
-  // the grouping of the pairs, as far as expert e is concerned
-  const bool mine = pe == e;
-  const bool below = (unsigned)pe < (unsigned)E && pe < e;
-  const uint64_t bm = __ballot(mine), bb = __ballot(below);
-  if (lane == 0) {
-    wcnt[wave][0] = __popcll(bm);
-    wcnt[wave][1] = __popcll(bb);
-  }
-  __syncthreads();
-  int cnt = 0, r0 = 0, rank = __popcll(bm & lanemask_lt());
+  int cnt = 0, xrow = 0;  // columns; staged row (token) of column col
+  if constexpr (kLg) {
+    __shared__ int32_t trank[kEmMaxT];  // e's place in token t's top-k, or -1
 #pragma unroll
-  for (int w = 0; w < kW; ++w) {
-    cnt += wcnt[w][0];
-    r0 += wcnt[w][1];
-    rank += w < wave ? wcnt[w][0] : 0;
-  }
-  if (mine && rank < kEmMaxT) colpair[rank] = tid;
-  if (rg == 0) {
-    if (mine) {
-      sorted_pair[r0 + rank] = tid;
-      pair_pos[tid] = r0 + rank;
+    for (int j = 0; j < kTokW; ++j) {
+      const int t = wave + kW * j;
+      if (t < T) {  // wave-uniform
+        const int r = expert_rank64(lgv[j], E, e);
+        if (lane == 0) trank[t] = r < k ? r : -1;
+        if (t == (int)blockIdx.x)
+          select_topk_radix64(lgv[j], E, k, idx_out + (size_t)t * k, w_out + (size_t)t * k,
+                              nullptr);
+      }
     }
-    if (tid == 0) {
-      offsets[e] = r0;
-      if (e == E - 1) offsets[E] = r0 + cnt;
+    __syncthreads();
+    // the columns are the tokens that chose e, in token (= pair) order
+    const int tr = lane < T ? trank[lane] : -1;
+    const uint64_t bm = __ballot(tr >= 0);
+    cnt = __popcll(bm);
+    if (rg == 0 && wave == 0) {
+      if (tr >= 0) em_list[e * kEmMaxT + __popcll(bm & lanemask_lt())] = lane * k + tr;
+      if (lane == 0) em_cnt[e] = cnt;
     }
+    if (cnt == 0) return;  // block-uniform
+    uint64_t mcol = bm;
+    for (int i = 0; i < col && i + 1 < cnt; ++i) mcol &= mcol - 1;
+    xrow = __ffsll((unsigned long long)mcol) - 1;
+  } else {
+    // the grouping of the pairs, as far as expert e is concerned
+    const bool mine = pe == e;
+    const bool below = (unsigned)pe < (unsigned)E && pe < e;
+    const uint64_t bm = __ballot(mine), bb = __ballot(below);
+    if (lane == 0) {
+      wcnt[wave][0] = __popcll(bm);
+      wcnt[wave][1] = __popcll(bb);
+    }
+    __syncthreads();
+    int r0 = 0, rank = __popcll(bm & lanemask_lt());
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      cnt += wcnt[w][0];
+      r0 += wcnt[w][1];
+      rank += w < wave ? wcnt[w][0] : 0;
+    }
+    if (mine && rank < kEmMaxT) colpair[rank] = tid;
+    if (rg == 0) {
+      if (mine) {
+        sorted_pair[r0 + rank] = tid;
+        pair_pos[tid] = r0 + rank;
+      }
+      if (tid == 0) {
+        offsets[e] = r0;
+        if (e == E - 1) offsets[E] = r0 + cnt;
+      }
+    }
+    __syncthreads();
+    if (cnt == 0) return;  // block-uniform
+    xrow = colpair[col < cnt ? col : 0] / k;
   }
-  __syncthreads();
-  if (cnt == 0) return;  // block-uniform
   const int ncol = cnt < kEmMaxT ? cnt : kEmMaxT;
-  const int xrow = colpair[col < ncol ? col : 0] / k;  // staged row of column col
 
   f32x4 tg = {0, 0, 0, 0}, tu = {0, 0, 0, 0};
   auto step = [&](int gi, int i) {
@@ -790,12 +844,18 @@ void gateup_w4_em(const uint16_t* __restrict__ x, const int32_t* __restrict__ to
 
 // Down, expert-major: block = (expert e, 64 kRT features); wave w owns the
 // row tiles 64 r + 16 w (r < kRT) of the block, so one staging of h per
-// group (and one seed) serves kRT row tiles of codes.
-template <int kDQ, int kWaves, int kSC, int kRT>
+// group (and one seed) serves kRT row tiles of codes.  With kLg the slot
+// range comes from the per-expert counts of the gate/up kernel (a wave sum
+// over the experts below e) and the (e, 0) blocks store expert_offsets,
+// sorted_pair and pair_pos from the experts' pair lists.
+template <int kDQ, int kWaves, int kSC, int kRT, bool kLg>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
 void down_w4_em(const uint16_t* __restrict__ hE, const int32_t* __restrict__ offsets,
                 int E, int d, int f, const uint8_t* __restrict__ codes,
-                const uint16_t* __restrict__ scales, float* __restrict__ y) {
+                const uint16_t* __restrict__ scales, float* __restrict__ y,
+                const int32_t* __restrict__ em_cnt, const int32_t* __restrict__ em_list,
+                int32_t* __restrict__ offsets_out, int32_t* __restrict__ sorted_pair,
+                int32_t* __restrict__ pair_pos) {
   extern __shared__ int32_t lds_i[];
   constexpr int kRows = 64 * kRT;
   const int G = f >> 7, RG = d / kRows;
@@ -809,9 +869,17 @@ void down_w4_em(const uint16_t* __restrict__ hE, const int32_t* __restrict__ off
   const int mb = rg * kRows;
   const size_t erow = (size_t)e * d;
 
-  // t = 0: the slot range, scales, codes and all 16 rows of h (rows past the
-  // expert's count hold stale values that feed only unstored columns)
-  const int lo = offsets[e], hi = offsets[e + 1];
+  // t = 0: the slot range (or every expert's count and e's pair list),
+  // scales, codes and all 16 rows of h (rows past the expert's count hold
+  // stale values that feed only unstored columns)
+  int lo = 0, hi = 0, cv = 0, pv = 0;
+  if constexpr (kLg) {
+    cv = lane < E ? em_cnt[lane] : 0;
+    pv = em_list[e * kEmMaxT + (tid & (kEmMaxT - 1))];
+  } else {
+    lo = offsets[e];
+    hi = offsets[e + 1];
+  }
   const uint16_t* hsrc = hE + ((size_t)e * kEmMaxT + st_tok) * f + 8 * st_pc;
   const uint8_t* cd[kRT];
 #pragma unroll
@@ -833,6 +901,23 @@ void down_w4_em(const uint16_t* __restrict__ hE, const int32_t* __restrict__ off
     sst.store(G, sc_lds);
   else
     stage_scales_rows64<kRT>(scales + (erow + mb) * G, 64, G, sc_lds);
+  if constexpr (kLg) {
+    int below = lane < e ? cv : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) below += __shfl_xor(below, o, kWave);
+    lo = below;
+    hi = lo + __builtin_amdgcn_readlane(cv, e);
+    if (rg == 0) {
+      if (tid < hi - lo) {
+        sorted_pair[lo + tid] = pv;
+        pair_pos[pv] = lo + tid;
+      }
+      if (tid == 0) {
+        offsets_out[e] = lo;
+        if (e == E - 1) offsets_out[E] = hi;
+      }
+    }
+  }
   const int cnt = hi - lo;
   if (cnt <= 0) return;  // block-uniform
   const int ncol = cnt < kEmMaxT ? cnt : kEmMaxT;
@@ -920,11 +1005,20 @@ hipError_t launch_ffn_decode_w4(const FfnArgs& a, uint16_t* h, hipStream_t s) {
 
 // Expert-major decode of at most 16 tokens (int4): gate/up also produces the
 // grouping (expert_offsets, sorted_pair, pair_pos) from topk_idx; hE is the
-// per-expert h scratch of em_h_bytes(E, f) bytes.
-size_t em_h_bytes(int E, int f) { return (size_t)E * kEmMaxT * f * sizeof(uint16_t); }
+// per-expert scratch of em_h_bytes(E, f) bytes: h [E][16][f] bf16, then the
+// per-expert pair counts [E] and pair lists [E][16] of the logits variant.
+static size_t em_a256(size_t b) { return (b + 255) & ~(size_t)255; }
+size_t em_h_bytes(int E, int f) {
+  return em_a256((size_t)E * kEmMaxT * f * sizeof(uint16_t)) + em_a256(sizeof(int32_t) * E) +
+         sizeof(int32_t) * (size_t)E * kEmMaxT;
+}
 
 // Every expert's blocks issue their first loads before knowing whether the
 // expert has pairs, so the path needs most experts active: 2 T k >= E.
+// The expert-major kernels can take the routing from the logits: E <= 64,
+// k <= 16.
+bool em_selects_topk(int T, int k, int E) { return T <= kEmMaxT && E <= 64 && k <= 16; }
+
 bool em_applies(int T, int k, int E, int d, int f, int format) {
   return format == 0 && T >= 1 && T <= kEmMaxT && 2LL * T * k >= E && d % 128 == 0 &&
          f % 128 == 0;
@@ -932,20 +1026,30 @@ bool em_applies(int T, int k, int E, int d, int f, int format) {
 
 hipError_t launch_ffn_decode_em(const FfnArgs& a, const int32_t* topk_idx, int32_t* offsets,
                                 int32_t* sorted_pair, int32_t* pair_pos, uint16_t* hE,
-                                hipStream_t s) {
+                                hipStream_t s, const float* logits, int32_t* idx_out,
+                                float* w_out) {
+  if (logits && (!em_selects_topk(a.T, a.k, a.E) || (int)(a.E * (a.f / 128)) < a.T))
+    return hipErrorInvalidValue;
+  int32_t* em_cnt =
+      (int32_t*)((char*)hE + em_a256((size_t)a.E * kEmMaxT * a.f * sizeof(uint16_t)));
+  int32_t* em_list = em_cnt + em_a256(sizeof(int32_t) * a.E) / sizeof(int32_t);
   {
     // 8-wave blocks of 128 features (f % 128 == 0 always holds here; 16-wave
     // blocks of 256 features measured slower: 29.4 against 25.2 us)
     const int G = a.d / 128;
     const size_t lds = sizeof(float) * 4 * G * 64 + sizeof(uint16_t) * 2 * 16 * kXRow;
     const int sc = scale_chunks(2, G, a.gu_scales);
-    auto kern = sc == 1   ? gateup_w4_em<kGuDQ, kGuWaves, 1, 8>
-                : sc == 2 ? gateup_w4_em<kGuDQ, kGuWaves, 2, 8>
-                : sc == 4 ? gateup_w4_em<kGuDQ, kGuWaves, 4, 8>
-                          : gateup_w4_em<kGuDQ, kGuWaves, 0, 8>;
+    auto pick = [&](auto lg) {
+      constexpr bool L = decltype(lg)::value;
+      return sc == 1   ? gateup_w4_em<kGuDQ, kGuWaves, 1, 8, L>
+             : sc == 2 ? gateup_w4_em<kGuDQ, kGuWaves, 2, 8, L>
+             : sc == 4 ? gateup_w4_em<kGuDQ, kGuWaves, 4, 8, L>
+                       : gateup_w4_em<kGuDQ, kGuWaves, 0, 8, L>;
+    };
+    auto kern = logits ? pick(std::true_type{}) : pick(std::false_type{});
     launch_k(kern, dim3(a.E * (a.f / 128)), dim3(512), lds, s, a.ev[0], a.ev[1], a.x, topk_idx,
              a.T, a.k, a.E, a.d, a.f, a.gu_codes, a.gu_scales, hE, offsets, sorted_pair,
-             pair_pos);
+             pair_pos, logits, em_cnt, em_list, idx_out, w_out);
   }
   {
     // kDnRT row tiles per wave when d allows (d % 128 == 0 always holds)
@@ -956,19 +1060,29 @@ hipError_t launch_ffn_decode_em(const FfnArgs& a, const int32_t* topk_idx, int32
     const int sc = scale_chunks(rt, G, a.dn_scales);
     if (rt == RT) {
       constexpr int DQ = kDnDQ / RT > 0 ? kDnDQ / RT : 1;  // same bytes in flight per wave
-      auto kern = sc == 1   ? down_w4_em<DQ, kDnWaves, 1, RT>
-                  : sc == 2 ? down_w4_em<DQ, kDnWaves, 2, RT>
-                  : sc == 4 ? down_w4_em<DQ, kDnWaves, 4, RT>
-                            : down_w4_em<DQ, kDnWaves, 0, RT>;
+      auto pick = [&](auto lg) {
+        constexpr bool L = decltype(lg)::value;
+        return sc == 1   ? down_w4_em<DQ, kDnWaves, 1, RT, L>
+               : sc == 2 ? down_w4_em<DQ, kDnWaves, 2, RT, L>
+               : sc == 4 ? down_w4_em<DQ, kDnWaves, 4, RT, L>
+                         : down_w4_em<DQ, kDnWaves, 0, RT, L>;
+      };
+      auto kern = logits ? pick(std::true_type{}) : pick(std::false_type{});
       launch_k(kern, dim3(a.E * (a.d / (64 * RT))), dim3(256), lds, s, a.ev[2], a.ev[3], hE,
-               offsets, a.E, a.d, a.f, a.dn_codes, a.dn_scales, a.y);
+               offsets, a.E, a.d, a.f, a.dn_codes, a.dn_scales, a.y, em_cnt, em_list, offsets,
+               sorted_pair, pair_pos);
     } else {
-      auto kern = sc == 1   ? down_w4_em<kDnDQ, kDnWaves, 1, 1>
-                  : sc == 2 ? down_w4_em<kDnDQ, kDnWaves, 2, 1>
-                  : sc == 4 ? down_w4_em<kDnDQ, kDnWaves, 4, 1>
-                            : down_w4_em<kDnDQ, kDnWaves, 0, 1>;
+      auto pick = [&](auto lg) {
+        constexpr bool L = decltype(lg)::value;
+        return sc == 1   ? down_w4_em<kDnDQ, kDnWaves, 1, 1, L>
+               : sc == 2 ? down_w4_em<kDnDQ, kDnWaves, 2, 1, L>
+               : sc == 4 ? down_w4_em<kDnDQ, kDnWaves, 4, 1, L>
+                         : down_w4_em<kDnDQ, kDnWaves, 0, 1, L>;
+      };
+      auto kern = logits ? pick(std::true_type{}) : pick(std::false_type{});
       launch_k(kern, dim3(a.E * (a.d / 64)), dim3(256), lds, s, a.ev[2], a.ev[3], hE, offsets,
-               a.E, a.d, a.f, a.dn_codes, a.dn_scales, a.y);
+               a.E, a.d, a.f, a.dn_codes, a.dn_scales, a.y, em_cnt, em_list, offsets,
+               sorted_pair, pair_pos);
     }
   }
   return hipGetLastError();

@@ -27,6 +27,9 @@ hipError_t launch_route(const void* x, const void* wr, const float* bias,
                         int T, int d, int E, int k, int32_t* topk_idx,
                         float* topk_w, void* ws, hipStream_t s);
 
+// Router logits [T][E] fp32 into `logits` (T <= 512; route_ws_bytes(T, E)).
+hipError_t launch_route_logits(const void* x, const void* wr, const float* bias, int T, int d,
+                               int E, float* logits, hipStream_t s);
 size_t route_permute_ws_bytes(int T, int k, int E);
 hipError_t launch_route_permute(const void* x, const void* wr, const float* bias, int T,
                                 int d, int E, int k, int32_t* topk_idx, float* topk_w,
@@ -75,9 +78,14 @@ hipError_t launch_ffn_prefill_bp(const FfnArgs& a, uint16_t* h, void* ws, hipStr
 // grouping comes out of its gate/up kernel; hE: em_h_bytes(E, f) of scratch
 size_t em_h_bytes(int E, int f);
 bool em_applies(int T, int k, int E, int d, int f, int format);
+bool em_selects_topk(int T, int k, int E);
+// topk_idx: the pairs' experts; or, with logits ([T][E] fp32) not null and
+// em_selects_topk, the kernels take each token's choice from the logits and
+// store the top-k to idx_out / w_out (topk_idx unused).
 hipError_t launch_ffn_decode_em(const FfnArgs& a, const int32_t* topk_idx, int32_t* offsets,
                                 int32_t* sorted_pair, int32_t* pair_pos, uint16_t* hE,
-                                hipStream_t s);
+                                hipStream_t s, const float* logits = nullptr,
+                                int32_t* idx_out = nullptr, float* w_out = nullptr);
 
 // read-budget bit allocation (alloc.hip)
 size_t bp_distortion_ws_bytes(int E, int d, int f);

@@ -18,6 +18,7 @@
 #include "kcommon.hpp"
 #include "launch.hpp"
 #include "permute_common.hpp"
+#include "route_common.hpp"
 
 namespace moe {
 namespace {
@@ -82,14 +83,6 @@ __device__ void select_topk(const float* __restrict__ lg, int E, int k,
 // index, exactly as better() orders them.  The wave arg-max of each round
 // is four DPP steps within rows of 16 lanes and four readlanes.  Also
 // copies the ids to idx_copy (LDS).
-__device__ __forceinline__ uint32_t ordered_f32(float f) {
-  const uint32_t u = (f == 0.0f) ? 0u : __float_as_uint(f);  // -0 orders as +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float unordered_f32(uint32_t o) {
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-
 template <int kCtrl>
 __device__ __forceinline__ uint64_t dpp_max(uint64_t v) {
   const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
@@ -148,58 +141,14 @@ __device__ void select_topk_reg(const float* __restrict__ lg, int E, int k,
   if (lane < k) w_out[lane] = my_ex / ssum;
 }
 
-// The same selection for E <= 64 (one logit per lane) by rank instead of k
-// arg-max rounds: a lane's rank is the number of the token's keys above its
-// own, counted against the wave's keys in LDS; ranks are distinct because
-// the keys are, so lanes of rank < k are the top-k in rank order.  The
-// weights use the same fp32 steps as above: m is the rank-0 logit, the
-// exponentials are summed in rank order from 0.  wl is this wave's
-// kTopkLds bytes of LDS.
-constexpr int kTopkLds = 64 * 8 + 32 * 4;
-
-__device__ __forceinline__ void select_topk_rank64(const float* __restrict__ lg, int E, int k,
-                                                   int32_t* __restrict__ idx_out,
-                                                   float* __restrict__ w_out,
-                                                   int32_t* __restrict__ idx_copy,
-                                                   char* wl) {
-  uint64_t* keys = (uint64_t*)wl;          // [64]
-  float* val = (float*)(wl + 64 * 8);      // [16] logit of rank r
-  float* exb = val + 16;                   // [16] exponential of rank r
+// The same selection for E <= 64 (one logit per lane) by ballots instead of
+// k arg-max rounds (select_topk_radix64), from the token's logits in memory.
+__device__ __forceinline__ void select_topk_64(const float* __restrict__ lg, int E, int k,
+                                               int32_t* __restrict__ idx_out,
+                                               float* __restrict__ w_out,
+                                               int32_t* __restrict__ idx_copy) {
   const int lane = threadIdx.x & 63;
-  const bool ok = lane < E;
-  const uint64_t key =
-      ok ? (((uint64_t)ordered_f32(lg[lane]) << 32) | (uint32_t)~(uint32_t)lane) : 0ull;
-  keys[lane] = key;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  int rank = 0;
-  for (int j = 0; j < E; j += 2) {  // E is even or the last pad key is 0
-    const u64x2 kv = *(const u64x2*)(keys + j);
-    rank += (kv[0] > key) + (kv[1] > key);
-  }
-  const bool sel = ok && rank < k;
-  const float v = unordered_f32((uint32_t)(key >> 32));
-  if (sel) val[rank] = v;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const float ex = expf(v - val[0]);
-  if (sel) exb[rank] = ex;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  float ssum = 0.0f;
-  for (int r = 0; r < k; ++r) ssum += exb[r];  // rank order
-  if (sel) {
-    idx_out[rank] = lane;
-    idx_copy[rank] = lane;
-    w_out[rank] = ex / ssum;
-  }
-  // the next token's writes to this wave's LDS come after every read above
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  select_topk_radix64(lane < E ? lg[lane] : 0.0f, E, k, idx_out, w_out, idx_copy);
 }
 
 // Stage TB activation rows (bf16) into LDS; rows past T are zero.
@@ -216,21 +165,28 @@ __device__ __forceinline__ void stage_x(const uint16_t* __restrict__ x, int T,
 }
 
 // Logits of TB tokens (rows of xs) for the experts of this lane group; the
-// group's 16 lanes are lanes 16*(tid/16) .. +15 of one wave.
+// group's 16 lanes are lanes 16*(tid/16) .. +15 of one wave.  Router-row
+// chunks are loaded kWindow at a time; load_window fills one window and
+// group_logits_from consumes a first window already loaded.
+__device__ __forceinline__ void load_window(const uint16_t* __restrict__ wrow, bool ok,
+                                            int nchunk, int c0, u32x4 (&wv)[kWindow]) {
+  const int l = threadIdx.x & 15;
+#pragma unroll
+  for (int q = 0; q < kWindow; ++q)
+    wv[q] = (ok && c0 + q < nchunk) ? *(const u32x4*)(wrow + 128 * (c0 + q) + 8 * l)
+                                    : u32x4{0u, 0u, 0u, 0u};
+}
+
 template <int TB>
-__device__ __forceinline__ void group_logits(const uint16_t* xs, int d,
-                                             const uint16_t* __restrict__ wrow,
-                                             bool ok, float acc[TB]) {
+__device__ __forceinline__ void group_logits_from(const uint16_t* xs, int d,
+                                                  const uint16_t* __restrict__ wrow, bool ok,
+                                                  u32x4 (&wv)[kWindow], float acc[TB]) {
   const int l = threadIdx.x & 15;
   const int nchunk = d >> 7;
 #pragma unroll
   for (int tt = 0; tt < TB; ++tt) acc[tt] = 0.0f;
   for (int c0 = 0; c0 < nchunk; c0 += kWindow) {
-    u32x4 wv[kWindow];
-#pragma unroll
-    for (int q = 0; q < kWindow; ++q)
-      wv[q] = (ok && c0 + q < nchunk) ? *(const u32x4*)(wrow + 128 * (c0 + q) + 8 * l)
-                                      : u32x4{0u, 0u, 0u, 0u};
+    if (c0 > 0) load_window(wrow, ok, nchunk, c0, wv);
 #pragma unroll
     for (int q = 0; q < kWindow; ++q) {
       if (c0 + q >= nchunk) break;
@@ -251,6 +207,15 @@ __device__ __forceinline__ void group_logits(const uint16_t* xs, int d,
 #pragma unroll
     for (int o = 8; o >= 1; o >>= 1) acc[tt] = acc[tt] + __shfl_xor(acc[tt], o, kWave);
   }
+}
+
+template <int TB>
+__device__ __forceinline__ void group_logits(const uint16_t* xs, int d,
+                                             const uint16_t* __restrict__ wrow,
+                                             bool ok, float acc[TB]) {
+  u32x4 wv[kWindow];
+  load_window(wrow, ok, d >> 7, 0, wv);
+  group_logits_from<TB>(xs, d, wrow, ok, wv, acc);
 }
 
 // Many tokens: 8 per 256-thread block, 16 lane groups over the experts.
@@ -299,13 +264,18 @@ __global__ __launch_bounds__(256) void route_logits_small(
   extern __shared__ uint16_t xs[];  // [d]
   const int neb = (E + 15) >> 4;
   const int t = blockIdx.x / neb, eb = blockIdx.x % neb;
-  stage_x<1, 256>(x, T, d, t, xs);
-  __syncthreads();
   const int G = threadIdx.x >> 4, l = threadIdx.x & 15;
   const int e = 16 * eb + G;
   const bool ok = e < E;
+  const uint16_t* wrow = wr + (size_t)(ok ? e : 0) * d;
+  // the router row's first window is requested before the activation row,
+  // so the two loads share one memory round trip
+  u32x4 wv[kWindow];
+  load_window(wrow, ok, d >> 7, 0, wv);
+  stage_x<1, 256>(x, T, d, t, xs);
+  __syncthreads();
   float acc[1];
-  group_logits<1>(xs, d, wr + (size_t)(ok ? e : 0) * d, ok, acc);
+  group_logits_from<1>(xs, d, wrow, ok, wv, acc);
   if (ok && l == 0) logits[(size_t)t * E + e] = acc[0] + (bias ? bias[e] : 0.0f);
 }
 
@@ -313,13 +283,11 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logi
                                                   int T, int E, int k,
                                                   int32_t* __restrict__ topk_idx,
                                                   float* __restrict__ topk_w) {
-  __shared__ __align__(16) char wl[4][kTopkLds];
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   if (E <= 64)
-    select_topk_rank64(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
-                       topk_w + (size_t)t * k, topk_idx + (size_t)t * k,
-                       wl[threadIdx.x >> 6]);
+    select_topk_64(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
+                   topk_w + (size_t)t * k, topk_idx + (size_t)t * k);
   else
     select_topk_reg(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
                     topk_w + (size_t)t * k, topk_idx + (size_t)t * k);
@@ -335,9 +303,8 @@ __global__ __launch_bounds__(1024) void route_token_block(
     const float* __restrict__ bias, int T, int d, int E, int k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   extern __shared__ float lds[];
-  float* lg = lds;                                            // [E]
-  char* wl = (char*)(lds + ((E + 3) & ~3));                   // kTopkLds
-  uint16_t* xs = (uint16_t*)(wl + kTopkLds);                  // [d]
+  float* lg = lds;                                  // [E]
+  uint16_t* xs = (uint16_t*)(lds + ((E + 3) & ~3));  // [d]
   const int t = blockIdx.x;
   stage_x<1, 1024>(x, T, d, t, xs);
   __syncthreads();
@@ -352,8 +319,8 @@ __global__ __launch_bounds__(1024) void route_token_block(
   __syncthreads();
   if (threadIdx.x < 64) {
     if (E <= 64)
-      select_topk_rank64(lg, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k,
-                         topk_idx + (size_t)t * k, wl);
+      select_topk_64(lg, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k,
+                     topk_idx + (size_t)t * k);
     else
       select_topk_reg(lg, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k,
                       topk_idx + (size_t)t * k);
@@ -367,13 +334,12 @@ __global__ __launch_bounds__(1024) void route_topk_permute(
     float* __restrict__ topk_w, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos) {
   extern __shared__ int32_t sh[];
-  __shared__ __align__(16) char wl[16][kTopkLds];
   const int P = T * k;
   int32_t* idx_lds = sh;
   for (int t = threadIdx.x >> 6; t < T; t += 16) {
     if (E <= 64)
-      select_topk_rank64(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
-                         topk_w + (size_t)t * k, idx_lds + t * k, wl[threadIdx.x >> 6]);
+      select_topk_64(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
+                     topk_w + (size_t)t * k, idx_lds + t * k);
     else
       select_topk_reg(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
                       topk_w + (size_t)t * k, idx_lds + t * k);
@@ -384,6 +350,18 @@ __global__ __launch_bounds__(1024) void route_topk_permute(
 
 }  // namespace
 
+// fp32 logits [T][E] only (T <= kSmallT), for a consumer that selects the
+// top-k itself.
+hipError_t launch_route_logits(const void* x, const void* wr, const float* bias, int T, int d,
+                               int E, float* logits, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (T > kSmallT) return hipErrorInvalidValue;
+  const int neb = (E + 15) / 16;
+  hipLaunchKernelGGL(route_logits_small, dim3(T * neb), dim3(256), sizeof(uint16_t) * d, s,
+                     (const uint16_t*)x, (const uint16_t*)wr, bias, T, d, E, logits);
+  return hipGetLastError();
+}
+
 size_t route_ws_bytes(int T, int E) {
   return T <= kSmallT ? sizeof(float) * (size_t)T * E : 0;
 }
@@ -393,7 +371,7 @@ hipError_t launch_route(const void* x, const void* wr, const float* bias,
                         float* topk_w, void* ws, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (T <= kTokenBlockT) {
-    const size_t lds = sizeof(float) * ((E + 3) & ~3) + kTopkLds + sizeof(uint16_t) * d;
+    const size_t lds = sizeof(float) * ((E + 3) & ~3) + sizeof(uint16_t) * d;
     hipLaunchKernelGGL(route_token_block, dim3(T), dim3(1024), lds, s, (const uint16_t*)x,
                        (const uint16_t*)wr, bias, T, d, E, k, topk_idx, topk_w);
   } else if (T <= kSmallT) {
