@@ -902,9 +902,11 @@ void down_w4_em(const uint16_t* __restrict__ hE, const int32_t* __restrict__ off
   else
     stage_scales_rows64<kRT>(scales + (erow + mb) * G, 64, G, sc_lds);
   if constexpr (kLg) {
-    int below = lane < e ? cv : 0;
+    // sum of the counts below e (each at most 16) bit by bit with ballots
+    int below = 0;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) below += __shfl_xor(below, o, kWave);
+    for (int b = 0; b < 5; ++b)
+      below += __popcll(__ballot(lane < e && ((cv >> b) & 1))) << b;
     lo = below;
     hi = lo + __builtin_amdgcn_readlane(cv, e);
     if (rg == 0) {
