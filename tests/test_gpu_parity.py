@@ -277,6 +277,35 @@ def test_layer_cfg1_decode(T):
     check_layer(DevLayer(cfg, T), HostLayer(cfg, T), moe.MOE_PATH_AUTO)
 
 
+@pytest.mark.parametrize("case", ["dup-rows", "zero-router"])
+@pytest.mark.parametrize("T", [3, 16])
+def test_layer_decode_router_ties(case, T):
+    """Whole layer with exactly equal logits (ties to the lower index) at a
+    few tokens, where the expert-major kernels take each token's choice from
+    the logits: duplicated router rows, and a zero router whose logits are
+    tied biases."""
+    note(f"layer decode ties {case} T={T}")
+    cfg = custom_cfg(22, d=256, E=16, k=4, f=256, bias_sigma=1.0)
+    dl, hl = DevLayer(cfg, T), HostLayer(cfg, T)
+    wr = hl.wr.copy()
+    if case == "dup-rows":
+        wr[7] = wr[2]
+        wr[9] = wr[2]
+        wr[11] = wr[4]
+        wr[15] = wr[0]
+        bias = None
+    else:
+        wr[:] = 0
+        bias = np.repeat(np.array([0.5, -1.0, 0.5, 2.0], np.float32), 4)
+    hl.wr, hl.bias = wr, bias
+    dl.wr = torch.from_numpy(wr.view(np.int16)).to(DEV)
+    dl.bias = None if bias is None else torch.from_numpy(bias).to(DEV)
+    lay, _ = check_layer(dl, hl, moe.MOE_PATH_AUTO)
+    if case == "zero-router":
+        # every token picks the four experts of bias 2.0 (12..15)
+        assert np.array_equal(lay.topk_idx.cpu().numpy(), np.tile([12, 13, 14, 15], (T, 1)))
+
+
 @pytest.mark.parametrize("T", [1, 16])
 def test_layer_cfg1_sequential_per_expert(T):
     """One launch per expert over the same routed pairs gives the fused result."""
