@@ -119,14 +119,19 @@ __global__ __launch_bounds__(kThreads) void perm_scatter(
   }
 }
 
-// Small batches (P <= kSmallP): one 1024-thread block, one launch.
+// Small batches (P <= kSmallP): one block, one launch (one wave for at most
+// 64 pairs, else 1024 threads).
 __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ idx,
                                                    int P, int E,
                                                    int32_t* __restrict__ offsets,
                                                    int32_t* __restrict__ sorted_pair,
                                                    int32_t* __restrict__ pair_pos) {
   extern __shared__ int32_t sh[];
-  permute_block(idx, P, E, offsets, sorted_pair, pair_pos, sh);
+  if (P <= 64) {
+    if (threadIdx.x < 64) permute_wave_small(idx, P, E, offsets, sorted_pair, pair_pos, sh);
+  } else {
+    permute_block(idx, P, E, offsets, sorted_pair, pair_pos, sh);
+  }
 }
 
 }  // namespace
@@ -142,8 +147,9 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int E,
                           int32_t* pair_pos, void* ws, hipStream_t s) {
   const int P = T * k;
   if (P <= kSmallP) {
-    hipLaunchKernelGGL(perm_small, dim3(1), dim3(1024), permute_block_lds_bytes(E),
-                       s, topk_idx, P, E, offsets, sorted_pair, pair_pos);
+    hipLaunchKernelGGL(perm_small, dim3(1), dim3(P <= 64 ? 64 : 1024),
+                       permute_block_lds_bytes(E), s, topk_idx, P, E, offsets, sorted_pair,
+                       pair_pos);
     return hipGetLastError();
   }
   const int nb = (P + kChunk - 1) / kChunk;

@@ -97,4 +97,69 @@ __device__ inline void permute_block(const int32_t* idx, int P, int E,
   }
 }
 
+// The same grouping of P <= 64 pairs by one wave (wave 0 of the block; no
+// block barrier): LDS atomics count the pairs of each expert, the wave scans
+// the counts (as above), and a pair's slot is its expert's start plus the
+// number of lower lanes with the same expert (ballots over the expert id
+// bits).  idx may live in global memory or in LDS; cnt is LDS of E ints.
+__device__ inline void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ inline void permute_wave_small(const int32_t* idx, int P, int E,
+                                          int32_t* __restrict__ offsets,
+                                          int32_t* __restrict__ sorted_pair,
+                                          int32_t* __restrict__ pair_pos, int32_t* cnt) {
+  const int lane = threadIdx.x & 63;
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  int e = lane < P ? idx[lane] : -1;
+  if ((unsigned)e >= (unsigned)E) e = -1;
+  wave_sync_lds();
+  if (e >= 0) atomicAdd(&cnt[e], 1);
+  wave_sync_lds();
+  const int per = (E + 63) >> 6;
+  int c[8], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int ee = lane * per + i;
+    c[i] = (i < per && ee < E) ? cnt[ee] : 0;
+    sum += c[i];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += v;
+  }
+  wave_sync_lds();  // every count is read before the starts overwrite them
+  int run = incl - sum;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int ee = lane * per + i;
+    if (i < per && ee < E) {
+      cnt[ee] = run;
+      offsets[ee] = run;
+      run += c[i];
+    }
+  }
+  if (lane == 63) offsets[E] = incl;
+  wave_sync_lds();
+  const uint32_t key = (uint32_t)(e < 0 ? 0x3FF : e);
+  uint64_t peers = ~0ull;
+#pragma unroll
+  for (int bit = 0; bit < 10; ++bit) {
+    const bool set = (key >> bit) & 1u;
+    const uint64_t m = __ballot(set);
+    peers &= set ? m : ~m;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  if (e >= 0) {
+    const int slot = cnt[e] + __popcll(peers & below);
+    sorted_pair[slot] = lane;
+    pair_pos[lane] = slot;
+  }
+}
+
 }  // namespace moe

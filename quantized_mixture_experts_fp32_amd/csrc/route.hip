@@ -327,16 +327,18 @@ __global__ __launch_bounds__(1024) void route_token_block(
   }
 }
 
-// Few tokens: top-k of every token (one wave per token, 16 waves) and the
-// grouping of the T*k pairs by expert, in one 1024-thread block.
+// Few tokens: top-k of every token (one wave per token) and the grouping of
+// the T*k pairs by expert, in one block: 1024 threads, or for at most 64
+// pairs one wave per token (at most 16) with the grouping by wave 0 alone.
 __global__ __launch_bounds__(1024) void route_topk_permute(
     const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos) {
   extern __shared__ int32_t sh[];
   const int P = T * k;
+  const int nw = blockDim.x >> 6;
   int32_t* idx_lds = sh;
-  for (int t = threadIdx.x >> 6; t < T; t += 16) {
+  for (int t = threadIdx.x >> 6; t < T; t += nw) {
     if (E <= 64)
       select_topk_64(logits + (size_t)t * E, E, k, topk_idx + (size_t)t * k,
                      topk_w + (size_t)t * k, idx_lds + t * k);
@@ -345,7 +347,12 @@ __global__ __launch_bounds__(1024) void route_topk_permute(
                       topk_w + (size_t)t * k, idx_lds + t * k);
   }
   __syncthreads();
-  permute_block(idx_lds, P, E, offsets, sorted_pair, pair_pos, sh + ((P + 3) & ~3));
+  if (P <= 64) {
+    if (threadIdx.x < 64)
+      permute_wave_small(idx_lds, P, E, offsets, sorted_pair, pair_pos, sh + ((P + 3) & ~3));
+  } else {
+    permute_block(idx_lds, P, E, offsets, sorted_pair, pair_pos, sh + ((P + 3) & ~3));
+  }
 }
 
 }  // namespace
@@ -411,7 +418,8 @@ hipError_t launch_route_permute(const void* x, const void* wr, const float* bias
                        (const uint16_t*)x, (const uint16_t*)wr, bias, T, d, E, logits);
     const int P = T * k;
     const size_t lds = sizeof(int32_t) * ((P + 3) & ~3) + permute_block_lds_bytes(E);
-    hipLaunchKernelGGL(route_topk_permute, dim3(1), dim3(1024), lds, s, logits, T, E, k,
+    const int threads = P <= 64 ? 64 * (T < 16 ? T : 16) : 1024;
+    hipLaunchKernelGGL(route_topk_permute, dim3(1), dim3(threads), lds, s, logits, T, E, k,
                        topk_idx, topk_w, offsets, sorted_pair, pair_pos);
     return hipGetLastError();
   }
