@@ -378,6 +378,17 @@ int moe_layer_forward_wq(const void* x_bf16, const void* wr_bf16, const float* b
         e = moe::launch_ffn_decode_em(a, topk_idx, expert_offsets, sorted_pair, pair_pos,
                                       (uint16_t*)ws_ffn, s);
     }
+  } else if (path == MOE_PATH_DECODE && moe::decode_selects_topk(T, k, E, d, f, format)) {
+    // at most 64 pairs: the decode gate/up routes the batch from the logits
+    float* logits = (float*)ws;  // route_ws_bytes(T, E) <= rp_b
+    a.logits = logits;
+    a.topk_idx_out = topk_idx;
+    a.topk_w_out = topk_w;
+    a.offsets_out = expert_offsets;
+    a.sorted_pair_out = sorted_pair;
+    a.pair_pos_out = pair_pos;
+    e = moe::launch_route_logits(x_bf16, wr_bf16, bias, T, d, E, logits, s);
+    if (e == hipSuccess) e = moe::launch_ffn(a, s);
   } else {
     e = moe::launch_route_permute(x_bf16, wr_bf16, bias, T, d, E, k, topk_idx, topk_w,
                                   expert_offsets, sorted_pair, pair_pos, ws, s);

@@ -36,6 +36,7 @@
 #include "kcommon.hpp"
 #include "launch.hpp"
 #include "route_common.hpp"
+#include "permute_common.hpp"
 #include "decode_common.hpp"
 
 namespace moe {
@@ -93,12 +94,22 @@ __device__ __forceinline__ void tile_group(const bf16x8 (&xp)[4], const f32x4 se
 // Work item = (token tile of up to 16*NT pairs, row group of RT = 4/KS row
 // tiles of 16 features).  Wave (rt, ks) streams gate and up codes of its row
 // tile over K slice ks with kDepth groups of codes and activations in flight.
-template <int KS, int NT, int kDepth, int kWaves>
+// With kLg (at most 64 pairs, E <= 64) the block routes the batch itself
+// from the router logits [T][E]: wave w selects the top-k of tokens w,
+// w + 4, ... (the routing kernels' ballot selection), wave 0 groups the
+// pairs (the one-wave counting sort), and block 0 stores every routing
+// output; the routing launch before it only computes logits.  (With E = 256
+// the arg-max selection in every block cost more than the launch it saves.)
+template <int KS, int NT, int kDepth, int kWaves, bool kLg>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
 void gateup_w4_decode(const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
                       const int32_t* __restrict__ sorted_pair, int E, int k, int P,
                       int d, int f, const uint8_t* __restrict__ codes,
-                      const uint16_t* __restrict__ scales, uint16_t* __restrict__ h) {
+                      const uint16_t* __restrict__ scales, uint16_t* __restrict__ h,
+                      const float* __restrict__ logits, int32_t* __restrict__ idx_out,
+                      float* __restrict__ w_out, int32_t* __restrict__ offsets_out,
+                      int32_t* __restrict__ sorted_pair_out,
+                      int32_t* __restrict__ pair_pos_out) {
   constexpr int RT = 4 / KS;
   extern __shared__ int32_t lds_i[];
   const int G = d >> 7, RG = f / (16 * RT);
@@ -106,8 +117,34 @@ void gateup_w4_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
   int32_t* sp_lds = lds_i + ((E + 1 + 3) & ~3);
   float* sc_lds = (float*)(sp_lds + ((min(P, kPairsInLds) + 3) & ~3));  // [2][G][16 RT]
   f32x4* red = (f32x4*)(sc_lds + 2 * G * 16 * RT);                       // [4][NT][2][64]
-  const int np = stage_routing(offsets, sorted_pair, E, P, off_lds, sp_lds);
-  __syncthreads();
+  int np;
+  if constexpr (kLg) {
+    int32_t* idx_lds = (int32_t*)(red + 4 * NT * 2 * 64);  // [64] experts of the pairs
+    int32_t* pp_lds = idx_lds + 64;                        // [64] slot of each pair
+    int32_t* cnt_lds = pp_lds + 64;                        // [E]
+    const bool store = blockIdx.x == 0;
+    const int T = P / k, lane = threadIdx.x & 63;
+    for (int t = threadIdx.x >> 6; t < T; t += 4) {  // wave-uniform
+      int32_t* io = store ? idx_out + (size_t)t * k : nullptr;
+      float* wo = store ? w_out + (size_t)t * k : nullptr;
+      select_topk_radix64(lane < E ? logits[(size_t)t * E + lane] : 0.0f, E, k, io, wo,
+                          idx_lds + t * k);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) permute_wave_small(idx_lds, P, E, off_lds, sp_lds, pp_lds, cnt_lds);
+    __syncthreads();
+    if (store) {
+      for (int i = threadIdx.x; i <= E; i += blockDim.x) offsets_out[i] = off_lds[i];
+      for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        sorted_pair_out[i] = sp_lds[i];
+        pair_pos_out[i] = pp_lds[i];
+      }
+    }
+    np = P;
+  } else {
+    np = stage_routing(offsets, sorted_pair, E, P, off_lds, sp_lds);
+    __syncthreads();
+  }
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, kq = lane >> 4;
@@ -555,10 +592,13 @@ void launch_gu_pair(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
   const long long work = mt * (a.f / (16 * RT));
   const int grid = (int)(work < cap ? work : cap);
   const size_t lds = off_b + sizeof(int32_t) * ((std::min<long long>(P, kPairsInLds) + 3) & ~3) +
-                     sizeof(float) * 2 * G * 16 * RT + sizeof(f32x4) * 4 * NT * 2 * 64;
-  launch_k(gateup_w4_decode<KS, NT, gu_depth<KS, NT>(), gu_waves<KS, NT>()>, dim3(grid),
-           dim3(256), lds, s, a.ev[0], a.ev[1], a.x, a.offsets, a.sorted_pair, a.E, a.k,
-           (int)P, a.d, a.f, a.gu_codes, a.gu_scales, h);
+                     sizeof(float) * 2 * G * 16 * RT + sizeof(f32x4) * 4 * NT * 2 * 64 +
+                     (a.logits ? sizeof(int32_t) * (128 + a.E) : 0);
+  auto kern = a.logits ? gateup_w4_decode<KS, NT, gu_depth<KS, NT>(), gu_waves<KS, NT>(), true>
+                       : gateup_w4_decode<KS, NT, gu_depth<KS, NT>(), gu_waves<KS, NT>(), false>;
+  launch_k(kern, dim3(grid), dim3(256), lds, s, a.ev[0], a.ev[1], a.x, a.offsets,
+           a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes, a.gu_scales, h, a.logits,
+           a.topk_idx_out, a.topk_w_out, a.offsets_out, a.sorted_pair_out, a.pair_pos_out);
 }
 
 template <int KS, int NT>
@@ -972,6 +1012,18 @@ void down_w4_em(const uint16_t* __restrict__ hE, const int32_t* __restrict__ off
 
 }  // namespace
 
+// Waves per K split for a kernel of row_tiles 16-row tiles.
+static int ks_of(long long row_tiles) {
+  return row_tiles < 2048 ? 4 : (row_tiles < 4096 ? 2 : 1);
+}
+
+bool decode_selects_topk(int T, int k, int E, int d, int f, int format) {
+  const long long P = (long long)T * k;
+  const long long active = P < E ? P : E;
+  return format == 0 /* int4 */ && T >= 1 && P <= 64 && E <= 64 && d % 128 == 0 &&
+         f % 128 == 0 && ks_of(active * (f / 16)) > 1;
+}
+
 // Split K over 1, 2 or 4 waves so that few active experts (a single
 // token touches k of them) still put enough waves on every CU.
 hipError_t launch_ffn_decode_w4(const FfnArgs& a, uint16_t* h, hipStream_t s) {
@@ -982,11 +1034,12 @@ hipError_t launch_ffn_decode_w4(const FfnArgs& a, uint16_t* h, hipStream_t s) {
   // one K slice per wave from 1024 row tiles up (measured: E = 256, T = 1
   // down 18.4 us with four slices, 14.6 with two, 11.5 with one); gate/up
   // keeps the split (forcing one or two slices at T = 1 was slower).
-  auto ks_of = [](long long row_tiles) { return row_tiles < 2048 ? 4 : (row_tiles < 4096 ? 2 : 1); };
   const int KSg = ks_of(active * (a.f / 16));
   const long long rt_d = active * (a.d / 16);
   const int KSd = rt_d < 1024 ? ks_of(rt_d) : 1;
   const bool nt2 = P > 2LL * a.E;
+  if (a.logits && (KSg == 1 || !decode_selects_topk(a.T, a.k, a.E, a.d, a.f, a.format)))
+    return hipErrorInvalidValue;
   if (nt2) {
     if (KSg == 4) launch_gu_pair<4, 2>(a, h, P, s);
     else if (KSg == 2) launch_gu_pair<2, 2>(a, h, P, s);

@@ -59,6 +59,16 @@ struct FfnArgs {
   void* ws;
   int path;  // resolved: 1 decode, 2 prefill
   hipEvent_t ev[4];  // optional: gate/up begin/end, down begin/end
+  // Optional (decode, at most 64 pairs): the router logits [T][E]; the
+  // decode gate/up then selects the top-k and groups the pairs itself and
+  // stores them to the routing outputs below (offsets and sorted_pair above
+  // point to the same buffers as offsets_out and sorted_pair_out).
+  const float* logits = nullptr;
+  int32_t* topk_idx_out = nullptr;
+  float* topk_w_out = nullptr;
+  int32_t* offsets_out = nullptr;
+  int32_t* sorted_pair_out = nullptr;
+  int32_t* pair_pos_out = nullptr;
 };
 size_t ffn_ws_bytes(int T, int k, int E, int d, int f, int format);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
@@ -68,6 +78,9 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 bool ffn_decode_bp_applies(long long P, int E, int f);
 hipError_t launch_ffn_decode_bp(const FfnArgs& a, uint16_t* h, hipStream_t s);
 hipError_t launch_ffn_decode_w4(const FfnArgs& a, uint16_t* h, hipStream_t s);
+// The int4 decode path can take the routing from logits (FfnArgs::logits):
+// at most 64 pairs, E <= 64, with the K-split gate/up kernel.
+bool decode_selects_topk(int T, int k, int E, int d, int f, int format);
 // prefill path for int4 experts (ffn_prefill.hip); ws: its own scratch
 size_t ffn_prefill_ws_bytes(int T, int k, int E, int d, int f);
 hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStream_t s);

@@ -77,70 +77,6 @@ __device__ void select_topk(const float* __restrict__ lg, int E, int k,
   if (lane < k) w_out[lane] = my_ex / ssum;
 }
 
-// The same selection with the token's logits held in registers (E <= 512,
-// up to 8 per lane), each as a 64-bit key (order-preserving logit bits,
-// inverted index): the largest key is the largest logit, ties to the lower
-// index, exactly as better() orders them.  The wave arg-max of each round
-// is four DPP steps within rows of 16 lanes and four readlanes.  Also
-// copies the ids to idx_copy (LDS).
-template <int kCtrl>
-__device__ __forceinline__ uint64_t dpp_max(uint64_t v) {
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, kCtrl, 0xF, 0xF, false);
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, kCtrl, 0xF, 0xF, false);
-  const uint64_t o = ((uint64_t)ohi << 32) | olo;
-  return o > v ? o : v;
-}
-
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
-  v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
-  v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
-  v = dpp_max<0x141>(v);  // row_half_mirror
-  v = dpp_max<0x140>(v);  // row_mirror: every lane holds its row's maximum
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  uint64_t m = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint64_t k = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
-                       (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
-    m = k > m ? k : m;
-  }
-  return m;
-}
-
-__device__ void select_topk_reg(const float* __restrict__ lg, int E, int k,
-                                int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-                                int32_t* __restrict__ idx_copy) {
-  const int lane = threadIdx.x & 63;
-  uint64_t key[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e = 64 * i + lane;
-    key[i] = (e < E) ? (((uint64_t)ordered_f32(lg[e]) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
-  }
-  float m = 0.0f, ssum = 0.0f, my_ex = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    uint64_t loc = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) loc = key[i] > loc ? key[i] : loc;
-    const uint64_t win = wave_max_key(loc);
-    const int be = (int)~(uint32_t)win;
-    const float bv = unordered_f32((uint32_t)(win >> 32));
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (64 * i + lane == be) key[i] = 0;
-    if (j == 0) m = bv;
-    const float ex = expf(bv - m);
-    ssum += ex;  // rank order, identical in every lane
-    if (lane == j) {
-      my_ex = ex;
-      idx_out[j] = be;
-      idx_copy[j] = be;
-    }
-  }
-  if (lane < k) w_out[lane] = my_ex / ssum;
-}
-
 // The same selection for E <= 64 (one logit per lane) by ballots instead of
 // k arg-max rounds (select_topk_radix64), from the token's logits in memory.
 __device__ __forceinline__ void select_topk_64(const float* __restrict__ lg, int E, int k,

@@ -278,12 +278,13 @@ def test_layer_cfg1_decode(T):
 
 
 @pytest.mark.parametrize("case", ["dup-rows", "zero-router"])
-@pytest.mark.parametrize("T", [3, 16])
+@pytest.mark.parametrize("T", [1, 2, 3, 16])
 def test_layer_decode_router_ties(case, T):
     """Whole layer with exactly equal logits (ties to the lower index) at a
-    few tokens, where the expert-major kernels take each token's choice from
-    the logits: duplicated router rows, and a zero router whose logits are
-    tied biases."""
+    few tokens, where the decode kernels take the routing from the logits
+    (T = 1, 2: the K-split gate/up selects and groups; T = 3, 16: the
+    expert-major kernels): duplicated router rows, and a zero router whose
+    logits are tied biases."""
     note(f"layer decode ties {case} T={T}")
     cfg = custom_cfg(22, d=256, E=16, k=4, f=256, bias_sigma=1.0)
     dl, hl = DevLayer(cfg, T), HostLayer(cfg, T)
