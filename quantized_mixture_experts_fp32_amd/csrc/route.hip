@@ -1,5 +1,5 @@
 // Router: fp32 logits in the fixed lane-group order, top-k by wavefront
-// shuffles, renormalised softmax weights.
+// ballots or arg-max rounds (route_common.hpp), renormalised softmax weights.
 // ExactMoE ("Every Expert Counts ...", Abstract): the router stays BF16 and
 // the top-k routing procedure is unchanged; the fixed summation order below
 // makes the selected expert ids reproducible bit for bit:
@@ -8,11 +8,13 @@
 //   are combined with acc_l += acc_(l xor o) for o = 8, 4, 2, 1; the logit
 //   is acc_0 + bias[e].  bf16 * bf16 products are exact in fp32, so fma and
 //   multiply-then-add give the same sums.
-// Two launch shapes share that order: for few tokens, (token, 16 experts)
-// blocks write logits to the workspace and a second launch selects the
-// top-k (many blocks even for one token); for many tokens, eight tokens per
-// 256-thread block with the top-k fused.  Activation rows are staged in LDS;
-// router rows are streamed with up to 16 outstanding 16-byte loads per lane.
+// Three launch shapes share that order: for few tokens, (token, 16 experts)
+// blocks write logits to the workspace, and a second launch (or the decode
+// FFN kernels themselves) selects the top-k (many blocks even for one
+// token); one 1024-thread block per token with the top-k fused (moe_route
+// at up to 16 tokens); for many tokens, eight tokens per 256-thread block
+// with the top-k fused.  Activation rows are staged in LDS; router rows are
+// streamed with up to 16 outstanding 16-byte loads per lane.
 #include <float.h>
 
 #include "kcommon.hpp"
