@@ -150,9 +150,14 @@ struct moe_cache {
   std::vector<hipEvent_t> copy_done;  // [chunk][stream]
   std::vector<hipEvent_t> ffn_done;   // [chunk]
   hipEvent_t last = nullptr;          // end of the last step on its stream
-  int32_t* host_need = nullptr;   // pinned [2E]: need | cnt
-  int32_t* host_vmap = nullptr;   // pinned [E]
-  int32_t* host_items = nullptr;  // pinned [E][2]: (expert, slot) needing scales
+  // pinned host memory that the kernels read or write directly (device
+  // aliases beside): no copy launches on the step's critical path
+  int32_t* host_need = nullptr;   // [2E]: need | cnt, written by the need kernel
+  int32_t* host_vmap = nullptr;   // [E], read by the remap kernel
+  int32_t* host_items = nullptr;  // [E][2]: (expert, slot) needing scales, read by the gather
+  int32_t* dev_need = nullptr;
+  int32_t* dev_vmap = nullptr;
+  int32_t* dev_items = nullptr;
   std::vector<int> item_begin;    // per chunk, into host_items
   uint8_t* d_gus = nullptr;       // device-resident scale bank [E] (1/32 of
   uint8_t* d_dns = nullptr;       // the int4 bank): slots take theirs by gather
@@ -181,7 +186,7 @@ size_t a256(size_t v) { return (v + 255) & ~(size_t)255; }
 // em scratch)
 struct CacheWs {
   void* route;
-  int32_t *need_cnt, *vmap, *items, *vidx, *offsets, *sorted_pair;
+  int32_t *vidx, *offsets, *sorted_pair;
   uint8_t* bits_v;
   void* perm;
   void* ffn;
@@ -199,9 +204,6 @@ CacheWs cache_ws(const moe_cache* c, int T, int k, char* base) {
     return p;
   };
   w.route = take(moe::route_ws_bytes(T, E) + 16);
-  w.need_cnt = (int32_t*)take(sizeof(int32_t) * 2 * E);
-  w.vmap = (int32_t*)take(sizeof(int32_t) * E);
-  w.items = (int32_t*)take(sizeof(int32_t) * 2 * E);
   w.vidx = (int32_t*)take(sizeof(int32_t) * (P + 1));
   w.bits_v = (uint8_t*)take(V + 1);
   w.offsets = (int32_t*)take(sizeof(int32_t) * (V + 1));
@@ -278,6 +280,9 @@ int moe_cache_create(int E, int d, int f, int format, int slots,
   if (e == hipSuccess) e = hipHostMalloc((void**)&c->host_need, sizeof(int32_t) * 2 * E);
   if (e == hipSuccess) e = hipHostMalloc((void**)&c->host_vmap, sizeof(int32_t) * E);
   if (e == hipSuccess) e = hipHostMalloc((void**)&c->host_items, sizeof(int32_t) * 2 * E);
+  if (e == hipSuccess) e = hipHostGetDevicePointer((void**)&c->dev_need, c->host_need, 0);
+  if (e == hipSuccess) e = hipHostGetDevicePointer((void**)&c->dev_vmap, c->host_vmap, 0);
+  if (e == hipSuccess) e = hipHostGetDevicePointer((void**)&c->dev_items, c->host_items, 0);
   if (e == hipSuccess) e = hipMalloc((void**)&c->d_gus, (size_t)E * c->gus_b);
   if (e == hipSuccess) e = hipMalloc((void**)&c->d_dns, (size_t)E * c->dns_b);
   if (e == hipSuccess)
@@ -526,12 +531,9 @@ extern "C" int moe_cache_forward(moe_cache* c, const void* x_bf16, const void* w
   const long long P = (long long)T * k;
   hipError_t r = moe::launch_route(x_bf16, wr_bf16, bias, T, d, E, k, topk_idx, topk_w,
                                    w.route, s);
-  if (r == hipSuccess)
-    r = moe::launch_cache_need(topk_idx, (int)P, k, E, c->format, bits_mode, bits, w.need_cnt,
+  if (r == hipSuccess)  // straight into pinned host memory
+    r = moe::launch_cache_need(topk_idx, (int)P, k, E, c->format, bits_mode, bits, c->dev_need,
                                s);
-  if (r == hipSuccess)
-    r = hipMemcpyAsync(c->host_need, w.need_cnt, sizeof(int32_t) * 2 * E,
-                       hipMemcpyDeviceToHost, s);
   if (r == hipSuccess) r = hipStreamSynchronize(s);  // the routing decides the copies
   if (r != hipSuccess) goto hip_error;
   {
@@ -559,14 +561,11 @@ extern "C" int moe_cache_forward(moe_cache* c, const void* x_bf16, const void* w
         }
     }
     c->item_begin[nch_all] = ni;
-    r = hipMemcpyAsync(w.vmap, c->host_vmap, sizeof(int32_t) * E, hipMemcpyHostToDevice, s);
-    if (r == hipSuccess && ni > 0)
-      r = hipMemcpyAsync(w.items, c->host_items, sizeof(int32_t) * 2 * ni,
-                         hipMemcpyHostToDevice, s);
+    // the remap and gather kernels read the map and the items from pinned
+    // host memory, which the host rewrites only after the next step's sync
     const bool per_expert = bits_mode == MOE_BITS_PER_EXPERT;
-    if (r == hipSuccess)
-      r = moe::launch_cache_remap(topk_idx, (int)P, E, w.vmap, w.vidx, per_expert ? bits : nullptr,
-                                  per_expert ? w.bits_v : nullptr, s);
+    r = moe::launch_cache_remap(topk_idx, (int)P, E, c->dev_vmap, w.vidx,
+                                per_expert ? bits : nullptr, per_expert ? w.bits_v : nullptr, s);
     if (r == hipSuccess) r = enqueue_chunk_loads(c, 0);
     if (r == hipSuccess) r = wait_chunk_loads(c, 0, s);
     if (r != hipSuccess) goto hip_error;
@@ -595,7 +594,7 @@ extern "C" int moe_cache_forward(moe_cache* c, const void* x_bf16, const void* w
     };
     auto gather_scales = [&](int ci) {
       const int i0 = c->item_begin[ci], n = c->item_begin[ci + 1] - i0;
-      return moe::launch_cache_scale_gather(w.items + 2 * i0, n, c->d_gus, c->d_dns, c->s_gus,
+      return moe::launch_cache_scale_gather(c->dev_items + 2 * i0, n, c->d_gus, c->d_dns, c->s_gus,
                                             c->s_dns, c->gus_b, c->dns_b, s);
     };
     auto path_of = [&](int ci) {
