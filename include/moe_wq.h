@@ -334,13 +334,14 @@ int moe_set_ffn_events(void *gateup_begin, void *gateup_end,
  *   slot_*: device arrays of `slots` experts in the same per-expert layout.
  *   Both stay owned by the caller and must outlive the cache.  The cache
  *   itself (host state, four copy streams, their events, small pinned
- *   staging buffers, and a device copy of all E experts' scales -- 1/32 of
- *   an int4 bank -- from which slots take their scales) is allocated here
- *   and freed by moe_cache_destroy.
+ *   buffers that its kernels read and write directly, and a device copy of
+ *   all E experts' scales -- 1/32 of an int4 bank -- from which slots take
+ *   their scales) is allocated here and freed by moe_cache_destroy.
  * moe_cache_forward -- one MoE layer step (as moe_layer_forward_wq: routing,
  *   grouping, expert FFN, combine) with the experts read from the slots:
- *   routes on `stream`, copies the per-expert request back and WAITS for it
- *   (the one host synchronisation of a step), assigns slots, issues the
+ *   routes on `stream`, writes the per-expert request to pinned host memory
+ *   and WAITS for it (the one host synchronisation of a step), assigns
+ *   slots, issues the
  *   host-to-device copies of missing experts (bitplane: missing plane
  *   ranges of resident experts, whole prefixes of new ones) on the copy
  *   streams, and runs the FFN on `stream` after them.  Resident experts keep
