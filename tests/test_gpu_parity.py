@@ -307,6 +307,17 @@ def test_layer_decode_router_ties(case, T):
         assert np.array_equal(lay.topk_idx.cpu().numpy(), np.tile([12, 13, 14, 15], (T, 1)))
 
 
+@pytest.mark.parametrize("E,k,T", [(16, 1, 16), (16, 1, 2), (32, 16, 1), (64, 8, 3), (48, 5, 7)])
+def test_layer_decode_topk_shapes(E, k, T):
+    """Routing from the logits inside the decode kernels at the extremes of k
+    (1 and 16), a single token choosing half the experts, and E not a
+    multiple of 64: ids, weights and grouping bit-exact or in tolerance as
+    for every layer."""
+    note(f"layer decode top-k shapes E={E} k={k} T={T}")
+    cfg = custom_cfg(23, d=256, E=E, k=k, f=256, bias_sigma=0.5)
+    check_layer(DevLayer(cfg, T), HostLayer(cfg, T), moe.MOE_PATH_AUTO)
+
+
 @pytest.mark.parametrize("T", [1, 16])
 def test_layer_cfg1_sequential_per_expert(T):
     """One launch per expert over the same routed pairs gives the fused result."""
