@@ -1,6 +1,7 @@
 // Top-k selection of one token by one wave, shared by the routing kernels and
-// the expert-major decode gate/up kernel (which selects the top-k of its few
-// tokens itself, from the logits).
+// the decode gate/up kernels that route a few tokens themselves from the
+// logits (the expert-major one ranks its own expert per token; the K-split
+// one selects the whole batch).
 // ExactMoE ("Every Expert Counts ...", Abstract): the top-k routing procedure
 // is unchanged; experts are ranked by logit, larger first, equal logits to
 // the lower index, and the k weights are the softmax over the selected
