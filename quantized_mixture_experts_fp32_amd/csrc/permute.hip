@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void perm_scatter(
     int32_t* __restrict__ pair_pos) {
   extern __shared__ int32_t sh[];
   int32_t* base = sh;             // [E] next slot per expert
-  int32_t* wave_cnt = sh + E;     // [4][E] pairs per wave in this round
+  int32_t* wave_cnt = sh + E;     // [4][E] pairs per wave in this pass
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += kThreads) {
     base[e] = first_slot[(size_t)blockIdx.x * E + e];
