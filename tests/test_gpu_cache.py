@@ -65,6 +65,21 @@ def test_cache_int4_steps(slots):
     cache.close()
 
 
+def test_cache_few_tokens():
+    # one or two tokens per step: the small-batch decode kernels over the
+    # slots, with replacements between steps
+    cfg = custom_cfg(24, d=256, E=16, k=4, f=256, bias_sigma=0.5)
+    dl = DevLayer(cfg, 2)
+    cache = make_cache(dl, 6)
+    for step, T in enumerate([1, 2, 1, 2, 1]):
+        note(f"cache few tokens T={T} step={step}")
+        check_step(cache, cfg, T, step)
+    st = cache.stats()
+    note(f"  stats {st}")
+    assert st["steps"] == 5 and st["loads_full"] >= 4
+    cache.close()
+
+
 @pytest.mark.parametrize("slots", [6, 2])
 def test_cache_bitplane_widths_grow(slots):
     # per-pair widths drawn per step: resident experts gain missing planes
