@@ -264,6 +264,51 @@ def test_bitplane_worked_example():
             assert oracle.dequant_bp(planes, scales, b)[0, 0] == v * s, b
 
 
+def test_bitplane_tie_worked_example():
+    """Exact half quotients round to the even code (round-half-even, as the
+    quantizer of the tiny int4 workload; PagedMoE's 8-bit code)."""
+    rows = {(r[0], r[1]): r[2:] for r in read_golden("quant_worked.txt")}
+    s16 = int(rows[("bp", "tie_scale_f16")][0], 16)
+    s = oracle.f16_to_f64(s16)
+    assert s == 2.0**-7
+    ws = [float(v) for v in rows[("bp", "tie_w_over_s")]]
+    w = np.zeros((1, 128), np.float32)
+    w[0, :len(ws)] = np.array(ws) * s
+    planes, scales = oracle.quantize_bp8(w)
+    assert scales[0, 0] == s16
+    assert list(_planes_to_u(planes)[0, :len(ws)]) == [
+        int(v) for v in rows[("bp", "tie_u")]]
+
+
+def test_bitplane_nearest_code_brute_force(rng):
+    """Every stored code is the nearest of all 256 codes u to w (distance
+    |w - s(u - 128)| in exact rationals), ties to the even code; a quarter of
+    the inputs are placed on exact half steps."""
+    R, K = 8, 256
+    w = rng.normal(0, 0.14, (R, K)).astype(np.float32)
+    # exact halves: the group's max is 127 * 2^-6 (s = 2^-6) and the rest are
+    # (n + 1/2) * 2^-6 for random n, all exactly representable in fp32
+    for r in range(0, R, 2):
+        n = rng.integers(-126, 126, 128)
+        w[r, :128] = ((n + 0.5) * 2.0**-6).astype(np.float32)
+        w[r, 0] = np.float32(127 * 2.0**-6)
+    planes, scales = oracle.quantize_bp8(w)
+    u = _planes_to_u(planes)
+    s = np.repeat(scales.view(np.float16).astype(np.float64), 128, axis=1)
+    codes = np.arange(256)
+    ties = 0
+    for r in range(R):
+        for i in range(K):
+            fw, fs = Fraction(float(w[r, i])), Fraction(float(s[r, i]))
+            dist = [abs(fw - fs * (c - 128)) for c in codes]
+            m = min(dist)
+            best = [c for c, dd in zip(codes, dist) if dd == m]
+            ties += len(best) > 1
+            want = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]
+            assert u[r, i] == want, (r, i, float(w[r, i] / s[r, i]))
+    assert ties >= 4 * 127
+
+
 def test_bitplane_prefix_properties(rng):
     R, K = 16, 256
     w = rng.normal(0, 0.14, (R, K)).astype(np.float32)
@@ -438,6 +483,33 @@ def test_ffn_closed_form_large_gate(rng):
     wgu[:f, 0] = -128.0
     h3, _ = oracle.expert_ffn(x, wgu, wd)
     assert np.all(np.abs(h3) < 1e-50)
+
+
+def test_ffn_silu_moderate_gates():
+    """h = bf16(silu(g) u) with silu(g) = g / (1 + e^-g) at gates where the
+    SiLU is far from its asymptotes, computed here with Python's math.exp and
+    rounded to bf16 by an exact-rational nearest search."""
+    d, f = 128, 128
+    gates = [0.5, -0.5, 1.0, -1.0, 2.0, -2.0, 4.0, -4.0]
+    ups = [1.0, 3.0, -2.0, 0.75, 5.0, -1.5, 0.25, 7.0]
+    x = np.zeros((1, d), np.uint16)
+    x[0, 0] = 0x3F80                                # x = e_0 (bf16 1.0)
+    wgu = np.zeros((2 * f, d))
+    wgu[:f, 0] = np.resize(gates, f)
+    wgu[f:, 0] = np.resize(ups, f)
+    wd = np.zeros((d, f))
+    wd[np.arange(d), np.arange(f) % f] = 1.0        # y_m = h_m
+    wd[1, :] = 0.0
+    wd[1, 0], wd[1, 2] = 2.0, -1.0                  # y_1 = 2 h_0 - h_2
+    h, y = oracle.expert_ffn(x, wgu, wd)
+    for n in range(f):
+        g, uu = wgu[n, 0], wgu[f + n, 0]
+        silu = g / (1.0 + math.exp(-g))
+        want = float(bf16_bits_to_f64(np.array([_bf16_nearest_exact(silu * uu)],
+                                               np.uint16))[0])
+        assert h[0, n] == want, (g, uu, h[0, n], want)
+    assert y[0, 0] == h[0, 0] and y[0, 5] == h[0, 5]
+    assert y[0, 1] == 2 * h[0, 0] - h[0, 2]
 
 
 def test_ffn_h_is_bf16_and_scales_exactly(rng):
