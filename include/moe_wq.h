@@ -208,6 +208,10 @@ int moe_route_permute(const void *x_bf16, const void *wr_bf16, const float *bias
  *     the same tolerance of the CPU definition).
  * Alignment: x, codes and y_pairs 16-byte aligned; scales 4-byte aligned.
  * Requires d % 128 == 0, d <= 8192, f % 128 == 0, E <= 512, 1 <= k <= 16.
+ * On the prefill path (chosen, or taken by MOE_PATH_AUTO when T > 16 and
+ * T*k > 8E) T * max(d, f) * 2 must not exceed 2^32 - 1 bytes (e.g. T <=
+ * 262143 at d = 8192); larger batches return MOE_ERR_UNSUPPORTED before any
+ * launch and are run as several calls.
  * ------------------------------------------------------------------- */
 size_t moe_ffn_ws_bytes(int T, int k, int E, int d, int f, int format);
 int moe_expert_ffn_wq(const void *x_bf16, const int32_t *expert_offsets,

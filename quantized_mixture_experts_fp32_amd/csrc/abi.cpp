@@ -224,6 +224,13 @@ static int ffn_check(const void* x_bf16, const int32_t* expert_offsets,
   // receives at most T pairs (one per token), so T <= 16 always streams
   if (*path == MOE_PATH_AUTO)
     *path = (P <= 8LL * E || T <= 16) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+  // the prefill kernels address a gathered activation row (gate/up: one of
+  // T tokens; down: one of an expert's at most T pairs) by a 32-bit byte
+  // offset of row * K * 2 from a uniform base
+  if (*path == MOE_PATH_PREFILL && (long long)T * (d > f ? d : f) * 2 > 0xFFFFFFFFLL)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "prefill: T * max(d, f) * 2 = %lld bytes exceeds 2^32 - 1; split the batch",
+                (long long)T * (d > f ? d : f) * 2);
   return MOE_OK;
 }
 
@@ -366,7 +373,9 @@ int moe_layer_forward_wq(const void* x_bf16, const void* wr_bf16, const float* b
     // the grouping comes out of the expert-major kernels; for E <= 64 they
     // take the routing (and select the top-k) from logits that the routing
     // launch spreads over (token, 16 experts) blocks
-    if (moe::em_selects_topk(T, k, E)) {
+    // (the logits variant needs a gate/up block b for every token b < T, i.e.
+    // E * f / 128 >= T; smaller layers route first and take topk_idx)
+    if (moe::em_selects_topk(T, k, E) && (long long)E * (f / 128) >= T) {
       float* logits = (float*)ws;  // route_ws_bytes(T, E) <= rp_b
       e = moe::launch_route_logits(x_bf16, wr_bf16, bias, T, d, E, logits, s);
       if (e == hipSuccess)

@@ -167,13 +167,20 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
   // 32 w + 4 i .. + 3 (1 KiB), lane l writing position l % 16 of row
   // 32 w + 4 i + l / 16; it reads the row's logical chunk (l % 16) ^ (t % 16).
   // Rows past the tile's end read the tile's first row (never stored).
-  const char* act_b = (const char*)act;
+  // Lane offsets are 32-bit and relative to a uniform 64-bit base row: the
+  // token row 0 (gate/up: rows < T) or the tile's first slot (down: its
+  // slots are consecutive), so they stay below T * K * 2 bytes, which the
+  // host checks against 2^32.
+  const size_t row0 = kGateUp ? 0 : (size_t)tl.r0;
+  const char* act_b = (const char*)(act + row0 * (size_t)K);
+  const uint2* gsum_b = gsum + row0 * (size_t)G;
   uint32_t srcoff[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int t = wave * 32 + 4 * i + (lane >> 4);
     const int slot = tl.r0 + (t < tl.cnt ? t : 0);
-    const uint32_t src_row = kGateUp ? (uint32_t)(sorted_pair[slot] / k_top) : (uint32_t)slot;
+    const uint32_t src_row =
+        kGateUp ? (uint32_t)(sorted_pair[slot] / k_top) : (uint32_t)(slot - (int)row0);
     srcoff[i] = src_row * (uint32_t)K * 2u + 16u * (uint32_t)((lane & 15) ^ (t & 15));
   }
   // group sums: wave w stages tokens 32 w .. + 31, two dwords per token
@@ -181,7 +188,8 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
   {
     const int t = wave * 32 + (lane >> 1);
     const int slot = tl.r0 + (t < tl.cnt ? t : 0);
-    const uint32_t src_row = kGateUp ? (uint32_t)(sorted_pair[slot] / k_top) : (uint32_t)slot;
+    const uint32_t src_row =
+        kGateUp ? (uint32_t)(sorted_pair[slot] / k_top) : (uint32_t)(slot - (int)row0);
     sumoff = src_row * (uint32_t)G * 8u + 4u * (uint32_t)(lane & 1);
   }
   // (the empty asm hides the offsets' loop invariance, so that the loads
@@ -197,7 +205,7 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
                                        (__attribute__((address_space(3))) void*)(ab + (wave * 32 + 4 * i) * kRowB),
                                        16, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds((const char*)(gsum + g) + sumoff,
+    __builtin_amdgcn_global_load_lds((const char*)(gsum_b + g) + sumoff,
                                      (__attribute__((address_space(3))) void*)(sbp + wave * 32),
                                      4, 0, 0);
   };
@@ -245,13 +253,18 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
       stage(g + 1, ab_next, sb_next);
       codes_load(g + 1, qn, scn);
     }
+    // a zero-scale group contributes nothing: the row keeps its running
+    // scale and its codes are masked to 0 (which convert to the offset 192
+    // that the offset MFMA cancels), whatever codes it holds
     float r[2];
+    uint32_t qmask[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const float sg = 0.125f * f16_bits_to_f32(sc[m]);
       const bool upd = sg != 0.0f;
       r[m] = upd ? ((s_cur[m] == 0.0f) ? 0.0f : s_cur[m] / sg) : 1.0f;
       s_cur[m] = upd ? sg : s_cur[m];
+      qmask[m] = upd ? 0xFFFFFFFFu : 0u;
     }
     // offset term and rescale, token block by token block
 #pragma unroll
@@ -287,7 +300,8 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
       }
       bf16x8 bfr[2];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) bfr[m] = w4_top(q[m][s2 >> 2][s2 & 3], 0x43404340u);
+      for (int m = 0; m < 2; ++m)
+        bfr[m] = w4_top(q[m][s2 >> 2][s2 & 3] & qmask[m], 0x43404340u);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -533,20 +547,28 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
     lo_s[m] = (uint32_t)brow[m] * (uint32_t)G;
   }
 
-  const char* act_b = (const char*)act;
+  // 32-bit lane offsets from a uniform base row, as in the int4 kernel; a
+  // tile lists slots of one (expert, width) in ascending order, so its
+  // first slot is the smallest and the offsets stay below T * K * 2 bytes
+  // (an expert receives at most T pairs).
+  const size_t row0 = kGateUp ? 0 : (size_t)bslot[tl.r0];
+  const char* act_b = (const char*)(act + row0 * (size_t)K);
+  const uint2* gsum_b = gsum + row0 * (size_t)G;
   uint32_t srcoff[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int t = wave * 32 + 4 * i + (lane >> 4);
     const int slot = bslot[tl.r0 + (t < tl.cnt ? t : 0)];
-    const uint32_t src_row = kGateUp ? (uint32_t)(sorted_pair[slot] / k_top) : (uint32_t)slot;
+    const uint32_t src_row =
+        kGateUp ? (uint32_t)(sorted_pair[slot] / k_top) : (uint32_t)(slot - (int)row0);
     srcoff[i] = src_row * (uint32_t)K * 2u + 16u * (uint32_t)((lane & 15) ^ (t & 15));
   }
   uint32_t sumoff;
   {
     const int t = wave * 32 + (lane >> 1);
     const int slot = bslot[tl.r0 + (t < tl.cnt ? t : 0)];
-    const uint32_t src_row = kGateUp ? (uint32_t)(sorted_pair[slot] / k_top) : (uint32_t)slot;
+    const uint32_t src_row =
+        kGateUp ? (uint32_t)(sorted_pair[slot] / k_top) : (uint32_t)(slot - (int)row0);
     sumoff = src_row * (uint32_t)G * 8u + 4u * (uint32_t)(lane & 1);
   }
   // (empty asm: as in the int4 kernel)
@@ -560,7 +582,7 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
                                        (__attribute__((address_space(3))) void*)(ab + (wave * 32 + 4 * i) * kRowB),
                                        16, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds((const char*)(gsum + g) + sumoff,
+    __builtin_amdgcn_global_load_lds((const char*)(gsum_b + g) + sumoff,
                                      (__attribute__((address_space(3))) void*)(sbp + wave * 32),
                                      4, 0, 0);
   };
@@ -588,13 +610,21 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
         U[m][kb] = *(const uint2*)(pe + ((size_t)g * 2048 + poff[pass][kb]) + o);
       }
   };
-  // zero the absent planes of a pass (keep mask uniform per pass)
+  // A group whose scale is 0 contributes nothing (its weights s * v are 0
+  // whatever the planes hold; the quantizer stores u = 128 there, whose
+  // b-bit prefix is 2^(7-b), not 0).  The lane's row keeps its running scale
+  // for such a group, all its plane words are masked to 0, and its offset
+  // column (offZ below) cancels what zero nibbles convert to, so the group
+  // adds exactly 0 up to the fp32 rounding of that cancellation.
+  bool zrow[2] = {false, false};
+  // zero the absent planes of a pass (keep mask uniform per pass) and every
+  // plane of a zero-scale row
   auto unit_fix = [&](uint2 (&U)[2][4], uint32_t kp) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const uint32_t km = (kp >> (8 * kb)) & 0xFFu ? 0xFFFFFFFFu : 0u;
+        const uint32_t km = ((kp >> (8 * kb)) & 0xFFu) && !zrow[m] ? 0xFFFFFFFFu : 0u;
         U[m][kb].x &= km;
         U[m][kb].y &= km;
       }
@@ -634,6 +664,15 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
     offv[2] = lo3 | (lo3 << 16);
   }
   const bf16x8 offB = __builtin_bit_cast(bf16x8, offv);
+  // offset column of a zero-scale row: zero nibbles convert to 2048 + 128
+  // (two passes) or 128 (one pass) per element, cancelled in K rows 0..2
+  u32x4 offz = {0u, 0u, 0u, 0u};
+  if (hh == 0) {
+    const uint32_t z3 = f32_to_bf16_rne(nb > 4 ? -2176.0f : -128.0f);
+    offz[0] = z3 | (z3 << 16);
+    offz[1] = z3;
+  }
+  const bf16x8 offZ = __builtin_bit_cast(bf16x8, offz);
   const uint32_t D0 = nb > 4 ? 0x45004500u : 0x43004300u;
 
   const int x16 = c32 & 15;
@@ -643,12 +682,15 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
   // rescale to group g's scale and add its offset term
   auto group_head = [&](const uint2* sbp, const uint32_t (&sc)[2]) {
     float r[2];
+    bf16x8 ob[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const float sg = smul * f16_bits_to_f32(sc[m]);
       const bool upd = sg != 0.0f;
       r[m] = upd ? ((s_cur[m] == 0.0f) ? 0.0f : s_cur[m] / sg) : 1.0f;
       s_cur[m] = upd ? sg : s_cur[m];
+      zrow[m] = !upd;
+      ob[m] = upd ? offB : offZ;
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -664,7 +706,7 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
       for (int m = 0; m < 2; ++m) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[t][m][i] *= r[m];
-        acc[t][m] = mfma32(sumA, offB, acc[t][m]);
+        acc[t][m] = mfma32(sumA, ob[m], acc[t][m]);
       }
     }
   };

@@ -21,10 +21,21 @@ def custom_cfg(cid, d, E, k, f, fmt="w4", bias_sigma=None):
                              bias_sigma=bias_sigma)
 
 
-class DevLayer:
-    """Device inputs of one layer configuration for a batch of T tokens."""
+def apply_zeros(w, tid, e, zero):
+    """Zero the blocks of zero = [(tensor id, expert, r0, r1, c0, c1)] that
+    fall on matrix tid of expert e (w is that expert's [rows][K] weights, a
+    numpy array or a torch view); the same spec serves device and host."""
+    for (zt, ze, r0, r1, c0, c1) in (zero or ()):
+        if zt == tid and ze == e:
+            w[r0:r1, c0:c1] = 0
 
-    def __init__(self, cfg, T, step=0):
+
+class DevLayer:
+    """Device inputs of one layer configuration for a batch of T tokens.
+    zero: optional blocks of the fp32 expert weights set to 0 before
+    quantization (see apply_zeros)."""
+
+    def __init__(self, cfg, T, step=0, zero=None):
         self.cfg, self.T = cfg, T
         d, E, f = cfg.d, cfg.E, cfg.f
         s = stream()
@@ -40,10 +51,14 @@ class DevLayer:
         q = moe.moe_quantize_w4 if cfg.fmt == "w4" else moe.moe_quantize_bitplane8
         w = torch.empty((E, 2 * f, d), dtype=torch.float32, device=DEV)
         synth.dev_fill_weight(cfg, synth.T_W_GATE_UP, w.data_ptr(), s)
+        for e in {z[1] for z in (zero or ())}:
+            apply_zeros(w[e], synth.T_W_GATE_UP, e, zero)
         self.guc, self.gus = q(w)
         del w
         w = torch.empty((E, d, f), dtype=torch.float32, device=DEV)
         synth.dev_fill_weight(cfg, synth.T_W_DOWN, w.data_ptr(), s)
+        for e in {z[1] for z in (zero or ())}:
+            apply_zeros(w[e], synth.T_W_DOWN, e, zero)
         self.dnc, self.dns = q(w)
         del w
         torch.cuda.synchronize()
@@ -69,20 +84,41 @@ class DevLayer:
 class HostLayer:
     """The oracle's copy of the same inputs (host generator + oracle quantizer)."""
 
-    def __init__(self, cfg, T, step=0):
+    def __init__(self, cfg, T, step=0, zero=None):
         self.cfg, self.T = cfg, T
         self.x = synth.host_x(cfg, T, step=step)
         self.wr = synth.host_router(cfg)
         self.bias = synth.host_bias(cfg)
+        self.zero = zero
         self._cache = {}
 
     def expert(self, e):
         if e not in self._cache:
             c = self.cfg
             q = oracle.quantize_w4 if c.fmt == "w4" else oracle.quantize_bp8
-            self._cache[e] = (q(synth.host_expert(c, synth.T_W_GATE_UP, e)),
-                              q(synth.host_expert(c, synth.T_W_DOWN, e)))
+            m = []
+            for tid in (synth.T_W_GATE_UP, synth.T_W_DOWN):
+                w = synth.host_expert(c, tid, e)
+                apply_zeros(w, tid, e, self.zero)
+                m.append(q(w))
+            self._cache[e] = tuple(m)
         return self._cache[e]
+
+    def y_rows(self, e, tokens, bits=None):
+        """The oracle's y rows of expert e for the listed tokens (bitplane:
+        at the per-row widths `bits`), dequantizing the expert once."""
+        (gq, gs), (dq, ds) = self.expert(int(e))
+        tokens = np.asarray(tokens, np.int64)
+        if bits is None:
+            wg, wd = oracle.dequant_w4(gq, gs), oracle.dequant_w4(dq, ds)
+            return oracle.expert_ffn(self.x[tokens], wg, wd)[1]
+        bits = np.asarray(bits)
+        y = np.zeros((len(tokens), self.cfg.d))
+        for b in np.unique(bits):
+            sel = np.nonzero(bits == b)[0]
+            wg, wd = oracle.dequant_bp(gq, gs, int(b)), oracle.dequant_bp(dq, ds, int(b))
+            y[sel] = oracle.expert_ffn(self.x[tokens[sel]], wg, wd)[1]
+        return y
 
 
 # nibble i of a code word holds element W4_NIBBLE_ELEMENT[i] of its 8

@@ -124,6 +124,12 @@ def test_ffn_validation(lib):
     assert _ffn(lib, wsb=need - 1) == W
     assert _ffn(lib, ws=ctypes.c_void_p(0x10010)) == I  # ws needs 256-byte alignment
     assert _ffn(lib, T=0, x=NULL, off=NULL, sp=NULL, y=NULL, ws=NULL, wsb=0) == moe.MOE_OK
+    # the prefill kernels' 32-bit row offsets: T * max(d, f) * 2 < 2^32
+    big = dict(T=262144, k=1, E=64, d=8192, f=1024, wsb=1 << 62)
+    assert _ffn(lib, path=2, **big) == U                       # explicit prefill
+    assert _ffn(lib, path=0, **big) == U                       # AUTO picks prefill
+    assert "2^32" in err(lib)
+    assert _ffn(lib, path=2, **dict(big, d=1024, f=8192)) == U  # down: K = f
 
 
 def test_combine_and_quantize_validation(lib):

@@ -1,0 +1,121 @@
+"""GPU parity of the whole layer on inputs that exercise the degenerate cases
+of every FFN kernel: all-zero weight groups (scale 0) at the start, in the
+middle and over a whole expert, on each decode and prefill path; and layers
+with one, two or three experts at batch sizes from 2 to 1000.  Every case
+goes through the C ABI and is compared with the CPU oracle as in the other
+layer tests (integers bit-exact, floating point within rel-L2 2e-3 and
+max-abs 3e-2 rms)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import quantized_mixture_experts_fp32_amd as moe
+from layer_data import DEV, DevLayer, HostLayer, custom_cfg
+from test_gpu_parity import check_layer, note
+
+pytestmark = pytest.mark.gpu
+
+GU, DN = synth.T_W_GATE_UP, synth.T_W_DOWN
+
+
+def zero_spec(d, f):
+    """Zeroed weight blocks (tensor, expert, rows, input columns):
+    expert 0: the first 128-group of every row of all three matrices (the
+      leading group of a row has scale 0);
+    expert 1: the second 128-group of every row (a middle group when the
+      input dimension is at least 384);
+    expert 2: every weight (the expert's output is exactly 0);
+    expert 3: the first group of gate/up rows 16..47 (two whole 16-row tiles
+      of the gate matrix) and all of down rows 0..15."""
+    return [(GU, 0, 0, 2 * f, 0, 128), (DN, 0, 0, d, 0, 128),
+            (GU, 1, 0, 2 * f, 128, 256), (DN, 1, 0, d, 128, 256),
+            (GU, 2, 0, 2 * f, 0, d), (DN, 2, 0, d, 0, f),
+            (GU, 3, 16, 48, 0, 128), (DN, 3, 0, 16, 0, f)]
+
+
+# (name, format, d, E, k, f, T, path, bits mode)
+ZERO_CASES = [
+    ("expert-major decode", "w4", 384, 16, 4, 384, 16, moe.MOE_PATH_AUTO, None),
+    ("K-split decode", "w4", 384, 16, 4, 384, 1, moe.MOE_PATH_AUTO, None),
+    ("single-slice decode", "w4", 384, 128, 4, 1664, 32, moe.MOE_PATH_DECODE, None),
+    ("int4 prefill", "w4", 384, 16, 4, 384, 300, moe.MOE_PATH_PREFILL, None),
+    ("bitplane single-slice decode", "bp8", 384, 128, 4, 1664, 32, moe.MOE_PATH_DECODE,
+     "pair"),
+    ("bitplane decode, few experts", "bp8", 384, 16, 4, 384, 1, moe.MOE_PATH_DECODE, "pair"),
+    ("bitplane prefill", "bp8", 384, 16, 4, 384, 300, moe.MOE_PATH_PREFILL, "pair"),
+    ("bitplane prefill, rank rule", "bp8", 384, 16, 8, 384, 300, moe.MOE_PATH_PREFILL,
+     "rank"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ZERO_CASES)))
+def test_layer_zero_weight_groups(case):
+    name, fmt, d, E, k, f, T, path, mode = ZERO_CASES[case]
+    note(f"zero weight groups: {name} d={d} E={E} k={k} f={f} T={T}")
+    cfg = custom_cfg(40 + case, d=d, E=E, k=k, f=f, fmt=fmt, bias_sigma=1.0)
+    zero = zero_spec(d, f)
+    dl, hl = DevLayer(cfg, T, zero=zero), HostLayer(cfg, T, zero=zero)
+    # experts 0..3 get a logit bias of +4 so that nearly every token picks
+    # them; the others keep a small random bias
+    bias = (np.random.default_rng(case).normal(0, 0.3, E)).astype(np.float32)
+    bias[:4] += 4.0
+    hl.bias = bias
+    dl.bias = torch.from_numpy(bias).to(DEV)
+    bm, bits = moe.MOE_BITS_NONE, None
+    if mode == "pair":
+        bm = moe.MOE_BITS_PER_PAIR
+        bits = np.random.default_rng(100 + case).integers(1, 9, T * k).astype(np.uint8)
+    elif mode == "rank":
+        bm = moe.MOE_BITS_RANK_RULE
+    lay, _ = check_layer(dl, hl, path, bm, bits)
+    off = lay.offsets.cpu().numpy()
+    cnt = np.diff(off)
+    assert (cnt[:4] > 0).all(), cnt[:4]
+    # the all-zero expert's rows are exactly zero
+    y = lay.y_pairs.cpu().numpy()
+    assert np.all(y[off[2]:off[3]] == 0.0)
+    # the zeroed groups really have scale 0 in the packed layer
+    gus = dl.gus.cpu().numpy().view(np.uint16)
+    assert np.all(gus[0][:, 0] == 0) and np.all(gus[1][:, 1] == 0) and np.all(gus[2] == 0)
+    # a weight whose scale is 0 is 0 whatever its code: random codes in the
+    # zero-scale groups of experts 0 and 1 leave every output bit unchanged
+    y0 = lay.y_pairs.clone()
+    o0 = lay.forward(dl.x, out_dtype=moe.MOE_OUT_F32, path=path).clone()
+    gen = torch.Generator(device="cpu").manual_seed(case)
+    blk = 1024 if fmt == "w4" else 2048            # bytes per 16-row tile and group
+    for codes, rows, K in ((dl.guc, 2 * f, d), (dl.dnc, d, f)):
+        for e, g in ((0, 0), (1, 1)):
+            v = codes[e].view(-1).view(rows // 16, K // 128, blk)
+            v[:, g, :] = torch.randint(0, 256, (rows // 16, blk), generator=gen,
+                                       dtype=torch.uint8).to(DEV)
+    o1 = lay.forward(dl.x, out_dtype=moe.MOE_OUT_F32, path=path).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(lay.y_pairs, y0), "codes under a zero scale changed y_pairs"
+    assert torch.equal(o1, o0)
+
+
+# (E, k) x T: layers with very few experts, every path
+SMALL_E = [(1, 1), (2, 2), (3, 2)]
+SMALL_T = [2, 5, 33, 1000]
+PATHS3 = [moe.MOE_PATH_AUTO, moe.MOE_PATH_DECODE, moe.MOE_PATH_PREFILL]
+
+
+@pytest.mark.parametrize("path", PATHS3)
+@pytest.mark.parametrize("T", SMALL_T)
+@pytest.mark.parametrize("E,k", SMALL_E)
+def test_layer_few_experts(E, k, T, path):
+    note(f"few experts: E={E} k={k} T={T} path={path}")
+    cfg = custom_cfg(60 + E, d=256, E=E, k=k, f=256, bias_sigma=0.5)
+    check_layer(DevLayer(cfg, T), HostLayer(cfg, T), path)
+
+
+@pytest.mark.parametrize("T", [2, 16])
+@pytest.mark.parametrize("E,k", [(1, 1), (2, 2), (4, 2)])
+def test_layer_entry_fewer_blocks_than_tokens(E, k, T):
+    """The layer entry's expert-major decode at f = 128: with E * f / 128
+    gate/up blocks below T there is no block per token to select the top-k
+    from the logits, so the layer routes first; results as for any layer."""
+    note(f"layer entry, E * f / 128 = {E} blocks, T={T}")
+    cfg = custom_cfg(70 + E, d=256, E=E, k=k, f=128, bias_sigma=0.5)
+    check_layer(DevLayer(cfg, T), HostLayer(cfg, T), moe.MOE_PATH_AUTO)

@@ -549,6 +549,34 @@ def test_layer_full_size_sampled(cid, T, path, bits_mode):
             o += rw[t, j] * yy[0]
         assert_close(o32[t], o, f"out t={t}")
         assert np.array_equal(o16[t], bf16_rne_bits(o32[t]))
+    if T <= 64:
+        # every pair and every token, the oracle dequantizing each expert once
+        note(f"  all {T} tokens: {int((cnt > 0).sum())} experts")
+        yref = np.zeros_like(y, dtype=np.float64)
+        for e in np.nonzero(cnt)[0]:
+            slots = np.arange(roff[e], roff[e + 1])
+            bits = None if pb is None else pb[rsp[slots]]
+            yref[slots] = hl.y_rows(e, rsp[slots] // cfg.k, bits)
+        assert_close(y, yref, "y_pairs all pairs")
+        oref = np.einsum("tj,tjd->td", rw, yref[rpp.reshape(T, cfg.k)])
+        assert_close(o32, oref, "out all tokens")
+        assert np.array_equal(o16, bf16_rne_bits(o32))
+    elif pb is None:
+        # whole 128-pair tiles of the prefill grouping: the hottest expert's
+        # first and last tile, and the last (ragged) tile of 8 more experts
+        # spread over the expert range
+        tile = 128
+        ragged = [e for e in np.nonzero(cnt % tile)[0] if e != hot]
+        pick = [ragged[i] for i in np.linspace(0, len(ragged) - 1, 8).astype(int)]
+        cases = [(hot, 0), (hot, (cnt[hot] - 1) // tile)] + [
+            (e, (cnt[e] - 1) // tile) for e in pick]
+        for e, c in cases:
+            lo = roff[e] + tile * c
+            hi = min(lo + tile, roff[e + 1])
+            slots = np.arange(lo, hi)
+            note(f"  expert {e} tile {c}: slots {lo}..{hi - 1}")
+            assert_close(y[slots], hl.y_rows(e, rsp[slots] // cfg.k),
+                         f"y tile e={e} c={c} ({hi - lo} pairs)")
 
 
 # ------------------------------------------------------ read-budget allocator
