@@ -266,6 +266,41 @@ int moe_layer_forward_wq(const void *x_bf16, const void *wr_bf16, const float *b
                          void *stream);
 
 /* ---------------------------------------------------------------------
+ * moe_layer_forward_wq_noalloc -- for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The step of moe_layer_forward_wq with the same
+ * arguments except the workspace, whose place is taken by a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES in device memory inside the library.  Outputs
+ * (bit for bit) and error codes as for moe_layer_forward_wq.
+ * Limit: moe_layer_ws_bytes(T, k, E, d, f, format) must not exceed
+ *   MOE_NOALLOC_SCRATCH_BYTES (32 MiB: every decode batch of up to 64 tokens
+ *   of the d = 4096, E = 256, f = 2048 layer fits in 16.1 MiB; a 4096-token
+ *   prefill of the OLMoE-shaped layer needs 67 MiB); a larger step returns
+ *   MOE_ERR_WORKSPACE before touching the device.
+ * Ownership: each GPU holds its own copy of the array, from the library's
+ *   load on that device until the process ends.  The first call on a device
+ *   looks up the array's address there (the device current at the call);
+ *   no call allocates or frees memory.  stream must belong to the current
+ *   device.
+ * Sharing: every call on one GPU uses that GPU's array, which keeps the last
+ *   call's contents; nothing in it needs to start at zero (each kernel
+ *   writes what it reads within the call).  Calls on one stream are ordered;
+ *   calls that overlap in time on one GPU (other streams or threads without
+ *   ordering between them) race on the array and give undefined results.
+ * ------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES (32 << 20)
+int moe_layer_forward_wq_noalloc(const void *x_bf16, const void *wr_bf16, const float *bias,
+                                 int T, int d, int E, int k, int f, int format,
+                                 int group_size, const uint8_t *gate_up_codes,
+                                 const uint16_t *gate_up_scales_f16,
+                                 const uint8_t *down_codes,
+                                 const uint16_t *down_scales_f16, const uint8_t *bits,
+                                 int bits_mode, int32_t *topk_idx, float *topk_w,
+                                 int32_t *expert_offsets, int32_t *sorted_pair,
+                                 int32_t *pair_pos, float *y_pairs, void *out,
+                                 int out_dtype, int path_hint, void *stream);
+
+/* ---------------------------------------------------------------------
  * moe_bp_distortion -- weight-space distortion of bitplane experts, the
  * offline half of read-budget bit allocation.
  * [DuoRate] "Two-Rate Per-Expert Precision Allocation for Mixture-of-Experts

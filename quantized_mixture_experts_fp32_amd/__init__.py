@@ -30,7 +30,8 @@ EXPORTS = ("moe_status_str", "moe_last_error", "moe_route_ws_bytes", "moe_route"
            "moe_permute", "moe_route_permute_ws_bytes", "moe_route_permute",
            "moe_ffn_ws_bytes", "moe_expert_ffn_wq", "moe_combine",
            "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events",
-           "moe_layer_ws_bytes", "moe_layer_forward_wq", "moe_bp_distortion_ws_bytes",
+           "moe_layer_ws_bytes", "moe_layer_forward_wq", "moe_layer_forward_wq_noalloc",
+           "moe_bp_distortion_ws_bytes",
            "moe_bp_distortion", "moe_allocate_bits", "moe_cache_create", "moe_cache_destroy",
            "moe_cache_ws_bytes", "moe_cache_forward", "moe_cache_stats", "moe_cache_slots",
            "moe_cache_reset", "moe_cache_plan")
@@ -78,6 +79,9 @@ def load_library():
     lib.moe_layer_forward_wq.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                          vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
                                          vp, i32, vp, sz, i32, vp]
+    lib.moe_layer_forward_wq_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                 i32, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                                 vp, vp, vp, vp, i32, i32, vp]
     lib.moe_bp_distortion_ws_bytes.argtypes = [i32, i32, i32]
     lib.moe_bp_distortion_ws_bytes.restype = sz
     lib.moe_bp_distortion.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
@@ -95,7 +99,8 @@ def load_library():
     lib.moe_cache_plan.argtypes = [i32, i32, i32, vp, vp, vp, ctypes.c_int64, vp, vp, vp, i32,
                                    vp, vp, i32, vp, vp]
     for name in ("moe_route", "moe_permute", "moe_route_permute", "moe_expert_ffn_wq",
-                 "moe_combine", "moe_layer_forward_wq", "moe_bp_distortion",
+                 "moe_combine", "moe_layer_forward_wq", "moe_layer_forward_wq_noalloc",
+                 "moe_bp_distortion",
                  "moe_allocate_bits", "moe_cache_create", "moe_cache_forward",
                  "moe_cache_stats", "moe_cache_slots", "moe_cache_reset", "moe_cache_plan",
                  "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events"):
@@ -294,6 +299,26 @@ def moe_layer_forward(x, wr, bias, k, f, gate_up_codes, gate_up_scales, down_cod
         _ptr(topk_idx), _ptr(topk_w), _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos),
         _ptr(y_pairs), _ptr(out), out_dtype, _ptr(ws), ws.numel() * ws.element_size(),
         path, _stream(stream)))
+    return out
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def moe_layer_forward_noalloc(x, wr, bias, k, f, gate_up_codes, gate_up_scales, down_codes,
+                              down_scales, topk_idx, topk_w, offsets, sorted_pair, pair_pos,
+                              y_pairs, out, fmt=MOE_FMT_W4_SYM, bits=None,
+                              bits_mode=MOE_BITS_NONE, out_dtype=MOE_OUT_F32,
+                              path=MOE_PATH_AUTO, stream=None):
+    """moe_layer_forward_wq_noalloc: the layer step with the library's fixed
+    device scratch in place of a workspace (nothing is allocated)."""
+    T, d = x.shape
+    E = wr.shape[0]
+    _check("moe_layer_forward_wq_noalloc", load_library().moe_layer_forward_wq_noalloc(
+        _ptr(x), _ptr(wr), _ptr(bias), T, d, E, k, f, fmt, MOE_GROUP, _ptr(gate_up_codes),
+        _ptr(gate_up_scales), _ptr(down_codes), _ptr(down_scales), _ptr(bits), bits_mode,
+        _ptr(topk_idx), _ptr(topk_w), _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos),
+        _ptr(y_pairs), _ptr(out), out_dtype, path, _stream(stream)))
     return out
 
 

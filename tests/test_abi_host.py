@@ -214,3 +214,15 @@ def test_bp_untile_matches_header_formula():
                 g, j = divmod(jj, 16)
                 off = ((n // 16) * (K // 128) + g) * 2048 + 256 * p + 16 * (n % 16) + j
                 assert pm[p, n, jj] == tiled[off], (p, n, jj)
+
+
+def test_noalloc_entry_refuses_oversize_on_host(lib):
+    """The allocation-free layer entry refuses a step whose workspace
+    exceeds its fixed scratch before touching the device (no GPU here)."""
+    T, k, E, d, f = 4096, 8, 64, 2048, 1024
+    assert lib.moe_layer_ws_bytes(T, k, E, d, f, 0) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    rc = lib.moe_layer_forward_wq_noalloc(FAKE, FAKE, NULL, T, d, E, k, f, 0, 128, FAKE,
+                                          FAKE, FAKE, FAKE, NULL, 0, FAKE, FAKE, FAKE,
+                                          FAKE, FAKE, FAKE, FAKE, 1, 0, NULL)
+    assert rc == moe.MOE_ERR_WORKSPACE
+    assert "scratch" in err(lib)
