@@ -4,13 +4,15 @@
 One step = one forward pass of the whole layer (route -> group pairs by
 expert -> expert SwiGLU FFN with in-kernel dequantization -> combine) over
 one batch of synthetic tokens, through the C ABI, with inputs and weights
-already resident in HBM.  The headline workload is the OLMoE-shaped decode
-layer (d=2048, E=64, top-8, f=1024, symmetric int4 group-128) at T=16.
+already resident in HBM.  The headline workload is the largest layer: d=4096,
+E=256 experts, top-8, f=2048, symmetric int4 group-128 experts (3.3 GB
+packed), router bias N(0,1), decoding T=64 tokens per step; its 8192-token
+prefill is reported beside it against the bf16 MFMA peak.
 
-Honest HBM numbers: the decode weight set (207.6 MB) fits the 256 MB
-Infinity Cache, so the timed loop rotates over several device copies of the
-packed experts (>= 1 GiB touched between reuses of a copy) and over 16
-distinct token batches.
+Honest HBM numbers: weight sets that fit the 256 MB Infinity Cache (the
+OLMoE-shaped layers, 207.6 MB) are rotated over several device copies of
+the packed experts (>= 1 GiB touched between reuses of a copy); every
+workload rotates over distinct token batches.
 
 Prints ONE JSON line (rank 0).  --gpus must be 1: this build runs on one GPU.
 """
@@ -40,8 +42,8 @@ def parse_args():
     ap.add_argument("--only-headline", action="store_true",
                     help="skip the secondary workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16,
+                    help="tokens of the headline batch in the one-thread oracle run")
     ap.add_argument("--workloads", default="",
                     help="comma list of name filters (spaces as _) for secondary workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -455,45 +457,59 @@ def run_workload(wl, warmup, hip, torch, np, synth, moe):
     return rec
 
 
-def cpu_baseline(target_s, np, synth, oracle):
-    """The oracle as it stands on the host cores: whole layer for batches of
-    the headline workload until about target_s seconds of work."""
-    cfg = synth.CONFIGS[1]
-    T = 16
-    wr = synth.host_router(cfg)
+def _omp_threads(n):
+    """Set the OpenMP thread count of the oracle library (libgomp)."""
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
+def cpu_baseline(np, synth, oracle, cid=4, T=64, sample_1t=16):
+    """The oracle as it stands on the host cores, on the headline batch: the
+    whole layer (route, grouping, per-expert dequantization and SwiGLU FFN in
+    fp64, combine), timed twice -- on one thread over the first `sample_1t`
+    tokens of the batch, and on every host core over the whole batch.
+    Expert quantization is offline on both sides and excluded (done up front
+    by a thread pool)."""
+    from concurrent.futures import ThreadPoolExecutor
+    cfg = synth.CONFIGS[cid]
+    x = synth.host_x(cfg, T, step=0)
+    wr, bias = synth.host_router(cfg), synth.host_bias(cfg)
+    _, idx, _ = oracle.route(x, wr, bias, cfg.k)
+    cores = len(os.sched_getaffinity(0))
     cache = {}
 
-    def expert(e):
-        if e not in cache:
-            cache[e] = (oracle.quantize_w4(synth.host_expert(cfg, synth.T_W_GATE_UP, e)),
-                        oracle.quantize_w4(synth.host_expert(cfg, synth.T_W_DOWN, e)))
-        return cache[e]
+    def pack(e):
+        _omp_threads(1)  # this pool thread's own OpenMP setting
+        return (oracle.quantize_w4(synth.host_expert(cfg, synth.T_W_GATE_UP, e)),
+                oracle.quantize_w4(synth.host_expert(cfg, synth.T_W_DOWN, e)))
 
-    xs = [synth.host_x(cfg, T, step=i) for i in range(64)]
-    # experts are packed offline on the GPU side too: quantize outside timing
-    for x in xs[:4]:
-        _, idx, _ = oracle.route(x, wr, None, cfg.k)
-        for e in np.unique(idx):
-            expert(int(e))
-    done, t0 = 0, time.perf_counter()
-    while True:
-        x = xs[done % 4]
-        oracle.layer(x, wr, None, cfg.k, cfg.f, expert)
-        done += 1
+    experts = [int(e) for e in np.unique(idx)]
+    t0 = time.perf_counter()
+    _omp_threads(1)
+    with ThreadPoolExecutor(cores) as pool:
+        for e, q in zip(experts, pool.map(pack, experts)):
+            cache[e] = q
+    prep = time.perf_counter() - t0
+    runs = []
+    for n, threads in ((sample_1t, 1), (T, cores)):
+        _omp_threads(threads)
+        t0 = time.perf_counter()
+        oracle.layer(x[:n], wr, bias, cfg.k, cfg.f, cache.__getitem__)
         el = time.perf_counter() - t0
-        if el >= target_s or done >= 64:
-            break
-    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-    return {"value": round(done * T / el, 3), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{done} batches of the headline workload (olmoe-decode-w4, "
-                      f"T={T} tokens = {T * cfg.k} pairs each): the whole layer in "
-                      f"the fp64 oracle (route, grouping, per-expert dequantization "
-                      f"and SwiGLU FFN, combine) with OpenMP over rows; expert "
-                      f"quantization excluded; {el:.1f} s"}
+        runs.append({"value": round(n / el, 3), "unit": "tokens/s", "cores": threads,
+                     "kind": "oracle",
+                     "sample": f"{n} of the {T} tokens of one headline batch ({cfg.name}, "
+                               f"{n * cfg.k} pairs): the whole layer in the fp64 oracle "
+                               f"(route, grouping, per-expert dequantization and SwiGLU "
+                               f"FFN, combine), {threads} OpenMP thread(s), {el:.2f} s; "
+                               f"measured on the sample itself, no extrapolation; "
+                               f"expert quantization excluded ({len(experts)} experts "
+                               f"packed up front in {prep:.1f} s)"})
+    _omp_threads(cores)
+    best = runs[1]
+    return dict(best, single_thread=runs[0])
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_w4_em_olmoe_T16.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gateup_w4_decode_e256_T64.txt")
 DECODE_SRC = os.path.join(ROOT, "quantized_mixture_experts_fp32_amd", "csrc", "ffn_decode.hip")
 
 
@@ -541,8 +557,11 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    head = Workload("olmoe-decode-w4 T=16", 1, 16, args.steps)
+    head = Workload("e256-w4 T=64", 4, 64, args.steps)
     secondary = [
+        Workload("e256-w4 T=8192", 4, 8192, max(3, args.steps // 40)),
+        Workload("e256-w4 T=1", 4, 1, args.steps),
+        Workload("olmoe-decode-w4 T=16", 1, 16, args.steps),
         Workload("olmoe-decode-w4 T=1", 1, 1, args.steps),
         Workload("olmoe-decode-w4 T=4", 1, 4, args.steps),
         Workload("olmoe-decode-w4 T=8", 1, 8, args.steps),
@@ -563,10 +582,7 @@ def main():
                  slots=64),
         Workload("olmoe-bitplane-cache16 T=16", 3, 16, max(20, args.steps // 4), mode="cache",
                  slots=16),
-        Workload("e256-w4 T=1", 4, 1, args.steps),
-        Workload("e256-w4 T=64", 4, 64, args.steps),
         Workload("olmoe-prefill-w4 T=4096", 2, 4096, max(5, args.steps // 10)),
-        Workload("e256-w4 T=8192", 4, 8192, max(3, args.steps // 40)),
     ]
     if args.workloads:
         keys = args.workloads.split(",")
@@ -578,43 +594,63 @@ def main():
         for wl in secondary:
             run = run_cache_workload if wl.mode == "cache" else run_workload
             others.append(run(wl, max(2, args.warmup // 4), hip, torch, np, synth, moe))
+    fused = {(r["config"], r["T"]): r for r in [head_rec] + others
+             if r.get("mode", "fused") == "fused" and "gateup_us" in r}
     for r in others:
-        if r.get("mode", "fused") != "fused" and r["T"] == head.T and r["config"] == \
-                head_rec["config"]:
-            r["fused_ms_per_step"] = head_rec["ms_per_step"]
-            r["fused_speedup"] = round(r["ms_per_step"] / head_rec["ms_per_step"], 3)
-            fk = head_rec["gateup_us"] + head_rec["down_us"]
+        f_rec = fused.get((r["config"], r["T"]))
+        if r.get("mode", "fused") in ("seq-active", "seq-all") and f_rec:
+            r["fused_ms_per_step"] = f_rec["ms_per_step"]
+            r["fused_speedup"] = round(r["ms_per_step"] / f_rec["ms_per_step"], 3)
+            fk = f_rec["gateup_us"] + f_rec["down_us"]
             r["fused_ffn_kernel_us_per_step"] = round(fk, 2)
             r["fused_kernel_speedup"] = round(r["ffn_kernel_us_per_step"] / fk, 3)
     base = None
     if not args.no_cpu_baseline:
         import oracle
-        base = cpu_baseline(args.cpu_seconds, np, synth, oracle)
+        base = cpu_baseline(np, synth, oracle, sample_1t=args.cpu_sample_tokens)
 
     achieved = head_rec["gateup_GBps"]
+    ffn_bytes = head_rec["gateup_bytes_avg"] + head_rec["down_bytes_avg"]
     line = {
         "metric": METRIC, "value": head_rec["tokens_per_s"], "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": head_rec["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "olmoe-decode-w4: one MoE layer, d=2048, E=64, top-8, "
-                               "f=1024, SwiGLU, symmetric int4 group-128 experts, "
-                               "T=16 tokens per step",
-                   "T": 16, "d": 2048, "E": 64, "k": 8, "f": 1024,
+        "config": {"workload": "e256-w4: one MoE layer, d=4096, E=256 experts, top-8, "
+                               "f=2048, SwiGLU, symmetric int4 group-128 experts (3.3 GB "
+                               "packed), router bias N(0,1), T=64 decode tokens per step",
+                   "T": 64, "d": 4096, "E": 256, "k": 8, "f": 2048,
                    "weights": "int4-g128 codes + fp16 scales",
                    "weight_copies_rotated": head_rec["weight_copies"],
-                   "token_batches_rotated": 16},
-        "roofline": {"bound": "hbm", "kernel": "expert gate/up (gateup_w4_em, moe_layer_forward_wq)",
+                   "token_batches_rotated": 16,
+                   "active_experts_avg": head_rec["active_experts_avg"]},
+        "roofline": {"bound": "hbm",
+                     "kernel": "expert gate/up, decode (gateup_w4_decode_lds)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic(),
                      "algorithmic_bytes_per_launch": head_rec["gateup_bytes_avg"],
-                     "avg_launch_us": head_rec["gateup_us"]},
+                     "avg_launch_us": head_rec["gateup_us"],
+                     "ffn": {"kernels": "gate/up + down",
+                             "algorithmic_bytes_per_step": ffn_bytes,
+                             "us_per_step": round(head_rec["gateup_us"] + head_rec["down_us"], 3),
+                             "achieved": head_rec["ffn_GBps"],
+                             "frac": round(head_rec["ffn_GBps"] / HBM_PEAK_GBS, 4)}},
         "cpu_baseline": base,
         "headline_detail": head_rec,
         "workloads": others,
     }
+    pf = fused.get(("e256-w4", 8192))
+    if pf:
+        line["roofline_prefill"] = {
+            "bound": "mfma", "workload": "e256-w4 T=8192 (65,536 pairs)",
+            "kernel": "expert gate/up, prefill (pf_w4_kernel<true>)",
+            "achieved": pf["gateup_TFLOPs"], "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+            "frac": round(pf["gateup_TFLOPs"] / MFMA_BF16_PEAK_TFS, 4),
+            "algorithmic_flops_per_launch": 4.0 * 8192 * 8 * 4096 * 2048,
+            "avg_launch_us": pf["gateup_us"],
+            "ffn_mfma_util_pct": pf["ffn_mfma_util_pct"]}
     print(json.dumps(line), flush=True)
 
 

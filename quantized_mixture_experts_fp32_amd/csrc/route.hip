@@ -349,12 +349,17 @@ hipError_t launch_route_permute(const void* x, const void* wr, const float* bias
                                 int d, int E, int k, int32_t* topk_idx, float* topk_w,
                                 int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                                 void* ws, hipStream_t s) {
-  if (T > 0 && T <= kSmallT) {
+  // One block selecting every token's top-k and grouping the pairs saves a
+  // launch, but past 64 pairs with more than 64 experts its sequential
+  // selections cost more than the launch (measured at E = 256, T = 64:
+  // 31 us against 6.9 us for one wave per token over 16 blocks plus 3.8 us
+  // for a separate one-block grouping); those shapes route, then permute.
+  const int P = T * k;
+  if (T > 0 && T <= kSmallT && (P <= 64 || E <= 64)) {
     float* logits = (float*)ws;
     const int neb = (E + 15) / 16;
     hipLaunchKernelGGL(route_logits_small, dim3(T * neb), dim3(256), sizeof(uint16_t) * d, s,
                        (const uint16_t*)x, (const uint16_t*)wr, bias, T, d, E, logits);
-    const int P = T * k;
     const size_t lds = sizeof(int32_t) * ((P + 3) & ~3) + permute_block_lds_bytes(E);
     const int threads = P <= 64 ? 64 * (T < 16 ? T : 16) : 1024;
     hipLaunchKernelGGL(route_topk_permute, dim3(1), dim3(threads), lds, s, logits, T, E, k,

@@ -150,6 +150,43 @@ def test_route_ties_and_shapes():
         np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("E,k", [(65, 8), (128, 1), (200, 3), (256, 8), (300, 8),
+                                 (512, 8), (256, 16)])
+@pytest.mark.parametrize("T", [17, 64, 333])
+def test_route_many_experts_ties(E, k, T):
+    """More than 64 experts and 17..512 tokens (one wave per token selects
+    over all E logits, then the pairs are grouped): exact logit ties from
+    duplicated router rows and tied biases, and a token whose logits are the
+    biases alone, must resolve to the lower index; routing and grouping
+    bit-exact."""
+    note(f"route many experts E={E} k={k} T={T}")
+    rng = np.random.default_rng(E * 7 + k + T)
+    d = 256
+    wr = (rng.normal(0, 1 / 16, (E, d)) * 256).round() / 256
+    for dst, src in ((E - 1, 0), (64 % E, 0), (E // 2, 3), (min(E - 1, 130), 3), (5, 4)):
+        wr[dst] = wr[src]
+    bias = np.zeros(E, np.float32)
+    bias[::7] = 0.25                                     # tied biases in every group
+    x = np.round(rng.normal(0, 1, (T, d)) * 64) / 64
+    x[T // 2] = 0.0                                     # this token: logits = bias
+    xb = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    wb = (np.asarray(wr, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    bt = torch.from_numpy(bias).to(DEV)
+    _, ridx, rw = oracle.route(xb, wb, bias, k)
+    idx, w = moe.moe_route(t_i16(xb), t_i16(wb), bt, k)
+    idx2, w2, off, sp, pp = moe.moe_route_permute(t_i16(xb), t_i16(wb), bt, k)
+    torch.cuda.synchronize()
+    for a, b in ((idx, w), (idx2, w2)):
+        assert np.array_equal(a.cpu().numpy(), ridx)
+        np.testing.assert_allclose(b.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
+    roff, rsp, rpp = oracle.permute(ridx, E)
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(sp.cpu().numpy(), rsp)
+    assert np.array_equal(pp.cpu().numpy(), rpp)
+    # the all-tied token picks the lowest-index experts of bias 0.25
+    assert list(ridx[T // 2]) == list(np.nonzero(bias == 0.25)[0][:k]) or k > (bias > 0).sum()
+
+
 # ---------------------------------------------------------------- permute
 @pytest.mark.parametrize("T,k,E,mode", [(0, 8, 16, "rand"), (1, 1, 1, "rand"),
                                         (33, 3, 5, "rand"), (1000, 8, 64, "one"),
