@@ -385,18 +385,22 @@ void down_w4_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
 // refills every slot in its steady state without a branch, so the compiler's
 // wait before each use counts exactly the loads issued after it: kDQ groups
 // stay in flight across the loop edge.
-template <int kDQ, int kWaves, int kSC>
+// kRT row tiles per wave and matrix: the item covers 64 kRT features, wave w
+// those at 16 (w + 4 r), r < kRT, of its gate and up matrices, all fed by
+// one staging of the tile's activations per 128-group.
+template <int kDQ, int kWaves, int kSC, int kRT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
 void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
                           const int32_t* __restrict__ sorted_pair, int E, int k, int P,
                           int d, int f, const uint8_t* __restrict__ codes,
                           const uint16_t* __restrict__ scales, uint16_t* __restrict__ h) {
   extern __shared__ int32_t lds_i[];
-  const int G = d >> 7, RG = f / 64;
+  const int G = d >> 7, RG = f / (64 * kRT);
   int32_t* off_lds = lds_i;
   int32_t* sp_lds = lds_i + ((E + 1 + 3) & ~3);
-  float* sc_lds = (float*)(sp_lds + ((min(P, kPairsInLds) + 3) & ~3));  // [2][G][64]
-  uint16_t* xs = (uint16_t*)(sc_lds + 2 * G * 64);                      // [2][16][kXRow]
+  // [gate, up][kRT][G][64]
+  float* sc_lds = (float*)(sp_lds + ((min(P, kPairsInLds) + 3) & ~3));
+  uint16_t* xs = (uint16_t*)(sc_lds + 2 * kRT * G * 64);  // [2][16][kXRow]
   const int np = stage_routing(offsets, sorted_pair, E, P, off_lds, sp_lds);
   __syncthreads();
 
@@ -404,11 +408,12 @@ void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restr
   const int col = lane & 15, kq = lane >> 4;
   const int st_tok = tid >> 4, st_pc = tid & 15;  // staged row and 16-byte piece
   const bf16x8 negoff = bf16_splat(kBf16NegOff);
+  const size_t rt_stride = (size_t)64 * (d >> 1);  // 64 rows apart
 
   for (int w = blockIdx.x;; w += gridDim.x) {
     TileInfo tl;
     if (!find_tile(off_lds, E, 16, w / RG, tl)) break;
-    const int nb = (w % RG) * 64, n0 = nb + 16 * wave;
+    const int nb = (w % RG) * 64 * kRT;
     const size_t erow = (size_t)tl.e * 2 * f;
     // rows past the tile stage a copy of its first row (never stored)
     const int sj = tl.r0 + (st_tok < tl.cnt ? st_tok : 0);
@@ -417,29 +422,44 @@ void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restr
     // for it after those loads would also wait for them
     asm volatile("" ::"v"(sp) : "memory");
     const uint16_t* xsrc = x + (size_t)(sp / k) * d + 8 * st_pc;
-    const uint8_t* cg = codes + (erow + n0) * (size_t)(d >> 1) + 64 * col + 16 * kq;
+    const uint8_t* cg = codes + (erow + nb + 16 * wave) * (size_t)(d >> 1) + 64 * col + 16 * kq;
     const uint8_t* cu = cg + (size_t)f * (d >> 1);
 
-    u32x4 qg[kDQ], qu[kDQ], xv[kDQ];
+    u32x4 qg[kDQ][kRT], qu[kDQ][kRT], xv[kDQ];
     auto load = [&](int g, int i) {
       xv[i] = *(const u32x4*)(xsrc + 128 * g);
-      qg[i] = *(const u32x4*)(cg + kTileGroupBytes * g);
-      qu[i] = *(const u32x4*)(cu + kTileGroupBytes * g);
+#pragma unroll
+      for (int r = 0; r < kRT; ++r) {
+        qg[i][r] = *(const u32x4*)(cg + r * rt_stride + kTileGroupBytes * g);
+        qu[i][r] = *(const u32x4*)(cu + r * rt_stride + kTileGroupBytes * g);
+      }
     };
     // the previous item's last barrier precedes these LDS writes; the first
-    // barrier of the group loop orders them before any read
-    ScaleStage<2, kSC ? kSC : 1> sst;
-    if (kSC) sst.fetch(scales + (erow + nb) * G, (size_t)f, G);
+    // barrier of the group loop orders them before any read.  Scale rows of
+    // one matrix are consecutive: kRT "matrices" of 64 rows each.
+    ScaleStage<kRT, kSC ? kSC : 1> ssg, ssu;
+    if (kSC) {
+      ssg.fetch(scales + (erow + nb) * G, 64, G);
+      ssu.fetch(scales + (erow + f + nb) * G, 64, G);
+    }
     __builtin_amdgcn_sched_barrier(0);  // scales first: their wait skips the codes
 #pragma unroll
     for (int i = 0; i < kDQ; ++i) load(i < G ? i : G - 1, i);
     __builtin_amdgcn_sched_barrier(0);
-    if (kSC)
-      sst.store(G, sc_lds);
-    else
-      stage_scales_rows64<2>(scales + (erow + nb) * G, (size_t)f, G, sc_lds);
+    if (kSC) {
+      ssg.store(G, sc_lds);
+      ssu.store(G, sc_lds + kRT * G * 64);
+    } else {
+      for (int r = 0; r < kRT; ++r) {
+        stage_scales_rows64<1>(scales + (erow + nb + 64 * r) * G, 0, G, sc_lds + r * G * 64);
+        stage_scales_rows64<1>(scales + (erow + f + nb + 64 * r) * G, 0, G,
+                               sc_lds + (kRT + r) * G * 64);
+      }
+    }
 
-    f32x4 tg = {0, 0, 0, 0}, tu = {0, 0, 0, 0};
+    f32x4 tg[kRT], tu[kRT];
+#pragma unroll
+    for (int r = 0; r < kRT; ++r) tg[r] = tu[r] = f32x4{0, 0, 0, 0};
     auto step = [&](int gi, int i) {
       // slot gi & 1 was last read in step gi - 2, before the barrier of step gi - 1
       uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
@@ -448,13 +468,17 @@ void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restr
       bf16x8 xp[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) xp[j] = *(const bf16x8*)(slot + col * kXRow + 32 * kq + 8 * j);
-      const f32x4 sg = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
-      const f32x4 su = *(const f32x4*)(sc_lds + (G + gi) * 64 + 16 * wave + 4 * kq);
       f32x4 seed = {0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < 4; ++j) seed = mfma16(negoff, xp[j], seed);
-      tile_group(xp, seed, qg[i], sg, tg);
-      tile_group(xp, seed, qu[i], su, tu);
+#pragma unroll
+      for (int r = 0; r < kRT; ++r) {
+        const f32x4 sg = *(const f32x4*)(sc_lds + (r * G + gi) * 64 + 16 * wave + 4 * kq);
+        const f32x4 su =
+            *(const f32x4*)(sc_lds + ((kRT + r) * G + gi) * 64 + 16 * wave + 4 * kq);
+        tile_group(xp, seed, qg[i][r], sg, tg[r]);
+        tile_group(xp, seed, qu[i][r], su, tu[r]);
+      }
     };
     // steady state: slot i is refilled right after its codes are used (the
     // new loads reuse its registers: no copy, hence no wait, at the edge)
@@ -480,28 +504,36 @@ void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restr
       if (g + kDQ + i < G) step(g + kDQ + i, i);
 
     if (col < tl.cnt) {
-      uint32_t hb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_rne(silu_f32(tg[i]) * tu[i]);
-      uint2 pk;
-      pk.x = hb[0] | (hb[1] << 16);
-      pk.y = hb[2] | (hb[3] << 16);
-      *(uint2*)(h + (size_t)(tl.r0 + col) * f + n0 + 4 * kq) = pk;
+      for (int r = 0; r < kRT; ++r) {
+        uint32_t hb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_rne(silu_f32(tg[r][i]) * tu[r][i]);
+        uint2 pk;
+        pk.x = hb[0] | (hb[1] << 16);
+        pk.y = hb[2] | (hb[3] << 16);
+        *(uint2*)(h + (size_t)(tl.r0 + col) * f + nb + 16 * (wave + 4 * r) + 4 * kq) = pk;
+      }
     }
     __syncthreads();  // the next item rewrites the scales and the slots
   }
 }
 
-template <int kDQ, int kWaves, int kSC>
+// Work item = (token tile of up to 16 pairs, 64 kRT output rows): wave w
+// streams the kRT row tiles at rows 16 (w + 4 r), r < kRT, of the item, all
+// fed by one staging of the tile's h per 128-group (the h staging, its
+// barrier and the seed MFMAs are shared by kRT row tiles); kDQ groups of
+// codes per row tile stay in flight.
+template <int kDQ, int kWaves, int kSC, int kRT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
 void down_w4_decode_lds(const uint16_t* __restrict__ h, const int32_t* __restrict__ offsets,
                         int E, int d, int f, const uint8_t* __restrict__ codes,
                         const uint16_t* __restrict__ scales, float* __restrict__ y) {
   extern __shared__ int32_t lds_i[];
-  const int G = f >> 7, RG = d / 64;
+  const int G = f >> 7, RG = d / (64 * kRT);
   int32_t* off_lds = lds_i;
-  float* sc_lds = (float*)(lds_i + ((E + 1 + 3) & ~3));  // [G][64]
-  uint16_t* xs = (uint16_t*)(sc_lds + G * 64);           // [2][16][kXRow]
+  float* sc_lds = (float*)(lds_i + ((E + 1 + 3) & ~3));  // [kRT][G][64]
+  uint16_t* xs = (uint16_t*)(sc_lds + kRT * G * 64);     // [2][16][kXRow]
   for (int i = threadIdx.x; i <= E; i += blockDim.x) off_lds[i] = offsets[i];
   __syncthreads();
 
@@ -513,18 +545,23 @@ void down_w4_decode_lds(const uint16_t* __restrict__ h, const int32_t* __restric
   for (int w = blockIdx.x;; w += gridDim.x) {
     TileInfo tl;
     if (!find_tile(off_lds, E, 16, w / RG, tl)) break;
-    const int mb = (w % RG) * 64, m0 = mb + 16 * wave;
+    const int mb = (w % RG) * 64 * kRT;
     const size_t erow = (size_t)tl.e * d;
     const uint16_t* hsrc = h + (size_t)(tl.r0 + (st_tok < tl.cnt ? st_tok : 0)) * f + 8 * st_pc;
-    const uint8_t* cd = codes + (erow + m0) * (size_t)(f >> 1) + 64 * col + 16 * kq;
+    const uint8_t* cd = codes + (erow + mb + 16 * wave) * (size_t)(f >> 1) + 64 * col + 16 * kq;
+    const size_t rt_stride = (size_t)64 * (f >> 1);  // 64 rows apart
 
-    u32x4 q[kDQ], hv[kDQ];
+    u32x4 q[kDQ][kRT], hv[kDQ];
     auto load = [&](int g, int i) {
       hv[i] = *(const u32x4*)(hsrc + 128 * g);
-      q[i] = *(const u32x4*)(cd + kTileGroupBytes * g);
+#pragma unroll
+      for (int r = 0; r < kRT; ++r)
+        q[i][r] = *(const u32x4*)(cd + r * rt_stride + kTileGroupBytes * g);
     };
-    ScaleStage<1, kSC ? kSC : 1> sst;
-    if (kSC) sst.fetch(scales + (erow + mb) * G, 0, G);
+    // scale rows mb .. mb + 64 kRT - 1 are consecutive: kRT "matrices" of
+    // 64 rows, 64 rows apart
+    ScaleStage<kRT, kSC ? kSC : 1> sst;
+    if (kSC) sst.fetch(scales + (erow + mb) * G, 64, G);
     __builtin_amdgcn_sched_barrier(0);  // scales first: their wait skips the codes
 #pragma unroll
     for (int i = 0; i < kDQ; ++i) load(i < G ? i : G - 1, i);
@@ -532,9 +569,12 @@ void down_w4_decode_lds(const uint16_t* __restrict__ h, const int32_t* __restric
     if (kSC)
       sst.store(G, sc_lds);
     else
-      stage_scales_rows64<1>(scales + (erow + mb) * G, 0, G, sc_lds);
+      for (int r = 0; r < kRT; ++r)
+        stage_scales_rows64<1>(scales + (erow + mb + 64 * r) * G, 0, G, sc_lds + r * G * 64);
 
-    f32x4 acc = {0, 0, 0, 0};
+    f32x4 acc[kRT];
+#pragma unroll
+    for (int r = 0; r < kRT; ++r) acc[r] = f32x4{0, 0, 0, 0};
     auto step = [&](int gi, int i) {
       uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
       *(u32x4*)(slot + st_tok * kXRow + 8 * st_pc) = hv[i];
@@ -542,11 +582,14 @@ void down_w4_decode_lds(const uint16_t* __restrict__ h, const int32_t* __restric
       bf16x8 xp[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) xp[j] = *(const bf16x8*)(slot + col * kXRow + 32 * kq + 8 * j);
-      const f32x4 sv = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
       f32x4 seed = {0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < 4; ++j) seed = mfma16(negoff, xp[j], seed);
-      tile_group(xp, seed, q[i], sv, acc);
+#pragma unroll
+      for (int r = 0; r < kRT; ++r) {
+        const f32x4 sv = *(const f32x4*)(sc_lds + (r * G + gi) * 64 + 16 * wave + 4 * kq);
+        tile_group(xp, seed, q[i][r], sv, acc[r]);
+      }
     };
     int g = 0;
     for (; g + 2 * kDQ <= G; g += kDQ) {
@@ -568,7 +611,11 @@ void down_w4_decode_lds(const uint16_t* __restrict__ h, const int32_t* __restric
     for (int i = 0; i < kDQ; ++i)
       if (g + kDQ + i < G) step(g + kDQ + i, i);
 
-    if (col < tl.cnt) *(f32x4*)(y + (size_t)(tl.r0 + col) * d + m0 + 4 * kq) = acc;
+    if (col < tl.cnt) {
+#pragma unroll
+      for (int r = 0; r < kRT; ++r)
+        *(f32x4*)(y + (size_t)(tl.r0 + col) * d + mb + 16 * (wave + 4 * r) + 4 * kq) = acc[r];
+    }
     __syncthreads();
   }
 }
@@ -620,51 +667,68 @@ void launch_dn_pair(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
 // Code groups in flight and occupancy of the LDS-staged kernels (measured
 // on MI355X: deeper code prefetch in gate/up costs the fourth wave).
 constexpr int kGuDQ = 2, kGuWaves = 4, kDnDQ = 4, kDnWaves = 4;
+// row tiles per wave of the single-slice down kernel, and its code groups in
+// flight per row tile
+constexpr int kDnLdsRT = 2, kDnLdsDQ = 2;
+// the same for the single-slice gate/up kernel
+constexpr int kGuLdsRT = 1, kGuLdsDQ = 2;
 // row tiles per wave of the expert-major down kernel: one h staging per
 // group serves four row tiles (measured at the OLMoE decode shape: 16.7 us
 // with one, 14.5 with two, 14.1 with four, 18.5 with eight; one group of
 // codes in flight per row tile, deeper was slower)
 constexpr int kDnRT = 4;
 
-void launch_gu_lds(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
+template <int kDQ, int kRT>
+void launch_gu_lds_rt(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
   const long long mt = (P + 15) / 16 + (P < a.E ? P : a.E);
   const size_t off_b = sizeof(int32_t) * ((a.E + 1 + 3) & ~3);
   const size_t xs_b = sizeof(uint16_t) * 2 * 16 * kXRow;
   const long long cap = 256LL * 8;
-  {
-    const int G = a.d / 128;
-    const long long work = mt * (a.f / 64);
-    const int grid = (int)(work < cap ? work : cap);
-    const size_t lds = off_b + sizeof(int32_t) * ((std::min<long long>(P, kPairsInLds) + 3) & ~3) +
-                       sizeof(float) * 2 * G * 64 + xs_b;
-    const int sc = scale_chunks(2, G, a.gu_scales);
-    auto kern = sc == 1   ? gateup_w4_decode_lds<kGuDQ, kGuWaves, 1>
-                : sc == 2 ? gateup_w4_decode_lds<kGuDQ, kGuWaves, 2>
-                : sc == 4 ? gateup_w4_decode_lds<kGuDQ, kGuWaves, 4>
-                          : gateup_w4_decode_lds<kGuDQ, kGuWaves, 0>;
-    launch_k(kern, dim3(grid), dim3(256), lds, s, a.ev[0], a.ev[1], a.x, a.offsets,
-             a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes, a.gu_scales, h);
-  }
+  const int G = a.d / 128;
+  const long long work = mt * (a.f / (64 * kRT));
+  const int grid = (int)(work < cap ? work : cap);
+  const size_t lds = off_b + sizeof(int32_t) * ((std::min<long long>(P, kPairsInLds) + 3) & ~3) +
+                     sizeof(float) * 2 * kRT * G * 64 + xs_b;
+  const int sc = scale_chunks(kRT, G, a.gu_scales);
+  auto kern = sc == 1   ? gateup_w4_decode_lds<kDQ, kGuWaves, 1, kRT>
+              : sc == 2 ? gateup_w4_decode_lds<kDQ, kGuWaves, 2, kRT>
+              : sc == 4 ? gateup_w4_decode_lds<kDQ, kGuWaves, 4, kRT>
+                        : gateup_w4_decode_lds<kDQ, kGuWaves, 0, kRT>;
+  launch_k(kern, dim3(grid), dim3(256), lds, s, a.ev[0], a.ev[1], a.x, a.offsets,
+           a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes, a.gu_scales, h);
+}
+
+void launch_gu_lds(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
+  if (a.f % (64 * kGuLdsRT) == 0)
+    launch_gu_lds_rt<kGuLdsDQ, kGuLdsRT>(a, h, P, s);
+  else
+    launch_gu_lds_rt<kGuDQ, 1>(a, h, P, s);
+}
+
+template <int kDQ, int kRT>
+void launch_dn_lds_rt(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
+  const long long mt = (P + 15) / 16 + (P < a.E ? P : a.E);
+  const size_t off_b = sizeof(int32_t) * ((a.E + 1 + 3) & ~3);
+  const size_t xs_b = sizeof(uint16_t) * 2 * 16 * kXRow;
+  const long long cap = 256LL * 8;
+  const int G = a.f / 128;
+  const long long work = mt * (a.d / (64 * kRT));
+  const int grid = (int)(work < cap ? work : cap);
+  const size_t lds = off_b + sizeof(float) * kRT * G * 64 + xs_b;
+  const int sc = scale_chunks(kRT, G, a.dn_scales);
+  auto kern = sc == 1   ? down_w4_decode_lds<kDQ, kDnWaves, 1, kRT>
+              : sc == 2 ? down_w4_decode_lds<kDQ, kDnWaves, 2, kRT>
+              : sc == 4 ? down_w4_decode_lds<kDQ, kDnWaves, 4, kRT>
+                        : down_w4_decode_lds<kDQ, kDnWaves, 0, kRT>;
+  launch_k(kern, dim3(grid), dim3(256), lds, s, a.ev[2], a.ev[3], h, a.offsets, a.E, a.d,
+           a.f, a.dn_codes, a.dn_scales, a.y);
 }
 
 void launch_dn_lds(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
-  const long long mt = (P + 15) / 16 + (P < a.E ? P : a.E);
-  const size_t off_b = sizeof(int32_t) * ((a.E + 1 + 3) & ~3);
-  const size_t xs_b = sizeof(uint16_t) * 2 * 16 * kXRow;
-  const long long cap = 256LL * 8;
-  {
-    const int G = a.f / 128;
-    const long long work = mt * (a.d / 64);
-    const int grid = (int)(work < cap ? work : cap);
-    const size_t lds = off_b + sizeof(float) * G * 64 + xs_b;
-    const int sc = scale_chunks(1, G, a.dn_scales);
-    auto kern = sc == 1   ? down_w4_decode_lds<kDnDQ, kDnWaves, 1>
-                : sc == 2 ? down_w4_decode_lds<kDnDQ, kDnWaves, 2>
-                : sc == 4 ? down_w4_decode_lds<kDnDQ, kDnWaves, 4>
-                          : down_w4_decode_lds<kDnDQ, kDnWaves, 0>;
-    launch_k(kern, dim3(grid), dim3(256), lds, s, a.ev[2], a.ev[3], h, a.offsets, a.E, a.d,
-             a.f, a.dn_codes, a.dn_scales, a.y);
-  }
+  if (a.d % (64 * kDnLdsRT) == 0)
+    launch_dn_lds_rt<kDnLdsDQ, kDnLdsRT>(a, h, P, s);
+  else
+    launch_dn_lds_rt<kDnDQ, 1>(a, h, P, s);
 }
 // ------------------------------------ expert-major, at most 16 tokens
 // With at most 16 tokens every expert receives at most 16 pairs (a token's
