@@ -88,6 +88,16 @@ __global__ __launch_bounds__(256) void group_sums(const uint16_t* __restrict__ r
   out[i] = uint2{hi | (mid << 16), lo};
 }
 
+// Barrier that opens a 128-group: every wave's direct-to-LDS loads of the
+// group's tile (issued one group earlier) must have landed before any wave
+// reads it, and s_barrier does not wait for vector memory by itself, so the
+// wait is explicit (it also covers the codes loaded one group ahead, which
+// the group consumes right after the barrier anyway).
+__device__ __forceinline__ void staged_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt untouched
+  __syncthreads();
+}
+
 // ------------------------------------------------------------- GEMM core
 // One block = one tile of up to 128 grouped rows (tokens) x one feature
 // block; every wave owns all 128 tokens (four 32-token blocks) and two
@@ -248,7 +258,7 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
   auto group_step = [&](int g, const uint8_t* ab, const uint2* sbp, uint8_t* ab_next,
                         uint2* sb_next, const u32x4 (&q)[2][2], const uint32_t (&sc)[2],
                         u32x4 (&qn)[2][2], uint32_t (&scn)[2]) {
-    __syncthreads();  // group g staged; every wave is done with the other buffer
+    staged_barrier();  // group g staged; every wave is done with the other buffer
     if (g + 1 < G) {
       stage(g + 1, ab_next, sb_next);
       codes_load(g + 1, qn, scn);
@@ -760,7 +770,7 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
     scales_load(0, sc);
     stage(0, abuf0, sbuf0);
     auto gstep = [&](int g, uint8_t* ab, uint2* sbp, uint8_t* ab_next, uint2* sb_next) {
-      __syncthreads();
+      staged_barrier();
       if (g + 1 < G) stage(g + 1, ab_next, sb_next);
       unit_load(g, 1, UB);
       group_head(sbp, sc);
@@ -786,7 +796,7 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
     auto gstep = [&](int g, uint8_t* ab, uint2* sbp, uint8_t* ab_next, uint2* sb_next,
                      uint2 (&U)[2][4], const uint32_t (&sc)[2], uint2 (&Un)[2][4],
                      uint32_t (&scn)[2]) {
-      __syncthreads();
+      staged_barrier();
       if (g + 1 < G) {
         stage(g + 1, ab_next, sb_next);
         unit_load(g + 1, 0, Un);
