@@ -41,6 +41,9 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-headline", action="store_true",
                     help="skip the secondary workloads")
+    ap.add_argument("--no-headline", action="store_true",
+                    help="run only the selected secondary workloads (for profiling one "
+                         "workload; the JSON line then has no headline value)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16,
                     help="tokens of the headline batch in the one-thread oracle run")
@@ -588,6 +591,12 @@ def main():
         keys = args.workloads.split(",")
         secondary = [w for w in secondary
                      if any(k in w.name.replace(" ", "_") for k in keys)]
+    if args.no_headline:
+        for wl in secondary:
+            run = run_cache_workload if wl.mode == "cache" else run_workload
+            print(json.dumps(run(wl, max(2, args.warmup // 4), hip, torch, np, synth, moe)),
+                  flush=True)
+        return
     head_rec = run_workload(head, args.warmup, hip, torch, np, synth, moe)
     others = []
     if not args.only_headline:

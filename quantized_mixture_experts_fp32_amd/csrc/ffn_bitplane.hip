@@ -10,19 +10,24 @@
 // Arithmetic.  With bit_p the plane-p bit of u (p = 0 most significant),
 //   sum_k v_b(u_k) x_k = sum_{p<b} 2^(7-p) S_p + c_b X,
 //   S_p = sum_k bit_p(u_k) x_k,  X = sum_k x_k,  c_b = v_b(0).
-// Per 128-group every plane p < max b is one chain of four MFMAs on exact
-// bf16 operands: the A value of a weight is 1 + bit * 2^(j-4) (1.0 with the
-// bit placed in mantissa bit j + 3, one v_bitop3 from a shifted plane word),
-// where j = k mod 4 is also the MFMA of the chain the element belongs to,
-// and the staged activation is x * 2^(4-j) (a power-of-two scaling, exact;
-// the bit sits as high in the mantissa as the four shifts allow, which
-// keeps the cancelled term X' small).
-// Each chain starts from -X' (X' = sum_k x_k 2^(4 - k mod 4), four MFMAs with
-// A = -1 shared by all planes and both matrices), so it ends at S_p.  Every
-// lane owns one token column, so it weights S_p by 2^(7-p) when p is below
-// its pair's bit-width and by 0 otherwise, adds c_b X (X from four more
-// MFMAs), and the fp16 group scale multiplies the group sum in fp32.
-// Dequantized weights are never rounded.
+// Planes are taken in pairs (2c, 2c + 1): the two-bit field
+// f = 2 bit_2c + bit_2c+1 of every weight gives
+//   2^(7-2c) S_2c + 2^(6-2c) S_2c+1 = 2^(6-2c) F_c,  F_c = sum_k f_k x_k,
+// so one MFMA chain per plane pair covers both planes.  The A value of a
+// weight is 1 + f 2^(pos-7): 1.0 with the field in mantissa bits pos and
+// pos + 1 (pos = 0, 2 or 4 by the weight's place in the operand), placed by
+// one v_bitop3 per two weights from a word holding the fields of 16
+// weights (two v_bitop3 merge the two plane words into such words for the
+// even and the odd weights).  The staged activation is x 2^(7-pos) (an
+// exact power-of-two scaling), so the product is x 2^(7-pos) + f x.  Each
+// chain starts from -X' (X' = sum_k x_k 2^(7-pos_k), four MFMAs with A = -1
+// shared by all chains and both matrices), so it ends at F_c.  A pair that
+// a column's odd width splits (b = 2c + 1) uses the half chain H_c of plane
+// 2c alone (field 2 bit_2c, the same scheme with a zero second plane), which
+// gives 2 S_2c.  Every lane owns one token column: it weights F_c by
+// 2^(6-2c) when b >= 2c + 2 and H_c by 2^(6-2c) when b = 2c + 1, adds c_b X
+// (X from four more MFMAs whose A is 2^(pos-7)), and the fp16 group scale
+// multiplies the group sum in fp32.  Dequantized weights are never rounded.
 //
 // Layout (ABI header): per 16-row tile and 128-group a 2 KiB block holds
 // the 8 planes (most significant first) of 256 bytes, row r's 16 bytes at
@@ -45,37 +50,64 @@ using namespace dec;
 
 constexpr int kBlockBytes = 8 * 256;  // 8 planes of one 16-row tile, one group
 
-// Plane word (elements 32kq + s, s = 0..31) -> A operands of the 4 MFMAs
-// of a chain: MFMA j, word d holds elements s = j + 4d (low half) and
-// s + 16 (high half) as 1 + bit * 2^(j-4): bit s moves to bit j + 3.
-__device__ __forceinline__ void bp_frags(uint32_t w, bf16x8 (&a)[4]) {
-  const uint32_t C = 0x3F803F80u;  // 1.0, 1.0
-  const uint32_t sh[4] = {w << 3, w >> 1, w >> 5, w >> 9};  // 4d - 3 to the right
+// Operand slot o = 4 j + d (MFMA j, 32-bit word d of the lane's A operand)
+// holds the fields at bits 2 i, 2 i + 1 (low half) and 2 i + 16, 2 i + 17
+// (high half) of the merged word of parity o / 8, i = o % 8: the weights
+// 2 i + par (low) and 2 i + 16 + par (high) of the lane's 32-weight slice.
+// The word is shifted right by kShift[i] so that the field sits at
+// mantissa bit kPos[i] = 2 i - kShift[i].
+constexpr int kShift[8] = {0, 0, 0, 6, 6, 6, 12, 12};
+constexpr int kPos[8] = {0, 2, 4, 0, 2, 4, 0, 2};
+
+// Plane words of planes p (high) and q (low) -> the field words of the even
+// (E) and odd (O) weights of the slice (bitop3 LUT 0xE4: a & c | b & ~c).
+__device__ __forceinline__ void bp_merge(uint32_t wp, uint32_t wq, uint32_t& E, uint32_t& O) {
+  E = __builtin_amdgcn_bitop3_b32(wp << 1, wq, 0xAAAAAAAAu, 0xE4);
+  O = __builtin_amdgcn_bitop3_b32(wp, wq >> 1, 0xAAAAAAAAu, 0xE4);
+}
+// Plane p alone (a zero second plane): fields 2 bit_p.
+__device__ __forceinline__ void bp_merge_half(uint32_t wp, uint32_t& E, uint32_t& O) {
+  E = (wp << 1) & 0xAAAAAAAAu;
+  O = wp & 0xAAAAAAAAu;
+}
+
+// Field words -> the A operands of the chain's four MFMAs (LUT 0xEA:
+// (a & b) | c; c = 1.0 in both halves).
+__device__ __forceinline__ void bp_frags(uint32_t E, uint32_t O, bf16x8 (&a)[4]) {
+  const uint32_t C = 0x3F803F80u;
+  const uint32_t w[2][3] = {{E, E >> 6, E >> 12}, {O, O >> 6, O >> 12}};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t M = (1u << (j + 3)) | (1u << (19 + j));
     u32x4 r;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) r[d] = __builtin_amdgcn_bitop3_b32(sh[d], M, C, 0xEA);  // (sh & M) | C
+    for (int d = 0; d < 4; ++d) {
+      const int o = 4 * j + d, par = o >> 3, i = o & 7;
+      const uint32_t M = (3u << kPos[i]) | (3u << (kPos[i] + 16));
+      r[d] = __builtin_amdgcn_bitop3_b32(w[par][kShift[i] / 6], M, C, 0xEA);
+    }
     a[j] = __builtin_bit_cast(bf16x8, r);
   }
 }
 
-// B fragment order of one staged token row (128 bf16): element k = 32 kq + r
-// goes to slot ((kq * 4 + j) * 4 + d) * 2 + h with j = r % 4, d = (r % 16) / 4,
-// h = r / 16, scaled by 2^(4 - j).
-__device__ __forceinline__ int bp_slot(int k) {
-  const int kq = k >> 5, r = k & 31;
-  return (((kq * 4 + (r & 3)) * 4 + ((r & 15) >> 2)) << 1) + (r >> 4);
+// Place of weight k (0..127) of a group in a staged token row (the B
+// fragment order), and the exponent of its scaling 2^(7 - pos).
+__device__ __forceinline__ int bp_slot(int k, int& sh) {
+  const int kq = k >> 5, e = k & 31;
+  const int h = (e >> 4) & 1, rem = e & 15, par = rem & 1, i = rem >> 1;
+  const int o = 8 * par + i, j = o >> 2, d = o & 3;
+  sh = 7 - kPos[i];
+  return 32 * kq + 8 * j + 2 * d + h;
 }
 
-// Stage 8 consecutive activations (16 bytes at element k0, k0 % 8 == 0).
+// Stage 8 consecutive activations (16 bytes at weight k0, k0 % 8 == 0).
 __device__ __forceinline__ void bp_stage8(uint16_t* __restrict__ row, int k0, u32x4 v) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t b = (v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-    const float f = __uint_as_float(b << 16) * (float)(1 << (4 - (i & 3)));
-    row[bp_slot(k0 + i)] = (uint16_t)(__float_as_uint(f) >> 16);
+    int sh;
+    const int slot = bp_slot(k0 + i, sh);
+    const float f = __uint_as_float(b << 16) * (float)(1 << sh);
+    row[slot] = (uint16_t)(__float_as_uint(f) >> 16);
   }
 }
 
@@ -84,64 +116,181 @@ __device__ __forceinline__ bf16x8 splat2(uint32_t bits16) {
   return __builtin_bit_cast(bf16x8, u32x4{p, p, p, p});
 }
 
-// Per-lane (token column) plane weights and compensation of bit-width b.
+// Per-lane (token column) chain weights and compensation of bit-width b:
+// wF[c] for the pair chain F_c, wH[c] for the half chain H_c.
 struct ColWeights {
-  float wp[8];
+  float wF[4], wH[4];
   float cb;
 };
 
 __device__ __forceinline__ ColWeights col_weights(int b) {
   ColWeights c;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) c.wp[p] = (p < b) ? (float)(1 << (7 - p)) : 0.0f;
+  for (int q = 0; q < 4; ++q) {
+    c.wF[q] = (b >= 2 * q + 2) ? (float)(1 << (6 - 2 * q)) : 0.0f;
+    c.wH[q] = (b == 2 * q + 1) ? (float)(1 << (6 - 2 * q)) : 0.0f;
+  }
   c.cb = (b < 8) ? (float)((1 << (7 - b)) - 128) : -128.0f;
   return c;
 }
 
-// One group of one 16-row matrix tile: sum over planes p < nb of the
-// weighted chains, plus c_b X, times the group scale, into acc.
-template <int NB>
-__device__ __forceinline__ void bp_group(const bf16x8 (&xf)[4], const f32x4 seed, const f32x4 dx,
-                                         const uint32_t (&pw)[NB], const ColWeights& cw,
-                                         const f32x4 sv, f32x4& acc) {
-  f32x4 comb;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) comb[i] = cw.cb * dx[i];
-#pragma unroll
-  for (int p = 0; p < NB; ++p) {
-    bf16x8 a[4];
-    bp_frags(pw[p], a);
-    f32x4 d = seed;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) d = mfma16(a[j], xf[j], d);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) comb[i] = fmaf(cw.wp[p], d[i], comb[i]);
-    __builtin_amdgcn_sched_barrier(0);  // one plane's fragments live at a time
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = fmaf(sv[i], comb[i], acc[i]);
-}
-
-// Seeds of a group: -X' (A = -1) and X (A = 2^(j-4) in MFMA j).
+// Seeds of a group: -X' (A = -1) and X (A = 2^(pos-7) per operand slot).
 __device__ __forceinline__ void bp_seeds(const bf16x8 (&xf)[4], f32x4& seed, f32x4& dx) {
   seed = f32x4{0, 0, 0, 0};
   dx = f32x4{0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
+    u32x4 r;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t e = (uint32_t)(120 + kPos[(4 * j + d) & 7]) << 7;  // 2^(pos-7)
+      r[d] = e | (e << 16);
+    }
     seed = mfma16(splat2(0xBF80u), xf[j], seed);
-    dx = mfma16(splat2((uint32_t)(123 + j) << 7), xf[j], dx);
+    dx = mfma16(__builtin_bit_cast(bf16x8, r), xf[j], dx);
   }
 }
 
-// Bit-width of the tile's column col and the tile's largest bit-width.
+// Chain t of a group of NB planes: the pair chains F_0 .. F_(NB/2 - 1), then
+// (odd NB) the half chain of the top plane.
+template <int NB>
+__device__ __forceinline__ void bp_chain_words(const uint32_t (&pw)[NB], int t, uint32_t& E,
+                                               uint32_t& O) {
+  if (2 * t + 1 < NB)
+    bp_merge(pw[2 * t], pw[2 * t + 1], E, O);
+  else
+    bp_merge_half(pw[2 * t], E, O);
+}
+template <int NB>
+__device__ __forceinline__ float bp_chain_weight(const ColWeights& cw, int t) {
+  return (2 * t + 1 < NB) ? cw.wF[t] : cw.wH[t];
+}
+
+// Gate and up tiles of one group, software-pipelined: the chains of step t
+// (gate and up, independent) run on the matrix core while the A operands of
+// step t + 1 are built and step t - 1's sums are weighted into the column
+// totals.  Half chains of odd widths below the tile's largest (hmask bit
+// c: some column has b = 2c + 1) come first, one at a time.
+template <int NB>
+__device__ __forceinline__ void bp_group2(const bf16x8 (&xf)[4], const f32x4 seed,
+                                          const f32x4 dx, const uint32_t (&pg)[NB],
+                                          const uint32_t (&pu)[NB], const ColWeights& cw,
+                                          uint32_t hmask, const f32x4 sg, const f32x4 su,
+                                          f32x4& tg, f32x4& tu) {
+  constexpr int NC = (NB + 1) / 2;
+  f32x4 cg, cu;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cg[i] = cu[i] = cw.cb * dx[i];
+#pragma unroll
+  for (int t = 0; t < NC + NB / 2; ++t) {
+    const bool half = t >= NC;
+    const int c = half ? t - NC : t;
+    if (half && !((hmask >> c) & 1u)) continue;
+    bf16x8 ag[4], au[4];
+    uint32_t E, O;
+    if (half) bp_merge_half(pg[2 * c], E, O); else bp_chain_words<NB>(pg, c, E, O);
+    bp_frags(E, O, ag);
+    if (half) bp_merge_half(pu[2 * c], E, O); else bp_chain_words<NB>(pu, c, E, O);
+    bp_frags(E, O, au);
+    f32x4 dg = seed, du = seed;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dg = mfma16(ag[j], xf[j], dg);
+      du = mfma16(au[j], xf[j], du);
+    }
+    const float w = half ? cw.wH[c] : bp_chain_weight<NB>(cw, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      cg[i] = fmaf(w, dg[i], cg[i]);
+      cu[i] = fmaf(w, du[i], cu[i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    tg[i] = fmaf(sg[i], cg[i], tg[i]);
+    tu[i] = fmaf(su[i], cu[i], tu[i]);
+  }
+}
+
+// One matrix, pipelined as bp_group2; each chain's four MFMAs run as two
+// independent pairs (MFMAs 0, 1 from the seed and 2, 3 from zero, added
+// after), so two chains are in flight.
+template <int NB>
+__device__ __forceinline__ void bp_group1(const bf16x8 (&xf)[4], const f32x4 seed,
+                                          const f32x4 dx, const uint32_t (&pw)[NB],
+                                          const ColWeights& cw, uint32_t hmask,
+                                          const f32x4 sv, f32x4& acc) {
+  constexpr int NC = (NB + 1) / 2;
+  f32x4 comb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) comb[i] = cw.cb * dx[i];
+  bf16x8 a[4];
+#pragma unroll
+  for (int c = 0; c < NB / 2; ++c) {
+    if (!((hmask >> c) & 1u)) continue;  // tile-uniform
+    uint32_t E, O;
+    bp_merge_half(pw[2 * c], E, O);
+    bp_frags(E, O, a);
+    f32x4 d = seed;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d = mfma16(a[j], xf[j], d);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) comb[i] = fmaf(cw.wH[c], d[i], comb[i]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    uint32_t E, O;
+    bp_chain_words<NB>(pw, 0, E, O);
+    bp_frags(E, O, a);
+  }
+  f32x4 d_prev = {0, 0, 0, 0};
+#pragma unroll
+  for (int t = 0; t < NC; ++t) {
+    f32x4 d0 = seed, d1 = {0, 0, 0, 0};
+    d0 = mfma16(a[0], xf[0], d0);
+    d1 = mfma16(a[2], xf[2], d1);
+    d0 = mfma16(a[1], xf[1], d0);
+    d1 = mfma16(a[3], xf[3], d1);
+    if (t > 0) {
+      const float w = bp_chain_weight<NB>(cw, t - 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) comb[i] = fmaf(w, d_prev[i], comb[i]);
+    }
+    if (t + 1 < NC) {
+      uint32_t E, O;
+      bp_chain_words<NB>(pw, t + 1, E, O);
+      bp_frags(E, O, a);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d_prev[i] = d0[i] + d1[i];
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  {
+    const float w = bp_chain_weight<NB>(cw, NC - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) comb[i] = fmaf(w, d_prev[i], comb[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = fmaf(sv[i], comb[i], acc[i]);
+}
+
+// Bit-width of the tile's column col, the tile's largest bit-width, and the
+// half-chain mask (bit c: some column has the odd width 2c + 1 below maxb).
 __device__ __forceinline__ int tile_bits(const int32_t* __restrict__ sp, int r0, int cnt, int col,
                                          int e, int k, int mode, const uint8_t* __restrict__ bits,
-                                         int& maxb) {
+                                         int& maxb, uint32_t& hmask) {
   const int b = col < cnt ? pair_bit_width(sp[r0 + col], e, k, mode, bits) : 1;
   int m = b;
+  uint32_t odd = (col < cnt && (b & 1)) ? 1u << (b >> 1) : 0u;
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) m = max(m, __shfl_xor(m, o, kWave));
+  for (int o = 1; o < 16; o <<= 1) {
+    m = max(m, __shfl_xor(m, o, kWave));
+    odd |= (uint32_t)__shfl_xor((int)odd, o, kWave);
+  }
   maxb = __builtin_amdgcn_readfirstlane(m);
+  // the top plane of an odd largest width is a chain of its own already
+  hmask = (uint32_t)__builtin_amdgcn_readfirstlane((int)odd) & ((1u << (maxb >> 1)) - 1u);
   return b;
 }
 
@@ -160,7 +309,7 @@ __device__ __forceinline__ void bp_gu_item(const uint16_t* __restrict__ xsrc,
                                            const uint8_t* __restrict__ pu, int G,
                                            const uint16_t* __restrict__ sc_src, size_t f,
                                            float* sc_lds, uint16_t* xs, const ColWeights& cw,
-                                           f32x4& tg, f32x4& tu) {
+                                           uint32_t hmask, f32x4& tg, f32x4& tu) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, kq = lane >> 4;
   const int st_tok = tid >> 4, st_pc = tid & 15;
@@ -196,8 +345,7 @@ __device__ __forceinline__ void bp_gu_item(const uint16_t* __restrict__ xsrc,
     const f32x4 su = *(const f32x4*)(sc_lds + (G + gi) * 64 + 16 * wave + 4 * kq);
     f32x4 seed, dx;
     bp_seeds(xf, seed, dx);
-    bp_group<NB>(xf, seed, dx, wg[i], cw, sg, tg);
-    bp_group<NB>(xf, seed, dx, wu[i], cw, su, tu);
+    bp_group2<NB>(xf, seed, dx, wg[i], wu[i], cw, hmask, sg, su, tg, tu);
   };
   int g = 0;
   for (; g + 2 * kDQ <= G; g += kDQ) {
@@ -246,7 +394,8 @@ void gateup_bp_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
     if (!find_tile(off_lds, E, 16, w / RG, tl)) break;
     const int nb = (w % RG) * 64, n0 = nb + 16 * wave;
     int maxb;
-    const int b = tile_bits(spp, tl.r0, tl.cnt, col, tl.e, k, bits_mode, bits, maxb);
+    uint32_t hmask;
+    const int b = tile_bits(spp, tl.r0, tl.cnt, col, tl.e, k, bits_mode, bits, maxb, hmask);
     const ColWeights cw = col_weights(b);
     const int sj = tl.r0 + (st_tok < tl.cnt ? st_tok : 0);
     const int sp = spp[sj];
@@ -261,12 +410,12 @@ void gateup_bp_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
     switch (maxb) {  // block-uniform
 #define BP_GU_CASE(N) \
   case N:             \
-    bp_gu_item<N, kDQ, kSC>(xsrc, pg, pu, G, sc_src, (size_t)f, sc_lds, xs, cw, tg, tu); \
+    bp_gu_item<N, kDQ, kSC>(xsrc, pg, pu, G, sc_src, (size_t)f, sc_lds, xs, cw, hmask, tg, tu); \
     break;
       BP_GU_CASE(1) BP_GU_CASE(2) BP_GU_CASE(3) BP_GU_CASE(4)
       BP_GU_CASE(5) BP_GU_CASE(6) BP_GU_CASE(7)
       default:
-        bp_gu_item<8, kDQ, kSC>(xsrc, pg, pu, G, sc_src, (size_t)f, sc_lds, xs, cw, tg, tu);
+        bp_gu_item<8, kDQ, kSC>(xsrc, pg, pu, G, sc_src, (size_t)f, sc_lds, xs, cw, hmask, tg, tu);
 #undef BP_GU_CASE
     }
     if (col < tl.cnt) {
@@ -287,7 +436,8 @@ template <int NB, int kDQ, int kSC>
 __device__ __forceinline__ void bp_dn_item(const uint16_t* __restrict__ hsrc,
                                            const uint8_t* __restrict__ pd, int G,
                                            const uint16_t* __restrict__ sc_src, float* sc_lds,
-                                           uint16_t* xs, const ColWeights& cw, f32x4& acc) {
+                                           uint16_t* xs, const ColWeights& cw, uint32_t hmask,
+                                           f32x4& acc) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, kq = lane >> 4;
   const int st_tok = tid >> 4, st_pc = tid & 15;
@@ -319,7 +469,7 @@ __device__ __forceinline__ void bp_dn_item(const uint16_t* __restrict__ hsrc,
     const f32x4 sv = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
     f32x4 seed, dx;
     bp_seeds(xf, seed, dx);
-    bp_group<NB>(xf, seed, dx, wd[i], cw, sv, acc);
+    bp_group1<NB>(xf, seed, dx, wd[i], cw, hmask, sv, acc);
   };
   int g = 0;
   for (; g + 2 * kDQ <= G; g += kDQ) {
@@ -365,7 +515,8 @@ void down_bp_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
     if (!find_tile(off_lds, E, 16, w / RG, tl)) break;
     const int mb = (w % RG) * 64, m0 = mb + 16 * wave;
     int maxb;
-    const int b = tile_bits(sorted_pair, tl.r0, tl.cnt, col, tl.e, k, bits_mode, bits, maxb);
+    uint32_t hmask;
+    const int b = tile_bits(sorted_pair, tl.r0, tl.cnt, col, tl.e, k, bits_mode, bits, maxb, hmask);
     const ColWeights cw = col_weights(b);
     const uint16_t* hsrc = h + (size_t)(tl.r0 + (st_tok < tl.cnt ? st_tok : 0)) * f + 8 * st_pc;
     const size_t rd0 = (size_t)tl.e * d + m0;
@@ -375,12 +526,12 @@ void down_bp_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
     switch (maxb) {  // block-uniform
 #define BP_DN_CASE(N) \
   case N:             \
-    bp_dn_item<N, kDQ, kSC>(hsrc, pd, G, sc_src, sc_lds, xs, cw, acc); \
+    bp_dn_item<N, kDQ, kSC>(hsrc, pd, G, sc_src, sc_lds, xs, cw, hmask, acc); \
     break;
       BP_DN_CASE(1) BP_DN_CASE(2) BP_DN_CASE(3) BP_DN_CASE(4)
       BP_DN_CASE(5) BP_DN_CASE(6) BP_DN_CASE(7)
       default:
-        bp_dn_item<8, kDQ, kSC>(hsrc, pd, G, sc_src, sc_lds, xs, cw, acc);
+        bp_dn_item<8, kDQ, kSC>(hsrc, pd, G, sc_src, sc_lds, xs, cw, hmask, acc);
 #undef BP_DN_CASE
     }
     if (col < tl.cnt) *(f32x4*)(y + (size_t)(tl.r0 + col) * d + m0 + 4 * kq) = acc;
