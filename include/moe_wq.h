@@ -452,6 +452,31 @@ int moe_quantize_bitplane8(const float *w, int E, int N, int K,
                            int group_size, uint8_t *planes,
                            uint16_t *scales_f16, void *stream);
 
+/* ---------------------------------------------------------------------
+ * Canonical code layouts -> the streaming layouts above (a pure
+ * rearrangement of bits, bit-exact; scales are already [E][N][K/128] in
+ * both and need no conversion).  For codes produced elsewhere in the plain
+ * row-major forms:
+ * moe_retile_w4 ([ExactMoE] Abstract: symmetric 4-bit codes, two per byte):
+ *   in  codes_canonical u8 [E][N][K/2]: byte (e, n, j) holds element 2j in
+ *       its low nibble and 2j + 1 in its high nibble (two's complement);
+ *   out codes, E*N*K/2 bytes in the tiled int4 layout of moe_expert_ffn_wq.
+ * moe_retile_bitplane8 ([PagedMoE] abstract: one 8-bit code per weight as
+ *   bitplanes whose lower precisions are prefixes):
+ *   in  planes_canonical u8 [E][8][N][K/8]: per expert 8 plane slabs, slab p
+ *       holding bit 7 - p of u (most significant first), bit i of byte
+ *       (n, j) for element 8j + i;
+ *   out planes, E*N*K bytes in the bitplane layout of moe_expert_ffn_wq.
+ * Requires N % 16 == 0, K % 128 == 0; device pointers 16-byte aligned; the
+ * input and output must not overlap (MOE_ERR_INVALID_ARG).  Gate/up codes
+ * are converted with N = 2f (gate rows, then up rows), down codes with
+ * N = d.  Stream-ordered; allocates nothing.
+ * ------------------------------------------------------------------- */
+int moe_retile_w4(const uint8_t *codes_canonical, int E, int N, int K, uint8_t *codes,
+                  void *stream);
+int moe_retile_bitplane8(const uint8_t *planes_canonical, int E, int N, int K,
+                         uint8_t *planes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,7 +34,7 @@ EXPORTS = ("moe_status_str", "moe_last_error", "moe_route_ws_bytes", "moe_route"
            "moe_bp_distortion_ws_bytes",
            "moe_bp_distortion", "moe_allocate_bits", "moe_cache_create", "moe_cache_destroy",
            "moe_cache_ws_bytes", "moe_cache_forward", "moe_cache_stats", "moe_cache_slots",
-           "moe_cache_reset", "moe_cache_plan")
+           "moe_cache_reset", "moe_cache_plan", "moe_retile_w4", "moe_retile_bitplane8")
 
 
 class MoeError(RuntimeError):
@@ -82,6 +82,8 @@ def load_library():
     lib.moe_layer_forward_wq_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                                  i32, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                                  vp, vp, vp, vp, i32, i32, vp]
+    lib.moe_retile_w4.argtypes = [vp, i32, i32, i32, vp, vp]
+    lib.moe_retile_bitplane8.argtypes = [vp, i32, i32, i32, vp, vp]
     lib.moe_bp_distortion_ws_bytes.argtypes = [i32, i32, i32]
     lib.moe_bp_distortion_ws_bytes.restype = sz
     lib.moe_bp_distortion.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
@@ -103,7 +105,8 @@ def load_library():
                  "moe_bp_distortion",
                  "moe_allocate_bits", "moe_cache_create", "moe_cache_forward",
                  "moe_cache_stats", "moe_cache_slots", "moe_cache_reset", "moe_cache_plan",
-                 "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events"):
+                 "moe_quantize_w4", "moe_quantize_bitplane8", "moe_set_ffn_events",
+                 "moe_retile_w4", "moe_retile_bitplane8"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -388,6 +391,30 @@ def moe_quantize_w4(w, codes=None, scales=None, stream=None):
     _check("moe_quantize_w4", load_library().moe_quantize_w4(
         _ptr(w), E, N, K, MOE_GROUP, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
+
+
+def moe_retile_w4(codes_canonical, N, K, codes=None, stream=None):
+    """Canonical row-major int4 codes u8 [E][N][K/2] -> the tiled layout
+    (a u8 tensor [E][N][K/2] as moe_quantize_w4 returns)."""
+    import torch
+    E = codes_canonical.shape[0]
+    if codes is None:
+        codes = _empty((E, N, K // 2), torch.uint8, codes_canonical)
+    _check("moe_retile_w4", load_library().moe_retile_w4(
+        _ptr(codes_canonical), E, N, K, _ptr(codes), _stream(stream)))
+    return codes
+
+
+def moe_retile_bitplane8(planes_canonical, N, K, planes=None, stream=None):
+    """Canonical plane slabs u8 [E][8][N][K/8] -> the bitplane streaming
+    layout (a u8 tensor [E][8][N][K/8] as moe_quantize_bitplane8 returns)."""
+    import torch
+    E = planes_canonical.shape[0]
+    if planes is None:
+        planes = _empty((E, 8, N, K // 8), torch.uint8, planes_canonical)
+    _check("moe_retile_bitplane8", load_library().moe_retile_bitplane8(
+        _ptr(planes_canonical), E, N, K, _ptr(planes), _stream(stream)))
+    return planes
 
 
 def moe_quantize_bitplane8(w, planes=None, scales=None, stream=None):

@@ -321,6 +321,41 @@ int moe_quantize_bitplane8(const float* w, int E, int N, int K, int group_size,
   return quantize_common(w, E, N, K, group_size, planes, scales_f16, 1, stream);
 }
 
+static int retile_check(const uint8_t* in, int E, int N, int K, const uint8_t* out,
+                        size_t bytes, const char* what) {
+  if (E < 0 || N < 0 || K <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: bad size", what);
+  if (K % MOE_GROUP) return fail(MOE_ERR_UNSUPPORTED, "%s: K=%d not a multiple of 128", what, K);
+  if (N % 16) return fail(MOE_ERR_UNSUPPORTED, "%s: N=%d not a multiple of 16", what, N);
+  if ((long long)E * N == 0) return ok();
+  if (!in || !out) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
+  if (!aligned(in, 16) || !aligned(out, 16))
+    return fail(MOE_ERR_INVALID_ARG, "%s: misaligned pointer", what);
+  const uintptr_t a = (uintptr_t)in, b = (uintptr_t)out;
+  if (a < b + bytes && b < a + bytes)
+    return fail(MOE_ERR_INVALID_ARG, "%s: input and output overlap", what);
+  return MOE_OK;
+}
+
+int moe_retile_w4(const uint8_t* codes_canonical, int E, int N, int K, uint8_t* codes,
+                  void* stream) {
+  const size_t bytes = (size_t)E * N * (K > 0 ? K : 0) / 2;
+  int rc = retile_check(codes_canonical, E, N, K, codes, bytes, "moe_retile_w4");
+  if (rc || (long long)E * N == 0) return rc;
+  return hip_status(moe::launch_retile_w4(codes_canonical, (long long)E * N, K, codes,
+                                          (hipStream_t)stream),
+                    "moe_retile_w4");
+}
+
+int moe_retile_bitplane8(const uint8_t* planes_canonical, int E, int N, int K,
+                         uint8_t* planes, void* stream) {
+  const size_t bytes = (size_t)E * N * (K > 0 ? K : 0);
+  int rc = retile_check(planes_canonical, E, N, K, planes, bytes, "moe_retile_bitplane8");
+  if (rc || (long long)E * N == 0) return rc;
+  return hip_status(moe::launch_retile_bp(planes_canonical, E, N, K, planes,
+                                          (hipStream_t)stream),
+                    "moe_retile_bitplane8");
+}
+
 }  // extern "C"
 
 static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }

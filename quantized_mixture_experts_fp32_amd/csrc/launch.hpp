@@ -128,4 +128,10 @@ hipError_t launch_combine(const float* y, const int32_t* pair_pos,
                           const float* topk_w, int T, int k, int d, void* out,
                           int out_f32, hipStream_t s);
 
+// Canonical -> streaming code layouts (retile.hip).
+hipError_t launch_retile_w4(const uint8_t* canon, long long R, int K, uint8_t* tiled,
+                            hipStream_t s);
+hipError_t launch_retile_bp(const uint8_t* canon, int E, int N, int K, uint8_t* tiled,
+                            hipStream_t s);
+
 }  // namespace moe

@@ -226,3 +226,18 @@ def test_noalloc_entry_refuses_oversize_on_host(lib):
                                           FAKE, FAKE, FAKE, FAKE, 1, 0, NULL)
     assert rc == moe.MOE_ERR_WORKSPACE
     assert "scratch" in err(lib)
+
+
+def test_retile_validation(lib):
+    """Shape and pointer checks of the canonical-layout conversions (no GPU)."""
+    U, I = moe.MOE_ERR_UNSUPPORTED, moe.MOE_ERR_INVALID_ARG
+    far = ctypes.c_void_p(0x4000000)
+    for fn in (lib.moe_retile_w4, lib.moe_retile_bitplane8):
+        assert fn(FAKE, 2, 16, 100, far, NULL) == U      # K not a multiple of 128
+        assert fn(FAKE, 2, 24, 256, far, NULL) == U      # N not a multiple of 16
+        assert fn(FAKE, -1, 16, 256, far, NULL) == I
+        assert fn(NULL, 2, 16, 256, far, NULL) == I
+        assert fn(ODD, 2, 16, 256, far, NULL) == I
+        assert fn(FAKE, 2, 16, 256, FAKE, NULL) == I     # in place
+        assert "overlap" in err(lib)
+        assert fn(NULL, 0, 16, 256, NULL, NULL) == moe.MOE_OK

@@ -84,6 +84,39 @@ def test_quantize_bit_exact(fmt):
             assert np.array_equal(s[e], ref[e][1]), (fmt, e)
 
 
+@pytest.mark.parametrize("fmt", ["w4", "bp8"])
+def test_retile_canonical_bit_exact(fmt):
+    """Canonical code layouts -> streaming layouts: untiling the output gives
+    back the input bytes, and the oracle's canonical codes of fp32 weights,
+    retiled, equal the library's own quantizer output bit for bit."""
+    rng = np.random.default_rng(21)
+    for (E, N, K) in [(1, 16, 128), (2, 48, 384), (3, 32, 2048)]:
+        note(f"retile {fmt} E={E} N={N} K={K}")
+        if fmt == "w4":
+            canon = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+            out = moe.moe_retile_w4(torch.from_numpy(canon).to(DEV), N, K)
+        else:
+            canon = rng.integers(0, 256, (E, 8, N, K // 8), dtype=np.uint8)
+            out = moe.moe_retile_bitplane8(torch.from_numpy(canon).to(DEV), N, K)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        for e in range(E):
+            assert np.array_equal(untile(o[e], fmt, N, K), canon[e].reshape(
+                untile(o[e], fmt, N, K).shape)), (fmt, e)
+        # oracle canonical codes of real weights, retiled == library quantizer
+        w = np.stack([_edge_weights(rng, N, K) for _ in range(E)])
+        if fmt == "w4":
+            ref = np.stack([oracle.quantize_w4(w[e])[0] for e in range(E)])
+            mine = moe.moe_retile_w4(torch.from_numpy(ref).to(DEV), N, K)
+            lib = moe.moe_quantize_w4(torch.from_numpy(w).to(DEV))[0]
+        else:
+            ref = np.stack([oracle.quantize_bp8(w[e])[0] for e in range(E)])
+            mine = moe.moe_retile_bitplane8(torch.from_numpy(ref).to(DEV), N, K)
+            lib = moe.moe_quantize_bitplane8(torch.from_numpy(w).to(DEV))[0]
+        torch.cuda.synchronize()
+        assert torch.equal(mine, lib), (fmt, E, N, K)
+
+
 # ----------------------------------------------------------------- router
 ROUTE_CASES = [(0, 16), (1, 16), (2, 4096), (3, 16), (4, 1), (4, 64), (4, 8192)]
 
