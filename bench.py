@@ -45,7 +45,7 @@ def parse_args():
                     help="run only the selected secondary workloads (for profiling one "
                          "workload; the JSON line then has no headline value)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=16,
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32,
                     help="tokens of the headline batch in the one-thread oracle run")
     ap.add_argument("--workloads", default="",
                     help="comma list of name filters (spaces as _) for secondary workloads")
@@ -465,7 +465,7 @@ def _omp_threads(n):
     ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
 
 
-def cpu_baseline(np, synth, oracle, cid=4, T=64, sample_1t=16):
+def cpu_baseline(np, synth, oracle, cid=4, T=64, sample_1t=32):
     """The oracle as it stands on the host cores, on the headline batch: the
     whole layer (route, grouping, per-expert dequantization and SwiGLU FFN in
     fp64, combine), timed twice -- on one thread over the first `sample_1t`
