@@ -41,6 +41,12 @@ struct PTile {
   int e, r0, cnt, maxb;
 };
 
+// Compile-time count of 32-token blocks in a tile (1..4).
+template <int N>
+struct TokBlocks {
+  static constexpr int value = N;
+};
+
 // One code word (elements 8j..8j+7, element 2i in nibble i, 2i+1 in
 // nibble 4+i) -> eight bf16 in element order: nibble c goes to mantissa
 // bits 3..6 and is XORed into D there.  D = 0x4340 (192.0): two's
@@ -228,130 +234,145 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
     }
   };
 
-  // Running totals are kept in units of the current group's scale / 8:
-  // before group g is added, acc *= s_prev / s_g (1 when unchanged); after
-  // the last group acc *= s / 8.  All-zero groups (s_g == 0) contribute nothing and keep
-  // s_prev.
-  f32x16 acc[4][2];  // [token block][B block]
+  // The tile's group loop is specialised for its count of 32-token blocks:
+  // a ragged last tile of an expert runs (and stages) only the token
+  // blocks it holds.
+  auto run = [&](auto ntb_c) {
+    constexpr int NTB = decltype(ntb_c)::value;
+    // Running totals are kept in units of the current group's scale / 8:
+    // before group g is added, acc *= s_prev / s_g (1 when unchanged); after
+    // the last group acc *= s / 8.  All-zero groups (s_g == 0) contribute nothing and keep
+    // s_prev.
+    f32x16 acc[NTB][2];  // [token block][B block]
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NTB; ++t)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][m][i] = 0.0f;
+    float s_cur[2] = {0.0f, 0.0f};
+
+    // B column of the offset MFMA: -192 in K rows 0..2 (lanes of half 0)
+    u32x4 negv = {0u, 0u, 0u, 0u};
+    if (hh == 0) {
+      negv[0] = 0xC340C340u;  // -192, -192
+      negv[1] = 0x0000C340u;  // -192, 0
+    }
+    const bf16x8 negB = __builtin_bit_cast(bf16x8, negv);
+
+    // fragment address of (token block 0, K step 0) in a staged buffer, and
+    // the chunk swizzle of K steps 1..7
+    const int x16 = c32 & 15;
+    const int rd_base = c32 * kRowB + 16 * ((8 * hh) ^ (x16 & 8));
+    const int rd_x = 16 * (x16 & 7);
+
+    auto group_step = [&](int g, const uint8_t* ab, const uint2* sbp, uint8_t* ab_next,
+                          uint2* sb_next, const u32x4 (&q)[2][2], const uint32_t (&sc)[2],
+                          u32x4 (&qn)[2][2], uint32_t (&scn)[2]) {
+      staged_barrier();  // group g staged; every wave is done with the other buffer
+      if (g + 1 < G) {
+        if (wave < NTB) stage(g + 1, ab_next, sb_next);
+        codes_load(g + 1, qn, scn);
+      }
+      // a zero-scale group contributes nothing: the row keeps its running
+      // scale and its codes are masked to 0 (which convert to the offset 192
+      // that the offset MFMA cancels), whatever codes it holds
+      float r[2];
+      uint32_t qmask[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const float sg = 0.125f * f16_bits_to_f32(sc[m]);
+        const bool upd = sg != 0.0f;
+        r[m] = upd ? ((s_cur[m] == 0.0f) ? 0.0f : s_cur[m] / sg) : 1.0f;
+        s_cur[m] = upd ? sg : s_cur[m];
+        qmask[m] = upd ? 0xFFFFFFFFu : 0u;
+      }
+      // offset term and rescale, token block by token block
+#pragma unroll
+      for (int t = 0; t < NTB; ++t) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (hh == 0) {
+          const uint2 ss = sbp[t * 32 + c32];
+          v[0] = ss.x;
+          v[1] = ss.y;
+        }
+        const bf16x8 sumA = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[t][m][i] *= r[m];
+          acc[t][m] = mfma32(sumA, negB, acc[t][m]);
+        }
+      }
+      const uint8_t* rd = ab + rd_base;
+      bf16x8 af[2][NTB];
+#pragma unroll
+      for (int t = 0; t < NTB; ++t)
+        af[0][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(rd + t * 32 * kRowB + rd_x));
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const int cur = s2 & 1;
+        if (s2 + 1 < 8) {
+          const int off = rd_x ^ (16 * (s2 + 1));
+#pragma unroll
+          for (int t = 0; t < NTB; ++t)
+            af[cur ^ 1][t] =
+                __builtin_bit_cast(bf16x8, *(const u32x4*)(rd + t * 32 * kRowB + off));
+        }
+        bf16x8 bfr[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          bfr[m] = w4_top(q[m][s2 >> 2][s2 & 3] & qmask[m], 0x43404340u);
+#pragma unroll
+        for (int t = 0; t < NTB; ++t)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) acc[t][m] = mfma32(af[cur][t], bfr[m], acc[t][m]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    u32x4 qa[2][2], qb[2][2];  // [B block][16-byte half] codes of groups g, g + 1
+    uint32_t sca[2], scb[2];
+    codes_load(0, qa, sca);
+    if (wave < NTB) stage(0, abuf0, sbuf0);
+    for (int g = 0; g < G; g += 2) {
+      group_step(g, abuf0, sbuf0, abuf1, sbuf1, qa, sca, qb, scb);
+      if (g + 1 < G) group_step(g + 1, abuf1, sbuf1, abuf0, sbuf0, qb, scb, qa, sca);
+    }
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[t][m][i] = 0.0f;
-  float s_cur[2] = {0.0f, 0.0f};
+      for (int t = 0; t < NTB; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][m][i] *= s_cur[m];
 
-  // B column of the offset MFMA: -192 in K rows 0..2 (lanes of half 0)
-  u32x4 negv = {0u, 0u, 0u, 0u};
-  if (hh == 0) {
-    negv[0] = 0xC340C340u;  // -192, -192
-    negv[1] = 0x0000C340u;  // -192, 0
-  }
-  const bf16x8 negB = __builtin_bit_cast(bf16x8, negv);
-
-  // fragment address of (token block 0, K step 0) in a staged buffer, and
-  // the chunk swizzle of K steps 1..7
-  const int x16 = c32 & 15;
-  const int rd_base = c32 * kRowB + 16 * ((8 * hh) ^ (x16 & 8));
-  const int rd_x = 16 * (x16 & 7);
-
-  auto group_step = [&](int g, const uint8_t* ab, const uint2* sbp, uint8_t* ab_next,
-                        uint2* sb_next, const u32x4 (&q)[2][2], const uint32_t (&sc)[2],
-                        u32x4 (&qn)[2][2], uint32_t (&scn)[2]) {
-    staged_barrier();  // group g staged; every wave is done with the other buffer
-    if (g + 1 < G) {
-      stage(g + 1, ab_next, sb_next);
-      codes_load(g + 1, qn, scn);
-    }
-    // a zero-scale group contributes nothing: the row keeps its running
-    // scale and its codes are masked to 0 (which convert to the offset 192
-    // that the offset MFMA cancels), whatever codes it holds
-    float r[2];
-    uint32_t qmask[2];
+    // ---- epilogue: lane owns feature brow (per B block) for 16 token rows
+    // of each token block: rows 8*(i/4) + 4*hh + i%4 of the 32-row block.
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const float sg = 0.125f * f16_bits_to_f32(sc[m]);
-      const bool upd = sg != 0.0f;
-      r[m] = upd ? ((s_cur[m] == 0.0f) ? 0.0f : s_cur[m] / sg) : 1.0f;
-      s_cur[m] = upd ? sg : s_cur[m];
-      qmask[m] = upd ? 0xFFFFFFFFu : 0u;
-    }
-    // offset term and rescale, token block by token block
+    for (int t = 0; t < NTB; ++t)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (hh == 0) {
-        const uint2 ss = sbp[t * 32 + c32];
-        v[0] = ss.x;
-        v[1] = ss.y;
+      for (int i = 0; i < 16; ++i) {
+        const int tok = t * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (tok >= tl.cnt) continue;
+        const size_t slot = (size_t)(tl.r0 + tok);
+        if (kGateUp) {
+          const float hv = silu_f32(acc[t][0][i]) * acc[t][1][i];
+          h_out[slot * N + brow[0]] = (uint16_t)f32_to_bf16_rne(hv);
+        } else {
+          if (bstore[0]) y_out[slot * N + brow[0]] = acc[t][0][i];
+          if (bstore[1]) y_out[slot * N + brow[1]] = acc[t][1][i];
+        }
       }
-      const bf16x8 sumA = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[t][m][i] *= r[m];
-        acc[t][m] = mfma32(sumA, negB, acc[t][m]);
-      }
-    }
-    const uint8_t* rd = ab + rd_base;
-    bf16x8 af[2][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      af[0][t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(rd + t * 32 * kRowB + rd_x));
-#pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) {
-      const int cur = s2 & 1;
-      if (s2 + 1 < 8) {
-        const int off = rd_x ^ (16 * (s2 + 1));
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          af[cur ^ 1][t] =
-              __builtin_bit_cast(bf16x8, *(const u32x4*)(rd + t * 32 * kRowB + off));
-      }
-      bf16x8 bfr[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-        bfr[m] = w4_top(q[m][s2 >> 2][s2 & 3] & qmask[m], 0x43404340u);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) acc[t][m] = mfma32(af[cur][t], bfr[m], acc[t][m]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
   };
-
-  u32x4 qa[2][2], qb[2][2];  // [B block][16-byte half] codes of groups g, g + 1
-  uint32_t sca[2], scb[2];
-  codes_load(0, qa, sca);
-  stage(0, abuf0, sbuf0);
-  for (int g = 0; g < G; g += 2) {
-    group_step(g, abuf0, sbuf0, abuf1, sbuf1, qa, sca, qb, scb);
-    if (g + 1 < G) group_step(g + 1, abuf1, sbuf1, abuf0, sbuf0, qb, scb, qa, sca);
-  }
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[t][m][i] *= s_cur[m];
-
-  // ---- epilogue: lane owns feature brow (per B block) for 16 token rows
-  // of each token block: rows 8*(i/4) + 4*hh + i%4 of the 32-row block.
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tok = t * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-      if (tok >= tl.cnt) continue;
-      const size_t slot = (size_t)(tl.r0 + tok);
-      if (kGateUp) {
-        const float hv = silu_f32(acc[t][0][i]) * acc[t][1][i];
-        h_out[slot * N + brow[0]] = (uint16_t)f32_to_bf16_rne(hv);
-      } else {
-        if (bstore[0]) y_out[slot * N + brow[0]] = acc[t][0][i];
-        if (bstore[1]) y_out[slot * N + brow[1]] = acc[t][1][i];
-      }
-    }
+  const int ntb = (tl.cnt + 31) >> 5;
+  if (ntb >= 4)
+    run(TokBlocks<4>{});
+  else if (ntb == 3)
+    run(TokBlocks<3>{});
+  else if (ntb == 2)
+    run(TokBlocks<2>{});
+  else
+    run(TokBlocks<1>{});
 }
 
 __global__ __launch_bounds__(1024) void pf_prep(const int32_t* __restrict__ offsets, int E,
