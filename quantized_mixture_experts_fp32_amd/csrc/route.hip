@@ -8,13 +8,14 @@
 //   are combined with acc_l += acc_(l xor o) for o = 8, 4, 2, 1; the logit
 //   is acc_0 + bias[e].  bf16 * bf16 products are exact in fp32, so fma and
 //   multiply-then-add give the same sums.
-// Three launch shapes share that order: for few tokens, (token, 16 experts)
-// blocks write logits to the workspace, and a second launch (or the decode
-// FFN kernels themselves) selects the top-k (many blocks even for one
-// token); one 1024-thread block per token with the top-k fused (moe_route
-// at up to 16 tokens); for many tokens, eight tokens per 256-thread block
-// with the top-k fused.  Activation rows are staged in LDS; router rows are
-// streamed with up to 16 outstanding 16-byte loads per lane.
+// Three launch shapes share that order: for few tokens, (one or two tokens,
+// 16 experts) blocks write logits to the workspace, and a second launch (or
+// the decode FFN kernels themselves) selects the top-k (many blocks even for
+// one token); one 1024-thread block per token with the top-k fused
+// (moe_route at up to 16 tokens); for many tokens, eight tokens per
+// 256-thread block, four experts per lane group at a time, with the top-k
+// fused.  Activation rows are staged in LDS; router rows are streamed with
+// several outstanding 16-byte loads per lane.
 #include <float.h>
 
 #include "kcommon.hpp"
@@ -156,7 +157,81 @@ __device__ __forceinline__ void group_logits(const uint16_t* xs, int d,
   group_logits_from<TB>(xs, d, wrow, ok, wv, acc);
 }
 
-// Many tokens: 8 per 256-thread block, 16 lane groups over the experts.
+// The same logits for NE experts per lane group at once: every activation
+// chunk read from LDS is unpacked once and used for the NE experts, and
+// every router chunk once for the TB tokens (per (token, expert) the
+// summation order is the one above).  W router chunks per expert are in
+// flight; a slot is refilled right after it is unpacked.  Loads past the
+// row's end, and rows of experts past E (given as any valid row), read
+// valid addresses and feed only unstored logits.
+template <int NE, int W>
+__device__ __forceinline__ void logits_prefetch(const uint16_t* const (&wrow)[NE], int nchunk,
+                                                u32x4 (&wv)[W][NE]) {
+  const int l = threadIdx.x & 15;
+#pragma unroll
+  for (int q = 0; q < W; ++q) {
+    const int c = q < nchunk ? q : nchunk - 1;
+#pragma unroll
+    for (int j = 0; j < NE; ++j) wv[q][j] = *(const u32x4*)(wrow[j] + 128 * c + 8 * l);
+  }
+}
+
+template <int TB, int NE, int W>
+__device__ __forceinline__ void group_logits_ne(const uint16_t* xs, int d,
+                                                const uint16_t* const (&wrow)[NE],
+                                                u32x4 (&wv)[W][NE], float (&acc)[TB][NE]) {
+  const int l = threadIdx.x & 15;
+  const int nchunk = d >> 7;
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+    for (int j = 0; j < NE; ++j) acc[tt][j] = 0.0f;
+  for (int c0 = 0; c0 < nchunk; c0 += W) {
+#pragma unroll
+    for (int q = 0; q < W; ++q) {
+      const int c = c0 + q;
+      if (c >= nchunk) break;
+      float wf[NE][8];
+#pragma unroll
+      for (int j = 0; j < NE; ++j)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          wf[j][2 * p] = lo_bf16(wv[q][j][p]);
+          wf[j][2 * p + 1] = hi_bf16(wv[q][j][p]);
+        }
+      {
+        const int cn = c + W < nchunk ? c + W : nchunk - 1;
+#pragma unroll
+        for (int j = 0; j < NE; ++j) wv[q][j] = *(const u32x4*)(wrow[j] + 128 * cn + 8 * l);
+      }
+      const int off = 128 * c + 8 * l;
+#pragma unroll
+      for (int tt = 0; tt < TB; ++tt) {
+        const u32x4 xv = *(const u32x4*)(xs + tt * d + off);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float x0 = lo_bf16(xv[p]), x1 = hi_bf16(xv[p]);
+#pragma unroll
+          for (int j = 0; j < NE; ++j) {
+            acc[tt][j] = fmaf(x0, wf[j][2 * p], acc[tt][j]);
+            acc[tt][j] = fmaf(x1, wf[j][2 * p + 1], acc[tt][j]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt)
+#pragma unroll
+    for (int j = 0; j < NE; ++j)
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) acc[tt][j] = acc[tt][j] + __shfl_xor(acc[tt][j], o, kWave);
+}
+
+// Many tokens: 8 per 256-thread block, 16 lane groups over the experts, four
+// experts per lane group at a time.
+constexpr int kTbNE = 4;
+
 __global__ __launch_bounds__(256) void route_tb8(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int T, int d, int E, int k,
@@ -169,16 +244,28 @@ __global__ __launch_bounds__(256) void route_tb8(
   stage_x<TB, 256>(x, T, d, t0, xs);
   __syncthreads();
   const int G = threadIdx.x >> 4, l = threadIdx.x & 15;
-  const int n_iter = (E + 15) >> 4;  // uniform trip count (shuffles inside)
+  constexpr int NE = kTbNE;
+  const int n_iter = (E + 16 * NE - 1) / (16 * NE);  // uniform trip count (shuffles inside)
   for (int it = 0; it < n_iter; ++it) {
-    const int e = G + 16 * it;
-    const bool ok = e < E;
-    float acc[TB];
-    group_logits<TB>(xs, d, wr + (size_t)(ok ? e : 0) * d, ok, acc);
-    if (ok && l == 0) {
-      const float b = bias ? bias[e] : 0.0f;
+    int e[NE];
+    const uint16_t* wrow[NE];
 #pragma unroll
-      for (int tt = 0; tt < TB; ++tt) logit_sh[tt * E + e] = acc[tt] + b;
+    for (int j = 0; j < NE; ++j) {
+      e[j] = G + 16 * (j + NE * it);
+      wrow[j] = wr + (size_t)(e[j] < E ? e[j] : 0) * d;
+    }
+    u32x4 wv[4][NE];
+    logits_prefetch<NE, 4>(wrow, d >> 7, wv);
+    float acc[TB][NE];
+    group_logits_ne<TB, NE, 4>(xs, d, wrow, wv, acc);
+    if (l == 0) {
+#pragma unroll
+      for (int j = 0; j < NE; ++j) {
+        if (e[j] >= E) continue;
+        const float b = bias ? bias[e[j]] : 0.0f;
+#pragma unroll
+        for (int tt = 0; tt < TB; ++tt) logit_sh[tt * E + e[j]] = acc[tt][j] + b;
+      }
     }
   }
   __syncthreads();
@@ -215,6 +302,35 @@ __global__ __launch_bounds__(256) void route_logits_small(
   float acc[1];
   group_logits_from<1>(xs, d, wrow, ok, wv, acc);
   if (ok && l == 0) logits[(size_t)t * E + e] = acc[0] + (bias ? bias[e] : 0.0f);
+}
+
+// Few tokens, more than one per block: block (TB tokens, 16 experts), one
+// lane group per expert; each router chunk serves the TB tokens, so the
+// router rows are read T / TB times instead of T times.
+template <int TB, int W>
+__global__ __launch_bounds__(256) void route_logits_tile(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int T, int d, int E, float* __restrict__ logits) {
+  extern __shared__ uint16_t xs[];  // [TB][d]
+  const int neb = (E + 15) >> 4;
+  const int t0 = (blockIdx.x / neb) * TB, eb = blockIdx.x % neb;
+  const int G = threadIdx.x >> 4, l = threadIdx.x & 15;
+  const int e = 16 * eb + G;
+  const bool ok = e < E;
+  const uint16_t* wrow[1] = {wr + (size_t)(ok ? e : 0) * d};
+  // the router rows' first chunks are requested before the activation rows
+  u32x4 wv[W][1];
+  logits_prefetch<1, W>(wrow, d >> 7, wv);
+  stage_x<TB, 256>(x, T, d, t0, xs);
+  __syncthreads();
+  float acc[TB][1];
+  group_logits_ne<TB, 1, W>(xs, d, wrow, wv, acc);
+  if (ok && l == 0) {
+    const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt)
+      if (t0 + tt < T) logits[(size_t)(t0 + tt) * E + e] = acc[tt][0] + b;
+  }
 }
 
 __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ logits,
@@ -295,15 +411,32 @@ __global__ __launch_bounds__(1024) void route_topk_permute(
 
 }  // namespace
 
+// fp32 logits [T][E] of up to kSmallT tokens into `logits`: two tokens per
+// block when that still gives at least 256 (token pair, 16-expert) blocks,
+// else one (measured at E = 256: T = 64, 200 and 512 route in 15.1, 24.9 and
+// 42.7 us with two tokens per block, 16.7, 31.0 and 58.9 with one; four or
+// eight tokens per block were slower than one).
+static void launch_logits_small(const void* x, const void* wr, const float* bias, int T, int d,
+                                int E, float* logits, hipStream_t s) {
+  const int neb = (E + 15) / 16;
+  const int tb = ((T + 1) / 2) * neb >= 256 ? 2 : 1;
+  const uint16_t* xp = (const uint16_t*)x;
+  const uint16_t* wp = (const uint16_t*)wr;
+  const size_t lds = sizeof(uint16_t) * (size_t)tb * d;
+  const dim3 grid(((T + tb - 1) / tb) * neb), blk(256);
+  if (tb == 2)
+    hipLaunchKernelGGL((route_logits_tile<2, 8>), grid, blk, lds, s, xp, wp, bias, T, d, E, logits);
+  else
+    hipLaunchKernelGGL(route_logits_small, grid, blk, lds, s, xp, wp, bias, T, d, E, logits);
+}
+
 // fp32 logits [T][E] only (T <= kSmallT), for a consumer that selects the
 // top-k itself.
 hipError_t launch_route_logits(const void* x, const void* wr, const float* bias, int T, int d,
                                int E, float* logits, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (T > kSmallT) return hipErrorInvalidValue;
-  const int neb = (E + 15) / 16;
-  hipLaunchKernelGGL(route_logits_small, dim3(T * neb), dim3(256), sizeof(uint16_t) * d, s,
-                     (const uint16_t*)x, (const uint16_t*)wr, bias, T, d, E, logits);
+  launch_logits_small(x, wr, bias, T, d, E, logits, s);
   return hipGetLastError();
 }
 
@@ -321,10 +454,7 @@ hipError_t launch_route(const void* x, const void* wr, const float* bias,
                        (const uint16_t*)wr, bias, T, d, E, k, topk_idx, topk_w);
   } else if (T <= kSmallT) {
     float* logits = (float*)ws;
-    const int neb = (E + 15) / 16;
-    hipLaunchKernelGGL(route_logits_small, dim3(T * neb), dim3(256),
-                       sizeof(uint16_t) * d, s, (const uint16_t*)x, (const uint16_t*)wr,
-                       bias, T, d, E, logits);
+    launch_logits_small(x, wr, bias, T, d, E, logits, s);
     hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k,
                        topk_idx, topk_w);
   } else {
@@ -350,16 +480,17 @@ hipError_t launch_route_permute(const void* x, const void* wr, const float* bias
                                 int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                                 void* ws, hipStream_t s) {
   // One block selecting every token's top-k and grouping the pairs saves a
-  // launch, but past 64 pairs with more than 64 experts its sequential
-  // selections cost more than the launch (measured at E = 256, T = 64:
-  // 31 us against 6.9 us for one wave per token over 16 blocks plus 3.8 us
-  // for a separate one-block grouping); those shapes route, then permute.
+  // launch, but its sequential selections cost more than the launch past 64
+  // pairs with more than 64 experts (measured at E = 256, T = 64: 31 us
+  // against 6.9 us for one wave per token over 16 blocks plus 3.8 us for a
+  // separate one-block grouping) and past 16 tokens with 64 experts (route
+  // and permute at E = 64, T = 32 / 64 / 128 / 512: 11.0 / 12.3 / 13.2 /
+  // 23.1 us separately, 14.4 / 21.6 / 35.4 / 118.6 us in one block); those
+  // shapes route, then permute.
   const int P = T * k;
-  if (T > 0 && T <= kSmallT && (P <= 64 || E <= 64)) {
+  if (T > 0 && T <= kSmallT && (P <= 64 || (E <= 64 && T <= 16))) {
     float* logits = (float*)ws;
-    const int neb = (E + 15) / 16;
-    hipLaunchKernelGGL(route_logits_small, dim3(T * neb), dim3(256), sizeof(uint16_t) * d, s,
-                       (const uint16_t*)x, (const uint16_t*)wr, bias, T, d, E, logits);
+    launch_logits_small(x, wr, bias, T, d, E, logits, s);
     const size_t lds = sizeof(int32_t) * ((P + 3) & ~3) + permute_block_lds_bytes(E);
     const int threads = P <= 64 ? 64 * (T < 16 ? T : 16) : 1024;
     hipLaunchKernelGGL(route_topk_permute, dim3(1), dim3(threads), lds, s, logits, T, E, k,

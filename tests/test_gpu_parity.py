@@ -134,10 +134,14 @@ def test_route_bit_exact(cid, T):
     np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
 
 
-@pytest.mark.parametrize("cid,T", ROUTE_CASES + [(1, 512), (1, 513)])
+@pytest.mark.parametrize("cid,T", ROUTE_CASES + [(1, 17), (1, 201), (0, 255), (1, 512),
+                                                  (1, 513)])
 def test_route_permute_bit_exact(cid, T):
     """The fused call equals the oracle's routing and grouping bit for bit
-    (both launch shapes: T <= 512 fused, larger T routed then permuted)."""
+    (every launch shape: one block selecting and grouping at few pairs,
+    logits of one or two tokens per block then top-k then grouping up to 512
+    tokens (T = 201: an odd count, the last block holds one token), eight
+    tokens per block beyond)."""
     cfg = synth.CONFIGS[cid]
     note(f"route+permute cfg{cid} T={T}")
     x, wr, bias = synth.host_x(cfg, T), synth.host_router(cfg), synth.host_bias(cfg)
