@@ -35,15 +35,28 @@ __global__ __launch_bounds__(kThreads) void perm_count(
 
 // One block, one thread per expert (E <= 512 < 1024 threads):
 // offsets[e] = exclusive scan of the totals; counts[b][e] is replaced in
-// place by the first slot of chunk b's pairs of expert e.
+// place by the first slot of chunk b's pairs of expert e.  Each thread
+// reads its column kScanBatch chunks at a time (independent loads in
+// flight instead of one dependent load per chunk).
+constexpr int kScanBatch = 16;
+
 __global__ __launch_bounds__(1024) void perm_scan(int nblocks, int E,
                                                   int32_t* __restrict__ counts,
                                                   int32_t* __restrict__ offsets) {
   __shared__ int32_t tot[1024];
   const int e = threadIdx.x;
   int32_t t = 0;
-  if (e < E)
-    for (int b = 0; b < nblocks; ++b) t += counts[(size_t)b * E + e];
+  if (e < E) {
+    int b = 0;
+    for (; b + kScanBatch <= nblocks; b += kScanBatch) {
+      int32_t v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) v[i] = counts[(size_t)(b + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) t += v[i];
+    }
+    for (; b < nblocks; ++b) t += counts[(size_t)b * E + e];
+  }
   tot[e] = (e < E) ? t : 0;
   __syncthreads();
   // Hillis-Steele inclusive scan over 1024 entries (integers: exact)
@@ -57,7 +70,18 @@ __global__ __launch_bounds__(1024) void perm_scan(int nblocks, int E,
     int32_t run = tot[e] - t;  // exclusive prefix
     offsets[e] = run;
     if (e == E - 1) offsets[E] = tot[e];
-    for (int b = 0; b < nblocks; ++b) {
+    int b = 0;
+    for (; b + kScanBatch <= nblocks; b += kScanBatch) {
+      int32_t v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) v[i] = counts[(size_t)(b + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) {
+        counts[(size_t)(b + i) * E + e] = run;
+        run += v[i];
+      }
+    }
+    for (; b < nblocks; ++b) {
       const int32_t c = counts[(size_t)b * E + e];
       counts[(size_t)b * E + e] = run;
       run += c;
