@@ -67,6 +67,15 @@ __device__ __forceinline__ bf16x8 w4_top(uint32_t w, uint32_t D) {
 // of the 128 bf16 elements, split exactly into three bf16 parts
 // (hi = bf16_rne(s), mid = bf16_rne(s - hi), lo = bf16_rne(s - hi - mid)),
 // stored as uint2 {hi | mid << 16, lo}.
+__device__ __forceinline__ uint2 split3_bf16(float s) {
+  const uint32_t hi = f32_to_bf16_rne(s);
+  const float r1 = s - __uint_as_float(hi << 16);
+  const uint32_t mid = f32_to_bf16_rne(r1);
+  const float r2 = r1 - __uint_as_float(mid << 16);
+  const uint32_t lo = f32_to_bf16_rne(r2);
+  return uint2{hi | (mid << 16), lo};
+}
+
 __global__ __launch_bounds__(256) void group_sums(const uint16_t* __restrict__ rows,
                                                   long long R, int K,
                                                   uint2* __restrict__ out) {
@@ -86,12 +95,7 @@ __global__ __launch_bounds__(256) void group_sums(const uint16_t* __restrict__ r
       s += __uint_as_float(v[q] & 0xFFFF0000u);
     }
   }
-  const uint32_t hi = f32_to_bf16_rne(s);
-  const float r1 = s - __uint_as_float(hi << 16);
-  const uint32_t mid = f32_to_bf16_rne(r1);
-  const float r2 = r1 - __uint_as_float(mid << 16);
-  const uint32_t lo = f32_to_bf16_rne(r2);
-  out[i] = uint2{hi | (mid << 16), lo};
+  out[i] = split3_bf16(s);
 }
 
 // Barrier that opens a 128-group: every wave's direct-to-LDS loads of the
@@ -134,7 +138,8 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
                   const PTile* __restrict__ tiles, const int* __restrict__ num_tiles,
                   int nfb,                                  // feature blocks per tile
                   uint16_t* __restrict__ h_out,             // gate/up: [P][N]
-                  float* __restrict__ y_out) {              // down:    [P][N]
+                  float* __restrict__ y_out,                // down:    [P][N]
+                  uint2* __restrict__ hsum_out) {           // gate/up: [P][N/128]
   // two staging buffers as distinct objects, so that reads of one are not
   // ordered behind the in-flight direct-to-LDS loads of the other
   __shared__ __attribute__((aligned(16))) uint8_t abuf0[kBufB];
@@ -348,6 +353,13 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
 
     // ---- epilogue: lane owns feature brow (per B block) for 16 token rows
     // of each token block: rows 8*(i/4) + 4*hh + i%4 of the 32-row block.
+    // gate/up also stages its bf16 h in LDS (row tok: the block's 128
+    // features, 16-byte chunks swizzled as the activation tile) for the
+    // group sums the down pass needs: the block's features are exactly one
+    // 128-group of the down GEMM's K.
+    uint16_t* hst = (uint16_t*)abuf0;
+    if (kGateUp) __syncthreads();  // every wave is done with the staging buffers
+    const int lf = wave * 32 + c32;  // gate/up: the lane's feature within the block
 #pragma unroll
     for (int t = 0; t < NTB; ++t)
 #pragma unroll
@@ -357,12 +369,33 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
         const size_t slot = (size_t)(tl.r0 + tok);
         if (kGateUp) {
           const float hv = silu_f32(acc[t][0][i]) * acc[t][1][i];
-          h_out[slot * N + brow[0]] = (uint16_t)f32_to_bf16_rne(hv);
+          const uint16_t hb = (uint16_t)f32_to_bf16_rne(hv);
+          h_out[slot * N + brow[0]] = hb;
+          hst[tok * 128 + 8 * ((lf >> 3) ^ (tok & 15)) + (lf & 7)] = hb;
         } else {
           if (bstore[0]) y_out[slot * N + brow[0]] = acc[t][0][i];
           if (bstore[1]) y_out[slot * N + brow[1]] = acc[t][1][i];
         }
       }
+    if (kGateUp) {
+      // the group sum of token tok's 128 h values, in element order (the
+      // same fp32 steps as group_sums), split into three bf16 parts
+      __syncthreads();
+      const int tok = tid;
+      if (tok < tl.cnt && tok < kBT) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          const u32x4 v = *(const u32x4*)(hst + tok * 128 + 8 * (c ^ (tok & 15)));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            sum += __uint_as_float(v[q] << 16);
+            sum += __uint_as_float(v[q] & 0xFFFF0000u);
+          }
+        }
+        hsum_out[(size_t)(tl.r0 + tok) * (size_t)(N >> 7) + fblk] = split3_bf16(sum);
+      }
+    }
   };
   const int ntb = (tl.cnt + 31) >> 5;
   if (ntb >= 4)
@@ -889,19 +922,15 @@ hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStr
                        (long long)a.T, a.d, xsum);
   }
   const unsigned mt8 = (unsigned)((mt + 7) & ~(size_t)7);
+  // gate/up writes h and its group sums (the down pass's offset terms)
   launch_k(pf_w4_kernel<true>, dim3(mt8 * (a.f / 128)), dim3(kThreads), 0, s, a.ev[0], a.ev[1],
            a.x, a.sorted_pair, a.k, a.d, a.f, a.gu_codes, a.gu_scales, xsum,
-           (const PTile*)tiles, (const int*)num_tiles, a.f / 128, h, (float*)nullptr);
-  {
-    const long long n = P * (a.f / 128);
-    hipLaunchKernelGGL(group_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, h, P,
-                       a.f, hsum);
-  }
+           (const PTile*)tiles, (const int*)num_tiles, a.f / 128, h, (float*)nullptr, hsum);
   const int dn_fb = (a.d + 255) / 256;
   launch_k(pf_w4_kernel<false>, dim3(mt8 * dn_fb), dim3(kThreads), 0, s, a.ev[2], a.ev[3],
            (const uint16_t*)h, a.sorted_pair, a.k, a.f, a.d, a.dn_codes, a.dn_scales,
            (const uint2*)hsum, (const PTile*)tiles, (const int*)num_tiles, dn_fb,
-           (uint16_t*)nullptr, a.y);
+           (uint16_t*)nullptr, a.y, (uint2*)nullptr);
   return hipGetLastError();
 }
 
