@@ -228,7 +228,7 @@ def test_route_many_experts_ties(E, k, T):
 @pytest.mark.parametrize("T,k,E,mode", [(0, 8, 16, "rand"), (1, 1, 1, "rand"),
                                         (33, 3, 5, "rand"), (1000, 8, 64, "one"),
                                         (4096, 8, 64, "skew"), (8192, 8, 256, "skew"),
-                                        (777, 16, 512, "rand")])
+                                        (777, 16, 512, "rand"), (2100, 8, 64, "skew")])
 def test_permute_bit_exact(T, k, E, mode):
     note(f"permute T={T} k={k} E={E} {mode}")
     rng = np.random.default_rng(T + k + E)
