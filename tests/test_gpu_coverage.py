@@ -1,7 +1,8 @@
 """GPU parity of the whole layer on inputs that exercise the degenerate cases
 of every FFN kernel: all-zero weight groups (scale 0) at the start, in the
-middle and over a whole expert, on each decode and prefill path; and layers
-with one, two or three experts at batch sizes from 2 to 1000.  Every case
+middle and over a whole expert, on each decode and prefill path; layers
+with one, two or three experts at batch sizes from 2 to 1000; and the
+interface's largest d, E, k and a wide f.  Every case
 goes through the C ABI and is compared with the CPU oracle as in the other
 layer tests (integers bit-exact, floating point within rel-L2 2e-3 and
 max-abs 3e-2 rms)."""
@@ -119,3 +120,24 @@ def test_layer_entry_fewer_blocks_than_tokens(E, k, T):
     note(f"layer entry, E * f / 128 = {E} blocks, T={T}")
     cfg = custom_cfg(70 + E, d=256, E=E, k=k, f=128, bias_sigma=0.5)
     check_layer(DevLayer(cfg, T), HostLayer(cfg, T), moe.MOE_PATH_AUTO)
+
+
+# (name, format, d, E, k, f, T, bits mode): the interface's largest model
+# width (d = 8192), expert count (E = 512) and top-k (k = 16), and a wide
+# FFN (f = 8192), through the whole layer on both paths
+EXTREME_CASES = [
+    ("d=8192", "w4", 8192, 8, 2, 256, 3, None),
+    ("E=512, k=16", "w4", 256, 512, 16, 128, 40, None),
+    ("f=8192", "w4", 256, 4, 2, 8192, 20, None),
+    ("bitplane d=8192, rank rule", "bp8", 8192, 16, 8, 128, 5, "rank"),
+]
+
+
+@pytest.mark.parametrize("path", [moe.MOE_PATH_DECODE, moe.MOE_PATH_PREFILL])
+@pytest.mark.parametrize("case", range(len(EXTREME_CASES)))
+def test_layer_extreme_shapes(case, path):
+    name, fmt, d, E, k, f, T, mode = EXTREME_CASES[case]
+    note(f"extreme shape: {name} d={d} E={E} k={k} f={f} T={T} path={path}")
+    cfg = custom_cfg(80 + case, d=d, E=E, k=k, f=f, fmt=fmt, bias_sigma=0.5)
+    bm = moe.MOE_BITS_RANK_RULE if mode == "rank" else moe.MOE_BITS_NONE
+    check_layer(DevLayer(cfg, T), HostLayer(cfg, T), path, bm)
