@@ -565,7 +565,8 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
                   const uint16_t* __restrict__ scales,      // [E][rows][K/128]
                   const uint2* __restrict__ gsum,           // [rows of act][K/128]
                   const PTile* __restrict__ tiles, const int* __restrict__ num_tiles, int nfb,
-                  uint16_t* __restrict__ h_out, float* __restrict__ y_out) {
+                  uint16_t* __restrict__ h_out, float* __restrict__ y_out,
+                  uint2* __restrict__ hsum_out) {  // gate/up: [P][N/128]
   __shared__ __attribute__((aligned(16))) uint8_t abuf0[kBufB];
   __shared__ __attribute__((aligned(16))) uint8_t abuf1[kBufB];
   __shared__ uint2 sbuf0[kBT];
@@ -872,6 +873,11 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[t][m][i] *= s_cur[m];
 
+  // gate/up also writes the down pass's group sums of h, as the int4
+  // kernel does (the block's features are one 128-group of the down K)
+  uint16_t* hst = (uint16_t*)abuf0;
+  if (kGateUp) __syncthreads();  // every wave is done with the staging buffers
+  const int lf = wave * 32 + c32;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -881,12 +887,32 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
       const size_t slot = (size_t)bslot[tl.r0 + tok];
       if (kGateUp) {
         const float hv = silu_f32(acc[t][0][i]) * acc[t][1][i];
-        h_out[slot * N + brow[0]] = (uint16_t)f32_to_bf16_rne(hv);
+        const uint16_t hb = (uint16_t)f32_to_bf16_rne(hv);
+        h_out[slot * N + brow[0]] = hb;
+        hst[tok * 128 + 8 * ((lf >> 3) ^ (tok & 15)) + (lf & 7)] = hb;
       } else {
         if (bstore[0]) y_out[slot * N + brow[0]] = acc[t][0][i];
         if (bstore[1]) y_out[slot * N + brow[1]] = acc[t][1][i];
       }
     }
+  if (kGateUp) {
+    __syncthreads();
+    const int tok = tid;
+    if (tok < tl.cnt && tok < kBT) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const u32x4 v = *(const u32x4*)(hst + tok * 128 + 8 * (c ^ (tok & 15)));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          sum += __uint_as_float(v[q] << 16);
+          sum += __uint_as_float(v[q] & 0xFFFF0000u);
+        }
+      }
+      const size_t slot = (size_t)bslot[tl.r0 + tok];
+      hsum_out[slot * (size_t)(N >> 7) + fblk] = split3_bf16(sum);
+    }
+  }
 }
 
 }  // namespace
@@ -958,17 +984,12 @@ hipError_t launch_ffn_prefill_bp(const FfnArgs& a, uint16_t* h, void* ws, hipStr
   launch_k(pf_bp_kernel<true>, dim3(mt8 * (a.f / 128)), dim3(kThreads), 0, s, a.ev[0], a.ev[1],
            a.x, a.sorted_pair, (const int32_t*)bslot, a.k, a.d, a.f, a.gu_codes, a.gu_scales,
            (const uint2*)xsum, (const PTile*)tiles, (const int*)num_tiles, a.f / 128, h,
-           (float*)nullptr);
-  {
-    const long long n = P * (a.f / 128);
-    hipLaunchKernelGGL(group_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, h, P,
-                       a.f, hsum);
-  }
+           (float*)nullptr, hsum);
   const int dn_fb = (a.d + 255) / 256;
   launch_k(pf_bp_kernel<false>, dim3(mt8 * dn_fb), dim3(kThreads), 0, s, a.ev[2], a.ev[3],
            (const uint16_t*)h, a.sorted_pair, (const int32_t*)bslot, a.k, a.f, a.d, a.dn_codes,
            a.dn_scales, (const uint2*)hsum, (const PTile*)tiles, (const int*)num_tiles, dn_fb,
-           (uint16_t*)nullptr, a.y);
+           (uint16_t*)nullptr, a.y, (uint2*)nullptr);
   return hipGetLastError();
 }
 
