@@ -183,11 +183,16 @@ int moe_route_permute(const void *x_bf16, const void *wr_bf16, const float *bias
  *     [E][d][f/128].
  *   MOE_FMT_BITPLANE8 (u = 8-bit offset code, w ~ s * (u - 128)): a matrix
  *   of R rows (as for int4) and K inputs is stored as u8
- *   [R/16][K/128][8][16][16]: for 16-row tile n/16 and group g a 2 KiB
- *   block holds the 8 planes, plane p (bit 7-p of u, most significant
- *   first) as 16 rows x 16 bytes; bit i of byte j of row n%16 belongs to
- *   element 128g + 8j + i.  The top b planes of every block are its first
- *   256 b bytes: a b-bit read loads only those.
+ *   [R/16][K/128][4][16][4][2][4]: for 16-row tile n/16 and group g a 2 KiB
+ *   block holds the 8 planes (plane p = bit 7-p of u, most significant
+ *   first) as 4 plane pairs c of 512 bytes (planes 2c, 2c+1); within pair c
+ *   row r = n%16 takes 32 bytes at 32 r, its quarter q (elements
+ *   128g + 32q .. 128g + 32q + 31) being the 4-byte word of plane 2c then
+ *   that of plane 2c+1, and bit i of a word belongs to element
+ *   128g + 32q + i.  Byte j of row r's 16 bytes of plane p is at
+ *   512 (p/2) + 32 r + 8 (j/4) + 4 (p%2) + j%4.  The top b planes of every
+ *   block lie in its first 512 ceil(b/2) bytes: a b-bit read loads only
+ *   those (an odd b brings plane b along).
  *     gate_up_codes: R = E*2f, K = d;  down_codes: R = E*d, K = f;
  *     scales as for int4.
  * Bit-widths (bitplane only): bits_mode MOE_BITS_PER_PAIR (bits u8 [T*k],

@@ -25,7 +25,6 @@
 namespace moe {
 namespace {
 
-constexpr int kBlockBytes = 8 * 16 * 16;  // one 16-row tile x 128-group, 8 planes
 
 __device__ __forceinline__ double dmul(double a, double b) { return a * b; }
 __device__ __forceinline__ double dadd(double a, double b) { return a + b; }
@@ -44,10 +43,17 @@ __global__ __launch_bounds__(256) void bp_row_distortion(const uint8_t* __restri
 #pragma unroll
   for (int b = 0; b < 8; ++b) acc[b] = 0.0;
   for (int g = 0; g < G; ++g) {
-    const uint8_t* blk = planes + ((n >> 4) * G + g) * kBlockBytes + (n & 15) * 16;
+    // row n's 32 bytes of each plane pair: quarters 0, 1 then 2, 3, each
+    // the word of the even plane followed by the word of the odd one
+    const uint8_t* blk = planes + ((n >> 4) * G + g) * kBpBlock + (n & 15) * 32;
     u32x4 pw[8];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) pw[p] = *(const u32x4*)(blk + 256 * p);
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 lo = *(const u32x4*)(blk + kBpPair * c);
+      const u32x4 hi = *(const u32x4*)(blk + kBpPair * c + 16);
+      pw[2 * c] = u32x4{lo[0], lo[2], hi[0], hi[2]};
+      pw[2 * c + 1] = u32x4{lo[1], lo[3], hi[1], hi[3]};
+    }
     int I[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int w = 0; w < 4; ++w)

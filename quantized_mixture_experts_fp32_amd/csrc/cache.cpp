@@ -416,8 +416,9 @@ int moe_cache_plan(int E, int slots, int format, int32_t* slot_expert, int32_t* 
 namespace {
 
 // Copies of a run of n loads (experts e.., slots s.., the same plane range)
-// on copy stream `st`: whole int4 experts, or the plane range [p0, p1) of
-// every 2 KiB bitplane block (a strided 2-D copy).  Scales come from the
+// on copy stream `st`: whole int4 experts, or the plane pairs that hold the
+// plane range [p0, p1) of every 2 KiB bitplane block (512 bytes per pair, a
+// strided 2-D copy; an odd bound brings its pair's other plane along).  Scales come from the
 // device-resident scale bank (cache_scale_gather on the compute stream).
 hipError_t enqueue_run(moe_cache* c, const moe::CacheLoad& l, int n, hipStream_t st,
                        int64_t* bytes) {
@@ -431,7 +432,8 @@ hipError_t enqueue_run(moe_cache* c, const moe::CacheLoad& l, int n, hipStream_t
     copy(c->s_gu + s * c->gu_b, c->h_gu + e * c->gu_b, m * c->gu_b);
     copy(c->s_dn + s * c->dn_b, c->h_dn + e * c->dn_b, m * c->dn_b);
   } else if (l.p1 > l.p0) {
-    const size_t w = (size_t)256 * (l.p1 - l.p0), off = (size_t)256 * l.p0;
+    const size_t c0 = (size_t)l.p0 / 2, c1 = ((size_t)l.p1 + 1) / 2;
+    const size_t w = 512 * (c1 - c0), off = 512 * c0;
     auto copy2d = [&](uint8_t* dst, const uint8_t* src, size_t blocks) {
       if (w == 2048) {  // all eight planes: the blocks are contiguous
         copy(dst, src, 2048 * blocks);

@@ -76,19 +76,21 @@ __global__ __launch_bounds__(1024) void ffn_prep(
 // ---------------------------------------------------------------- weights
 // bitplane: one dword per plane p < maxb holds bit 7-p of the lane's 32
 // elements (bit position = element offset).  Planes are stored per 16-row
-// tile and 128-group as a 2 KiB block of 8 planes x 16 rows x 16 bytes;
-// tb = codes + (row / 16) * G * 2048 + (row % 16) * 16.  For class b the
+// tile and 128-group as a 2 KiB block of plane pairs (kcommon.hpp);
+// tb = codes + (row / 16) * G * 2048 + 32 * (row % 16).  For class b the
 // K-values are v_b = (u with 8-b low bits cleared) + 2^(7-b) - 128, or
 // u - 128 for b = 8.
 __device__ __forceinline__ const uint8_t* bp_tile(const uint8_t* codes, size_t row, int G) {
-  return codes + (row >> 4) * (size_t)G * 2048 + 16 * (row & 15);
+  return codes + (row >> 4) * (size_t)G * kBpBlock + 32 * (row & 15);
 }
 
 __device__ __forceinline__ void bp_load(const uint8_t* tb, int g, int kq, int maxb,
                                         uint32_t pl[8]) {
 #pragma unroll
   for (int p = 0; p < 8; ++p)
-    pl[p] = (p < maxb) ? *(const uint32_t*)(tb + (size_t)g * 2048 + 256 * p + 4 * kq) : 0u;
+    pl[p] = (p < maxb) ? *(const uint32_t*)(tb + (size_t)g * kBpBlock + kBpPair * (p >> 1) +
+                                           8 * kq + 4 * (p & 1))
+                       : 0u;
 }
 
 __device__ __forceinline__ void bp_frags(const uint32_t pl[8], int b,

@@ -29,11 +29,13 @@
 // (X from four more MFMAs whose A is 2^(pos-7)), and the fp16 group scale
 // multiplies the group sum in fp32.  Dequantized weights are never rounded.
 //
-// Layout (ABI header): per 16-row tile and 128-group a 2 KiB block holds
-// the 8 planes (most significant first) of 256 bytes, row r's 16 bytes at
-// 16 r; bit i of byte j is element 8j + i.  Lane (row, kq) reads the word
-// kq of its row: elements 32 kq .. 32 kq + 31.  A b-plane read touches the
-// first 256 b bytes of each block.
+// Layout (ABI header, kcommon.hpp): per 16-row tile and 128-group a 2 KiB
+// block holds four plane pairs of 512 bytes (most significant first); row
+// r's quarter kq of pair c is the 8 bytes at 512 c + 32 r + 8 kq, the word
+// of plane 2c then that of plane 2c + 1, bit i of a word being element
+// 32 kq + i.  Lane (row, kq) fetches a pair with one 8-byte load (an odd
+// width's last plane with a 4-byte one); a b-plane read touches the first
+// 512 ceil(b / 2) bytes of each block.
 //
 // Work decomposition as for the int4 decode kernels with a single K slice:
 // block = token tile of up to 16 pairs of one expert x 4 row tiles of 16
@@ -48,7 +50,7 @@ namespace moe {
 namespace {
 using namespace dec;
 
-constexpr int kBlockBytes = 8 * 256;  // 8 planes of one 16-row tile, one group
+constexpr int kBlockBytes = kBpBlock;  // 8 planes of one 16-row tile, one group
 
 // Operand slot o = 4 j + d (MFMA j, 32-bit word d of the lane's A operand)
 // holds the fields at bits 2 i, 2 i + 1 (low half) and 2 i + 16, 2 i + 17
@@ -318,9 +320,17 @@ __device__ __forceinline__ void bp_gu_item(const uint16_t* __restrict__ xsrc,
   auto load = [&](int g, int i) {
     xv[i] = *(const u32x4*)(xsrc + 128 * g);
 #pragma unroll
-    for (int p = 0; p < NB; ++p) {
-      wg[i][p] = *(const uint32_t*)(pg + (size_t)g * kBlockBytes + 256 * p);
-      wu[i][p] = *(const uint32_t*)(pu + (size_t)g * kBlockBytes + 256 * p);
+    for (int c = 0; c < NB / 2; ++c) {
+      const uint2 a = *(const uint2*)(pg + (size_t)g * kBlockBytes + kBpPair * c);
+      const uint2 b = *(const uint2*)(pu + (size_t)g * kBlockBytes + kBpPair * c);
+      wg[i][2 * c] = a.x;
+      wg[i][2 * c + 1] = a.y;
+      wu[i][2 * c] = b.x;
+      wu[i][2 * c + 1] = b.y;
+    }
+    if (NB & 1) {
+      wg[i][NB - 1] = *(const uint32_t*)(pg + (size_t)g * kBlockBytes + kBpPair * (NB / 2));
+      wu[i][NB - 1] = *(const uint32_t*)(pu + (size_t)g * kBlockBytes + kBpPair * (NB / 2));
     }
   };
   ScaleStage<2, kSC ? kSC : 1> sst;
@@ -403,8 +413,8 @@ void gateup_bp_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
     const uint16_t* xsrc = x + (size_t)(sp / k) * d + 8 * st_pc;
     // plane words: tiles of 16 rows; row n0 + col of gate, f + n0 + col of up
     const size_t rg = (size_t)tl.e * 2 * f + n0, ru = rg + f;
-    const uint8_t* pg = planes + (rg >> 4) * (size_t)G * kBlockBytes + 16 * col + 4 * kq;
-    const uint8_t* pu = planes + (ru >> 4) * (size_t)G * kBlockBytes + 16 * col + 4 * kq;
+    const uint8_t* pg = planes + (rg >> 4) * (size_t)G * kBlockBytes + 32 * col + 8 * kq;
+    const uint8_t* pu = planes + (ru >> 4) * (size_t)G * kBlockBytes + 32 * col + 8 * kq;
     const uint16_t* sc_src = scales + ((size_t)tl.e * 2 * f + nb) * G;
     f32x4 tg = {0, 0, 0, 0}, tu = {0, 0, 0, 0};
     switch (maxb) {  // block-uniform
@@ -446,8 +456,13 @@ __device__ __forceinline__ void bp_dn_item(const uint16_t* __restrict__ hsrc,
   auto load = [&](int g, int i) {
     hv[i] = *(const u32x4*)(hsrc + 128 * g);
 #pragma unroll
-    for (int p = 0; p < NB; ++p)
-      wd[i][p] = *(const uint32_t*)(pd + (size_t)g * kBlockBytes + 256 * p);
+    for (int c = 0; c < NB / 2; ++c) {
+      const uint2 a = *(const uint2*)(pd + (size_t)g * kBlockBytes + kBpPair * c);
+      wd[i][2 * c] = a.x;
+      wd[i][2 * c + 1] = a.y;
+    }
+    if (NB & 1)
+      wd[i][NB - 1] = *(const uint32_t*)(pd + (size_t)g * kBlockBytes + kBpPair * (NB / 2));
   };
   ScaleStage<1, kSC ? kSC : 1> sst;
   if (kSC) sst.fetch(sc_src, 0, G);
@@ -520,7 +535,7 @@ void down_bp_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
     const ColWeights cw = col_weights(b);
     const uint16_t* hsrc = h + (size_t)(tl.r0 + (st_tok < tl.cnt ? st_tok : 0)) * f + 8 * st_pc;
     const size_t rd0 = (size_t)tl.e * d + m0;
-    const uint8_t* pd = planes + (rd0 >> 4) * (size_t)G * kBlockBytes + 16 * col + 4 * kq;
+    const uint8_t* pd = planes + (rd0 >> 4) * (size_t)G * kBlockBytes + 32 * col + 8 * kq;
     const uint16_t* sc_src = scales + ((size_t)tl.e * d + mb) * G;
     f32x4 acc = {0, 0, 0, 0};
     switch (maxb) {  // block-uniform

@@ -561,7 +561,7 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
                   const int32_t* __restrict__ sorted_pair,  // gate/up: gather
                   const int32_t* __restrict__ bslot,        // tile rows -> slots
                   int k_top, int K, int N,
-                  const uint8_t* __restrict__ planes,       // [E*rows/16][K/128][8][16][16]
+                  const uint8_t* __restrict__ planes,       // [E*rows/16][K/128] 2 KiB blocks
                   const uint16_t* __restrict__ scales,      // [E][rows][K/128]
                   const uint2* __restrict__ gsum,           // [rows of act][K/128]
                   const PTile* __restrict__ tiles, const int* __restrict__ num_tiles, int nfb,
@@ -598,17 +598,19 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
     brow[0] = bstore[0] ? n0 + c32 : c32;
     brow[1] = bstore[1] ? n0 + 32 + c32 : c32;
   }
-  // lane half hh reads bytes 8 hh .. 8 hh + 7 of its row's 16 bytes per
-  // plane: elements 64 hh .. 64 hh + 63 of the group, the int4 lane split.
-  // Addresses are a uniform base (expert, group, plane) plus a 32-bit lane
-  // offset within the expert (its nrows * K bytes).
-  const uint8_t* pe = planes + ebase * (size_t)K;  // 2 KiB blocks: 16 rows x 8 planes per group
+  // lane half hh reads quarters 2 hh and 2 hh + 1 of its row in each plane
+  // pair (one 16-byte load at 512 c + 32 r + 16 hh of the group's block:
+  // both planes' words of the two quarters): elements 64 hh .. 64 hh + 63
+  // of the group, the int4 lane split.  Addresses are a uniform base
+  // (expert, group, pair) plus a 32-bit lane offset within the expert (its
+  // nrows * K bytes).
+  const uint8_t* pe = planes + ebase * (size_t)K;  // 2 KiB blocks: 16 rows x 4 plane pairs
   const uint16_t* se = scales + ebase * (size_t)G;
   uint32_t lo_p[2], lo_s[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    lo_p[m] = (uint32_t)(brow[m] >> 4) * (uint32_t)G * 2048u + 16u * (uint32_t)(brow[m] & 15) +
-              8u * (uint32_t)hh;
+    lo_p[m] = (uint32_t)(brow[m] >> 4) * (uint32_t)G * 2048u + 32u * (uint32_t)(brow[m] & 15) +
+              16u * (uint32_t)hh;
     lo_s[m] = (uint32_t)brow[m] * (uint32_t)G;
   }
 
@@ -653,26 +655,33 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
   };
 
   // A pass reads four plane words per B block: nibble bit kb of pass j is
-  // plane 4 j + 3 - kb, at byte offset poff[j][kb] of the group's 2 KiB
-  // block; planes at or past the width read the last present one and are
-  // masked to zero (keep[j] holds 0xFF in the bytes kept).
-  uint32_t poff[2][4], keep[2] = {0u, 0u};
+  // plane 4 j + 3 - kb, from pair 2 j + pi (pi = 0: planes 4 j, 4 j + 1;
+  // pi = 1: planes 4 j + 2, 4 j + 3) at byte offset poff[j][pi] of the
+  // group's 2 KiB block; pairs at or past the width read the last present
+  // one and planes at or past the width are masked to zero (keep[j] holds
+  // 0xFF in the bytes kept).
+  uint32_t poff[2][2], keep[2] = {0u, 0u};
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 2; ++j) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int p = 4 * j + 3 - kb;
-      poff[j][kb] = 256u * (uint32_t)min(p, nb - 1);
-      keep[j] |= p < nb ? 0xFFu << (8 * kb) : 0u;
-    }
-  auto unit_load = [&](int g, int pass, uint2 (&U)[2][4]) {
+    for (int pi = 0; pi < 2; ++pi)
+      poff[j][pi] = (uint32_t)kBpPair * (uint32_t)min(2 * j + pi, (nb - 1) >> 1);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      keep[j] |= 4 * j + 3 - kb < nb ? 0xFFu << (8 * kb) : 0u;
+  }
+  // U[m][pi] keeps the loaded order: words (plane 4 j + 2 pi, quarter
+  // 2 hh), (plane 4 j + 2 pi + 1, quarter 2 hh), then the same for quarter
+  // 2 hh + 1; nibble bit kb's plane 4 j + 3 - kb is pi = (3 - kb) / 2,
+  // s = (3 - kb) % 2, its words U[m][pi][s] and U[m][pi][2 + s].
+  auto unit_load = [&](int g, int pass, u32x4 (&U)[2][2]) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int pi = 0; pi < 2; ++pi) {
         uint32_t o = lo_p[m];
         asm volatile("" : "+v"(o));  // keep the uniform-base + offset form
-        U[m][kb] = *(const uint2*)(pe + ((size_t)g * 2048 + poff[pass][kb]) + o);
+        U[m][pi] = *(const u32x4*)(pe + ((size_t)g * 2048 + poff[pass][pi]) + o);
       }
   };
   // A group whose scale is 0 contributes nothing (its weights s * v are 0
@@ -684,21 +693,25 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
   bool zrow[2] = {false, false};
   // zero the absent planes of a pass (keep mask uniform per pass) and every
   // plane of a zero-scale row
-  auto unit_fix = [&](uint2 (&U)[2][4], uint32_t kp) {
+  auto unit_fix = [&](u32x4 (&U)[2][2], uint32_t kp) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const uint32_t km = ((kp >> (8 * kb)) & 0xFFu) && !zrow[m] ? 0xFFFFFFFFu : 0u;
-        U[m][kb].x &= km;
-        U[m][kb].y &= km;
+        const int pi = (3 - kb) >> 1, s = (3 - kb) & 1;
+        U[m][pi][s] &= km;
+        U[m][pi][2 + s] &= km;
       }
   };
   // step s2's word: byte b = byte s2 of the source of nibble bit (0, 2,
   // 1, 3)[b]
-  auto code_word = [&](const uint2 (&S)[4], int s2) {
+  auto code_word = [&](const u32x4 (&S)[2], int s2) {
     const int sh = 8 * (s2 & 3);
-    auto byte = [&](int kb) { return (((s2 < 4) ? S[kb].x : S[kb].y) >> sh) & 0xFFu; };
+    auto byte = [&](int kb) {
+      const int pi = (3 - kb) >> 1, s = (3 - kb) & 1;
+      return (S[pi][(s2 < 4 ? 0 : 2) + s] >> sh) & 0xFFu;
+    };
     return nib_transpose2(byte(0) | (byte(2) << 8) | (byte(1) << 16) | (byte(3) << 24));
   };
 
@@ -778,7 +791,7 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
   // The B fragments of K step s2 + 1 are converted in the same scheduling
   // region as the MFMAs of step s2 (independent work the VALU does while
   // the matrix core runs).
-  auto run_pass = [&](const uint8_t* ab, const uint2 (&U)[2][4], uint32_t D) {
+  auto run_pass = [&](const uint8_t* ab, const u32x4 (&U)[2][2], uint32_t D) {
     const uint8_t* rd = ab + rd_base;
     bf16x8 af[2][4];
 #pragma unroll
@@ -819,7 +832,7 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
   if (nb > 4) {
     // two passes per group: UA = planes 0..3 of group g (loaded one group
     // ahead), UB = planes 4..7 (loaded at the group's start)
-    uint2 UA[2][4], UB[2][4];
+    u32x4 UA[2][2], UB[2][2];
     uint32_t sc[2];
     unit_load(0, 0, UA);
     scales_load(0, sc);
@@ -843,13 +856,13 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
       if (g + 1 < G) gstep(g + 1, abuf1, sbuf1, abuf0, sbuf0);
     }
   } else {
-    uint2 UA[2][4], UB[2][4];
+    u32x4 UA[2][2], UB[2][2];
     uint32_t sca[2], scb[2];
     unit_load(0, 0, UA);
     scales_load(0, sca);
     stage(0, abuf0, sbuf0);
     auto gstep = [&](int g, uint8_t* ab, uint2* sbp, uint8_t* ab_next, uint2* sb_next,
-                     uint2 (&U)[2][4], const uint32_t (&sc)[2], uint2 (&Un)[2][4],
+                     u32x4 (&U)[2][2], const uint32_t (&sc)[2], u32x4 (&Un)[2][2],
                      uint32_t (&scn)[2]) {
       staged_barrier();
       if (g + 1 < G) {

@@ -14,6 +14,18 @@ typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// Bitplane storage: per 16-row tile and 128-group a 2 KiB block.  Planes 2c
+// and 2c + 1 form pair c at bytes 512 c .. 512 c + 511; within a pair row r
+// takes 32 bytes at 32 r, and its quarter q (elements 32 q .. 32 q + 31 of
+// the group) is 4 bytes of plane 2c followed by 4 bytes of plane 2c + 1, so
+// one 8-byte load fetches both planes of a lane's 32-weight slice.  Bit i of
+// a quarter's plane word is element 32 q + i.
+constexpr int kBpBlock = 2048;
+constexpr int kBpPair = 512;
+__host__ __device__ constexpr int bp_byte(int p, int r, int j) {  // plane p, row r, byte j < 16
+  return kBpPair * (p >> 1) + 32 * r + 8 * (j >> 2) + 4 * (p & 1) + (j & 3);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);
 }

@@ -66,18 +66,19 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(
         u[h] = (int)r;
       }
       // elements 2*lane and 2*lane+1 of the group: byte lane/4 of the row's
-      // 16 bytes of each plane, bit positions 2*(lane%4) and +1; planes of a
-      // 16-row tile and group form one 2 KiB block (8 planes x 16 rows x 16)
+      // 16 bytes of each plane, bit positions 2*(lane%4) and +1, stored in
+      // the 2 KiB block of the row's 16-row tile and group (kcommon.hpp)
       const long long row = grp / G;  // over all E*N rows; N % 16 == 0
       const long long g = grp % G;
-      uint8_t* blk = codes + ((row >> 4) * G + g) * 2048 + (row & 15) * 16 + (lane >> 2);
+      uint8_t* blk = codes + ((row >> 4) * G + g) * kBpBlock;
+      const int r16 = (int)(row & 15), j = lane >> 2;
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
         uint32_t bits = (((u[0] >> (7 - p)) & 1) | (((u[1] >> (7 - p)) & 1) << 1))
                         << (2 * (lane & 3));
         bits |= __shfl_xor(bits, 1, kWave);
         bits |= __shfl_xor(bits, 2, kWave);
-        if ((lane & 3) == 0) blk[256 * p] = (uint8_t)bits;
+        if ((lane & 3) == 0) blk[bp_byte(p, r16, j)] = (uint8_t)bits;
       }
     }
   }

@@ -8,8 +8,9 @@
 //  bitplane8 (PagedMoE, abstract: one 8-bit code per weight stored as
 //    bitplanes whose lower precisions are prefixes): canonical per expert 8
 //    plane slabs [8][N][K/8], slab p holding bit 7 - p, bit i of byte (n, j)
-//    for element 8j + i.  Streaming: [N/16][K/128][8][16][16] bytes per
-//    expert, the same bytes regrouped per 16-row tile and 128-group.
+//    for element 8j + i.  Streaming: per 16-row tile and 128-group a 2 KiB
+//    block of four plane pairs, a row's two words of one pair and quarter
+//    side by side (kcommon.hpp); the same bytes regrouped.
 #include "kcommon.hpp"
 #include "launch.hpp"
 
@@ -41,9 +42,10 @@ __global__ __launch_bounds__(256) void retile_w4_kernel(const uint32_t* __restri
   tiled[i] = out;
 }
 
-// One thread per 16-byte piece of the output (one plane of one row of one
-// tile and group).
-__global__ __launch_bounds__(256) void retile_bp_kernel(const u32x4* __restrict__ canon,
+// One thread per 16-byte piece of the output: half hf of row rr's 32 bytes
+// of plane pair c in one tile and group, i.e. quarters 2 hf and 2 hf + 1 of
+// planes 2c and 2c + 1 (bytes 8 hf .. 8 hf + 7 of each plane's 16).
+__global__ __launch_bounds__(256) void retile_bp_kernel(const uint2* __restrict__ canon,
                                                         int E, int N, int K,
                                                         u32x4* __restrict__ tiled) {
   const int G = K >> 7;
@@ -52,15 +54,19 @@ __global__ __launch_bounds__(256) void retile_bp_kernel(const u32x4* __restrict_
   if (i >= (long long)E * per_e) return;
   const long long e = i / per_e;
   const long long w = i % per_e;
-  // tiled piece w of expert e: [N/16][G][8][16]
-  const int rr = (int)(w & 15);
-  const int p = (int)((w >> 4) & 7);
+  // piece w of expert e: block tg = w / 128, then pair, row, half
+  const int hf = (int)(w & 1);
+  const int rr = (int)((w >> 1) & 15);
+  const int c = (int)((w >> 5) & 3);
   const long long tg = w >> 7;
   const long long t = tg / G;
   const int g = (int)(tg % G);
   const long long n = 16 * t + rr;
-  // canonical piece: slab p, row n, bytes 16 g .. 16 g + 15
-  tiled[i] = canon[e * per_e + ((long long)p * N + n) * G + g];
+  // canonical: slab p, row n, bytes 16 g + 8 hf .. 16 g + 8 hf + 7
+  const uint2* ce = canon + 2 * e * per_e;
+  const uint2 a = ce[(((long long)(2 * c) * N + n) * G + g) * 2 + hf];
+  const uint2 b = ce[(((long long)(2 * c + 1) * N + n) * G + g) * 2 + hf];
+  tiled[i] = u32x4{a.x, b.x, a.y, b.y};
 }
 
 }  // namespace
@@ -79,7 +85,7 @@ hipError_t launch_retile_bp(const uint8_t* canon, int E, int N, int K, uint8_t* 
   const long long n = (long long)E * N * (K / 128) * 8;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(retile_bp_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     (const u32x4*)canon, E, N, K, (u32x4*)tiled);
+                     (const uint2*)canon, E, N, K, (u32x4*)tiled);
   return hipGetLastError();
 }
 

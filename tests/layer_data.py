@@ -143,10 +143,12 @@ def w4_untile(codes, N, K):
 
 def bp_untile(planes, N, K):
     """The library's bitplanes of one N x K matrix (include/moe_wq.h: per
-    16-row tile and 128-group a block of 8 planes x 16 rows x 16 bytes) ->
-    the oracle's plane-major layout [8][N][K/8].  A pure byte permutation."""
-    t = np.asarray(planes, np.uint8).reshape(N // 16, K // 128, 8, 16, 16)
-    return t.transpose(2, 0, 3, 1, 4).reshape(8, N, K // 8)
+    16-row tile and 128-group a 2 KiB block [pair c][row r][quarter q]
+    [plane 2c + s][4 bytes]) -> the oracle's plane-major layout [8][N][K/8].
+    A pure byte permutation."""
+    t = np.asarray(planes, np.uint8).reshape(N // 16, K // 128, 4, 16, 4, 2, 4)
+    # axes: tile, g, c, r, q, s, b  ->  [c, s][tile, r][g, q, b]
+    return t.transpose(2, 5, 0, 3, 1, 4, 6).reshape(8, N, K // 8)
 
 
 def untile(codes, fmt, N, K):

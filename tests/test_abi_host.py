@@ -199,8 +199,8 @@ def test_w4_untile_matches_header_formula():
 
 def test_bp_untile_matches_header_formula():
     """The tests' untiling of bitplanes follows the ABI header: plane p of
-    row n, byte j of group g lives at ((n/16)*(K/128) + g)*2048 + 256 p +
-    16 (n%16) + j."""
+    row n, byte j of group g lives at ((n/16)*(K/128) + g)*2048 +
+    512 (p/2) + 32 (n%16) + 8 (j/4) + 4 (p%2) + j%4."""
     import sys
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from layer_data import bp_untile
@@ -212,7 +212,8 @@ def test_bp_untile_matches_header_formula():
         for n in range(N):
             for jj in range(K // 8):
                 g, j = divmod(jj, 16)
-                off = ((n // 16) * (K // 128) + g) * 2048 + 256 * p + 16 * (n % 16) + j
+                off = (((n // 16) * (K // 128) + g) * 2048 + 512 * (p // 2) + 32 * (n % 16)
+                       + 8 * (j // 4) + 4 * (p % 2) + j % 4)
                 assert pm[p, n, jj] == tiled[off], (p, n, jj)
 
 

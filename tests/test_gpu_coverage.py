@@ -141,3 +141,37 @@ def test_layer_extreme_shapes(case, path):
     cfg = custom_cfg(80 + case, d=d, E=E, k=k, f=f, fmt=fmt, bias_sigma=0.5)
     bm = moe.MOE_BITS_RANK_RULE if mode == "rank" else moe.MOE_BITS_NONE
     check_layer(DevLayer(cfg, T), HostLayer(cfg, T), path, bm)
+
+
+@pytest.mark.parametrize("path", [moe.MOE_PATH_DECODE, moe.MOE_PATH_PREFILL])
+def test_bitplane_reads_stay_in_prefix(path):
+    """A b-bit read of a bitplane expert touches only the plane pairs that
+    hold its top b planes, the first 512 ceil(b / 2) bytes of every 2 KiB
+    block (include/moe_wq.h): random bytes written past them, in both
+    matrices of every expert, leave every output bit unchanged.  Per-expert
+    widths 1..8 cover the odd widths whose last pair is read half."""
+    cfg = custom_cfg(19, d=256, E=8, k=2, f=384, fmt="bp8", bias_sigma=0.3)
+    T = 40 if path == moe.MOE_PATH_DECODE else 700
+    widths = np.array([1, 2, 3, 4, 5, 6, 7, 8], np.uint8)
+    dl = DevLayer(cfg, T)
+    hl = HostLayer(cfg, T)
+    note(f"bitplane prefix reads path={path} T={T}")
+    lay, _ = check_layer(dl, hl, path, moe.MOE_BITS_PER_EXPERT, widths)
+    assert (np.diff(lay.offsets.cpu().numpy()) > 0).all()
+    bits = torch.from_numpy(widths).to(DEV)
+    lay = dl.layer(moe.MOE_BITS_PER_EXPERT, bits)
+    o0 = lay.forward(dl.x, out_dtype=moe.MOE_OUT_F32, path=path).clone()
+    y0 = lay.y_pairs.clone()
+    gen = torch.Generator(device="cpu").manual_seed(19)
+    for codes, rows, K in ((dl.guc, 2 * cfg.f, cfg.d), (dl.dnc, cfg.d, cfg.f)):
+        for e, b in enumerate(widths):
+            keep = 512 * ((int(b) + 1) // 2)
+            if keep == 2048:
+                continue
+            v = codes[e].view(-1).view(rows // 16, K // 128, 2048)
+            v[:, :, keep:] = torch.randint(0, 256, (rows // 16, K // 128, 2048 - keep),
+                                           generator=gen, dtype=torch.uint8).to(DEV)
+    o1 = lay.forward(dl.x, out_dtype=moe.MOE_OUT_F32, path=path).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(lay.y_pairs, y0), "bytes past the prefix pairs changed y_pairs"
+    assert torch.equal(o1, o0)
