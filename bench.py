@@ -267,8 +267,13 @@ def run_workload(wl, warmup, hip, torch, np, synth, moe):
         dist_np = dist.cpu().numpy()
         cnt_np = counts.cpu().numpy()
         uni = int(wl.budget_bits)
+        # the storage layout fetches whole plane pairs: an odd width also
+        # brings its pair's other plane
+        fetched = sum(int(c) * sum(expert_bytes(cfg, 2 * ((int(b) + 1) // 2)))
+                      for c, b in zip(cnt_np, bits_np))
         alloc = {"budget_bits_per_weight": wl.budget_bits, "budget_bytes": budget,
-                 "read_bytes": int(read_t.cpu()[0]), "lambda": float(lam_t.cpu()[0]),
+                 "read_bytes": int(read_t.cpu()[0]), "read_bytes_fetched_pairs": fetched,
+                 "lambda": float(lam_t.cpu()[0]),
                  "bits_histogram": {int(b): int((bits_np == b).sum()) for b in np.unique(bits_np)},
                  "distortion_table_ms": round(hip.ms(ev[0], ev[1]), 3),
                  "allocator_us": round(1e3 * hip.ms(ev[2], ev[3]), 2),

@@ -337,7 +337,9 @@ int moe_bp_distortion(const uint8_t *gate_up_planes,
  * routing frequency cancels from each expert's decision, which is
  *   b_e(lambda) = argmin_{b_min <= b <= b_max} fma(lambda, R(b), dist[e][b-1])
  * (ties to the larger b), with R(b) = b*3df/8 + 3df/64 bytes read (planes
- * plus scales); a bisection on lambda meets the budget:
+ * plus scales; the b planes a b-bit prefix needs -- the bitplane layout
+ * fetches whole plane pairs, so an odd b moves one more plane of bytes);
+ * a bisection on lambda meets the budget:
  *   read(lambda) = sum_e counts[e] * R(b_e(lambda)) (exact int64);
  *   lambda = 0 if read(0) <= budget_bytes; otherwise hi = 1, doubled (at
  *   most 1023 times) until read(hi) <= budget, then 64 halvings of [lo, hi]
