@@ -38,10 +38,11 @@
 // 512 ceil(b / 2) bytes of each block.
 //
 // Work decomposition as for the int4 decode kernels with a single K slice:
-// block = token tile of up to 16 pairs of one expert x 4 row tiles of 16
-// features; the tile's activations are staged in LDS per group by the
-// block (scaled and ordered for the B fragments); plane words stream kDQ
-// groups ahead.
+// block = token tile of up to 16 pairs of one expert x 4 waves, each wave
+// two 16-row tiles (gate/up: the gate and up tiles of 16 features; down:
+// two row tiles 64 rows apart); the tile's activations are staged in LDS
+// per group by the block (scaled and ordered for the B fragments); plane
+// words stream kDQ groups ahead.
 #include "kcommon.hpp"
 #include "launch.hpp"
 #include "decode_common.hpp"
@@ -215,68 +216,6 @@ __device__ __forceinline__ void bp_group2(const bf16x8 (&xf)[4], const f32x4 see
   }
 }
 
-// One matrix, pipelined as bp_group2; each chain's four MFMAs run as two
-// independent pairs (MFMAs 0, 1 from the seed and 2, 3 from zero, added
-// after), so two chains are in flight.
-template <int NB>
-__device__ __forceinline__ void bp_group1(const bf16x8 (&xf)[4], const f32x4 seed,
-                                          const f32x4 dx, const uint32_t (&pw)[NB],
-                                          const ColWeights& cw, uint32_t hmask,
-                                          const f32x4 sv, f32x4& acc) {
-  constexpr int NC = (NB + 1) / 2;
-  f32x4 comb;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) comb[i] = cw.cb * dx[i];
-  bf16x8 a[4];
-#pragma unroll
-  for (int c = 0; c < NB / 2; ++c) {
-    if (!((hmask >> c) & 1u)) continue;  // tile-uniform
-    uint32_t E, O;
-    bp_merge_half(pw[2 * c], E, O);
-    bp_frags(E, O, a);
-    f32x4 d = seed;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) d = mfma16(a[j], xf[j], d);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) comb[i] = fmaf(cw.wH[c], d[i], comb[i]);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  {
-    uint32_t E, O;
-    bp_chain_words<NB>(pw, 0, E, O);
-    bp_frags(E, O, a);
-  }
-  f32x4 d_prev = {0, 0, 0, 0};
-#pragma unroll
-  for (int t = 0; t < NC; ++t) {
-    f32x4 d0 = seed, d1 = {0, 0, 0, 0};
-    d0 = mfma16(a[0], xf[0], d0);
-    d1 = mfma16(a[2], xf[2], d1);
-    d0 = mfma16(a[1], xf[1], d0);
-    d1 = mfma16(a[3], xf[3], d1);
-    if (t > 0) {
-      const float w = bp_chain_weight<NB>(cw, t - 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) comb[i] = fmaf(w, d_prev[i], comb[i]);
-    }
-    if (t + 1 < NC) {
-      uint32_t E, O;
-      bp_chain_words<NB>(pw, t + 1, E, O);
-      bp_frags(E, O, a);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) d_prev[i] = d0[i] + d1[i];
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  {
-    const float w = bp_chain_weight<NB>(cw, NC - 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) comb[i] = fmaf(w, d_prev[i], comb[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = fmaf(sv[i], comb[i], acc[i]);
-}
-
 // Bit-width of the tile's column col, the tile's largest bit-width, and the
 // half-chain mask (bit c: some column has the odd width 2c + 1 below maxb).
 __device__ __forceinline__ int tile_bits(const int32_t* __restrict__ sp, int r0, int cnt, int col,
@@ -299,42 +238,46 @@ __device__ __forceinline__ int tile_bits(const int32_t* __restrict__ sp, int r0,
 // ------------------------------------------------------------- gate / up
 // One work item reading the NB planes of its tile's largest bit-width (NB is
 // a compile-time constant, chosen per item by a block-uniform switch, so
-// every load of the group loop is unconditional).  The loop refills each
+// every load of the group loop is unconditional).  Each wave computes two
+// 16-row tiles that share the staged activations and whose chains
+// interleave on the matrix core: the gate and up tiles of the same
+// features (gate/up), or two row tiles 64 rows apart (down).  Tile t starts
+// at pt[t]; its scale rows start t mat_stride rows past sc_src.  The loop refills each
 // slot right after its use in a branch-free steady state: the compiler's
 // waits then count exactly the loads issued after the one needed, and kDQ
 // groups stay in flight across the loop edge.  Scales are fetched before
 // the plane words and written to LDS after them.  Rows past the tile stage a
 // copy of its first row (they feed only unstored columns).
 template <int NB, int kDQ, int kSC>
-__device__ __forceinline__ void bp_gu_item(const uint16_t* __restrict__ xsrc,
-                                           const uint8_t* __restrict__ pg,
-                                           const uint8_t* __restrict__ pu, int G,
-                                           const uint16_t* __restrict__ sc_src, size_t f,
-                                           float* sc_lds, uint16_t* xs, const ColWeights& cw,
-                                           uint32_t hmask, f32x4& tg, f32x4& tu) {
+__device__ __forceinline__ void bp_item(const uint16_t* __restrict__ xsrc,
+                                        const uint8_t* const (&pt)[2], int G,
+                                        const uint16_t* __restrict__ sc_src, size_t mat_stride,
+                                        float* sc_lds, uint16_t* xs, const ColWeights& cw,
+                                        uint32_t hmask, f32x4 (&acc)[2]) {
+  constexpr int NT = 2;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, kq = lane >> 4;
   const int st_tok = tid >> 4, st_pc = tid & 15;
-  uint32_t wg[kDQ][NB], wu[kDQ][NB];
+  uint32_t wv[kDQ][NT][NB];
   u32x4 xv[kDQ];
   auto load = [&](int g, int i) {
     xv[i] = *(const u32x4*)(xsrc + 128 * g);
 #pragma unroll
-    for (int c = 0; c < NB / 2; ++c) {
-      const uint2 a = *(const uint2*)(pg + (size_t)g * kBlockBytes + kBpPair * c);
-      const uint2 b = *(const uint2*)(pu + (size_t)g * kBlockBytes + kBpPair * c);
-      wg[i][2 * c] = a.x;
-      wg[i][2 * c + 1] = a.y;
-      wu[i][2 * c] = b.x;
-      wu[i][2 * c + 1] = b.y;
-    }
-    if (NB & 1) {
-      wg[i][NB - 1] = *(const uint32_t*)(pg + (size_t)g * kBlockBytes + kBpPair * (NB / 2));
-      wu[i][NB - 1] = *(const uint32_t*)(pu + (size_t)g * kBlockBytes + kBpPair * (NB / 2));
-    }
+    for (int c = 0; c < NB / 2; ++c)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint2 a = *(const uint2*)(pt[t] + (size_t)g * kBlockBytes + kBpPair * c);
+        wv[i][t][2 * c] = a.x;
+        wv[i][t][2 * c + 1] = a.y;
+      }
+    if (NB & 1)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        wv[i][t][NB - 1] =
+            *(const uint32_t*)(pt[t] + (size_t)g * kBlockBytes + kBpPair * (NB / 2));
   };
   ScaleStage<2, kSC ? kSC : 1> sst;
-  if (kSC) sst.fetch(sc_src, f, G);
+  if (kSC) sst.fetch(sc_src, mat_stride, G);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < kDQ; ++i) load(i < G ? i : G - 1, i);
@@ -342,7 +285,7 @@ __device__ __forceinline__ void bp_gu_item(const uint16_t* __restrict__ xsrc,
   if (kSC)
     sst.store(G, sc_lds);
   else
-    stage_scales_rows64<2>(sc_src, f, G, sc_lds);
+    stage_scales_rows64<2>(sc_src, mat_stride, G, sc_lds);
   auto step = [&](int gi, int i) {
     // slot gi & 1 was last read in step gi - 2, before the barrier of step gi - 1
     uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
@@ -351,11 +294,13 @@ __device__ __forceinline__ void bp_gu_item(const uint16_t* __restrict__ xsrc,
     bf16x8 xf[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) xf[j] = *(const bf16x8*)(slot + col * kXRow + 8 * (kq * 4 + j));
-    const f32x4 sg = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
-    const f32x4 su = *(const f32x4*)(sc_lds + (G + gi) * 64 + 16 * wave + 4 * kq);
+    f32x4 sv[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      sv[t] = *(const f32x4*)(sc_lds + (t * G + gi) * 64 + 16 * wave + 4 * kq);
     f32x4 seed, dx;
     bp_seeds(xf, seed, dx);
-    bp_group2<NB>(xf, seed, dx, wg[i], wu[i], cw, hmask, sg, su, tg, tu);
+    bp_group2<NB>(xf, seed, dx, wv[i][0], wv[i][1], cw, hmask, sv[0], sv[1], acc[0], acc[1]);
   };
   int g = 0;
   for (; g + 2 * kDQ <= G; g += kDQ) {
@@ -378,6 +323,11 @@ __device__ __forceinline__ void bp_gu_item(const uint16_t* __restrict__ xsrc,
     if (g + kDQ + i < G) step(g + kDQ + i, i);
 }
 
+// Gate/up: item = (token tile of up to 16 pairs, 64 features); wave w
+// computes features 16 w .. 16 w + 15 of the gate and up matrices.  (Two
+// such feature tiles per wave, one group of planes in flight instead of
+// two, read the same bytes per wave but were slower: 56.3 against 52.2 us
+// at the OLMoE-shaped layer, T = 16.)
 template <int kDQ, int kWaves, int kSC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
 void gateup_bp_decode(const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
@@ -411,27 +361,29 @@ void gateup_bp_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
     const int sp = spp[sj];
     asm volatile("" ::"v"(sp) : "memory");  // routing value taken before any plane load
     const uint16_t* xsrc = x + (size_t)(sp / k) * d + 8 * st_pc;
-    // plane words: tiles of 16 rows; row n0 + col of gate, f + n0 + col of up
-    const size_t rg = (size_t)tl.e * 2 * f + n0, ru = rg + f;
-    const uint8_t* pg = planes + (rg >> 4) * (size_t)G * kBlockBytes + 32 * col + 8 * kq;
-    const uint8_t* pu = planes + (ru >> 4) * (size_t)G * kBlockBytes + 32 * col + 8 * kq;
+    // plane words: tiles of 16 rows, (gate n0, up n0) = rows n0 and f + n0
+    const size_t rg = (size_t)tl.e * 2 * f + n0;
+    const uint8_t* pt[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      pt[t] = planes + ((rg + t * (size_t)f) >> 4) * (size_t)G * kBlockBytes + 32 * col + 8 * kq;
     const uint16_t* sc_src = scales + ((size_t)tl.e * 2 * f + nb) * G;
-    f32x4 tg = {0, 0, 0, 0}, tu = {0, 0, 0, 0};
+    f32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
     switch (maxb) {  // block-uniform
 #define BP_GU_CASE(N) \
   case N:             \
-    bp_gu_item<N, kDQ, kSC>(xsrc, pg, pu, G, sc_src, (size_t)f, sc_lds, xs, cw, hmask, tg, tu); \
+    bp_item<N, kDQ, kSC>(xsrc, pt, G, sc_src, f, sc_lds, xs, cw, hmask, acc); \
     break;
       BP_GU_CASE(1) BP_GU_CASE(2) BP_GU_CASE(3) BP_GU_CASE(4)
       BP_GU_CASE(5) BP_GU_CASE(6) BP_GU_CASE(7)
       default:
-        bp_gu_item<8, kDQ, kSC>(xsrc, pg, pu, G, sc_src, (size_t)f, sc_lds, xs, cw, hmask, tg, tu);
+        bp_item<8, kDQ, kSC>(xsrc, pt, G, sc_src, f, sc_lds, xs, cw, hmask, acc);
 #undef BP_GU_CASE
     }
     if (col < tl.cnt) {
       uint32_t hb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_rne(silu_f32(tg[i]) * tu[i]);
+      for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_rne(silu_f32(acc[0][i]) * acc[1][i]);
       uint2 pk;
       pk.x = hb[0] | (hb[1] << 16);
       pk.y = hb[2] | (hb[3] << 16);
@@ -442,82 +394,22 @@ void gateup_bp_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
 }
 
 // ------------------------------------------------------------------ down
-template <int NB, int kDQ, int kSC>
-__device__ __forceinline__ void bp_dn_item(const uint16_t* __restrict__ hsrc,
-                                           const uint8_t* __restrict__ pd, int G,
-                                           const uint16_t* __restrict__ sc_src, float* sc_lds,
-                                           uint16_t* xs, const ColWeights& cw, uint32_t hmask,
-                                           f32x4& acc) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col = lane & 15, kq = lane >> 4;
-  const int st_tok = tid >> 4, st_pc = tid & 15;
-  uint32_t wd[kDQ][NB];
-  u32x4 hv[kDQ];
-  auto load = [&](int g, int i) {
-    hv[i] = *(const u32x4*)(hsrc + 128 * g);
-#pragma unroll
-    for (int c = 0; c < NB / 2; ++c) {
-      const uint2 a = *(const uint2*)(pd + (size_t)g * kBlockBytes + kBpPair * c);
-      wd[i][2 * c] = a.x;
-      wd[i][2 * c + 1] = a.y;
-    }
-    if (NB & 1)
-      wd[i][NB - 1] = *(const uint32_t*)(pd + (size_t)g * kBlockBytes + kBpPair * (NB / 2));
-  };
-  ScaleStage<1, kSC ? kSC : 1> sst;
-  if (kSC) sst.fetch(sc_src, 0, G);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < kDQ; ++i) load(i < G ? i : G - 1, i);
-  __builtin_amdgcn_sched_barrier(0);
-  if (kSC)
-    sst.store(G, sc_lds);
-  else
-    stage_scales_rows64<1>(sc_src, 0, G, sc_lds);
-  auto step = [&](int gi, int i) {
-    uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
-    bp_stage8(slot + st_tok * kXRow, 8 * st_pc, hv[i]);
-    __syncthreads();
-    bf16x8 xf[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xf[j] = *(const bf16x8*)(slot + col * kXRow + 8 * (kq * 4 + j));
-    const f32x4 sv = *(const f32x4*)(sc_lds + gi * 64 + 16 * wave + 4 * kq);
-    f32x4 seed, dx;
-    bp_seeds(xf, seed, dx);
-    bp_group1<NB>(xf, seed, dx, wd[i], cw, hmask, sv, acc);
-  };
-  int g = 0;
-  for (; g + 2 * kDQ <= G; g += kDQ) {
-#pragma unroll
-    for (int i = 0; i < kDQ; ++i) {
-      step(g + i, i);
-      __builtin_amdgcn_sched_barrier(0);  // the slot's words are consumed first
-      load(g + i + kDQ, i);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kDQ; ++i) {
-    if (g + i >= G) break;
-    step(g + i, i);
-    if (g + i + kDQ < G) load(g + i + kDQ, i);
-  }
-#pragma unroll
-  for (int i = 0; i < kDQ; ++i)
-    if (g + kDQ + i < G) step(g + kDQ + i, i);
-}
-
+// Down with two row tiles per wave: item = (token tile of up to 16 pairs,
+// 128 output rows); wave w computes rows 16 w .. 16 w + 15 and 64 + 16 w ..
+// of the item through the gate/up item loop, so the h staging, its barrier
+// and the seed MFMAs of a group serve two row tiles, and the two tiles'
+// chains interleave on the matrix core.
 template <int kDQ, int kWaves, int kSC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves, 8)))
 void down_bp_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ offsets,
-                    const int32_t* __restrict__ sorted_pair, int E, int k, int d, int f,
-                    const uint8_t* __restrict__ planes, const uint16_t* __restrict__ scales,
-                    int bits_mode, const uint8_t* __restrict__ bits, float* __restrict__ y) {
+                     const int32_t* __restrict__ sorted_pair, int E, int k, int d, int f,
+                     const uint8_t* __restrict__ planes, const uint16_t* __restrict__ scales,
+                     int bits_mode, const uint8_t* __restrict__ bits, float* __restrict__ y) {
   extern __shared__ int32_t lds_i[];
-  const int G = f >> 7, RG = d / 64;
+  const int G = f >> 7, RG = d / 128;
   int32_t* off_lds = lds_i;
-  float* sc_lds = (float*)(lds_i + ((E + 1 + 3) & ~3));  // [G][64]
-  uint16_t* xs = (uint16_t*)(sc_lds + G * 64);           // [2][16][kXRow]
+  float* sc_lds = (float*)(lds_i + ((E + 1 + 3) & ~3));  // [2][G][64]
+  uint16_t* xs = (uint16_t*)(sc_lds + 2 * G * 64);       // [2][16][kXRow]
   for (int i = threadIdx.x; i <= E; i += blockDim.x) off_lds[i] = offsets[i];
   __syncthreads();
 
@@ -528,28 +420,35 @@ void down_bp_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
   for (int w = blockIdx.x;; w += gridDim.x) {
     TileInfo tl;
     if (!find_tile(off_lds, E, 16, w / RG, tl)) break;
-    const int mb = (w % RG) * 64, m0 = mb + 16 * wave;
+    const int mb = (w % RG) * 128, m0 = mb + 16 * wave;
     int maxb;
     uint32_t hmask;
     const int b = tile_bits(sorted_pair, tl.r0, tl.cnt, col, tl.e, k, bits_mode, bits, maxb, hmask);
     const ColWeights cw = col_weights(b);
     const uint16_t* hsrc = h + (size_t)(tl.r0 + (st_tok < tl.cnt ? st_tok : 0)) * f + 8 * st_pc;
-    const size_t rd0 = (size_t)tl.e * d + m0;
-    const uint8_t* pd = planes + (rd0 >> 4) * (size_t)G * kBlockBytes + 32 * col + 8 * kq;
+    const size_t r0 = (size_t)tl.e * d + m0;
+    const uint8_t* pt[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      pt[t] = planes + ((r0 + 64 * t) >> 4) * (size_t)G * kBlockBytes + 32 * col + 8 * kq;
     const uint16_t* sc_src = scales + ((size_t)tl.e * d + mb) * G;
-    f32x4 acc = {0, 0, 0, 0};
+    f32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
     switch (maxb) {  // block-uniform
 #define BP_DN_CASE(N) \
   case N:             \
-    bp_dn_item<N, kDQ, kSC>(hsrc, pd, G, sc_src, sc_lds, xs, cw, hmask, acc); \
+    bp_item<N, kDQ, kSC>(hsrc, pt, G, sc_src, 64, sc_lds, xs, cw, hmask, acc); \
     break;
       BP_DN_CASE(1) BP_DN_CASE(2) BP_DN_CASE(3) BP_DN_CASE(4)
       BP_DN_CASE(5) BP_DN_CASE(6) BP_DN_CASE(7)
       default:
-        bp_dn_item<8, kDQ, kSC>(hsrc, pd, G, sc_src, sc_lds, xs, cw, hmask, acc);
+        bp_item<8, kDQ, kSC>(hsrc, pt, G, sc_src, 64, sc_lds, xs, cw, hmask, acc);
 #undef BP_DN_CASE
     }
-    if (col < tl.cnt) *(f32x4*)(y + (size_t)(tl.r0 + col) * d + m0 + 4 * kq) = acc;
+    if (col < tl.cnt) {
+      float* yr = y + (size_t)(tl.r0 + col) * d + m0 + 4 * kq;
+      *(f32x4*)yr = acc[0];
+      *(f32x4*)(yr + 64) = acc[1];
+    }
     __syncthreads();
   }
 }
@@ -589,10 +488,10 @@ hipError_t launch_ffn_decode_bp(const FfnArgs& a, uint16_t* h, hipStream_t s) {
   }
   {
     const int G = a.f / 128;
-    const long long work = mt * (a.d / 64);
+    const long long work = mt * (a.d / 128);
     const int grid = (int)(work < cap ? work : cap);
-    const size_t lds = off_b + sizeof(float) * G * 64 + xs_b;
-    const int sc = scale_chunks(1, G, a.dn_scales);
+    const size_t lds = off_b + sizeof(float) * 2 * G * 64 + xs_b;
+    const int sc = scale_chunks(2, G, a.dn_scales);
     auto kern = sc == 1   ? down_bp_decode<kBpDnDQ, kBpDnWaves, 1>
                 : sc == 2 ? down_bp_decode<kBpDnDQ, kBpDnWaves, 2>
                 : sc == 4 ? down_bp_decode<kBpDnDQ, kBpDnWaves, 4>
