@@ -102,15 +102,19 @@ __device__ __forceinline__ int bp_slot(int k, int& sh) {
   return 32 * kq + 8 * j + 2 * d + h;
 }
 
+// bf16 bits of x 2^sh (exact: a power-of-two scaling).
+__device__ __forceinline__ uint16_t bp_scaled(uint32_t b16, int sh) {
+  const float f = __uint_as_float(b16 << 16) * (float)(1 << sh);
+  return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
 // Stage 8 consecutive activations (16 bytes at weight k0, k0 % 8 == 0).
 __device__ __forceinline__ void bp_stage8(uint16_t* __restrict__ row, int k0, u32x4 v) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint32_t b = (v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
     int sh;
     const int slot = bp_slot(k0 + i, sh);
-    const float f = __uint_as_float(b << 16) * (float)(1 << sh);
-    row[slot] = (uint16_t)(__float_as_uint(f) >> 16);
+    row[slot] = bp_scaled((v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu, sh);
   }
 }
 
@@ -247,8 +251,10 @@ __device__ __forceinline__ int tile_bits(const int32_t* __restrict__ sp, int r0,
 // waits then count exactly the loads issued after the one needed, and kDQ
 // groups stay in flight across the loop edge.  Scales are fetched before
 // the plane words and written to LDS after them.  Rows past the tile stage a
-// copy of its first row (they feed only unstored columns).
-template <int NB, int kDQ, int kSC>
+// copy of its first row (they feed only unstored columns).  kStaged: the
+// activation rows are stored already in the staged order and scaling (h as
+// the gate/up kernel writes it), so staging is a plain copy.
+template <int NB, int kDQ, int kSC, bool kStaged>
 __device__ __forceinline__ void bp_item(const uint16_t* __restrict__ xsrc,
                                         const uint8_t* const (&pt)[2], int G,
                                         const uint16_t* __restrict__ sc_src, size_t mat_stride,
@@ -289,7 +295,10 @@ __device__ __forceinline__ void bp_item(const uint16_t* __restrict__ xsrc,
   auto step = [&](int gi, int i) {
     // slot gi & 1 was last read in step gi - 2, before the barrier of step gi - 1
     uint16_t* slot = xs + (gi & 1) * 16 * kXRow;
-    bp_stage8(slot + st_tok * kXRow, 8 * st_pc, xv[i]);
+    if (kStaged)
+      *(u32x4*)(slot + st_tok * kXRow + 8 * st_pc) = xv[i];
+    else
+      bp_stage8(slot + st_tok * kXRow, 8 * st_pc, xv[i]);
     __syncthreads();
     bf16x8 xf[4];
 #pragma unroll
@@ -372,22 +381,33 @@ void gateup_bp_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
     switch (maxb) {  // block-uniform
 #define BP_GU_CASE(N) \
   case N:             \
-    bp_item<N, kDQ, kSC>(xsrc, pt, G, sc_src, f, sc_lds, xs, cw, hmask, acc); \
+    bp_item<N, kDQ, kSC, false>(xsrc, pt, G, sc_src, f, sc_lds, xs, cw, hmask, acc); \
     break;
       BP_GU_CASE(1) BP_GU_CASE(2) BP_GU_CASE(3) BP_GU_CASE(4)
       BP_GU_CASE(5) BP_GU_CASE(6) BP_GU_CASE(7)
       default:
-        bp_item<8, kDQ, kSC>(xsrc, pt, G, sc_src, f, sc_lds, xs, cw, hmask, acc);
+        bp_item<8, kDQ, kSC, false>(xsrc, pt, G, sc_src, f, sc_lds, xs, cw, hmask, acc);
 #undef BP_GU_CASE
     }
     if (col < tl.cnt) {
+      // h is stored per 128-group of the down pass's K in that pass's staged
+      // order and scaling (feature n at bp_slot(n % 128), times 2^sh), so the
+      // down kernel stages it with plain copies; the values are the bf16
+      // roundings of silu(g) u, scaled exactly.
+      // The lane's four features k .. k + 3 (k % 4 == 0) sit at bp_slot(k)
+      // + 0, 16, 2, 18 with the scalings of operand indices 2m, 2m, 2m + 1,
+      // 2m + 1 (m = (k % 16) / 4; kPos[i] = 2 (i % 3)).
+      uint16_t* hr = h + (size_t)(tl.r0 + col) * f + ((n0 >> 7) << 7);
+      const int k4 = (n0 + 4 * kq) & 127, m = (k4 & 15) >> 2;
+      const int s0 = 32 * (k4 >> 5) + 8 * (m >> 1) + 4 * (m & 1) + ((k4 >> 4) & 1);
+      const int sh0 = 7 - 2 * ((2 * m) % 3), sh1 = 7 - 2 * ((2 * m + 1) % 3);
       uint32_t hb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_rne(silu_f32(acc[0][i]) * acc[1][i]);
-      uint2 pk;
-      pk.x = hb[0] | (hb[1] << 16);
-      pk.y = hb[2] | (hb[3] << 16);
-      *(uint2*)(h + (size_t)(tl.r0 + col) * f + n0 + 4 * kq) = pk;
+      hr[s0] = bp_scaled(hb[0], sh0);
+      hr[s0 + 16] = bp_scaled(hb[1], sh0);
+      hr[s0 + 2] = bp_scaled(hb[2], sh1);
+      hr[s0 + 18] = bp_scaled(hb[3], sh1);
     }
     __syncthreads();  // the next item rewrites the scales and the slots
   }
@@ -436,12 +456,12 @@ void down_bp_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
     switch (maxb) {  // block-uniform
 #define BP_DN_CASE(N) \
   case N:             \
-    bp_item<N, kDQ, kSC>(hsrc, pt, G, sc_src, 64, sc_lds, xs, cw, hmask, acc); \
+    bp_item<N, kDQ, kSC, true>(hsrc, pt, G, sc_src, 64, sc_lds, xs, cw, hmask, acc); \
     break;
       BP_DN_CASE(1) BP_DN_CASE(2) BP_DN_CASE(3) BP_DN_CASE(4)
       BP_DN_CASE(5) BP_DN_CASE(6) BP_DN_CASE(7)
       default:
-        bp_item<8, kDQ, kSC>(hsrc, pt, G, sc_src, 64, sc_lds, xs, cw, hmask, acc);
+        bp_item<8, kDQ, kSC, true>(hsrc, pt, G, sc_src, 64, sc_lds, xs, cw, hmask, acc);
 #undef BP_DN_CASE
     }
     if (col < tl.cnt) {
