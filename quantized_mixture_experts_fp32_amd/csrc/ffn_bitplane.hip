@@ -14,20 +14,23 @@
 // f = 2 bit_2c + bit_2c+1 of every weight gives
 //   2^(7-2c) S_2c + 2^(6-2c) S_2c+1 = 2^(6-2c) F_c,  F_c = sum_k f_k x_k,
 // so one MFMA chain per plane pair covers both planes.  The A value of a
-// weight is 1 + f 2^(pos-7): 1.0 with the field in mantissa bits pos and
-// pos + 1 (pos = 0, 2 or 4 by the weight's place in the operand), placed by
-// one v_bitop3 per two weights from a word holding the fields of 16
-// weights (two v_bitop3 merge the two plane words into such words for the
-// even and the odd weights).  The staged activation is x 2^(7-pos) (an
-// exact power-of-two scaling), so the product is x 2^(7-pos) + f x.  Each
-// chain starts from -X' (X' = sum_k x_k 2^(7-pos_k), four MFMAs with A = -1
-// shared by all chains and both matrices), so it ends at F_c.  A pair that
+// weight is 2^(7-pos) + f: 2^(7-pos) with the field in mantissa bits pos
+// and pos + 1 (pos = 0, 2 or 4 by the weight's place in the operand; the
+// mantissa ulp of 2^(7-pos) is 2^(pos-7), so the field adds f exactly),
+// placed by one v_bitop3 per two weights from a word holding the fields of
+// 16 weights (two v_bitop3 merge the two plane words into such words for
+// the even and the odd weights).  The product with the staged activation
+// is x 2^(7-pos) + f x.  Each chain starts from -X' (X' = sum_k x_k
+// 2^(7-pos_k), four MFMAs with A = -2^(7-pos) shared by all chains and both
+// matrices), so it ends at F_c.  A pair that
 // a column's odd width splits (b = 2c + 1) uses the half chain H_c of plane
 // 2c alone (field 2 bit_2c, the same scheme with a zero second plane), which
 // gives 2 S_2c.  Every lane owns one token column: it weights F_c by
 // 2^(6-2c) when b >= 2c + 2 and H_c by 2^(6-2c) when b = 2c + 1, adds c_b X
-// (X from four more MFMAs whose A is 2^(pos-7)), and the fp16 group scale
+// (X from four more MFMAs whose A is 1), and the fp16 group scale
 // multiplies the group sum in fp32.  Dequantized weights are never rounded.
+// Activations are staged in the operand order (a permutation of each
+// 128-group, bp_run) and unscaled.
 //
 // Layout (ABI header, kcommon.hpp): per 16-row tile and 128-group a 2 KiB
 // block holds four plane pairs of 512 bytes (most significant first); row
@@ -74,10 +77,14 @@ __device__ __forceinline__ void bp_merge_half(uint32_t wp, uint32_t& E, uint32_t
   O = wp & 0xAAAAAAAAu;
 }
 
+// bf16 2^(7 - pos) of operand slot i in both halves (sign bit: negated).
+__device__ constexpr uint32_t bp_pow2(int i, uint32_t sign = 0) {
+  return (sign | (uint32_t)(134 - kPos[i]) << 7) * 0x10001u;
+}
+
 // Field words -> the A operands of the chain's four MFMAs (LUT 0xEA:
-// (a & b) | c; c = 1.0 in both halves).
+// (a & b) | c; c = 2^(7 - pos) in both halves).
 __device__ __forceinline__ void bp_frags(uint32_t E, uint32_t O, bf16x8 (&a)[4]) {
-  const uint32_t C = 0x3F803F80u;
   const uint32_t w[2][3] = {{E, E >> 6, E >> 12}, {O, O >> 6, O >> 12}};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -86,36 +93,30 @@ __device__ __forceinline__ void bp_frags(uint32_t E, uint32_t O, bf16x8 (&a)[4])
     for (int d = 0; d < 4; ++d) {
       const int o = 4 * j + d, par = o >> 3, i = o & 7;
       const uint32_t M = (3u << kPos[i]) | (3u << (kPos[i] + 16));
-      r[d] = __builtin_amdgcn_bitop3_b32(w[par][kShift[i] / 6], M, C, 0xEA);
+      r[d] = __builtin_amdgcn_bitop3_b32(w[par][kShift[i] / 6], M, bp_pow2(i), 0xEA);
     }
     a[j] = __builtin_bit_cast(bf16x8, r);
   }
 }
 
-// Place of weight k (0..127) of a group in a staged token row (the B
-// fragment order), and the exponent of its scaling 2^(7 - pos).
-__device__ __forceinline__ int bp_slot(int k, int& sh) {
-  const int kq = k >> 5, e = k & 31;
-  const int h = (e >> 4) & 1, rem = e & 15, par = rem & 1, i = rem >> 1;
-  const int o = 8 * par + i, j = o >> 2, d = o & 3;
-  sh = 7 - kPos[i];
-  return 32 * kq + 8 * j + 2 * d + h;
+// Staged order of a 128-group (the B fragment order): weight k sits at
+// slot 32 (k / 32) + 8 j + 2 d + h, with h = (k / 16) % 2 and operand index
+// o = 4 j + d = 8 (k % 2) + (k % 16) / 2.  The weights k0 + t and
+// k0 + 16 + t (k0 % 32 = 4 m, m < 4, t < 4) fill the two 8-byte runs at
+// s0 = 32 (k0 / 32) + 8 (m / 2) + 4 (m % 2) and s0 + 16: run s0 holds
+// k0, k0 + 16, k0 + 2, k0 + 18 and run s0 + 16 holds k0 + 1, k0 + 17,
+// k0 + 3, k0 + 19.
+__device__ __forceinline__ int bp_run(int k0) {
+  const int m = (k0 & 15) >> 2;
+  return 32 * (k0 >> 5) + 8 * (m >> 1) + 4 * (m & 1);
 }
 
-// bf16 bits of x 2^sh (exact: a power-of-two scaling).
-__device__ __forceinline__ uint16_t bp_scaled(uint32_t b16, int sh) {
-  const float f = __uint_as_float(b16 << 16) * (float)(1 << sh);
-  return (uint16_t)(__float_as_uint(f) >> 16);
-}
-
-// Stage 8 consecutive activations (16 bytes at weight k0, k0 % 8 == 0).
-__device__ __forceinline__ void bp_stage8(uint16_t* __restrict__ row, int k0, u32x4 v) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int sh;
-    const int slot = bp_slot(k0 + i, sh);
-    row[slot] = bp_scaled((v[i >> 1] >> (16 * (i & 1))) & 0xFFFFu, sh);
-  }
+// Stage the 8 weights of one thread: lo = weights k0 .. k0 + 3, hi =
+// k0 + 16 .. k0 + 19 (bf16 pairs), into the runs at s0 and s0 + 16.
+__device__ __forceinline__ void bp_stage8(uint16_t* __restrict__ row, int s0, u32x4 v) {
+  const uint32_t lx = v[0], ly = v[1], hx = v[2], hy = v[3];
+  *(uint2*)(row + s0) = uint2{(lx & 0xFFFFu) | (hx << 16), (ly & 0xFFFFu) | (hy << 16)};
+  *(uint2*)(row + s0 + 16) = uint2{(lx >> 16) | (hx & 0xFFFF0000u), (ly >> 16) | (hy & 0xFFFF0000u)};
 }
 
 __device__ __forceinline__ bf16x8 splat2(uint32_t bits16) {
@@ -141,7 +142,7 @@ __device__ __forceinline__ ColWeights col_weights(int b) {
   return c;
 }
 
-// Seeds of a group: -X' (A = -1) and X (A = 2^(pos-7) per operand slot).
+// Seeds of a group: -X' (A = -2^(7-pos) per operand slot) and X (A = 1).
 __device__ __forceinline__ void bp_seeds(const bf16x8 (&xf)[4], f32x4& seed, f32x4& dx) {
   seed = f32x4{0, 0, 0, 0};
   dx = f32x4{0, 0, 0, 0};
@@ -149,12 +150,9 @@ __device__ __forceinline__ void bp_seeds(const bf16x8 (&xf)[4], f32x4& seed, f32
   for (int j = 0; j < 4; ++j) {
     u32x4 r;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t e = (uint32_t)(120 + kPos[(4 * j + d) & 7]) << 7;  // 2^(pos-7)
-      r[d] = e | (e << 16);
-    }
-    seed = mfma16(splat2(0xBF80u), xf[j], seed);
-    dx = mfma16(__builtin_bit_cast(bf16x8, r), xf[j], dx);
+    for (int d = 0; d < 4; ++d) r[d] = bp_pow2((4 * j + d) & 7, 0x8000u);
+    seed = mfma16(__builtin_bit_cast(bf16x8, r), xf[j], seed);
+    dx = mfma16(splat2(0x3F80u), xf[j], dx);
   }
 }
 
@@ -252,8 +250,11 @@ __device__ __forceinline__ int tile_bits(const int32_t* __restrict__ sp, int r0,
 // groups stay in flight across the loop edge.  Scales are fetched before
 // the plane words and written to LDS after them.  Rows past the tile stage a
 // copy of its first row (they feed only unstored columns).  kStaged: the
-// activation rows are stored already in the staged order and scaling (h as
-// the gate/up kernel writes it), so staging is a plain copy.
+// activation rows are stored already in the staged order (h as the gate/up
+// kernel writes it): xsrc points at the thread's 16 bytes of group 0 and
+// staging is a plain copy.  Otherwise xsrc points at weight k0 of group 0
+// (k0 = 32 (st_pc / 4) + 4 (st_pc % 4)) and the thread loads weights
+// k0 .. k0 + 3 and k0 + 16 .. k0 + 19 and stores them as two runs.
 template <int NB, int kDQ, int kSC, bool kStaged>
 __device__ __forceinline__ void bp_item(const uint16_t* __restrict__ xsrc,
                                         const uint8_t* const (&pt)[2], int G,
@@ -267,7 +268,12 @@ __device__ __forceinline__ void bp_item(const uint16_t* __restrict__ xsrc,
   uint32_t wv[kDQ][NT][NB];
   u32x4 xv[kDQ];
   auto load = [&](int g, int i) {
-    xv[i] = *(const u32x4*)(xsrc + 128 * g);
+    if (kStaged) {
+      xv[i] = *(const u32x4*)(xsrc + 128 * g);
+    } else {
+      const uint2 lo = *(const uint2*)(xsrc + 128 * g), hi = *(const uint2*)(xsrc + 128 * g + 16);
+      xv[i] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
 #pragma unroll
     for (int c = 0; c < NB / 2; ++c)
 #pragma unroll
@@ -298,7 +304,7 @@ __device__ __forceinline__ void bp_item(const uint16_t* __restrict__ xsrc,
     if (kStaged)
       *(u32x4*)(slot + st_tok * kXRow + 8 * st_pc) = xv[i];
     else
-      bp_stage8(slot + st_tok * kXRow, 8 * st_pc, xv[i]);
+      bp_stage8(slot + st_tok * kXRow, bp_run(32 * (st_pc >> 2) + 4 * (st_pc & 3)), xv[i]);
     __syncthreads();
     bf16x8 xf[4];
 #pragma unroll
@@ -369,7 +375,7 @@ void gateup_bp_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
     const int sj = tl.r0 + (st_tok < tl.cnt ? st_tok : 0);
     const int sp = spp[sj];
     asm volatile("" ::"v"(sp) : "memory");  // routing value taken before any plane load
-    const uint16_t* xsrc = x + (size_t)(sp / k) * d + 8 * st_pc;
+    const uint16_t* xsrc = x + (size_t)(sp / k) * d + 32 * (st_pc >> 2) + 4 * (st_pc & 3);
     // plane words: tiles of 16 rows, (gate n0, up n0) = rows n0 and f + n0
     const size_t rg = (size_t)tl.e * 2 * f + n0;
     const uint8_t* pt[2];
@@ -391,23 +397,19 @@ void gateup_bp_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
     }
     if (col < tl.cnt) {
       // h is stored per 128-group of the down pass's K in that pass's staged
-      // order and scaling (feature n at bp_slot(n % 128), times 2^sh), so the
-      // down kernel stages it with plain copies; the values are the bf16
-      // roundings of silu(g) u, scaled exactly.
-      // The lane's four features k .. k + 3 (k % 4 == 0) sit at bp_slot(k)
-      // + 0, 16, 2, 18 with the scalings of operand indices 2m, 2m, 2m + 1,
-      // 2m + 1 (m = (k % 16) / 4; kPos[i] = 2 (i % 3)).
+      // order, so the down kernel stages it with plain copies.  The lane's
+      // features k4 .. k4 + 3 (k4 % 4 == 0) sit at s + 0, 16, 2, 18 with
+      // s = bp_run(k4) + (k4 / 16) % 2.
       uint16_t* hr = h + (size_t)(tl.r0 + col) * f + ((n0 >> 7) << 7);
-      const int k4 = (n0 + 4 * kq) & 127, m = (k4 & 15) >> 2;
-      const int s0 = 32 * (k4 >> 5) + 8 * (m >> 1) + 4 * (m & 1) + ((k4 >> 4) & 1);
-      const int sh0 = 7 - 2 * ((2 * m) % 3), sh1 = 7 - 2 * ((2 * m + 1) % 3);
-      uint32_t hb[4];
+      const int k4 = (n0 + 4 * kq) & 127, s = bp_run(k4) + ((k4 >> 4) & 1);
+      uint16_t hb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_rne(silu_f32(acc[0][i]) * acc[1][i]);
-      hr[s0] = bp_scaled(hb[0], sh0);
-      hr[s0 + 16] = bp_scaled(hb[1], sh0);
-      hr[s0 + 2] = bp_scaled(hb[2], sh1);
-      hr[s0 + 18] = bp_scaled(hb[3], sh1);
+      for (int i = 0; i < 4; ++i)
+        hb[i] = (uint16_t)f32_to_bf16_rne(silu_f32(acc[0][i]) * acc[1][i]);
+      hr[s] = hb[0];
+      hr[s + 16] = hb[1];
+      hr[s + 2] = hb[2];
+      hr[s + 18] = hb[3];
     }
     __syncthreads();  // the next item rewrites the scales and the slots
   }
