@@ -486,72 +486,100 @@ __device__ __forceinline__ bf16x8 w4_top_bp(uint32_t w, uint32_t D) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Pairs of one expert grouped by width: counts per (expert, width) by
-// ballots over each expert's slots, width-ordered slot lists (stable), and
-// the 128-pair tiles of every (expert, width).  One 1024-thread block.
-__global__ __launch_bounds__(1024) void bp_pf_prep(const int32_t* __restrict__ offsets,
+// Pairs of one expert grouped by width, in two launches of one 256-thread
+// block per expert.  bp_pf_count: cnt[8 e + w] = pairs of expert e with
+// width w + 1 (ballots over the expert's slots).  bp_pf_scatter: the
+// expert's slots listed by width, each width in slot order (stable), and
+// the 128-pair tiles of every (expert, width), numbered in (expert, width)
+// order; the block of the last expert stores the tile count.
+__global__ __launch_bounds__(256) void bp_pf_count(const int32_t* __restrict__ offsets,
                                                    const int32_t* __restrict__ sorted_pair,
-                                                   int E, int k, int mode,
+                                                   int k, int mode,
                                                    const uint8_t* __restrict__ bits,
-                                                   int32_t* __restrict__ bslot,
-                                                   PTile* __restrict__ tiles,
-                                                   int* __restrict__ num_tiles) {
-  extern __shared__ int32_t lds[];
-  int32_t* cnt = lds;              // [E][8]
-  int32_t* sbase = lds + 8 * E;    // [E][8] first bslot index of (e, width)
-  int32_t* tbase = lds + 16 * E;   // [E][8] first tile of (e, width)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                                                   int32_t* __restrict__ cnt) {
+  __shared__ int32_t part[4][8];
+  const int e = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lo = offsets[e], n = offsets[e + 1] - lo;
+  int c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int i0 = 0; i0 < n; i0 += 256) {
+    const int i = i0 + (int)threadIdx.x;
+    const int b = i < n ? pair_bit_width(sorted_pair[lo + i], e, k, mode, bits) : 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) c[w] += __popcll(__ballot(b == w + 1));
+  }
+  if (lane < 8) {
+    int v = c[0];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) v = lane == w ? c[w] : v;
+    part[wave][lane] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 8) {
+    const int w = threadIdx.x;
+    cnt[8 * e + w] = part[0][w] + part[1][w] + part[2][w] + part[3][w];
+  }
+}
+
+__global__ __launch_bounds__(256) void bp_pf_scatter(const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ sorted_pair,
+                                                     int E, int k, int mode,
+                                                     const uint8_t* __restrict__ bits,
+                                                     const int32_t* __restrict__ cnt,
+                                                     int32_t* __restrict__ bslot,
+                                                     PTile* __restrict__ tiles,
+                                                     int* __restrict__ num_tiles) {
+  __shared__ int32_t red[4];
+  __shared__ int32_t sbase[8], tbase[8];
+  __shared__ int32_t chunk[4][8];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // tiles of the experts below e
+  int t = 0;
+  for (int j = tid; j < 8 * e; j += 256) t += (cnt[j] + kBT - 1) / kBT;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, kWave);
+  if (lane == 0) red[wave] = t;
+  __syncthreads();
+  if (tid < 8) {
+    int sb = offsets[e], tb = red[0] + red[1] + red[2] + red[3];
+    for (int w = 0; w < tid; ++w) {
+      sb += cnt[8 * e + w];
+      tb += (cnt[8 * e + w] + kBT - 1) / kBT;
+    }
+    sbase[tid] = sb;
+    tbase[tid] = tb;
+    const int nw = cnt[8 * e + tid];
+    for (int c2 = 0; c2 * kBT < nw; ++c2)
+      tiles[tb + c2] = PTile{e, sb + c2 * kBT, min(kBT, nw - c2 * kBT), tid + 1};
+    if (e == E - 1 && tid == 7) *num_tiles = tb + (nw + kBT - 1) / kBT;
+  }
+  __syncthreads();
+  // slot lists: 256 slots per round; a slot's place within its width is the
+  // count of earlier slots of that width (earlier rounds, earlier waves of
+  // this round, lower lanes of its wave)
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  for (int e = wave; e < E; e += 16) {
-    const int lo = offsets[e], n = offsets[e + 1] - lo;
-    int c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int i0 = 0; i0 < n; i0 += 64) {
-      const int i = i0 + lane;
-      const int b = i < n ? pair_bit_width(sorted_pair[lo + i], e, k, mode, bits) : 0;
+  const int lo = offsets[e], n = offsets[e + 1] - lo;
+  int run[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int i0 = 0; i0 < n; i0 += 256) {
+    const int i = i0 + tid;
+    const int b = i < n ? pair_bit_width(sorted_pair[lo + i], e, k, mode, bits) : 0;
+    uint64_t mine = 0;
+    int cw = 0;
 #pragma unroll
-      for (int w = 0; w < 8; ++w) c[w] += __popcll(__ballot(b == w + 1));
+    for (int w = 0; w < 8; ++w) {
+      const uint64_t m = __ballot(b == w + 1);
+      if (b == w + 1) mine = m;
+      if (lane == w) cw = __popcll(m);
     }
-    if (lane < 8) {
-      int v = c[0];
+    if (lane < 8) chunk[wave][lane] = cw;
+    __syncthreads();
+    if (b) {
+      int pos = sbase[b - 1] + run[b - 1] + __popcll(mine & below);
+      for (int v = 0; v < wave; ++v) pos += chunk[v][b - 1];
+      bslot[pos] = lo + i;
+    }
 #pragma unroll
-      for (int w = 1; w < 8; ++w) v = lane == w ? c[w] : v;
-      cnt[8 * e + lane] = v;
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int tiles_run = 0;
-    for (int e = 0; e < E; ++e) {
-      int s = offsets[e];
-      for (int w = 0; w < 8; ++w) {
-        sbase[8 * e + w] = s;
-        tbase[8 * e + w] = tiles_run;
-        s += cnt[8 * e + w];
-        tiles_run += (cnt[8 * e + w] + kBT - 1) / kBT;
-      }
-    }
-    *num_tiles = tiles_run;
-  }
-  __syncthreads();
-  for (int e = wave; e < E; e += 16) {
-    const int lo = offsets[e], n = offsets[e + 1] - lo;
-    int run[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int i0 = 0; i0 < n; i0 += 64) {
-      const int i = i0 + lane;
-      const int b = i < n ? pair_bit_width(sorted_pair[lo + i], e, k, mode, bits) : 0;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const uint64_t m = __ballot(b == w + 1);
-        if (b == w + 1) bslot[sbase[8 * e + w] + run[w] + __popcll(m & below)] = lo + i;
-        run[w] += __popcll(m);
-      }
-    }
-    for (int w = lane; w < 8; w += 64) {
-      const int nw = cnt[8 * e + w];
-      for (int c2 = 0; c2 * kBT < nw; ++c2)
-        tiles[tbase[8 * e + w] + c2] =
-            PTile{e, sbase[8 * e + w] + c2 * kBT, min(kBT, nw - c2 * kBT), w + 1};
-    }
+    for (int w = 0; w < 8; ++w) run[w] += chunk[0][w] + chunk[1][w] + chunk[2][w] + chunk[3][w];
+    __syncthreads();  // the next round rewrites chunk
   }
 }
 
@@ -941,7 +969,8 @@ size_t ffn_prefill_ws_bytes(int T, int k, int E, int d, int f) {
   const size_t tiles = pf_max_tiles(P, E);
   auto a256 = [](size_t v) { return (v + 255) & ~(size_t)255; };
   return 256 + a256(tiles * sizeof(PTile)) + a256((size_t)T * (d / 128) * 8) +
-         a256((size_t)P * (f / 128) * 8) + a256((size_t)P * sizeof(int32_t));
+         a256((size_t)P * (f / 128) * 8) + a256((size_t)P * sizeof(int32_t)) +
+         a256((size_t)E * 8 * sizeof(int32_t));
 }
 
 hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStream_t s) {
@@ -973,7 +1002,8 @@ hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStr
   return hipGetLastError();
 }
 
-// Bitplane experts, prefill: tiles of one expert and one width (bp_pf_prep),
+// Bitplane experts, prefill: tiles of one expert and one width (bp_pf_count,
+// bp_pf_scatter),
 // then the same two GEMM launches with plane words in place of codes.
 hipError_t launch_ffn_prefill_bp(const FfnArgs& a, uint16_t* h, void* ws, hipStream_t s) {
   const long long P = (long long)a.T * a.k;
@@ -985,9 +1015,12 @@ hipError_t launch_ffn_prefill_bp(const FfnArgs& a, uint16_t* h, void* ws, hipStr
   uint2* xsum = (uint2*)(w + 256 + a256(mt * sizeof(PTile)));
   uint2* hsum = (uint2*)((char*)xsum + a256((size_t)a.T * (a.d / 128) * 8));
   int32_t* bslot = (int32_t*)((char*)hsum + a256((size_t)P * (a.f / 128) * 8));
+  int32_t* cnt = (int32_t*)((char*)bslot + a256((size_t)P * sizeof(int32_t)));
 
-  hipLaunchKernelGGL(bp_pf_prep, dim3(1), dim3(1024), sizeof(int32_t) * 24 * a.E, s, a.offsets,
-                     a.sorted_pair, a.E, a.k, a.bits_mode, a.bits, bslot, tiles, num_tiles);
+  hipLaunchKernelGGL(bp_pf_count, dim3(a.E), dim3(256), 0, s, a.offsets, a.sorted_pair, a.k,
+                     a.bits_mode, a.bits, cnt);
+  hipLaunchKernelGGL(bp_pf_scatter, dim3(a.E), dim3(256), 0, s, a.offsets, a.sorted_pair, a.E,
+                     a.k, a.bits_mode, a.bits, (const int32_t*)cnt, bslot, tiles, num_tiles);
   {
     const long long n = (long long)a.T * (a.d / 128);
     hipLaunchKernelGGL(group_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.x,
