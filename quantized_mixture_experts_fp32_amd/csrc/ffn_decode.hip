@@ -187,12 +187,35 @@ void gateup_w4_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
         for (int j = 0; j < 4; ++j) v[c][j] = *(const u32x4*)(xg + 8 * j);
       }
     };
+    // The item's scales: with at most 1024 of them, G % 4 == 0 and 8-byte
+    // aligned rows, one 8-byte piece (4 groups of one row) per thread,
+    // fetched before the code loads so that both share one round trip
+    // (staging them one by one after the barrier costs a round trip per
+    // 256 scales); otherwise staged one by one.
+    const int nsc = 2 * 16 * RT * G;
+    const bool vsc = (G & 3) == 0 && nsc <= 4 * 256 && ((uintptr_t)scales & 7) == 0;
+    const int scc = min((int)threadIdx.x, nsc / 4 - 1);
+    const int sc_m = (4 * scc) / (16 * RT * G), sc_rem = 4 * scc - sc_m * 16 * RT * G;
+    uint2 scv = {0u, 0u};
+    if (vsc)
+      scv = *(const uint2*)(scales + (erow + nb + (size_t)sc_m * f) * G + sc_rem);
 #pragma unroll
     for (int i = 0; i < kDepth; ++i)
       if (gb + i < ge) load(gb + i, qg[i], qu[i], xv[i]);
 
     __syncthreads();  // previous item is done with sc_lds / red
-    stage_scales_f32(scales + (erow + nb) * G, (size_t)f, 2, 16 * RT, G, sc_lds);
+    if (vsc) {
+      if ((int)threadIdx.x < nsc / 4) {
+        const int r = sc_rem / G, g0 = sc_rem % G;
+        float* dd = sc_lds + (sc_m * G + g0) * (16 * RT) + r;
+        dd[0] = f16_bits_to_f32(scv.x & 0xFFFFu);
+        dd[16 * RT] = f16_bits_to_f32(scv.x >> 16);
+        dd[32 * RT] = f16_bits_to_f32(scv.y & 0xFFFFu);
+        dd[48 * RT] = f16_bits_to_f32(scv.y >> 16);
+      }
+    } else {
+      stage_scales_f32(scales + (erow + nb) * G, (size_t)f, 2, 16 * RT, G, sc_lds);
+    }
     __syncthreads();
 
     f32x4 tg[NT], tu[NT];
@@ -622,9 +645,11 @@ void down_w4_decode_lds(const uint16_t* __restrict__ h, const int32_t* __restric
 
 // kDepth: 128-groups of codes + activations in flight per wave; kWaves:
 // the occupancy the register allocation is held to (measured on MI355X:
-// occupancy matters more than prefetch depth, and spilling variants lose).
+// occupancy matters more than prefetch depth, and spilling variants lose;
+// the single-tile K-split gate/up at three waves per SIMD was 33 % slower
+// than at four).
 template <int KS, int NT> constexpr int gu_depth() { return 1; }
-template <int KS, int NT> constexpr int gu_waves() { return NT == 1 ? (KS == 1 ? 4 : 3) : 2; }
+template <int KS, int NT> constexpr int gu_waves() { return NT == 1 ? 4 : 2; }
 template <int KS, int NT> constexpr int dn_depth() { return NT == 1 ? 2 : 1; }
 template <int KS, int NT> constexpr int dn_waves() { return NT == 1 ? 4 : 2; }
 
