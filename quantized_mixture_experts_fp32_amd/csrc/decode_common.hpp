@@ -57,13 +57,30 @@ __device__ __forceinline__ bf16x8 bf16_splat(uint32_t bits16) {
 // HBM: all of a wave's code, scale and activation loads are issued together.
 constexpr int kPairsInLds = 4096;
 
+// For 256-thread blocks.  Loads are issued four per thread at a time
+// (indices clamped in range), then stored, so that staging takes one round
+// trip per 1024 entries instead of one per 256.
 __device__ __forceinline__ int stage_routing(const int32_t* __restrict__ offsets,
                                              const int32_t* __restrict__ sorted_pair,
                                              int E, int P, int32_t* off_lds,
                                              int32_t* sp_lds) {
-  for (int i = threadIdx.x; i <= E; i += blockDim.x) off_lds[i] = offsets[i];
   const int np = P <= kPairsInLds ? P : 0;
-  for (int i = threadIdx.x; i < np; i += blockDim.x) sp_lds[i] = sorted_pair[i];
+  constexpr int bd = 256;
+  for (int i0 = threadIdx.x; i0 <= E || i0 < np; i0 += 4 * bd) {
+    int32_t vo[4], vs[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * bd;
+      vo[u] = offsets[i <= E ? i : E];
+      vs[u] = np ? sorted_pair[i < np ? i : np - 1] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * bd;
+      if (i <= E) off_lds[i] = vo[u];
+      if (i < np) sp_lds[i] = vs[u];
+    }
+  }
   return np;
 }
 
