@@ -749,8 +749,15 @@ void launch_dn_lds_rt(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s)
            a.f, a.dn_codes, a.dn_scales, a.y);
 }
 
+// kDnLdsRT row tiles per wave, unless that leaves fewer than two blocks per
+// CU (a token or two: then one row tile per wave with kDnDQ groups in
+// flight; measured at E = 256, T = 1: 11.8 -> 11.2 us, OLMoE-shaped T = 1:
+// 6.2 -> 5.7 us; at E = 256, T = 64 two row tiles stay faster, 82.6 against
+// 95.7 us).
 void launch_dn_lds(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
-  if (a.d % (64 * kDnLdsRT) == 0)
+  const long long mt = (P + 15) / 16 + (P < a.E ? P : a.E);
+  const bool few = mt * (a.d / (64 * kDnLdsRT)) < 512;
+  if (a.d % (64 * kDnLdsRT) == 0 && !few)
     launch_dn_lds_rt<kDnLdsDQ, kDnLdsRT>(a, h, P, s);
   else
     launch_dn_lds_rt<kDnDQ, 1>(a, h, P, s);
