@@ -90,6 +90,50 @@ __device__ __forceinline__ void tile_group(const bf16x8 (&xp)[4], const f32x4 se
   for (int i = 0; i < 4; ++i) acc[i] = fmaf(sv[i], p[i], acc[i]);
 }
 
+// Routing of a K-split gate/up block.  With kLg the block selects and
+// groups the batch itself from the router logits [T][E] (block 0 stores
+// every routing output; scratch: 128 + E ints of LDS); otherwise it stages
+// expert_offsets and sorted_pair.  Returns the pairs staged in sp_lds (0:
+// sorted_pair is read from global memory).
+template <bool kLg>
+__device__ __forceinline__ int ks_route(const int32_t* __restrict__ offsets,
+                                        const int32_t* __restrict__ sorted_pair, int E, int k,
+                                        int P, const float* __restrict__ logits,
+                                        int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                        int32_t* __restrict__ offsets_out,
+                                        int32_t* __restrict__ sorted_pair_out,
+                                        int32_t* __restrict__ pair_pos_out, int32_t* off_lds,
+                                        int32_t* sp_lds, int32_t* scratch) {
+  if constexpr (kLg) {
+    int32_t* idx_lds = scratch;      // [64] experts of the pairs
+    int32_t* pp_lds = idx_lds + 64;  // [64] slot of each pair
+    int32_t* cnt_lds = pp_lds + 64;  // [E]
+    const bool store = blockIdx.x == 0;
+    const int T = P / k, lane = threadIdx.x & 63;
+    for (int t = threadIdx.x >> 6; t < T; t += 4) {  // wave-uniform
+      int32_t* io = store ? idx_out + (size_t)t * k : nullptr;
+      float* wo = store ? w_out + (size_t)t * k : nullptr;
+      select_topk_radix64(lane < E ? logits[(size_t)t * E + lane] : 0.0f, E, k, io, wo,
+                          idx_lds + t * k);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) permute_wave_small(idx_lds, P, E, off_lds, sp_lds, pp_lds, cnt_lds);
+    __syncthreads();
+    if (store) {
+      for (int i = threadIdx.x; i <= E; i += blockDim.x) offsets_out[i] = off_lds[i];
+      for (int i = threadIdx.x; i < P; i += blockDim.x) {
+        sorted_pair_out[i] = sp_lds[i];
+        pair_pos_out[i] = pp_lds[i];
+      }
+    }
+    return P;
+  } else {
+    const int np = stage_routing(offsets, sorted_pair, E, P, off_lds, sp_lds);
+    __syncthreads();
+    return np;
+  }
+}
+
 // ------------------------------------------------------------- gate / up
 // Work item = (token tile of up to 16*NT pairs, row group of RT = 4/KS row
 // tiles of 16 features).  Wave (rt, ks) streams gate and up codes of its row
@@ -117,34 +161,9 @@ void gateup_w4_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
   int32_t* sp_lds = lds_i + ((E + 1 + 3) & ~3);
   float* sc_lds = (float*)(sp_lds + ((min(P, kPairsInLds) + 3) & ~3));  // [2][G][16 RT]
   f32x4* red = (f32x4*)(sc_lds + 2 * G * 16 * RT);                       // [4][NT][2][64]
-  int np;
-  if constexpr (kLg) {
-    int32_t* idx_lds = (int32_t*)(red + 4 * NT * 2 * 64);  // [64] experts of the pairs
-    int32_t* pp_lds = idx_lds + 64;                        // [64] slot of each pair
-    int32_t* cnt_lds = pp_lds + 64;                        // [E]
-    const bool store = blockIdx.x == 0;
-    const int T = P / k, lane = threadIdx.x & 63;
-    for (int t = threadIdx.x >> 6; t < T; t += 4) {  // wave-uniform
-      int32_t* io = store ? idx_out + (size_t)t * k : nullptr;
-      float* wo = store ? w_out + (size_t)t * k : nullptr;
-      select_topk_radix64(lane < E ? logits[(size_t)t * E + lane] : 0.0f, E, k, io, wo,
-                          idx_lds + t * k);
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) permute_wave_small(idx_lds, P, E, off_lds, sp_lds, pp_lds, cnt_lds);
-    __syncthreads();
-    if (store) {
-      for (int i = threadIdx.x; i <= E; i += blockDim.x) offsets_out[i] = off_lds[i];
-      for (int i = threadIdx.x; i < P; i += blockDim.x) {
-        sorted_pair_out[i] = sp_lds[i];
-        pair_pos_out[i] = pp_lds[i];
-      }
-    }
-    np = P;
-  } else {
-    np = stage_routing(offsets, sorted_pair, E, P, off_lds, sp_lds);
-    __syncthreads();
-  }
+  const int np = ks_route<kLg>(offsets, sorted_pair, E, k, P, logits, idx_out, w_out,
+                               offsets_out, sorted_pair_out, pair_pos_out, off_lds, sp_lds,
+                               (int32_t*)(red + 4 * NT * 2 * 64));
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, kq = lane >> 4;
@@ -280,6 +299,225 @@ void gateup_w4_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
         pk.y = hb[2] | (hb[3] << 16);
         *(uint2*)(h + (size_t)(tl.r0 + 16 * c + col) * f + n0 + 4 * kq) = pk;
       }
+    }
+  }
+}
+
+// ------------------------------------------------- gate / up, one token
+// The K-split gate/up of a one-token batch (every tile holds one pair
+// unless the caller's top-k ids repeat an expert) streams its codes through
+// LDS: direct-to-LDS loads hold no registers, so each wave keeps three
+// groups of codes in flight at four waves per SIMD (the register kernel
+// above holds one), and the token's activations for the wave's K slice are
+// staged once per item instead of loaded per group.  Each step refills the
+// slot it has just read, with the group three ahead (groups past the slice
+// re-read its last group), so that the loads in flight after any step's
+// codes are exactly the two later groups' four: a step waits with
+// vmcnt(4) for its codes and reads its slot, scales and activations with
+// inline LDS reads that wait for themselves (the compiler would wait for
+// every direct-to-LDS load in flight before any LDS read it emits, which
+// leaves nothing in flight).  Work items, operands, MFMA order and the
+// K-slice reduction are those of the kernel above (the same fp32
+// results).  A tile of several pairs (repeated ids) reads its columns'
+// activations from global memory instead.
+constexpr int kT1MaxGps = 8;  // groups per K slice that the staged activations hold
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+template <int KS, bool kLg>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void gateup_w4_decode_t1(const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
+                         const int32_t* __restrict__ sorted_pair, int E, int k, int P,
+                         int d, int f, const uint8_t* __restrict__ codes,
+                         const uint16_t* __restrict__ scales, uint16_t* __restrict__ h,
+                         const float* __restrict__ logits, int32_t* __restrict__ idx_out,
+                         float* __restrict__ w_out, int32_t* __restrict__ offsets_out,
+                         int32_t* __restrict__ sorted_pair_out,
+                         int32_t* __restrict__ pair_pos_out) {
+  constexpr int RT = 4 / KS;
+  constexpr int kSlot = 2 * kTileGroupBytes;  // gate and up tiles of one group
+  // [slot][wave] codes in flight
+  __shared__ __attribute__((aligned(16))) uint8_t ring[3 * 4 * kSlot];
+  // [wave][kT1MaxGps * 128] activations of the wave's K slice; after the
+  // group loop the K-slice partial sums [wave][2][64] (f32x4) of the reduction
+  __shared__ __attribute__((aligned(16))) uint16_t xsl[4 * kT1MaxGps * 128];
+  extern __shared__ int32_t lds_i[];
+  const int G = d >> 7, RG = f / (16 * RT);
+  int32_t* off_lds = lds_i;
+  int32_t* sp_lds = lds_i + ((E + 1 + 3) & ~3);
+  float* sc_lds = (float*)(sp_lds + ((min(P, kPairsInLds) + 3) & ~3));  // [2][G][16 RT]
+  const int np = ks_route<kLg>(offsets, sorted_pair, E, k, P, logits, idx_out, w_out,
+                               offsets_out, sorted_pair_out, pair_pos_out, off_lds, sp_lds,
+                               (int32_t*)(sc_lds + 2 * G * 16 * RT));
+  f32x4* red = (f32x4*)xsl;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int rt = wave / KS, ks = wave % KS;
+  const int gps = G / KS;  // the launch requires G % KS == 0 and gps <= kT1MaxGps
+  const int gb = ks * gps;
+  const bf16x8 negoff = bf16_splat(kBf16NegOff);
+  uint8_t* const slot0 = ring + wave * kSlot;  // slot j at + j * 4 * kSlot
+  uint16_t* const xw = xsl + wave * (kT1MaxGps * 128);
+  // LDS byte addresses of the lane's reads: its 16 bytes of a slot, its
+  // activations of group gb, its scales of group 0 (gate; up G * 16 RT
+  // floats further)
+  const uint32_t a_slot = lds_addr(slot0) + 16 * lane;
+  const uint32_t a_x = lds_addr(xw) + 2 * (32 * kq);
+  const uint32_t a_sc = lds_addr(sc_lds) + 4 * (16 * rt + 4 * kq);
+  const uint32_t sc_up = 4 * (G * 16 * RT);
+
+  for (int w = blockIdx.x;; w += gridDim.x) {
+    TileInfo tl;
+    if (!find_tile(off_lds, E, 16, w / RG, tl)) break;
+    const int nb = (w % RG) * 16 * RT, n0 = nb + 16 * rt;
+    const size_t erow = (size_t)tl.e * 2 * f;
+    // the lane's column (past the tile's end: its first row, not stored)
+    const int jj = col < tl.cnt ? col : 0;
+    const int pcol = np ? sp_lds[tl.r0 + jj] : sorted_pair[tl.r0 + jj];
+    const int p0 = __shfl(pcol, 0, kWave);
+    const uint16_t* xrow = x + (size_t)(p0 / k) * d;
+    const uint16_t* xr = x + (size_t)(pcol / k) * d + 32 * kq;
+    const uint8_t* cg = codes + (erow + n0) * (size_t)(d >> 1) + 64 * col + 16 * kq;
+    const uint8_t* cu = cg + (size_t)f * (d >> 1);
+    // group g (clamped to the slice) of gate and up codes into slot j
+    auto dma = [&](int j, int g) {
+      g = min(g, gb + gps - 1);
+      uint8_t* dst = slot0 + j * 4 * kSlot;
+      __builtin_amdgcn_global_load_lds(cg + kTileGroupBytes * g,
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(cu + kTileGroupBytes * g,
+                                       (__attribute__((address_space(3))) void*)(dst + kTileGroupBytes),
+                                       16, 0, 0);
+    };
+
+    // scales as in the kernel above
+    const int nsc = 2 * 16 * RT * G;
+    const bool vsc = (G & 3) == 0 && nsc <= 4 * 256 && ((uintptr_t)scales & 7) == 0;
+    const int scc = min((int)threadIdx.x, nsc / 4 - 1);
+    const int sc_m = (4 * scc) / (16 * RT * G), sc_rem = 4 * scc - sc_m * 16 * RT * G;
+    uint2 scv = {0u, 0u};
+    if (vsc)
+      scv = *(const uint2*)(scales + (erow + nb + (size_t)sc_m * f) * G + sc_rem);
+    // Every wave is done with the previous item's scales and reduction
+    // (xsl): their LDS reads have returned.  A bare barrier: a fence would
+    // wait for the scale load.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    {
+      // the token's activations of the slice in element order (2 KiB: lane
+      // l of load i brings elements 8 (l + 64 i) .. + 7 of the slice;
+      // elements past it repeat its last 8 and are never read)
+      const int lim = (gb + gps) * 128 - 8;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int el = min(gb * 128 + 8 * (lane + 64 * i), lim);
+        __builtin_amdgcn_global_load_lds(xrow + el,
+                                         (__attribute__((address_space(3))) void*)(xw + 512 * i),
+                                         16, 0, 0);
+      }
+    }
+    dma(0, gb);
+    dma(1, gb + 1);
+    dma(2, gb + 2);
+    if (vsc) {
+      if ((int)threadIdx.x < nsc / 4) {
+        const int r = sc_rem / G, g0 = sc_rem % G;
+        float* dd = sc_lds + (sc_m * G + g0) * (16 * RT) + r;
+        dd[0] = f16_bits_to_f32(scv.x & 0xFFFFu);
+        dd[16 * RT] = f16_bits_to_f32(scv.x >> 16);
+        dd[32 * RT] = f16_bits_to_f32(scv.y & 0xFFFFu);
+        dd[48 * RT] = f16_bits_to_f32(scv.y >> 16);
+      }
+    } else {
+      stage_scales_f32(scales + (erow + nb) * G, (size_t)f, 2, 16 * RT, G, sc_lds);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the scales are written
+    __builtin_amdgcn_s_barrier();
+
+    f32x4 tg = {0, 0, 0, 0}, tu = {0, 0, 0, 0};
+    auto run = [&](auto one_c) {
+      constexpr bool kOne = decltype(one_c)::value;
+      for (int i = 0; i < gps; ++i) {
+        const int gi = gb + i, j = i % 3;
+        const uint32_t as = a_slot + j * 4 * kSlot, ac = a_sc + 4 * (gi * 16 * RT);
+        u32x4 qg, qu;
+        f32x4 sg, su;
+        bf16x8 xp[4];
+        if constexpr (kOne) {
+          const uint32_t ax = a_x + 256 * i;
+          asm volatile(
+              "s_waitcnt vmcnt(4)\n\t"
+              "ds_read_b128 %0, %8\n\t"
+              "ds_read_b128 %1, %8 offset:1024\n\t"
+              "ds_read_b128 %2, %9\n\t"
+              "ds_read_b128 %3, %10\n\t"
+              "ds_read_b128 %4, %11\n\t"
+              "ds_read_b128 %5, %11 offset:16\n\t"
+              "ds_read_b128 %6, %11 offset:32\n\t"
+              "ds_read_b128 %7, %11 offset:48\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(qg), "=&v"(qu), "=&v"(sg), "=&v"(su), "=&v"(xp[0]), "=&v"(xp[1]),
+                "=&v"(xp[2]), "=&v"(xp[3])
+              : "v"(as), "v"(ac), "v"(ac + sc_up), "v"(ax)
+              : "memory");
+        } else {
+          asm volatile(
+              "s_waitcnt vmcnt(4)\n\t"
+              "ds_read_b128 %0, %4\n\t"
+              "ds_read_b128 %1, %4 offset:1024\n\t"
+              "ds_read_b128 %2, %5\n\t"
+              "ds_read_b128 %3, %6\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(qg), "=&v"(qu), "=&v"(sg), "=&v"(su)
+              : "v"(as), "v"(ac), "v"(ac + sc_up)
+              : "memory");
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xp[q] = *(const bf16x8*)(xr + 128 * gi + 8 * q);
+        }
+        f32x4 seed = {0, 0, 0, 0};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) seed = mfma16(negoff, xp[q], seed);
+        tile_group(xp, seed, qg, sg, tg);
+        tile_group(xp, seed, qu, su, tu);
+        dma(j, gi + 3);
+      }
+    };
+    if (tl.cnt == 1)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
+    // the re-reads past the slice land before xsl and the slots are reused
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+    if (KS > 1) {
+      if (ks > 0) {
+        red[(wave * 2 + 0) * 64 + lane] = tg;
+        red[(wave * 2 + 1) * 64 + lane] = tu;
+      }
+      __syncthreads();
+      if (ks == 0) {
+        for (int s2 = 1; s2 < KS; ++s2) {
+          const f32x4 g2 = red[((wave + s2) * 2 + 0) * 64 + lane];
+          const f32x4 u2 = red[((wave + s2) * 2 + 1) * 64 + lane];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            tg[q] = tg[q] + g2[q];
+            tu[q] = tu[q] + u2[q];
+          }
+        }
+      }
+    }
+    if (ks == 0 && col < tl.cnt) {
+      uint32_t hb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hb[q] = f32_to_bf16_rne(silu_f32(tg[q]) * tu[q]);
+      uint2 pk;
+      pk.x = hb[0] | (hb[1] << 16);
+      pk.y = hb[2] | (hb[3] << 16);
+      *(uint2*)(h + (size_t)(tl.r0 + col) * f + n0 + 4 * kq) = pk;
     }
   }
 }
@@ -668,6 +906,31 @@ void launch_gu_pair(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
                      (a.logits ? sizeof(int32_t) * (128 + a.E) : 0);
   auto kern = a.logits ? gateup_w4_decode<KS, NT, gu_depth<KS, NT>(), gu_waves<KS, NT>(), true>
                        : gateup_w4_decode<KS, NT, gu_depth<KS, NT>(), gu_waves<KS, NT>(), false>;
+  launch_k(kern, dim3(grid), dim3(256), lds, s, a.ev[0], a.ev[1], a.x, a.offsets,
+           a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes, a.gu_scales, h, a.logits,
+           a.topk_idx_out, a.topk_w_out, a.offsets_out, a.sorted_pair_out, a.pair_pos_out);
+}
+
+// The one-token K-split gate/up (LDS-streamed codes) applies when every K
+// slice is full and fits the staged activations.
+static bool gu_t1_applies(const FfnArgs& a, int KS) {
+  const int G = a.d / 128;
+  return a.T == 1 && (KS == 2 || KS == 4) && G % KS == 0 && G / KS <= kT1MaxGps;
+}
+
+template <int KS>
+void launch_gu_t1(const FfnArgs& a, uint16_t* h, long long P, hipStream_t s) {
+  constexpr int RT = 4 / KS;
+  const long long mt = (P + 15) / 16 + (P < a.E ? P : a.E);
+  const size_t off_b = sizeof(int32_t) * ((a.E + 1 + 3) & ~3);
+  const long long cap = 256LL * 8;
+  const int G = a.d / 128;
+  const long long work = mt * (a.f / (16 * RT));
+  const int grid = (int)(work < cap ? work : cap);
+  const size_t lds = off_b + sizeof(int32_t) * ((std::min<long long>(P, kPairsInLds) + 3) & ~3) +
+                     sizeof(float) * 2 * G * 16 * RT +
+                     (a.logits ? sizeof(int32_t) * (128 + a.E) : 0);
+  auto kern = a.logits ? gateup_w4_decode_t1<KS, true> : gateup_w4_decode_t1<KS, false>;
   launch_k(kern, dim3(grid), dim3(256), lds, s, a.ev[0], a.ev[1], a.x, a.offsets,
            a.sorted_pair, a.E, a.k, (int)P, a.d, a.f, a.gu_codes, a.gu_scales, h, a.logits,
            a.topk_idx_out, a.topk_w_out, a.offsets_out, a.sorted_pair_out, a.pair_pos_out);
@@ -1144,9 +1407,16 @@ hipError_t launch_ffn_decode_w4(const FfnArgs& a, uint16_t* h, hipStream_t s) {
     else if (KSd == 2) launch_dn_pair<2, 2>(a, h, P, s);
     else launch_dn_pair<1, 2>(a, h, P, s);
   } else {
-    if (KSg == 4) launch_gu_pair<4, 1>(a, h, P, s);
-    else if (KSg == 2) launch_gu_pair<2, 1>(a, h, P, s);
-    else launch_gu_lds(a, h, P, s);
+    if (gu_t1_applies(a, KSg)) {
+      if (KSg == 4) launch_gu_t1<4>(a, h, P, s);
+      else launch_gu_t1<2>(a, h, P, s);
+    } else if (KSg == 4) {
+      launch_gu_pair<4, 1>(a, h, P, s);
+    } else if (KSg == 2) {
+      launch_gu_pair<2, 1>(a, h, P, s);
+    } else {
+      launch_gu_lds(a, h, P, s);
+    }
     if (KSd == 4) launch_dn_pair<4, 1>(a, h, P, s);
     else if (KSd == 2) launch_dn_pair<2, 1>(a, h, P, s);
     else launch_dn_lds(a, h, P, s);

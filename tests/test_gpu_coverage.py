@@ -1,8 +1,10 @@
 """GPU parity of the whole layer on inputs that exercise the degenerate cases
 of every FFN kernel: all-zero weight groups (scale 0) at the start, in the
 middle and over a whole expert, on each decode and prefill path; layers
-with one, two or three experts at batch sizes from 2 to 1000; and the
-interface's largest d, E, k and a wide f.  Every case
+with one, two or three experts at batch sizes from 2 to 1000; the
+interface's largest d, E, k and a wide f; and one-token layers on the
+K-split gate/up that streams its codes through LDS, including a token whose
+top-k ids repeat an expert.  Every case
 goes through the C ABI and is compared with the CPU oracle as in the other
 layer tests (integers bit-exact, floating point within rel-L2 2e-3 and
 max-abs 3e-2 rms)."""
@@ -12,7 +14,8 @@ import torch
 
 import synth
 import quantized_mixture_experts_fp32_amd as moe
-from layer_data import DEV, DevLayer, HostLayer, custom_cfg
+import oracle
+from layer_data import DEV, DevLayer, HostLayer, assert_close, custom_cfg
 from test_gpu_parity import check_layer, note
 
 pytestmark = pytest.mark.gpu
@@ -47,6 +50,8 @@ ZERO_CASES = [
     ("bitplane prefill", "bp8", 384, 16, 4, 384, 300, moe.MOE_PATH_PREFILL, "pair"),
     ("bitplane prefill, rank rule", "bp8", 384, 16, 8, 384, 300, moe.MOE_PATH_PREFILL,
      "rank"),
+    ("one-token K-split decode, LDS-streamed codes", "w4", 1024, 16, 6, 384, 1,
+     moe.MOE_PATH_AUTO, None),
 ]
 
 
@@ -175,3 +180,41 @@ def test_bitplane_reads_stay_in_prefix(path):
     torch.cuda.synchronize()
     assert torch.equal(lay.y_pairs, y0), "bytes past the prefix pairs changed y_pairs"
     assert torch.equal(o1, o0)
+
+
+# (d, E, k, f): one-token layers on the K-split gate/up that streams its
+# codes through LDS, with K slices of 1, 3, 5, 7 and 8 groups (three slots
+# in flight: slices shorter than, equal to and past one round of slots),
+# four and two K slices per item, and the routing taken inside the kernel
+# (E <= 64) or staged from the routing launch (E > 64); E > 2 k keeps the
+# layer entry off the expert-major kernels
+ONE_TOKEN = [(512, 8, 2, 256), (1536, 32, 8, 256), (2560, 32, 8, 512), (3584, 32, 8, 512),
+             (2048, 32, 8, 4096), (1024, 128, 8, 256)]
+
+
+@pytest.mark.parametrize("d,E,k,f", ONE_TOKEN)
+def test_layer_one_token_ksplit(d, E, k, f):
+    note(f"one-token K-split decode d={d} E={E} k={k} f={f}")
+    cfg = custom_cfg(90 + ONE_TOKEN.index((d, E, k, f)), d=d, E=E, k=k, f=f,
+                     bias_sigma=0.5)
+    check_layer(DevLayer(cfg, 1), HostLayer(cfg, 1), moe.MOE_PATH_AUTO)
+
+
+def test_one_token_repeated_expert_ids():
+    """One token whose top-k ids (given by the caller) name an expert three
+    times: that expert's tile holds three pairs, which the one-token K-split
+    gate/up computes from activations read from global memory instead of its
+    staged row; every pair row against the oracle."""
+    cfg = custom_cfg(98, d=1024, E=16, k=4, f=384)
+    note("one token, repeated expert ids [3, 3, 7, 3]")
+    dl, hl = DevLayer(cfg, 1), HostLayer(cfg, 1)
+    ids = np.array([[3, 3, 7, 3]], np.int32)
+    off, sp, _ = moe.moe_permute(torch.from_numpy(ids).to(DEV), cfg.E)
+    y = moe.moe_expert_ffn_wq(dl.x, off, sp, cfg.k, cfg.f, dl.guc, dl.gus, dl.dnc, dl.dns,
+                              path=moe.MOE_PATH_DECODE)
+    torch.cuda.synchronize()
+    roff, rsp, _ = oracle.permute(ids, cfg.E)
+    assert np.array_equal(off.cpu().numpy(), roff)
+    assert np.array_equal(sp.cpu().numpy(), rsp)
+    ref = oracle.expert_outputs(hl.x, ids, roff, rsp, hl.expert, "w4", cfg.f)
+    assert_close(y.cpu().numpy(), ref, "y_pairs")
