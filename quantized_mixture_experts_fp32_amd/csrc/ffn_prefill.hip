@@ -408,6 +408,27 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
     run(TokBlocks<1>{});
 }
 
+// Block-wide exclusive scan of v over the 1024 threads (sc: 1024 ints of
+// LDS); returns the sum over threads below, and the total in *total.
+__device__ __forceinline__ int pf_scan(int v, int* sc, int* total) {
+  const int e = threadIdx.x;
+  sc[e] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int u = (e >= off) ? sc[e - off] : 0;
+    __syncthreads();
+    sc[e] += u;
+    __syncthreads();
+  }
+  const int r = sc[e] - v;
+  *total = sc[1023];
+  __syncthreads();
+  return r;
+}
+
+// Tiles of up to 128 slots of one expert, heaviest first: every expert's
+// full tiles (experts ascending), then the ragged last tiles by their count
+// of 32-token blocks, 4 down to 1, so that the lighter blocks fill the tail.
 __global__ __launch_bounds__(1024) void pf_prep(const int32_t* __restrict__ offsets, int E,
                                                 PTile* __restrict__ tiles,
                                                 int* __restrict__ num_tiles) {
@@ -418,19 +439,18 @@ __global__ __launch_bounds__(1024) void pf_prep(const int32_t* __restrict__ offs
     lo = offsets[e];
     n = offsets[e + 1] - lo;
   }
-  const int nt = (n + kBT - 1) / kBT;
-  sc[e] = nt;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = (e >= off) ? sc[e - off] : 0;
-    __syncthreads();
-    sc[e] += v;
-    __syncthreads();
+  const int nf = n / kBT, rem = n - nf * kBT, nb = (rem + 31) >> 5;
+  int total;
+  const int basef = pf_scan(nf, sc, &total);
+  for (int c = 0; c < nf; ++c) tiles[basef + c] = PTile{e, lo + c * kBT, kBT, 8};
+  int base = total;
+  for (int v = 4; v >= 1; --v) {
+    int tv;
+    const int pos = pf_scan(nb == v ? 1 : 0, sc, &tv);
+    if (nb == v) tiles[base + pos] = PTile{e, lo + nf * kBT, rem, 8};
+    base += tv;
   }
-  const int base = sc[e] - nt;
-  for (int c = 0; c < nt; ++c)
-    tiles[base + c] = PTile{e, lo + c * kBT, min(kBT, n - c * kBT), 8};
-  if (e == 1023) *num_tiles = sc[1023];
+  if (e == 0) *num_tiles = base;
 }
 
 // ============================================ bitplane experts, prefill
