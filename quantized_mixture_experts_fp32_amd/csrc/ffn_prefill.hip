@@ -510,8 +510,9 @@ __device__ __forceinline__ bf16x8 w4_top_bp(uint32_t w, uint32_t D) {
 // block per expert.  bp_pf_count: cnt[8 e + w] = pairs of expert e with
 // width w + 1 (ballots over the expert's slots).  bp_pf_scatter: the
 // expert's slots listed by width, each width in slot order (stable), and
-// the 128-pair tiles of every (expert, width), numbered in (expert, width)
-// order; the block of the last expert stores the tile count.
+// the 128-pair tiles of every (expert, width), listed in (expert, width)
+// order for the down pass and widest first for the gate/up pass; the block
+// of the last expert stores the tile count.
 __global__ __launch_bounds__(256) void bp_pf_count(const int32_t* __restrict__ offsets,
                                                    const int32_t* __restrict__ sorted_pair,
                                                    int k, int mode,
@@ -547,29 +548,57 @@ __global__ __launch_bounds__(256) void bp_pf_scatter(const int32_t* __restrict__
                                                      const int32_t* __restrict__ cnt,
                                                      int32_t* __restrict__ bslot,
                                                      PTile* __restrict__ tiles,
+                                                     PTile* __restrict__ tiles_wide,
                                                      int* __restrict__ num_tiles) {
-  __shared__ int32_t red[4];
-  __shared__ int32_t sbase[8], tbase[8];
+  __shared__ int32_t redb[4][8], redt[4][8];
+  __shared__ int32_t sbase[8];
   __shared__ int32_t chunk[4][8];
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // tiles of the experts below e
-  int t = 0;
-  for (int j = tid; j < 8 * e; j += 256) t += (cnt[j] + kBT - 1) / kBT;
+  // Two lists of the same tiles.  tiles: expert-major (experts ascending,
+  // widths ascending within an expert), so that an expert's tiles of
+  // different widths, which read the same leading planes, run close
+  // together.  tiles_wide: widest first (width 8 down to 1, experts
+  // ascending within a width), so that the two-pass tiles of widths above
+  // 4 start first and one-pass tiles fill the tail.  Thread tid counts the
+  // tiles of width tid % 8 + 1 of the experts below e and of all experts.
+  int tb_below = 0, tb_all = 0;
+  for (int j = tid; j < 8 * E; j += 256) {
+    const int tl = (cnt[j] + kBT - 1) / kBT;
+    tb_all += tl;
+    if ((j >> 3) < e) tb_below += tl;
+  }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, kWave);
-  if (lane == 0) red[wave] = t;
+  for (int o = 8; o < 64; o <<= 1) {
+    tb_below += __shfl_xor(tb_below, o, kWave);
+    tb_all += __shfl_xor(tb_all, o, kWave);
+  }
+  if (lane < 8) {
+    redb[wave][lane] = tb_below;
+    redt[wave][lane] = tb_all;
+  }
   __syncthreads();
   if (tid < 8) {
-    int sb = offsets[e], tb = red[0] + red[1] + red[2] + red[3];
-    for (int w = 0; w < tid; ++w) {
-      sb += cnt[8 * e + w];
-      tb += (cnt[8 * e + w] + kBT - 1) / kBT;
+    // expert-major: tiles of all widths of the experts below e, then of
+    // the narrower widths of e; widest first: tiles of the wider widths,
+    // then of this width of the experts below e
+    int sb = offsets[e], tb = 0, tw = 0;
+    for (int w = 0; w < 8; ++w) {
+      const int below = redb[0][w] + redb[1][w] + redb[2][w] + redb[3][w];
+      tb += below;
+      if (w < tid) {
+        sb += cnt[8 * e + w];
+        tb += (cnt[8 * e + w] + kBT - 1) / kBT;
+      }
+      if (w > tid) tw += redt[0][w] + redt[1][w] + redt[2][w] + redt[3][w];
+      if (w == tid) tw += below;
     }
     sbase[tid] = sb;
-    tbase[tid] = tb;
     const int nw = cnt[8 * e + tid];
-    for (int c2 = 0; c2 * kBT < nw; ++c2)
-      tiles[tb + c2] = PTile{e, sb + c2 * kBT, min(kBT, nw - c2 * kBT), tid + 1};
+    for (int c2 = 0; c2 * kBT < nw; ++c2) {
+      const PTile t = PTile{e, sb + c2 * kBT, min(kBT, nw - c2 * kBT), tid + 1};
+      tiles[tb + c2] = t;
+      tiles_wide[tw + c2] = t;
+    }
     if (e == E - 1 && tid == 7) *num_tiles = tb + (nw + kBT - 1) / kBT;
   }
   __syncthreads();
@@ -990,7 +1019,7 @@ size_t ffn_prefill_ws_bytes(int T, int k, int E, int d, int f) {
   auto a256 = [](size_t v) { return (v + 255) & ~(size_t)255; };
   return 256 + a256(tiles * sizeof(PTile)) + a256((size_t)T * (d / 128) * 8) +
          a256((size_t)P * (f / 128) * 8) + a256((size_t)P * sizeof(int32_t)) +
-         a256((size_t)E * 8 * sizeof(int32_t));
+         a256((size_t)E * 8 * sizeof(int32_t)) + a256(tiles * sizeof(PTile));
 }
 
 hipError_t launch_ffn_prefill_w4(const FfnArgs& a, uint16_t* h, void* ws, hipStream_t s) {
@@ -1036,11 +1065,13 @@ hipError_t launch_ffn_prefill_bp(const FfnArgs& a, uint16_t* h, void* ws, hipStr
   uint2* hsum = (uint2*)((char*)xsum + a256((size_t)a.T * (a.d / 128) * 8));
   int32_t* bslot = (int32_t*)((char*)hsum + a256((size_t)P * (a.f / 128) * 8));
   int32_t* cnt = (int32_t*)((char*)bslot + a256((size_t)P * sizeof(int32_t)));
+  PTile* tiles_wide = (PTile*)((char*)cnt + a256((size_t)a.E * 8 * sizeof(int32_t)));
 
   hipLaunchKernelGGL(bp_pf_count, dim3(a.E), dim3(256), 0, s, a.offsets, a.sorted_pair, a.k,
                      a.bits_mode, a.bits, cnt);
   hipLaunchKernelGGL(bp_pf_scatter, dim3(a.E), dim3(256), 0, s, a.offsets, a.sorted_pair, a.E,
-                     a.k, a.bits_mode, a.bits, (const int32_t*)cnt, bslot, tiles, num_tiles);
+                     a.k, a.bits_mode, a.bits, (const int32_t*)cnt, bslot, tiles, tiles_wide,
+                     num_tiles);
   {
     const long long n = (long long)a.T * (a.d / 128);
     hipLaunchKernelGGL(group_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.x,
@@ -1049,7 +1080,7 @@ hipError_t launch_ffn_prefill_bp(const FfnArgs& a, uint16_t* h, void* ws, hipStr
   const unsigned mt8 = (unsigned)((mt + 7) & ~(size_t)7);
   launch_k(pf_bp_kernel<true>, dim3(mt8 * (a.f / 128)), dim3(kThreads), 0, s, a.ev[0], a.ev[1],
            a.x, a.sorted_pair, (const int32_t*)bslot, a.k, a.d, a.f, a.gu_codes, a.gu_scales,
-           (const uint2*)xsum, (const PTile*)tiles, (const int*)num_tiles, a.f / 128, h,
+           (const uint2*)xsum, (const PTile*)tiles_wide, (const int*)num_tiles, a.f / 128, h,
            (float*)nullptr, hsum);
   const int dn_fb = (a.d + 255) / 256;
   launch_k(pf_bp_kernel<false>, dim3(mt8 * dn_fb), dim3(kThreads), 0, s, a.ev[2], a.ev[3],
