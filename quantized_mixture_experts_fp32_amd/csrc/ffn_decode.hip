@@ -1456,19 +1456,28 @@ hipError_t launch_ffn_decode_em(const FfnArgs& a, const int32_t* topk_idx, int32
   int32_t* em_list = em_cnt + em_a256(sizeof(int32_t) * a.E) / sizeof(int32_t);
   {
     // 8-wave blocks of 128 features (f % 128 == 0 always holds here; 16-wave
-    // blocks of 256 features measured slower: 29.4 against 25.2 us)
+    // blocks of 256 features measured slower: 29.4 against 25.2 us); at most
+    // four tokens, whose few active experts leave CUs idle, take 4-wave
+    // blocks of 64 features (OLMoE-shaped layer, same-box A/B: T = 4 step
+    // 39.1 -> 38.0 us; T = 8 and 16 were 2-4 % slower that way)
     const int G = a.d / 128;
     const size_t lds = sizeof(float) * 4 * G * 64 + sizeof(uint16_t) * 2 * 16 * kXRow;
     const int sc = scale_chunks(2, G, a.gu_scales);
-    auto pick = [&](auto lg) {
+    const bool w4 = a.T <= 4;
+    auto pick = [&](auto lg, auto kw) {
       constexpr bool L = decltype(lg)::value;
-      return sc == 1   ? gateup_w4_em<kGuDQ, kGuWaves, 1, 8, L>
-             : sc == 2 ? gateup_w4_em<kGuDQ, kGuWaves, 2, 8, L>
-             : sc == 4 ? gateup_w4_em<kGuDQ, kGuWaves, 4, 8, L>
-                       : gateup_w4_em<kGuDQ, kGuWaves, 0, 8, L>;
+      constexpr int W = decltype(kw)::value;
+      return sc == 1   ? gateup_w4_em<kGuDQ, kGuWaves, 1, W, L>
+             : sc == 2 ? gateup_w4_em<kGuDQ, kGuWaves, 2, W, L>
+             : sc == 4 ? gateup_w4_em<kGuDQ, kGuWaves, 4, W, L>
+                       : gateup_w4_em<kGuDQ, kGuWaves, 0, W, L>;
     };
-    auto kern = logits ? pick(std::true_type{}) : pick(std::false_type{});
-    launch_k(kern, dim3(a.E * (a.f / 128)), dim3(512), lds, s, a.ev[0], a.ev[1], a.x, topk_idx,
+    using W4 = std::integral_constant<int, 4>;
+    using W8 = std::integral_constant<int, 8>;
+    auto kern = logits ? (w4 ? pick(std::true_type{}, W4{}) : pick(std::true_type{}, W8{}))
+                       : (w4 ? pick(std::false_type{}, W4{}) : pick(std::false_type{}, W8{}));
+    launch_k(kern, dim3(a.E * (a.f / (w4 ? 64 : 128))), dim3(w4 ? 256 : 512), lds, s, a.ev[0],
+             a.ev[1], a.x, topk_idx,
              a.T, a.k, a.E, a.d, a.f, a.gu_codes, a.gu_scales, hE, offsets, sorted_pair,
              pair_pos, logits, em_cnt, em_list, idx_out, w_out);
   }
