@@ -373,8 +373,9 @@ void pf_w4_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
           h_out[slot * N + brow[0]] = hb;
           hst[tok * 128 + 8 * ((lf >> 3) ^ (tok & 15)) + (lf & 7)] = hb;
         } else {
-          if (bstore[0]) y_out[slot * N + brow[0]] = acc[t][0][i];
-          if (bstore[1]) y_out[slot * N + brow[1]] = acc[t][1][i];
+          // y rows are read once, by the combine: streamed past the caches
+          if (bstore[0]) __builtin_nontemporal_store(acc[t][0][i], y_out + slot * N + brow[0]);
+          if (bstore[1]) __builtin_nontemporal_store(acc[t][1][i], y_out + slot * N + brow[1]);
         }
       }
     if (kGateUp) {
@@ -981,8 +982,9 @@ void pf_bp_kernel(const uint16_t* __restrict__ act,       // x [T][K] or h [P][K
         h_out[slot * N + brow[0]] = hb;
         hst[tok * 128 + 8 * ((lf >> 3) ^ (tok & 15)) + (lf & 7)] = hb;
       } else {
-        if (bstore[0]) y_out[slot * N + brow[0]] = acc[t][0][i];
-        if (bstore[1]) y_out[slot * N + brow[1]] = acc[t][1][i];
+        // y rows are read once, by the combine: streamed past the caches
+        if (bstore[0]) __builtin_nontemporal_store(acc[t][0][i], y_out + slot * N + brow[0]);
+        if (bstore[1]) __builtin_nontemporal_store(acc[t][1][i], y_out + slot * N + brow[1]);
       }
     }
   if (kGateUp) {
