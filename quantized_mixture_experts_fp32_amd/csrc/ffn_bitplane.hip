@@ -361,7 +361,9 @@ __device__ __forceinline__ void bp_item(const uint16_t* __restrict__ xsrc,
     for (int c = 0; c < NB / 2; ++c)
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const uint2 a = *(const uint2*)(pt[t] + (size_t)g * kBlockBytes + kBpPair * c);
+        // plane words are read once per step: nontemporal, as the int4 codes
+        const u32x2 a =
+            __builtin_nontemporal_load((const u32x2*)(pt[t] + (size_t)g * kBlockBytes + kBpPair * c));
         wv[i][t][2 * c] = a.x;
         wv[i][t][2 * c + 1] = a.y;
       }
@@ -369,7 +371,7 @@ __device__ __forceinline__ void bp_item(const uint16_t* __restrict__ xsrc,
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         wv[i][t][NB - 1] =
-            *(const uint32_t*)(pt[t] + (size_t)g * kBlockBytes + kBpPair * (NB / 2));
+            __builtin_nontemporal_load((const uint32_t*)(pt[t] + (size_t)g * kBlockBytes + kBpPair * (NB / 2)));
   };
   ScaleStage<2, kSC ? kSC : 1> sst;
   if (kSC) sst.fetch(sc_src, mat_stride, G);

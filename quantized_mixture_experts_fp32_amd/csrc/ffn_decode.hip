@@ -45,6 +45,12 @@ using namespace dec;
 
 constexpr int kTileGroupBytes = 16 * 64;  // one 16-row tile x one 128-group
 
+// Code loads carry the nontemporal hint: a decode step reads each activated
+// expert's codes once, and streaming them past the caches keeps the
+// activations, h, the scales and the routing resident in L2 and the
+// Infinity Cache.  (The one-token kernel's direct-to-LDS code loads keep
+// the default policy, which measured faster there.)
+
 // One code word (elements 8j..8j+7, even ones in nibbles 0-3, odd ones in
 // nibbles 4-7) -> bf16 (136 + q) of the 8 elements in order.
 // bitop3 LUT 0x6A: out = B ? (x ^ D) : D.  B selects bits 0-3 of each half,
@@ -196,8 +202,8 @@ void gateup_w4_decode(const uint16_t* __restrict__ x, const int32_t* __restrict_
 
     u32x4 qg[kDepth], qu[kDepth], xv[kDepth][NT][4];
     auto load = [&](int g, u32x4& a, u32x4& b, u32x4 (&v)[NT][4]) {
-      a = *(const u32x4*)(cg + kTileGroupBytes * g);
-      b = *(const u32x4*)(cu + kTileGroupBytes * g);
+      a = __builtin_nontemporal_load((const u32x4*)(cg + kTileGroupBytes * g));
+      b = __builtin_nontemporal_load((const u32x4*)(cu + kTileGroupBytes * g));
 #pragma unroll
       for (int c = 0; c < NT; ++c) {
         if (c >= nch) break;
@@ -563,7 +569,7 @@ void down_w4_decode(const uint16_t* __restrict__ h, const int32_t* __restrict__ 
 
     u32x4 q[kDepth], hv[kDepth][NT][4];
     auto load = [&](int g, u32x4& a, u32x4 (&v)[NT][4]) {
-      a = *(const u32x4*)(cd + kTileGroupBytes * g);
+      a = __builtin_nontemporal_load((const u32x4*)(cd + kTileGroupBytes * g));
 #pragma unroll
       for (int c = 0; c < NT; ++c) {
         if (c >= nch) break;
@@ -691,8 +697,8 @@ void gateup_w4_decode_lds(const uint16_t* __restrict__ x, const int32_t* __restr
       xv[i] = *(const u32x4*)(xsrc + 128 * g);
 #pragma unroll
       for (int r = 0; r < kRT; ++r) {
-        qg[i][r] = *(const u32x4*)(cg + r * rt_stride + kTileGroupBytes * g);
-        qu[i][r] = *(const u32x4*)(cu + r * rt_stride + kTileGroupBytes * g);
+        qg[i][r] = __builtin_nontemporal_load((const u32x4*)(cg + r * rt_stride + kTileGroupBytes * g));
+        qu[i][r] = __builtin_nontemporal_load((const u32x4*)(cu + r * rt_stride + kTileGroupBytes * g));
       }
     };
     // the previous item's last barrier precedes these LDS writes; the first
@@ -817,7 +823,7 @@ void down_w4_decode_lds(const uint16_t* __restrict__ h, const int32_t* __restric
       hv[i] = *(const u32x4*)(hsrc + 128 * g);
 #pragma unroll
       for (int r = 0; r < kRT; ++r)
-        q[i][r] = *(const u32x4*)(cd + r * rt_stride + kTileGroupBytes * g);
+        q[i][r] = __builtin_nontemporal_load((const u32x4*)(cd + r * rt_stride + kTileGroupBytes * g));
     };
     // scale rows mb .. mb + 64 kRT - 1 are consecutive: kRT "matrices" of
     // 64 rows, 64 rows apart
@@ -1105,8 +1111,8 @@ void gateup_w4_em(const uint16_t* __restrict__ x, const int32_t* __restrict__ to
   u32x4 qg[kDQ], qu[kDQ], xv[kDQ];
   auto load = [&](int g, int i) {
     xv[i] = *(const u32x4*)(xsrc + 128 * g);
-    qg[i] = *(const u32x4*)(cg + kTileGroupBytes * g);
-    qu[i] = *(const u32x4*)(cu + kTileGroupBytes * g);
+    qg[i] = __builtin_nontemporal_load((const u32x4*)(cg + kTileGroupBytes * g));
+    qu[i] = __builtin_nontemporal_load((const u32x4*)(cu + kTileGroupBytes * g));
   };
   // scales: 4 waves take gate and up as two 64-row matrices; 8 or 16 waves
   // take gate then up as runs of kMat 64-row chunks
@@ -1288,7 +1294,7 @@ void down_w4_em(const uint16_t* __restrict__ hE, const int32_t* __restrict__ off
   auto load = [&](int g, int i) {
     hv[i] = *(const u32x4*)(hsrc + 128 * g);
 #pragma unroll
-    for (int r = 0; r < kRT; ++r) q[i][r] = *(const u32x4*)(cd[r] + kTileGroupBytes * g);
+    for (int r = 0; r < kRT; ++r) q[i][r] = __builtin_nontemporal_load((const u32x4*)(cd[r] + kTileGroupBytes * g));
   };
   ScaleStage<kRT, kSC ? kSC : 1> sst;
   if (kSC) sst.fetch(scales + (erow + mb) * G, 64, G);
